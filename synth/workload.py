@@ -1,0 +1,170 @@
+"""Workload shapes and seeded random inputs.
+
+Shapes follow the Qwen3-Next-80B-A3B and Qwen3.6-35B-A3B families as the pages
+describe them: each layer routes a token to 10 of 512 experts (80B) or 8 of
+256 (35B) (cheshm.ai news article on Swiftlet, paragraph on how it works), and
+the 80B model has 48 layers (Swiftlet field test at alphalab.site, section
+explaining MoE expert streaming). Hidden size 2048, expert intermediate 512,
+group size 64 and the value distributions are the workload recipe of this
+project; the pages do not print them.
+
+Every tensor has its own numpy SeedSequence built from
+``[seed, layer, expert_or_slot, tensor_id]`` so any single expert can be
+regenerated on its own (the oracle recomputes only what it samples).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional, Tuple
+
+import numpy as np
+
+# tensor ids inside a SeedSequence key
+_GATE, _UP, _DOWN = 0, 1, 2
+_ROUTER, _SHARED_GATE, _BIAS, _PERM = 3, 4, 5, 6
+_TOKENS = 7
+_LAYER_SLOT = 1 << 20   # "expert" field used for per-layer, non-expert tensors
+_TOKEN_SLOT = 1 << 21   # "layer" field used for token streams
+
+WEIGHT_STD = 0.02       # routed/shared expert, router and shared-gate weights
+ZIPF_S = 1.1            # popularity exponent of the pooled-stack workload
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    hidden: int
+    n_experts: int
+    top_k: int
+    inter: int
+    shared_inter: int
+    bits: int
+    group: int
+    n_layers: int
+    n_tokens: int
+    seed: int = 0
+    bias: str = "none"            # "none" | "normal" | "zipf"
+    zipf_lambda: float = 0.0
+    pool_budget: Optional[int] = None   # bytes of HBM expert pool, None = all resident
+    norm_topk: int = 1
+    description: str = ""
+
+    def replace(self, **kw) -> "Config":
+        return dataclasses.replace(self, **kw)
+
+
+GiB = 1 << 30
+
+CONFIGS: Dict[str, Config] = {
+    "tiny": Config(
+        "tiny", hidden=256, n_experts=16, top_k=2, inter=128, shared_inter=128, bits=4, group=64,
+        n_layers=1, n_tokens=8, seed=0,
+        description="tiny MoE layer: H 256, 16 experts, top-2, I 128, int4 g64, 8 tokens"),
+    "decode80b": Config(
+        "decode80b", hidden=2048, n_experts=512, top_k=10, inter=512, shared_inter=512, bits=4, group=64,
+        n_layers=1, n_tokens=1024, seed=0,
+        description="80B-shaped single MoE layer, batch-1 decode, 1024 sequential tokens, all experts in HBM"),
+    "stack35b_int8": Config(
+        "stack35b_int8", hidden=2048, n_experts=256, top_k=8, inter=512, shared_inter=512, bits=8, group=64,
+        n_layers=40, n_tokens=512, seed=0,
+        description="35B-shaped 40-layer MoE stack, int8, batch-1 decode, 512 tokens, all experts in HBM"),
+    "stack35b_int4": Config(
+        "stack35b_int4", hidden=2048, n_experts=256, top_k=8, inter=512, shared_inter=512, bits=4, group=64,
+        n_layers=40, n_tokens=512, seed=0,
+        description="35B-shaped 40-layer MoE stack, int4, batch-1 decode, 512 tokens, all experts in HBM"),
+    "prefill80b": Config(
+        "prefill80b", hidden=2048, n_experts=512, top_k=10, inter=512, shared_inter=512, bits=4, group=64,
+        n_layers=1, n_tokens=2048, seed=0, bias="normal",
+        description="80B-shaped MoE layer, 2048-token batched prefill, router bias ~N(0,1) per expert"),
+    "pool80b": Config(
+        "pool80b", hidden=2048, n_experts=512, top_k=10, inter=512, shared_inter=512, bits=4, group=64,
+        n_layers=48, n_tokens=1024, seed=0, bias="zipf", zipf_lambda=0.6, pool_budget=2 * GiB,
+        description="80B-shaped 48-layer stack decode, experts in pinned host memory, 2 GiB HBM pool"),
+    "resident80b": Config(
+        "resident80b", hidden=2048, n_experts=512, top_k=10, inter=512, shared_inter=512, bits=4, group=64,
+        n_layers=48, n_tokens=1024, seed=0, bias="zipf", zipf_lambda=0.6, pool_budget=None,
+        description="80B-shaped 48-layer stack decode with every expert resident in HBM"),
+}
+
+
+def get_config(name: str, **overrides) -> Config:
+    cfg = CONFIGS[name]
+    return cfg.replace(**overrides) if overrides else cfg
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(k) for k in key])))
+
+
+def _normal(shape, *key: int, std: float = WEIGHT_STD) -> np.ndarray:
+    n = int(np.prod(shape))
+    a = _rng(*key).standard_normal(n, dtype=np.float32)
+    if std != 1.0:
+        a *= np.float32(std)
+    return a.reshape(shape)
+
+
+def expert_weights(seed: int, layer: int, expert: int, hidden: int, inter: int
+                   ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """fp32 gate [inter][hidden], up [inter][hidden], down [hidden][inter], each ~N(0, 0.02)."""
+    wg = _normal((inter, hidden), seed, layer, expert, _GATE)
+    wu = _normal((inter, hidden), seed, layer, expert, _UP)
+    wd = _normal((hidden, inter), seed, layer, expert, _DOWN)
+    return wg, wu, wd
+
+
+def shared_expert_weights(seed: int, layer: int, n_experts: int, hidden: int, shared_inter: int):
+    """The shared expert is drawn as expert index ``n_experts`` of its layer."""
+    return expert_weights(seed, layer, n_experts, hidden, shared_inter)
+
+
+def router_weight(seed: int, layer: int, hidden: int, n_experts: int) -> np.ndarray:
+    """fp32 W_r [hidden][n_experts] ~N(0, 0.02)."""
+    return _normal((hidden, n_experts), seed, layer, _LAYER_SLOT, _ROUTER)
+
+
+def shared_gate(seed: int, layer: int, hidden: int) -> np.ndarray:
+    """fp32 g_s [hidden] ~N(0, 0.02): the shared expert's sigmoid gate vector."""
+    return _normal((hidden,), seed, layer, _LAYER_SLOT, _SHARED_GATE)
+
+
+def router_bias(cfg: Config, layer: int) -> Optional[np.ndarray]:
+    """Per-expert fp32 bias added to the router logits, or None.
+
+    "normal": rho[e] ~ N(0, 1) (skews the prefill bucket sizes).
+    "zipf":   rho[e] = -lambda * s * ln(rank(e)), rank a seeded permutation of 1..E,
+              so exp(rho) follows a Zipf(s) popularity law when lambda = 1.
+    """
+    E = cfg.n_experts
+    if cfg.bias == "none":
+        return None
+    if cfg.bias == "normal":
+        return _normal((E,), cfg.seed, layer, _LAYER_SLOT, _BIAS, std=1.0)
+    if cfg.bias == "zipf":
+        rank = _rng(cfg.seed, layer, _LAYER_SLOT, _PERM).permutation(E).astype(np.float64) + 1.0
+        return (-cfg.zipf_lambda * ZIPF_S * np.log(rank)).astype(np.float32)
+    raise ValueError(f"unknown bias kind {cfg.bias!r}")
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even); returns the uint16 bit patterns."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def tokens(seed: int, n_tokens: int, hidden: int, stream: int = 0) -> np.ndarray:
+    """bf16 activations ~N(0,1) as uint16 bit patterns, shape [n_tokens][hidden].
+
+    Row t depends only on (seed, stream, t), so a prefix of a longer stream is
+    the same tokens.
+    """
+    out = np.empty((n_tokens, hidden), dtype=np.uint16)
+    for t in range(n_tokens):
+        row = _rng(seed, _TOKEN_SLOT, stream, _TOKENS, t).standard_normal(hidden, dtype=np.float32)
+        out[t] = f32_to_bf16_bits(row)
+    return out
