@@ -161,15 +161,23 @@ class LayerResult(NamedTuple):
     gamma: np.ndarray    # float64 [T], sigmoid(x . g_s)
 
 
-def layer_forward(x: np.ndarray, lw: LayerWeights, k: int, norm_topk: int = 1) -> LayerResult:
+def layer_forward(x: np.ndarray, lw: LayerWeights, k: int, norm_topk: int = 1,
+                  sel: Optional[np.ndarray] = None) -> LayerResult:
     """out[t] = sum_{j<k} w[t,j] * y_{idx[t,j]}(x_t) + sigmoid(x_t . g_s) * y_shared(x_t).
 
     Tokens are grouped by expert so each used expert is applied once to all of
-    its tokens; every output row is still the plain definition.
+    its tokens; every output row is still the plain definition. ``sel`` [T][k]
+    replaces the top-k selection (used only to re-evaluate a token whose
+    selection legitimately differs at a near-tie); the weights are still the
+    definition's, computed from the exact logits over that selection.
     """
     x = np.atleast_2d(np.asarray(x, dtype=np.float64))
     T, H = x.shape
     rt = route(x, lw.w_r, lw.rho, k, norm_topk)
+    if sel is not None:
+        sel = np.asarray(sel, dtype=np.int32).reshape(T, k)
+        w = np.stack([route_weights(rt.logits[t], sel[t], norm_topk) for t in range(T)])
+        rt = Route(sel.copy(), w, rt.logits)
     gamma = sigmoid(x @ np.asarray(lw.g_s, dtype=np.float32).astype(np.float64))
     contrib = np.zeros((T, k, H))
     for e in np.unique(rt.idx):
@@ -186,14 +194,19 @@ class StackResult(NamedTuple):
     routes: List[Route]          # per layer
 
 
-def stack_forward(x0: np.ndarray, layers: List[LayerWeights], k: int, norm_topk: int = 1) -> StackResult:
-    """Residual stack without attention or norms: r0 = x0; x_l = bf16(r_l); r_{l+1} = r_l + out_l(x_l)."""
+def stack_forward(x0: np.ndarray, layers: List[LayerWeights], k: int, norm_topk: int = 1,
+                  sels: Optional[List[np.ndarray]] = None) -> StackResult:
+    """Residual stack without attention or norms: r0 = x0; x_l = bf16(r_l); r_{l+1} = r_l + out_l(x_l).
+
+    ``sels`` (per layer, [T][k]) replaces the top-k selections, as in layer_forward.
+    The returned routes keep the oracle's own logits for every layer.
+    """
     r = np.atleast_2d(np.asarray(x0, dtype=np.float64)).copy()
     r0 = r.copy()
     routes = []
-    for lw in layers:
+    for l, lw in enumerate(layers):
         xl = quant.bf16_rne_from_f64(r)
-        res = layer_forward(xl, lw, k, norm_topk)
+        res = layer_forward(xl, lw, k, norm_topk, None if sels is None else sels[l])
         r = r + res.out
         routes.append(res.route)
     return StackResult(r, r - r0, routes)

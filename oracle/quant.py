@@ -131,7 +131,7 @@ def quantize(w: np.ndarray, bits: int) -> QMatrix:
 
     Per row n and group j (columns 64j..64j+63), all arithmetic in IEEE fp32:
       lo, hi = min, max of the group
-      s = fp16(fl32(fl32(hi - lo) / (2^bits - 1)))      c = fp16(lo)
+      s = fp16(fl32(fl32(hi - lo) / (2^bits - 1)))      c = fp16(lo)   (a -0 minimum becomes +0)
       q_i = clamp(rne(fl32(fl32(w_i - c) / s)), 0, 2^bits - 1), and q_i = 0 when s == 0.
     Non-finite weights, or a scale or bias that overflows fp16, raise ValueError.
     """
@@ -144,7 +144,7 @@ def quantize(w: np.ndarray, bits: int) -> QMatrix:
         raise ValueError("non-finite weight")
     N, K = w.shape
     g = w.reshape(N, K // GROUP, GROUP)
-    lo = g.min(axis=2)
+    lo = g.min(axis=2) + np.float32(0)     # a -0 minimum is stored as +0
     hi = g.max(axis=2)
     qmax = np.float32((1 << bits) - 1)
     with np.errstate(over="ignore"):

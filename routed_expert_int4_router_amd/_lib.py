@@ -1,0 +1,305 @@
+"""ctypes binding of libmoe.so (the C ABI declared in include/moe.h).
+
+Argument marshalling only: every step of the MoE path runs in the library's
+HIP kernels. torch is used for device memory and streams; numpy for host
+buffers. The library must have been built (routed_expert_int4_router_amd.build);
+loading fails loudly otherwise, and there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe.so")
+
+MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ESTATE = 0, -1, -2, -3, -4
+STORE_DEVICE, STORE_HOST = 0, 1
+_STATUS_NAMES = {MOE_EINVAL: "MOE_EINVAL", MOE_ENOMEM: "MOE_ENOMEM", MOE_EHIP: "MOE_EHIP", MOE_ESTATE: "MOE_ESTATE"}
+
+# every symbol moe.h declares
+EXPORTS = [
+    "moe_expert_bytes", "moe_expert_stride", "moe_blob_offset", "moe_pack", "moe_unpack",
+    "moe_model_create", "moe_model_set_layer", "moe_model_set_experts", "moe_model_host_blob",
+    "moe_model_destroy", "moe_layer_forward", "moe_layer_decode", "moe_stack_decode", "moe_debug_routing",
+    "moe_pool_create", "moe_pool_reset", "moe_pool_stats", "moe_pool_trace", "moe_pool_destroy",
+    "moe_pool_simulate", "moe_last_error",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("hidden", "n_experts", "top_k", "inter", "shared_inter", "bits", "group", "n_layers", "norm_topk")]
+
+
+class PoolStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in
+                ("accesses", "hits", "misses", "evictions", "h2d_bytes", "requested_bytes")]
+
+    def as_dict(self):
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m routed_expert_int4_router_amd.build`")
+        # torch ships its own HIP runtime (libamdhip64.so.7). Loading torch first
+        # makes libmoe's libamdhip64.so.7 dependency resolve to that same copy, so
+        # torch's device pointers and streams and libmoe's kernels share one runtime.
+        import torch  # noqa: F401
+        L = ctypes.CDLL(LIB_PATH)
+        maps = open("/proc/self/maps").read()
+        runtimes = {ln.split()[-1] for ln in maps.splitlines() if "libamdhip64" in ln}
+        if len(runtimes) > 1:
+            raise ImportError(f"two HIP runtimes loaded in one process: {sorted(runtimes)}")
+        P, I32, I64, SZ, U64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_uint64
+        CP = ctypes.POINTER(Config)
+        sig = {
+            "moe_expert_bytes": (SZ, [CP, I32]),
+            "moe_expert_stride": (SZ, [CP, I32]),
+            "moe_blob_offset": (U64, [U64, U64, U64]),
+            "moe_pack": (I32, [CP, I32, P, P, P, I64, P, SZ]),
+            "moe_unpack": (I32, [CP, I32, P, P, P]),
+            "moe_model_create": (I32, [CP, I32, ctypes.POINTER(P)]),
+            "moe_model_set_layer": (I32, [P, I32, P, P, P, P]),
+            "moe_model_set_experts": (I32, [P, I64, I64, P]),
+            "moe_model_host_blob": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(SZ)]),
+            "moe_model_destroy": (None, [P]),
+            "moe_layer_forward": (I32, [P, I32, P, I32, P, P]),
+            "moe_layer_decode": (I32, [P, I32, P, I32, P, P]),
+            "moe_stack_decode": (I32, [P, P, P, I32, P, P]),
+            "moe_debug_routing": (I32, [P, P, P, SZ, ctypes.POINTER(SZ)]),
+            "moe_pool_create": (I32, [P, SZ, ctypes.POINTER(P)]),
+            "moe_pool_reset": (I32, [P]),
+            "moe_pool_stats": (I32, [P, ctypes.POINTER(PoolStats)]),
+            "moe_pool_trace": (I32, [P, P, P, SZ, ctypes.POINTER(SZ)]),
+            "moe_pool_destroy": (None, [P]),
+            "moe_pool_simulate": (I32, [I64, I32, I64, P, P, P]),
+            "moe_last_error": (ctypes.c_char_p, []),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def last_error() -> str:
+    return lib().moe_last_error().decode()
+
+
+def _check(st: int) -> None:
+    if st != MOE_OK:
+        raise MoeError(st, last_error())
+
+
+def make_config(hidden, n_experts, top_k, inter, shared_inter=None, bits=4, group=64, n_layers=1,
+                norm_topk=1) -> Config:
+    return Config(hidden, n_experts, top_k, inter, inter if shared_inter is None else shared_inter, bits, group,
+                  n_layers, norm_topk)
+
+
+def config_of(obj) -> Config:
+    """Config from any object with the moe_config field names (a dataclass, a namespace)."""
+    if isinstance(obj, Config):
+        return obj
+    return make_config(obj.hidden, obj.n_experts, obj.top_k, obj.inter, obj.shared_inter, obj.bits, obj.group,
+                       obj.n_layers, getattr(obj, "norm_topk", 1))
+
+
+def _ptr(a) -> int:
+    """Address of a numpy array or torch tensor (contiguous)."""
+    if a is None:
+        return None
+    if isinstance(a, np.ndarray):
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("array must be C-contiguous")
+        return a.ctypes.data
+    if hasattr(a, "data_ptr"):
+        if not a.is_contiguous():
+            raise ValueError("tensor must be contiguous")
+        return a.data_ptr()
+    return int(a)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def expert_bytes(cfg, inter: Optional[int] = None) -> int:
+    c = config_of(cfg)
+    return int(lib().moe_expert_bytes(ctypes.byref(c), c.inter if inter is None else inter))
+
+
+def expert_stride(cfg, inter: Optional[int] = None) -> int:
+    c = config_of(cfg)
+    return int(lib().moe_expert_stride(ctypes.byref(c), c.inter if inter is None else inter))
+
+
+def blob_offset(base: int, gid: int, stride: int) -> int:
+    return int(lib().moe_blob_offset(base, gid, stride))
+
+
+def pack(cfg, w_gate: np.ndarray, w_up: np.ndarray, w_down: np.ndarray, inter: Optional[int] = None,
+         out: Optional[np.ndarray] = None) -> np.ndarray:
+    """Pack n experts (fp32 [n][I][H], [n][I][H], [n][H][I], or one expert without the n axis)."""
+    c = config_of(cfg)
+    inter = c.inter if inter is None else inter
+    wg = np.ascontiguousarray(w_gate, dtype=np.float32)
+    wu = np.ascontiguousarray(w_up, dtype=np.float32)
+    wd = np.ascontiguousarray(w_down, dtype=np.float32)
+    n = 1 if wg.ndim == 2 else wg.shape[0]
+    stride = expert_stride(c, inter)
+    if out is None:
+        out = np.empty(n * stride, dtype=np.uint8)
+    _check(lib().moe_pack(ctypes.byref(c), inter, _ptr(wg), _ptr(wu), _ptr(wd), n, _ptr(out), out.nbytes))
+    return out
+
+
+def unpack(cfg, record: np.ndarray, inter: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    c = config_of(cfg)
+    inter = c.inter if inter is None else inter
+    rec = np.ascontiguousarray(record, dtype=np.uint8)
+    q = np.empty(3 * c.hidden * inter, dtype=np.uint8)
+    sc = np.empty(3 * c.hidden * inter // 64 * 2, dtype=np.uint16)
+    _check(lib().moe_unpack(ctypes.byref(c), inter, _ptr(rec), _ptr(q), _ptr(sc)))
+    return q, sc
+
+
+def pool_simulate(n_slots: int, gids: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    g = np.ascontiguousarray(gids, dtype=np.int64)
+    steps, k = g.shape
+    hit = np.empty(steps * k, dtype=np.uint8)
+    victim = np.empty(steps * k, dtype=np.int64)
+    _check(lib().moe_pool_simulate(n_slots, k, steps, _ptr(g), _ptr(hit), _ptr(victim)))
+    return hit, victim
+
+
+class Model:
+    """A model handle: resident dense weights + routed experts in HBM or pinned host memory."""
+
+    def __init__(self, cfg, storage: int = STORE_DEVICE):
+        self.cfg = config_of(cfg)
+        self.storage = storage
+        h = ctypes.c_void_p()
+        _check(lib().moe_model_create(ctypes.byref(self.cfg), storage, ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if self._h:
+            lib().moe_model_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_layer(self, layer: int, router_w: np.ndarray, router_bias: Optional[np.ndarray], shared_record: np.ndarray,
+                  shared_gate: np.ndarray):
+        rw = np.ascontiguousarray(router_w, dtype=np.float32)
+        rb = None if router_bias is None else np.ascontiguousarray(router_bias, dtype=np.float32)
+        sr = np.ascontiguousarray(shared_record, dtype=np.uint8)
+        sg = np.ascontiguousarray(shared_gate, dtype=np.float32)
+        _check(lib().moe_model_set_layer(self._h, layer, _ptr(rw), _ptr(rb), _ptr(sr), _ptr(sg)))
+
+    def set_experts(self, first_gid: int, records: np.ndarray):
+        recs = np.ascontiguousarray(records, dtype=np.uint8)
+        stride = expert_stride(self.cfg)
+        n = recs.nbytes // stride
+        _check(lib().moe_model_set_experts(self._h, first_gid, n, _ptr(recs)))
+
+    def host_blob(self) -> np.ndarray:
+        p = ctypes.c_void_p()
+        n = ctypes.c_size_t()
+        _check(lib().moe_model_host_blob(self._h, ctypes.byref(p), ctypes.byref(n)))
+        return np.ctypeslib.as_array((ctypes.c_uint8 * n.value).from_address(p.value))
+
+    def layer_forward(self, layer: int, x, out, n_tok: Optional[int] = None, stream=None):
+        n = x.shape[0] if n_tok is None else n_tok
+        _check(lib().moe_layer_forward(self._h, layer, _ptr(x), n, _ptr(out), _stream(stream)))
+
+    def layer_decode(self, layer: int, x, out, n_tok: Optional[int] = None, stream=None):
+        n = x.shape[0] if n_tok is None else n_tok
+        _check(lib().moe_layer_decode(self._h, layer, _ptr(x), n, _ptr(out), _stream(stream)))
+
+    def stack_decode(self, x0, out, pool: Optional["Pool"] = None, n_tok: Optional[int] = None, stream=None):
+        n = x0.shape[0] if n_tok is None else n_tok
+        _check(lib().moe_stack_decode(self._h, None if pool is None else pool.handle, _ptr(x0), n, _ptr(out),
+                                      _stream(stream)))
+
+    def debug_routing(self, cap: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+        n = ctypes.c_size_t()
+        _check(lib().moe_debug_routing(self._h, None, None, 0, ctypes.byref(n)))
+        steps = n.value if cap is None else min(cap, n.value)
+        k = self.cfg.top_k
+        idx = np.empty((steps, k), dtype=np.int32)
+        w = np.empty((steps, k), dtype=np.float32)
+        _check(lib().moe_debug_routing(self._h, _ptr(idx), _ptr(w), steps, ctypes.byref(n)))
+        return idx, w
+
+
+class Pool:
+    """Bounded HBM expert pool of a host-storage model."""
+
+    def __init__(self, model: Model, budget_bytes: int):
+        self.model = model
+        h = ctypes.c_void_p()
+        _check(lib().moe_pool_create(model.handle, budget_bytes, ctypes.byref(h)))
+        self._h = h
+
+    @property
+    def handle(self):
+        return self._h
+
+    def close(self):
+        if self._h:
+            lib().moe_pool_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reset(self):
+        _check(lib().moe_pool_reset(self._h))
+
+    def stats(self) -> dict:
+        s = PoolStats()
+        _check(lib().moe_pool_stats(self._h, ctypes.byref(s)))
+        return s.as_dict()
+
+    def trace(self) -> Tuple[np.ndarray, np.ndarray]:
+        n = ctypes.c_size_t()
+        _check(lib().moe_pool_trace(self._h, None, None, 0, ctypes.byref(n)))
+        hit = np.empty(n.value, dtype=np.uint8)
+        victim = np.empty(n.value, dtype=np.int64)
+        _check(lib().moe_pool_trace(self._h, _ptr(hit), _ptr(victim), n.value, ctypes.byref(n)))
+        return hit, victim

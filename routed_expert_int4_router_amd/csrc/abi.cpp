@@ -1,0 +1,554 @@
+// C ABI of libmoe: model and pool handles, weight upload, the decode and
+// stack entry points, and the pool's miss path (pinned host blob ->
+// hipMemcpyAsync on a side stream -> HBM slot).
+//
+// Pages: routed experts streamed on demand into a bounded slot pool with LFU +
+// recency eviction while the dense core (router, shared experts) stays
+// resident (cheshm.ai news article, paragraph on how it works; paotong.dev
+// commentary, paragraphs on the resident set and the bounded pool); a miss
+// reads the expert's record with one call at base + index * stride
+// (paotong.dev, paragraph on the fetch path; alphalab.site field test,
+// section on SSD reads). Here the blob is pinned host memory and the read is
+// a host-to-device copy into the victim slot.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+#include "pool_policy.h"
+#include "prefill.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr uint64_t kModelMagic = 0x4d4f454d4f44454cull;  // "MOEMODEL"
+constexpr uint64_t kPoolMagic = 0x4d4f45504f4f4c21ull;
+
+std::mutex g_live_mu;
+std::set<const void*> g_live;
+
+void live_add(const void* p) {
+  std::lock_guard<std::mutex> g(g_live_mu);
+  g_live.insert(p);
+}
+void live_del(const void* p) {
+  std::lock_guard<std::mutex> g(g_live_mu);
+  g_live.erase(p);
+}
+bool live_has(const void* p) {
+  std::lock_guard<std::mutex> g(g_live_mu);
+  return g_live.count(p) != 0;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+#define HIP_TRY(expr, what)                 \
+  do {                                      \
+    hipError_t e_ = (expr);                 \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+}  // namespace
+
+struct moe_model {
+  uint64_t magic = kModelMagic;
+  moe_config cfg{};
+  int32_t storage = MOE_STORE_DEVICE;
+  int device = 0;
+  Geometry geo{};
+  size_t rec_bytes = 0, stride = 0, shared_stride = 0;
+  uint8_t* experts = nullptr;       // device (STORE_DEVICE) or pinned host (STORE_HOST)
+  size_t experts_bytes = 0;
+  uint8_t* shared = nullptr;        // device [L] records
+  float* wr_rows = nullptr;         // device [L][E+1][H]
+  float* bias = nullptr;            // device [L][E]
+  float* logits = nullptr;          // device [E+1]
+  float* h = nullptr;               // device [(k+1)][I]
+  float* rbuf = nullptr;            // device [H]
+  uint16_t* xbuf = nullptr;         // device [2][H]
+  int32_t* route_idx = nullptr;     // device [route_cap][k]
+  float* route_w = nullptr;         // device [route_cap][k]
+  float* route_gamma = nullptr;     // device [route_cap]
+  size_t route_cap = 0;             // steps
+  size_t route_steps = 0;           // steps recorded by the last call
+  std::vector<uint8_t> layer_set;
+  void* prefill = nullptr;          // prefill workspace (prefill.hip)
+};
+
+struct moe_pool {
+  uint64_t magic = kPoolMagic;
+  moe_model* model = nullptr;
+  int64_t n_slots = 0;
+  uint8_t* arena = nullptr;         // device [n_slots][stride]
+  PoolTable table{1};
+  hipStream_t copy_stream = nullptr;
+  hipEvent_t copies_done = nullptr;
+  hipEvent_t route_ready = nullptr;
+  int32_t* host_route = nullptr;    // pinned, mapped [k]
+  int32_t* host_route_dev = nullptr;
+};
+
+namespace {
+
+moe_status check_model(moe_model* m, const char* fn) {
+  if (!m) return fail(MOE_EINVAL, std::string(fn) + ": model is NULL");
+  if (!live_has(m) || m->magic != kModelMagic) return fail(MOE_ESTATE, std::string(fn) + ": not a live model handle");
+  return MOE_OK;
+}
+
+moe_status check_pool(const moe_pool* p, const char* fn) {
+  if (!p) return fail(MOE_EINVAL, std::string(fn) + ": pool is NULL");
+  if (!live_has(p) || p->magic != kPoolMagic) return fail(MOE_ESTATE, std::string(fn) + ": not a live pool handle");
+  return MOE_OK;
+}
+
+moe_status ensure_route_cap(moe_model* m, size_t steps) {
+  if (steps <= m->route_cap) return MOE_OK;
+  size_t cap = std::max<size_t>(steps, 2 * m->route_cap);
+  HIP_TRY(hipDeviceSynchronize(), "route log resize");
+  hipFree(m->route_idx);
+  hipFree(m->route_w);
+  hipFree(m->route_gamma);
+  m->route_idx = nullptr;
+  m->route_w = nullptr;
+  m->route_gamma = nullptr;
+  m->route_cap = 0;
+  const size_t k = (size_t)m->cfg.top_k;
+  if (hipMalloc(&m->route_idx, cap * k * sizeof(int32_t)) != hipSuccess ||
+      hipMalloc(&m->route_w, cap * k * sizeof(float)) != hipSuccess ||
+      hipMalloc(&m->route_gamma, cap * sizeof(float)) != hipSuccess)
+    return fail(MOE_ENOMEM, "route log allocation failed");
+  m->route_cap = cap;
+  return MOE_OK;
+}
+
+StepBuffers step_buffers(moe_model* m, const uint16_t* x, size_t step) {
+  StepBuffers b;
+  b.x = x;
+  b.logits = m->logits;
+  b.route_idx = m->route_idx + step * (size_t)m->cfg.top_k;
+  b.route_w = m->route_w + step * (size_t)m->cfg.top_k;
+  b.route_gamma = m->route_gamma + step;
+  b.h = m->h;
+  return b;
+}
+
+ExpertSource resident_source(moe_model* m, int layer) {
+  ExpertSource s{};
+  s.base = m->experts;
+  s.stride = m->stride;
+  s.gid_base = (int64_t)layer * m->cfg.n_experts;
+  s.use_table = 0;
+  return s;
+}
+
+const float* layer_wr(moe_model* m, int layer) {
+  return m->wr_rows + (size_t)layer * (m->cfg.n_experts + 1) * m->cfg.hidden;
+}
+const float* layer_bias(moe_model* m, int layer) { return m->bias + (size_t)layer * m->cfg.n_experts; }
+const uint8_t* layer_shared(moe_model* m, int layer) { return m->shared + (size_t)layer * m->shared_stride; }
+
+// One token through one layer on the decode kernels.
+moe_status decode_step(moe_model* m, int layer, const StepBuffers& b, const ExpertSource& src,
+                       const ResidualArgs& r, hipStream_t s) {
+  HIP_TRY(launch_router(m->geo, layer_wr(m, layer), layer_bias(m, layer), b, s), "router launch");
+  HIP_TRY(launch_gateup(m->geo, src, layer_shared(m, layer), b, s), "gate/up launch");
+  HIP_TRY(launch_down(m->geo, src, layer_shared(m, layer), b, r, s), "down launch");
+  return MOE_OK;
+}
+
+moe_status check_forward_args(moe_model* m, int32_t layer, const void* x, int32_t n_tok, const void* out,
+                              const char* fn) {
+  moe_status st = check_model(m, fn);
+  if (st) return st;
+  if (layer < 0 || layer >= m->cfg.n_layers) return fail(MOE_EINVAL, std::string(fn) + ": layer out of range");
+  if (n_tok < 0 || n_tok > 65536) return fail(MOE_EINVAL, std::string(fn) + ": n_tok must be in [0, 65536]");
+  if (n_tok > 0 && (!x || !out)) return fail(MOE_EINVAL, std::string(fn) + ": NULL pointer");
+  if (m->storage != MOE_STORE_DEVICE)
+    return fail(MOE_ESTATE, std::string(fn) + ": experts are in host storage; use moe_stack_decode with a pool");
+  if (n_tok > 0 && !m->layer_set[(size_t)layer])
+    return fail(MOE_ESTATE, std::string(fn) + ": moe_model_set_layer was not called for this layer");
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_model_create(const moe_config* cfg, int32_t storage, moe_model** out) {
+  clear_error();
+  if (!out) return fail(MOE_EINVAL, "moe_model_create: out is NULL");
+  *out = nullptr;
+  std::string why = check_config(cfg);
+  if (!why.empty()) return fail(MOE_EINVAL, "moe_model_create: " + why);
+  if (storage != MOE_STORE_DEVICE && storage != MOE_STORE_HOST)
+    return fail(MOE_EINVAL, "moe_model_create: storage must be MOE_STORE_DEVICE or MOE_STORE_HOST");
+  Geometry g{};
+  g.H = cfg->hidden;
+  g.I = cfg->inter;
+  g.E = cfg->n_experts;
+  g.k = cfg->top_k;
+  g.bits = cfg->bits;
+  g.norm_topk = cfg->norm_topk;
+  RecordLayout lay = record_layout(*cfg, cfg->inter);
+  g.gate_codes = lay.gate_codes;
+  g.up_codes = lay.up_codes;
+  g.down_codes = lay.down_codes;
+  g.gate_sc = lay.gate_sc;
+  g.up_sc = lay.up_sc;
+  g.down_sc = lay.down_sc;
+  if (!decode_shape_supported(g))
+    return fail(MOE_EINVAL, "moe_model_create: shape not supported (n_experts <= 1024, (top_k+1)*inter <= 15360)");
+
+  moe_model* m = new moe_model();
+  m->cfg = *cfg;
+  m->storage = storage;
+  m->geo = g;
+  m->rec_bytes = record_bytes(*cfg, cfg->inter);
+  m->stride = record_stride(*cfg, cfg->inter);
+  m->shared_stride = record_stride(*cfg, cfg->shared_inter);
+  m->layer_set.assign((size_t)cfg->n_layers, 0);
+  hipGetDevice(&m->device);
+  const size_t L = cfg->n_layers, E = cfg->n_experts, H = cfg->hidden;
+  m->experts_bytes = L * E * m->stride;
+  bool ok = true;
+  hipError_t e = hipSuccess;
+  if (storage == MOE_STORE_DEVICE) {
+    e = hipMalloc(&m->experts, m->experts_bytes);
+    ok = ok && e == hipSuccess;
+    if (ok) ok = hipMemset(m->experts, 0, m->experts_bytes) == hipSuccess;
+  } else {
+    e = hipHostMalloc(&m->experts, m->experts_bytes, hipHostMallocDefault);
+    ok = ok && e == hipSuccess;
+  }
+  ok = ok && hipMalloc(&m->shared, L * m->shared_stride) == hipSuccess;
+  ok = ok && hipMalloc(&m->wr_rows, L * (E + 1) * H * sizeof(float)) == hipSuccess;
+  ok = ok && hipMalloc(&m->bias, L * E * sizeof(float)) == hipSuccess;
+  ok = ok && hipMalloc(&m->logits, (E + 1) * sizeof(float)) == hipSuccess;
+  ok = ok && hipMalloc(&m->h, (size_t)(cfg->top_k + 1) * cfg->inter * sizeof(float)) == hipSuccess;
+  ok = ok && hipMalloc(&m->rbuf, H * sizeof(float)) == hipSuccess;
+  ok = ok && hipMalloc(&m->xbuf, 2 * H * sizeof(uint16_t)) == hipSuccess;
+  if (ok) ok = hipMemset(m->bias, 0, L * E * sizeof(float)) == hipSuccess;
+  if (ok) ok = hipMemset(m->shared, 0, L * m->shared_stride) == hipSuccess;
+  if (ok) ok = hipMemset(m->wr_rows, 0, L * (E + 1) * H * sizeof(float)) == hipSuccess;
+  if (ok) ok = hipDeviceSynchronize() == hipSuccess;
+  if (!ok) {
+    live_add(m);
+    moe_model_destroy(m);
+    return fail(MOE_ENOMEM, "moe_model_create: allocation failed");
+  }
+  live_add(m);
+  moe_status st = ensure_route_cap(m, 1);
+  if (st) {
+    moe_model_destroy(m);
+    return st;
+  }
+  *out = m;
+  return MOE_OK;
+}
+
+moe_status moe_model_set_layer(moe_model* m, int32_t layer, const float* router_w, const float* router_bias,
+                               const void* shared_record, const float* shared_gate) {
+  clear_error();
+  moe_status st = check_model(m, "moe_model_set_layer");
+  if (st) return st;
+  if (layer < 0 || layer >= m->cfg.n_layers) return fail(MOE_EINVAL, "moe_model_set_layer: layer out of range");
+  if (!router_w || !shared_record || !shared_gate) return fail(MOE_EINVAL, "moe_model_set_layer: NULL pointer");
+  const size_t E = m->cfg.n_experts, H = m->cfg.hidden;
+  std::vector<float> rows((E + 1) * H);
+  for (size_t h = 0; h < H; ++h)
+    for (size_t e = 0; e < E; ++e) rows[e * H + h] = router_w[h * E + e];
+  std::memcpy(rows.data() + E * H, shared_gate, H * sizeof(float));
+  HIP_TRY(hipMemcpy((void*)layer_wr(m, layer), rows.data(), rows.size() * sizeof(float), hipMemcpyHostToDevice),
+          "moe_model_set_layer: router upload");
+  if (router_bias) {
+    HIP_TRY(hipMemcpy((void*)layer_bias(m, layer), router_bias, E * sizeof(float), hipMemcpyHostToDevice),
+            "moe_model_set_layer: bias upload");
+  } else {
+    HIP_TRY(hipMemset((void*)layer_bias(m, layer), 0, E * sizeof(float)), "moe_model_set_layer: bias clear");
+  }
+  const size_t sb = record_bytes(m->cfg, m->cfg.shared_inter);
+  HIP_TRY(hipMemcpy((void*)layer_shared(m, layer), shared_record, sb, hipMemcpyHostToDevice),
+          "moe_model_set_layer: shared expert upload");
+  HIP_TRY(hipDeviceSynchronize(), "moe_model_set_layer");
+  m->layer_set[(size_t)layer] = 1;
+  return MOE_OK;
+}
+
+moe_status moe_model_set_experts(moe_model* m, int64_t first_gid, int64_t n, const void* records) {
+  clear_error();
+  moe_status st = check_model(m, "moe_model_set_experts");
+  if (st) return st;
+  const int64_t total = (int64_t)m->cfg.n_layers * m->cfg.n_experts;
+  if (first_gid < 0 || n < 0 || first_gid + n > total)
+    return fail(MOE_EINVAL, "moe_model_set_experts: gid range outside [0, L*E)");
+  if (n == 0) return MOE_OK;
+  if (!records) return fail(MOE_EINVAL, "moe_model_set_experts: records is NULL");
+  uint8_t* dst = m->experts + (size_t)first_gid * m->stride;
+  const size_t bytes = (size_t)n * m->stride;
+  if (m->storage == MOE_STORE_DEVICE) {
+    HIP_TRY(hipMemcpy(dst, records, bytes, hipMemcpyHostToDevice), "moe_model_set_experts: upload");
+  } else {
+    std::memcpy(dst, records, bytes);
+  }
+  return MOE_OK;
+}
+
+moe_status moe_model_host_blob(moe_model* m, void** ptr, size_t* bytes) {
+  clear_error();
+  moe_status st = check_model(m, "moe_model_host_blob");
+  if (st) return st;
+  if (!ptr || !bytes) return fail(MOE_EINVAL, "moe_model_host_blob: NULL pointer");
+  if (m->storage != MOE_STORE_HOST) return fail(MOE_ESTATE, "moe_model_host_blob: model keeps experts in HBM");
+  *ptr = m->experts;
+  *bytes = m->experts_bytes;
+  return MOE_OK;
+}
+
+void moe_model_destroy(moe_model* m) {
+  if (!m || !live_has(m) || m->magic != kModelMagic) return;
+  hipDeviceSynchronize();
+  if (m->storage == MOE_STORE_HOST) hipHostFree(m->experts);
+  else hipFree(m->experts);
+  hipFree(m->shared);
+  hipFree(m->wr_rows);
+  hipFree(m->bias);
+  hipFree(m->logits);
+  hipFree(m->h);
+  hipFree(m->rbuf);
+  hipFree(m->xbuf);
+  hipFree(m->route_idx);
+  hipFree(m->route_w);
+  hipFree(m->route_gamma);
+  prefill_free(m->prefill);
+  m->magic = 0;
+  live_del(m);
+  delete m;
+}
+
+moe_status moe_layer_decode(moe_model* m, int32_t layer, const uint16_t* x, int32_t n_tok, float* out,
+                            void* stream) {
+  clear_error();
+  moe_status st = check_forward_args(m, layer, x, n_tok, out, "moe_layer_decode");
+  if (st) return st;
+  if (n_tok == 0) return MOE_OK;
+  st = ensure_route_cap(m, (size_t)n_tok);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t H = m->cfg.hidden;
+  const ExpertSource src = resident_source(m, layer);
+  for (int t = 0; t < n_tok; ++t) {
+    StepBuffers b = step_buffers(m, x + (size_t)t * H, (size_t)t);
+    ResidualArgs r{out + (size_t)t * H, nullptr, nullptr, nullptr};
+    st = decode_step(m, layer, b, src, r, s);
+    if (st) return st;
+  }
+  m->route_steps = (size_t)n_tok;
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(moe_model* m, int32_t layer, const uint16_t* x, int32_t n_tok, float* out,
+                             void* stream) {
+  clear_error();
+  moe_status st = check_forward_args(m, layer, x, n_tok, out, "moe_layer_forward");
+  if (st) return st;
+  if (n_tok == 0) return MOE_OK;
+  if ((int64_t)n_tok * m->cfg.top_k >= 4 * (int64_t)m->cfg.n_experts && prefill_supported(m->cfg)) {
+    st = ensure_route_cap(m, (size_t)n_tok);
+    if (st) return st;
+    PrefillArgs a{};
+    a.cfg = m->cfg;
+    a.geo = m->geo;
+    a.experts = m->experts + (size_t)layer * m->cfg.n_experts * m->stride;
+    a.stride = m->stride;
+    a.shared = layer_shared(m, layer);
+    a.wr_rows = layer_wr(m, layer);
+    a.bias = layer_bias(m, layer);
+    a.x = x;
+    a.n_tok = n_tok;
+    a.out = out;
+    a.route_idx = m->route_idx;
+    a.route_w = m->route_w;
+    a.route_gamma = m->route_gamma;
+    st = prefill_forward(&m->prefill, a, static_cast<hipStream_t>(stream));
+    if (st) return st;
+    m->route_steps = (size_t)n_tok;
+    return MOE_OK;
+  }
+  return moe_layer_decode(m, layer, x, n_tok, out, stream);
+}
+
+moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, int32_t n_tok, float* out,
+                            void* stream) {
+  clear_error();
+  moe_status st = check_model(m, "moe_stack_decode");
+  if (st) return st;
+  if (n_tok < 0 || n_tok > 65536) return fail(MOE_EINVAL, "moe_stack_decode: n_tok must be in [0, 65536]");
+  if (n_tok > 0 && (!x0 || !out)) return fail(MOE_EINVAL, "moe_stack_decode: NULL pointer");
+  if (pool) {
+    st = check_pool(pool, "moe_stack_decode");
+    if (st) return st;
+    if (pool->model != m) return fail(MOE_ESTATE, "moe_stack_decode: pool belongs to another model");
+  } else if (m->storage != MOE_STORE_DEVICE) {
+    return fail(MOE_ESTATE, "moe_stack_decode: experts are in host storage; a pool is required");
+  }
+  for (int l = 0; l < m->cfg.n_layers; ++l)
+    if (!m->layer_set[(size_t)l]) return fail(MOE_ESTATE, "moe_stack_decode: a layer was not set");
+  if (n_tok == 0) return MOE_OK;
+  const int L = m->cfg.n_layers, k = m->cfg.top_k, E = m->cfg.n_experts;
+  const size_t H = m->cfg.hidden;
+  st = ensure_route_cap(m, (size_t)n_tok * L);
+  if (st) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<int64_t> gids((size_t)k), slots((size_t)k);
+  std::vector<uint8_t> miss((size_t)k);
+  for (int t = 0; t < n_tok; ++t) {
+    for (int l = 0; l < L; ++l) {
+      const size_t step = (size_t)t * L + l;
+      const uint16_t* xl = (l == 0) ? x0 + (size_t)t * H : m->xbuf + (size_t)(l & 1) * H;
+      StepBuffers b = step_buffers(m, xl, step);
+      ResidualArgs r{};
+      r.out = (l == L - 1) ? out + (size_t)t * H : m->rbuf;
+      r.r_in = (l == 0) ? nullptr : m->rbuf;
+      r.x_res = (l == 0) ? x0 + (size_t)t * H : nullptr;
+      r.x_next = (l == L - 1) ? nullptr : m->xbuf + (size_t)((l + 1) & 1) * H;
+      if (!pool) {
+        st = decode_step(m, l, b, resident_source(m, l), r, s);
+        if (st) return st;
+        continue;
+      }
+      // pool: top-k on the device, then the host decides hits, misses and victims
+      HIP_TRY(launch_router(m->geo, layer_wr(m, l), layer_bias(m, l), b, s), "router launch");
+      HIP_TRY(launch_topk(m->geo, b, pool->host_route_dev, s), "top-k launch");
+      HIP_TRY(hipEventRecord(pool->route_ready, s), "event record");
+      HIP_TRY(hipEventSynchronize(pool->route_ready), "route sync");
+      for (int j = 0; j < k; ++j) gids[(size_t)j] = (int64_t)l * E + pool->host_route[j];
+      pool->table.step(gids.data(), k, slots.data(), miss.data());
+      bool any_miss = false;
+      ExpertSource src{};
+      src.base = pool->arena;
+      src.stride = m->stride;
+      src.use_table = 1;
+      for (int j = 0; j < k; ++j) {
+        src.table[j] = slots[(size_t)j];
+        if (miss[(size_t)j]) {
+          any_miss = true;
+          HIP_TRY(hipMemcpyAsync(pool->arena + (size_t)slots[(size_t)j] * m->stride,
+                                 m->experts + (size_t)gids[(size_t)j] * m->stride, m->rec_bytes,
+                                 hipMemcpyHostToDevice, pool->copy_stream),
+                  "miss copy");
+        }
+      }
+      if (any_miss) {
+        HIP_TRY(hipEventRecord(pool->copies_done, pool->copy_stream), "event record");
+        HIP_TRY(hipStreamWaitEvent(s, pool->copies_done, 0), "stream wait");
+      }
+      HIP_TRY(launch_gateup(m->geo, src, layer_shared(m, l), b, s), "gate/up launch");
+      HIP_TRY(launch_down(m->geo, src, layer_shared(m, l), b, r, s), "down launch");
+    }
+  }
+  if (pool) HIP_TRY(hipStreamSynchronize(s), "moe_stack_decode: final sync");
+  m->route_steps = (size_t)n_tok * L;
+  return MOE_OK;
+}
+
+moe_status moe_debug_routing(moe_model* m, int32_t* idx, float* w, size_t cap, size_t* n_steps) {
+  clear_error();
+  moe_status st = check_model(m, "moe_debug_routing");
+  if (st) return st;
+  if (!n_steps) return fail(MOE_EINVAL, "moe_debug_routing: n_steps is NULL");
+  HIP_TRY(hipDeviceSynchronize(), "moe_debug_routing: sync");
+  *n_steps = m->route_steps;
+  const size_t n = std::min(cap, m->route_steps);
+  const size_t k = (size_t)m->cfg.top_k;
+  if (n && idx) HIP_TRY(hipMemcpy(idx, m->route_idx, n * k * sizeof(int32_t), hipMemcpyDeviceToHost), "copy idx");
+  if (n && w) HIP_TRY(hipMemcpy(w, m->route_w, n * k * sizeof(float), hipMemcpyDeviceToHost), "copy w");
+  return MOE_OK;
+}
+
+moe_status moe_pool_create(moe_model* m, size_t budget_bytes, moe_pool** out) {
+  clear_error();
+  if (!out) return fail(MOE_EINVAL, "moe_pool_create: out is NULL");
+  *out = nullptr;
+  moe_status st = check_model(m, "moe_pool_create");
+  if (st) return st;
+  if (m->storage != MOE_STORE_HOST) return fail(MOE_ESTATE, "moe_pool_create: the model keeps its experts in HBM");
+  const int64_t slots = (int64_t)(budget_bytes / m->stride);
+  if (slots < m->cfg.top_k)
+    return fail(MOE_EINVAL, "moe_pool_create: budget holds " + std::to_string(slots) + " slots, fewer than top_k");
+  moe_pool* p = new moe_pool();
+  p->model = m;
+  p->n_slots = slots;
+  p->table = PoolTable(slots);
+  bool ok = hipMalloc(&p->arena, (size_t)slots * m->stride) == hipSuccess;
+  ok = ok && hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&p->copies_done, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipEventCreateWithFlags(&p->route_ready, hipEventDisableTiming) == hipSuccess;
+  ok = ok && hipHostMalloc(&p->host_route, kMaxTopK * sizeof(int32_t), hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
+  ok = ok && hipHostGetDevicePointer((void**)&p->host_route_dev, p->host_route, 0) == hipSuccess;
+  live_add(p);
+  if (!ok) {
+    moe_pool_destroy(p);
+    return fail(MOE_ENOMEM, "moe_pool_create: allocation failed");
+  }
+  *out = p;
+  return MOE_OK;
+}
+
+moe_status moe_pool_reset(moe_pool* p) {
+  clear_error();
+  moe_status st = check_pool(p, "moe_pool_reset");
+  if (st) return st;
+  p->table.reset();
+  return MOE_OK;
+}
+
+moe_status moe_pool_stats(const moe_pool* p, moe_pool_stats_t* out) {
+  clear_error();
+  moe_status st = check_pool(p, "moe_pool_stats");
+  if (st) return st;
+  if (!out) return fail(MOE_EINVAL, "moe_pool_stats: out is NULL");
+  out->accesses = p->table.accesses;
+  out->hits = p->table.hits;
+  out->misses = p->table.misses;
+  out->evictions = p->table.evictions;
+  out->h2d_bytes = p->table.misses * (uint64_t)p->model->rec_bytes;
+  out->requested_bytes = p->table.accesses * (uint64_t)p->model->rec_bytes;
+  return MOE_OK;
+}
+
+moe_status moe_pool_trace(const moe_pool* p, uint8_t* hit, int64_t* victim, size_t cap, size_t* n) {
+  clear_error();
+  moe_status st = check_pool(p, "moe_pool_trace");
+  if (st) return st;
+  if (!n) return fail(MOE_EINVAL, "moe_pool_trace: n is NULL");
+  *n = p->table.trace_hit.size();
+  const size_t c = std::min(cap, *n);
+  if (hit) std::copy(p->table.trace_hit.begin(), p->table.trace_hit.begin() + (ptrdiff_t)c, hit);
+  if (victim) std::copy(p->table.trace_victim.begin(), p->table.trace_victim.begin() + (ptrdiff_t)c, victim);
+  return MOE_OK;
+}
+
+void moe_pool_destroy(moe_pool* p) {
+  if (!p || !live_has(p) || p->magic != kPoolMagic) return;
+  hipDeviceSynchronize();
+  hipFree(p->arena);
+  if (p->copy_stream) hipStreamDestroy(p->copy_stream);
+  if (p->copies_done) hipEventDestroy(p->copies_done);
+  if (p->route_ready) hipEventDestroy(p->route_ready);
+  if (p->host_route) hipHostFree(p->host_route);
+  p->magic = 0;
+  live_del(p);
+  delete p;
+}
+
+}  // extern "C"

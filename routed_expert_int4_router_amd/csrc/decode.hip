@@ -1,0 +1,598 @@
+// Batch-1 decode kernels of the routed MoE step for gfx950 (wave64).
+//
+// One token-layer runs as three dependent launches:
+//   router   : E+1 fp64-accumulated dot products (router logits + shared gate)
+//   gateup   : per wave, top-k of the logits (wave shuffles), then the int4/int8
+//              group-dequant GEMV of gate and up rows and SwiGLU -> h (fp32)
+//   down     : down-projection GEMV of the k+1 experts on h, weighted combine
+//              with the renormalised router weights and the sigmoid shared gate,
+//              optional residual update of a layer stack.
+// Pages: top-k routing per layer (10 of 512 / 8 of 256), resident router and
+// shared experts, fixed-stride expert blobs, MLX-style int4/int8 group
+// quantisation (cheshm.ai news article, paragraphs on how it works and on the
+// code base; paotong.dev commentary, paragraphs on the principle and the fetch
+// path); renormalised top-k weights (alphalab.site field test, section on the
+// 35B correctness fix). The decode loop being dispatch-bound (paotong.dev,
+// paragraph on the bounded pool) is why the token-layer is only three launches.
+//
+// Weight reads are 16-byte (dwordx4) loads of packed codes; each lane owns a
+// contiguous 16-byte chunk of a code row, consecutive lanes own consecutive
+// chunks, so a wave-wide load covers contiguous row bytes. Codes become floats
+// exactly (v_cvt_f32_ubyte*) and the group scale and bias are applied once per
+// chunk: dot = s * sum(q * x) + c * sum(x).
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int kWave = 64;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream(const uint8_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float f16f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+
+__device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xFFu); }
+__device__ __forceinline__ float ub1(uint32_t v) { return (float)((v >> 8) & 0xFFu); }
+__device__ __forceinline__ float ub2(uint32_t v) { return (float)((v >> 16) & 0xFFu); }
+__device__ __forceinline__ float ub3(uint32_t v) { return (float)(v >> 24); }
+
+// sum over the chunk of code * x; x holds EPC = 128 / BITS consecutive elements.
+template <int BITS>
+__device__ __forceinline__ float chunk_dot(const uint4 c, const float* x) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  float a0 = 0.f, a1 = 0.f;
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t lo = w[t] & 0x0F0F0F0Fu, hi = (w[t] >> 4) & 0x0F0F0F0Fu;
+      const float* xx = x + 8 * t;
+      a0 = fmaf(ub0(lo), xx[0], a0);
+      a1 = fmaf(ub0(hi), xx[1], a1);
+      a0 = fmaf(ub1(lo), xx[2], a0);
+      a1 = fmaf(ub1(hi), xx[3], a1);
+      a0 = fmaf(ub2(lo), xx[4], a0);
+      a1 = fmaf(ub2(hi), xx[5], a1);
+      a0 = fmaf(ub3(lo), xx[6], a0);
+      a1 = fmaf(ub3(hi), xx[7], a1);
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const float* xx = x + 4 * t;
+      a0 = fmaf(ub0(w[t]), xx[0], a0);
+      a1 = fmaf(ub1(w[t]), xx[1], a1);
+      a0 = fmaf(ub2(w[t]), xx[2], a0);
+      a1 = fmaf(ub3(w[t]), xx[3], a1);
+    }
+  }
+  return a0 + a1;
+}
+
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Total order key of a logit: larger key = larger logit; NaN ranks with -inf;
+// -0 ranks with +0. Key 0 is below every real logit (used for "removed").
+__device__ __forceinline__ uint32_t order_key(float v) {
+  if (v != v) v = -INFINITY;
+  if (v == 0.0f) v = 0.0f;
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t k) {
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// Wave-wide top-k: every lane returns the same sel_e[j] / sel_l[j] for j < k,
+// ordered by (logit descending, index ascending).
+template <int NPL>
+__device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int E, int k, int* sel_e,
+                                          float* sel_l) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t key[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = (e < E) ? order_key(logits[e]) : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k) {
+      uint32_t bu = 0u;
+      uint32_t be = 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < NPL; ++i) {
+        if (key[i] > bu) {
+          bu = key[i];
+          be = (uint32_t)(lane + kWave * i);
+        }
+      }
+      uint32_t hi = bu, lo = ~be;  // max over (key, -index)
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t ohi = __shfl_xor(hi, off, kWave);
+        const uint32_t olo = __shfl_xor(lo, off, kWave);
+        if (ohi > hi || (ohi == hi && olo > lo)) {
+          hi = ohi;
+          lo = olo;
+        }
+      }
+      const int e = (int)(~lo);
+      sel_e[j] = e;
+      sel_l[j] = key_value(hi);
+#pragma unroll
+      for (int i = 0; i < NPL; ++i)
+        if (lane + kWave * i == e) key[i] = 0u;
+    }
+  }
+}
+
+// Routing weights of the selection: renormalised softmax over the k selected
+// logits (norm_topk = 1) or the plain softmax probabilities (norm_topk = 0).
+template <int NPL>
+__device__ __forceinline__ void route_weights(const float* __restrict__ logits, int E, int k, int norm_topk,
+                                              const float* sel_l, float* w) {
+  const float m = sel_l[0];
+  float z[kMaxTopK];
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    z[j] = (j < k) ? expf(sel_l[j] - m) : 0.f;
+    s += z[j];
+  }
+  if (!norm_topk) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float part = 0.f;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int e = lane + kWave * i;
+      if (e < E) part += expf(logits[e] - m);
+    }
+    s = wave_sum_f32(part);
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) w[j] = z[j] / s;
+}
+
+// ------------------------------------------------------------------ router ---
+// One wave per output row; lanes stride over the hidden dimension in float4 /
+// 4 x bf16 steps. Products of a bf16 and an fp32 are exact in fp64, so the
+// fp64 sum rounded once to fp32 is the exactly rounded logit except in
+// vanishingly rare near-ties.
+__global__ void __launch_bounds__(256) router_kernel(Geometry g, const float* __restrict__ wr,
+                                                     const float* __restrict__ bias, StepBuffers b) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row > g.E) return;
+  const float4* w4 = reinterpret_cast<const float4*>(wr + (size_t)row * g.H);
+  const uint2* x4 = reinterpret_cast<const uint2*>(b.x);
+  double acc = 0.0;
+  for (int i = lane; i < g.H / 4; i += kWave) {
+    const float4 w = w4[i];
+    const uint2 xv = x4[i];
+    acc += (double)bf16f(xv.x & 0xFFFFu) * (double)w.x;
+    acc += (double)bf16f(xv.x >> 16) * (double)w.y;
+    acc += (double)bf16f(xv.y & 0xFFFFu) * (double)w.z;
+    acc += (double)bf16f(xv.y >> 16) * (double)w.w;
+  }
+  acc = wave_sum_f64(acc);
+  if (lane == 0) {
+    if (row < g.E && bias) acc += (double)bias[row];
+    b.logits[row] = (float)acc;
+  }
+}
+
+// -------------------------------------------------------------------- topk ---
+template <int NPL>
+__global__ void __launch_bounds__(64) topk_kernel(Geometry g, StepBuffers b, int32_t* host_route) {
+  int sel_e[kMaxTopK];
+  float sel_l[kMaxTopK], w[kMaxTopK];
+  wave_topk<NPL>(b.logits, g.E, g.k, sel_e, sel_l);
+  route_weights<NPL>(b.logits, g.E, g.k, g.norm_topk, sel_l, w);
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < g.k && lane == j) {
+      b.route_idx[j] = sel_e[j];
+      b.route_w[j] = w[j];
+      if (host_route) host_route[j] = sel_e[j];
+    }
+  }
+  if (lane == 0) b.route_gamma[0] = 1.0f / (1.0f + expf(-b.logits[g.E]));
+}
+
+__device__ __forceinline__ const uint8_t* expert_record(const ExpertSource& src, int j, int e) {
+  const int64_t r = src.use_table ? src.table[j] : (src.gid_base + e);
+  return src.base + (uint64_t)r * src.stride;
+}
+
+// ------------------------------------------------------------------ gateup ---
+// Wave task: RPW * RW consecutive rows i of one expert slot j (slot k = shared).
+// Lane (r, c): r = lane / LPR selects the row inside a group of RPW rows,
+// c = lane % LPR the first 16-byte chunk; it owns chunks c + LPR * it.
+template <int BITS, int LPR, int IT, int RW, int NPL>
+__global__ void __launch_bounds__(256) gateup_kernel(Geometry g, ExpertSource src, const uint8_t* __restrict__ shared_rec,
+                                                     StepBuffers b, int waves_per_expert, int total_waves) {
+  constexpr int EPC = 128 / BITS;  // elements per 16-byte chunk
+  constexpr int RPW = kWave / LPR;
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wave >= total_waves) return;
+  const int lane = threadIdx.x & 63;
+  const int j = wave / waves_per_expert;
+  const int row0 = (wave % waves_per_expert) * (RPW * RW);
+  const int rsub = lane / LPR, c0 = lane % LPR;
+
+  const uint8_t* rec;
+  if (j == g.k) {
+    rec = shared_rec;
+  } else if (src.use_table) {
+    rec = expert_record(src, j, 0);
+  } else {
+    int sel_e[kMaxTopK];
+    float sel_l[kMaxTopK];
+    wave_topk<NPL>(b.logits, g.E, g.k, sel_e, sel_l);
+    int e = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q)
+      if (q == j) e = sel_e[q];
+    rec = expert_record(src, j, e);
+    if (wave == 0) {
+      float w[kMaxTopK];
+      route_weights<NPL>(b.logits, g.E, g.k, g.norm_topk, sel_l, w);
+#pragma unroll
+      for (int q = 0; q < kMaxTopK; ++q) {
+        if (q < g.k && lane == q) {
+          b.route_idx[q] = sel_e[q];
+          b.route_w[q] = w[q];
+        }
+      }
+      if (lane == 0) b.route_gamma[0] = 1.0f / (1.0f + expf(-b.logits[g.E]));
+    }
+  }
+
+  const size_t row_bytes = (size_t)g.H * BITS / 8;
+  const int groups = g.H / 64;
+  // issue all weight loads first
+  uint4 cg[RW][IT], cu[RW][IT];
+  uint32_t sg[RW][IT], su[RW][IT];
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr) {
+    const int i = row0 + rsub + RPW * rr;
+    const uint8_t* grow = rec + g.gate_codes + (size_t)i * row_bytes;
+    const uint8_t* urow = rec + g.up_codes + (size_t)i * row_bytes;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int ch = c0 + LPR * it;
+      cg[rr][it] = ld_stream(grow + 16 * ch);
+      cu[rr][it] = ld_stream(urow + 16 * ch);
+      const int grp = ch * EPC / 64;
+      sg[rr][it] = *reinterpret_cast<const uint32_t*>(rec + g.gate_sc + ((size_t)i * groups + grp) * 4);
+      su[rr][it] = *reinterpret_cast<const uint32_t*>(rec + g.up_sc + ((size_t)i * groups + grp) * 4);
+    }
+  }
+  // activations of this lane's chunks
+  float xv[IT][EPC];
+  float xs[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int ch = c0 + LPR * it;
+    const uint4* xp = reinterpret_cast<const uint4*>(b.x + (size_t)ch * EPC);
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < EPC / 8; ++q) {
+      const uint4 v = xp[q];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        xv[it][8 * q + 2 * t] = bf16f(w[t] & 0xFFFFu);
+        xv[it][8 * q + 2 * t + 1] = bf16f(w[t] >> 16);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < EPC; ++q) s += xv[it][q];
+    xs[it] = s;
+  }
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr) {
+    float ag = 0.f, au = 0.f;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const float dg = chunk_dot<BITS>(cg[rr][it], xv[it]);
+      const float du = chunk_dot<BITS>(cu[rr][it], xv[it]);
+      ag += f16f(sg[rr][it] & 0xFFFFu) * dg + f16f(sg[rr][it] >> 16) * xs[it];
+      au += f16f(su[rr][it] & 0xFFFFu) * du + f16f(su[rr][it] >> 16) * xs[it];
+    }
+    ag = group_sum<LPR>(ag);
+    au = group_sum<LPR>(au);
+    if (c0 == 0) {
+      const int i = row0 + rsub + RPW * rr;
+      const float silu = ag / (1.0f + expf(-ag));
+      b.h[(size_t)j * g.I + i] = silu * au;
+    }
+  }
+}
+
+// -------------------------------------------------------------------- down ---
+// Block: RPW * R output rows, 4 waves; wave w handles expert slots j = w, w+4, ...
+// (slot k = shared expert, weight gamma). Lane (r, c) owns chunks c + LPR * it of
+// rows r + RPW * rr. h of all k+1 slots is staged in LDS once per block.
+template <int BITS, int LPR, int IT, int R>
+__global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src, const uint8_t* __restrict__ shared_rec,
+                                                   StepBuffers b, ResidualArgs res) {
+  constexpr int EPC = 128 / BITS;
+  constexpr int RPW = kWave / LPR;
+  constexpr int RB = RPW * R;
+  extern __shared__ __align__(16) float smem[];
+  float* sh_h = smem;                                 // [(k+1)][I]
+  float* sh_part = smem + (size_t)(g.k + 1) * g.I;    // [4][RB]
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int rsub = lane / LPR, c0 = lane % LPR;
+  const int hrow0 = blockIdx.x * RB;
+  const size_t row_bytes = (size_t)g.I * BITS / 8;
+  const int groups = g.I / 64;
+  const int nslots = g.k + 1;
+
+  // issue weight loads of this wave's experts (up to 4 slots per wave: k <= 15)
+  constexpr int MS = (kMaxTopK + 1 + 3) / 4;  // 5
+  uint4 cd[MS][R][IT];
+  uint32_t sd[MS][R][IT];
+  int e_of[MS];
+#pragma unroll
+  for (int m = 0; m < MS; ++m) {
+    const int j = wv + 4 * m;
+    e_of[m] = 0;
+    if (j < nslots) {
+      const uint8_t* rec;
+      if (j == g.k) {
+        rec = shared_rec;
+      } else {
+        const int e = src.use_table ? 0 : b.route_idx[j];
+        rec = expert_record(src, j, e);
+      }
+#pragma unroll
+      for (int rr = 0; rr < R; ++rr) {
+        const int hr = hrow0 + rsub + RPW * rr;
+        const uint8_t* drow = rec + g.down_codes + (size_t)hr * row_bytes;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const int ch = c0 + LPR * it;
+          cd[m][rr][it] = ld_stream(drow + 16 * ch);
+          sd[m][rr][it] = *reinterpret_cast<const uint32_t*>(rec + g.down_sc + ((size_t)hr * groups + ch * EPC / 64) * 4);
+        }
+      }
+    }
+  }
+  // stage h
+  {
+    const int n4 = nslots * g.I / 4;
+    const float4* src4 = reinterpret_cast<const float4*>(b.h);
+    float4* dst4 = reinterpret_cast<float4*>(sh_h);
+    for (int q = threadIdx.x; q < n4; q += 256) dst4[q] = src4[q];
+  }
+  __syncthreads();
+
+  float acc[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) acc[rr] = 0.f;
+#pragma unroll
+  for (int m = 0; m < MS; ++m) {
+    const int j = wv + 4 * m;
+    if (j < nslots) {
+      const float wj = (j == g.k) ? b.route_gamma[0] : b.route_w[j];
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int ch = c0 + LPR * it;
+        float hv[EPC];
+        const float4* hp = reinterpret_cast<const float4*>(sh_h + (size_t)j * g.I + ch * EPC);
+#pragma unroll
+        for (int q = 0; q < EPC / 4; ++q) {
+          const float4 v = hp[q];
+          hv[4 * q] = v.x;
+          hv[4 * q + 1] = v.y;
+          hv[4 * q + 2] = v.z;
+          hv[4 * q + 3] = v.w;
+        }
+        float hs = 0.f;
+#pragma unroll
+        for (int q = 0; q < EPC; ++q) hs += hv[q];
+#pragma unroll
+        for (int rr = 0; rr < R; ++rr) {
+          const float d = chunk_dot<BITS>(cd[m][rr][it], hv);
+          const float c = f16f(sd[m][rr][it] & 0xFFFFu) * d + f16f(sd[m][rr][it] >> 16) * hs;
+          acc[rr] = fmaf(wj, c, acc[rr]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
+    const float v = group_sum<LPR>(acc[rr]);
+    if (c0 == 0) sh_part[wv * RB + rsub + RPW * rr] = v;
+  }
+  __syncthreads();
+  if (threadIdx.x < RB) {
+    const int hr = hrow0 + threadIdx.x;
+    const float o = ((sh_part[threadIdx.x] + sh_part[RB + threadIdx.x]) + sh_part[2 * RB + threadIdx.x]) +
+                    sh_part[3 * RB + threadIdx.x];
+    if (res.r_in || res.x_res) {
+      const float r = (res.r_in ? res.r_in[hr] : bf16f(res.x_res[hr])) + o;
+      res.out[hr] = r;
+      if (res.x_next) res.x_next[hr] = to_bf16_rne(r);
+    } else {
+      res.out[hr] = o;
+    }
+  }
+}
+
+// ------------------------------------------------------------- dispatchers ---
+
+int npl_for(int E) {
+  int n = (E + 63) / 64;
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+int lpr_for(int chunks) { return chunks < 64 ? chunks : 64; }
+
+template <int BITS, int LPR, int IT, int NPL>
+hipError_t gateup_rw(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                     hipStream_t s) {
+  constexpr int RPW = kWave / LPR;
+  int rw = g.I / RPW;
+  rw = rw >= 4 ? 4 : (rw >= 2 ? 2 : 1);
+  const int wpe = g.I / (RPW * rw);
+  const int total = (g.k + 1) * wpe;
+  const dim3 grid((total + 3) / 4), block(256);
+  if (rw == 4) hipLaunchKernelGGL((gateup_kernel<BITS, LPR, IT, 4, NPL>), grid, block, 0, s, g, src, shared_rec, b, wpe, total);
+  else if (rw == 2) hipLaunchKernelGGL((gateup_kernel<BITS, LPR, IT, 2, NPL>), grid, block, 0, s, g, src, shared_rec, b, wpe, total);
+  else hipLaunchKernelGGL((gateup_kernel<BITS, LPR, IT, 1, NPL>), grid, block, 0, s, g, src, shared_rec, b, wpe, total);
+  return hipGetLastError();
+}
+
+template <int BITS, int LPR, int IT>
+hipError_t gateup_npl(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                      hipStream_t s) {
+  switch (npl_for(g.E)) {
+    case 1: return gateup_rw<BITS, LPR, IT, 1>(g, src, shared_rec, b, s);
+    case 2: return gateup_rw<BITS, LPR, IT, 2>(g, src, shared_rec, b, s);
+    case 4: return gateup_rw<BITS, LPR, IT, 4>(g, src, shared_rec, b, s);
+    case 8: return gateup_rw<BITS, LPR, IT, 8>(g, src, shared_rec, b, s);
+    case 16: return gateup_rw<BITS, LPR, IT, 16>(g, src, shared_rec, b, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int BITS>
+hipError_t gateup_bits(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                       hipStream_t s) {
+  const int chunks = g.H * BITS / 128;
+  const int lpr = lpr_for(chunks), it = chunks / lpr;
+  if (it == 1) {
+    switch (lpr) {
+      case 2: return gateup_npl<BITS, 2, 1>(g, src, shared_rec, b, s);
+      case 4: return gateup_npl<BITS, 4, 1>(g, src, shared_rec, b, s);
+      case 8: return gateup_npl<BITS, 8, 1>(g, src, shared_rec, b, s);
+      case 16: return gateup_npl<BITS, 16, 1>(g, src, shared_rec, b, s);
+      case 32: return gateup_npl<BITS, 32, 1>(g, src, shared_rec, b, s);
+      case 64: return gateup_npl<BITS, 64, 1>(g, src, shared_rec, b, s);
+    }
+  } else if (it == 2) {
+    return gateup_npl<BITS, 64, 2>(g, src, shared_rec, b, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int BITS, int LPR, int IT>
+hipError_t down_r(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                  const ResidualArgs& r, hipStream_t s) {
+  constexpr int RPW = kWave / LPR;
+  int R = g.H / (RPW * 256);
+  R = R >= 4 ? 4 : (R >= 2 ? 2 : 1);
+  while (R > 1 && g.H % (RPW * R)) R >>= 1;
+  const int RB = RPW * R;
+  if (g.H % RB) return hipErrorInvalidValue;
+  const size_t lds = ((size_t)(g.k + 1) * g.I + 4 * RB) * sizeof(float);
+  const dim3 grid(g.H / RB), block(256);
+  if (R == 4) hipLaunchKernelGGL((down_kernel<BITS, LPR, IT, 4>), grid, block, lds, s, g, src, shared_rec, b, r);
+  else if (R == 2) hipLaunchKernelGGL((down_kernel<BITS, LPR, IT, 2>), grid, block, lds, s, g, src, shared_rec, b, r);
+  else hipLaunchKernelGGL((down_kernel<BITS, LPR, IT, 1>), grid, block, lds, s, g, src, shared_rec, b, r);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t down_bits(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                     const ResidualArgs& r, hipStream_t s) {
+  const int chunks = g.I * BITS / 128;
+  const int lpr = lpr_for(chunks), it = chunks / lpr;
+  if (it == 1) {
+    switch (lpr) {
+      case 2: return down_r<BITS, 2, 1>(g, src, shared_rec, b, r, s);
+      case 4: return down_r<BITS, 4, 1>(g, src, shared_rec, b, r, s);
+      case 8: return down_r<BITS, 8, 1>(g, src, shared_rec, b, r, s);
+      case 16: return down_r<BITS, 16, 1>(g, src, shared_rec, b, r, s);
+      case 32: return down_r<BITS, 32, 1>(g, src, shared_rec, b, r, s);
+      case 64: return down_r<BITS, 64, 1>(g, src, shared_rec, b, r, s);
+    }
+  } else if (it == 2) {
+    return down_r<BITS, 64, 2>(g, src, shared_rec, b, r, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool decode_shape_supported(const Geometry& g) {
+  if (g.bits != 4 && g.bits != 8) return false;
+  const int cg = g.H * g.bits / 128, cd = g.I * g.bits / 128;
+  if (cg < 2 || cg > 128 || cd < 2 || cd > 128) return false;
+  if (g.k < 1 || g.k > kMaxTopK || g.E > 1024 || g.E < g.k) return false;
+  if ((size_t)(g.k + 1) * g.I > 15360) return false;  // h staged in <= 60 KiB of LDS
+  return true;
+}
+
+hipError_t launch_router(const Geometry& g, const float* wr_rows, const float* bias, const StepBuffers& b,
+                         hipStream_t s) {
+  const dim3 grid((g.E + 1 + 3) / 4), block(256);
+  hipLaunchKernelGGL(router_kernel, grid, block, 0, s, g, wr_rows, bias, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const Geometry& g, const StepBuffers& b, int32_t* host_route, hipStream_t s) {
+  switch (npl_for(g.E)) {
+    case 1: hipLaunchKernelGGL(topk_kernel<1>, dim3(1), dim3(64), 0, s, g, b, host_route); break;
+    case 2: hipLaunchKernelGGL(topk_kernel<2>, dim3(1), dim3(64), 0, s, g, b, host_route); break;
+    case 4: hipLaunchKernelGGL(topk_kernel<4>, dim3(1), dim3(64), 0, s, g, b, host_route); break;
+    case 8: hipLaunchKernelGGL(topk_kernel<8>, dim3(1), dim3(64), 0, s, g, b, host_route); break;
+    case 16: hipLaunchKernelGGL(topk_kernel<16>, dim3(1), dim3(64), 0, s, g, b, host_route); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gateup(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec,
+                         const StepBuffers& b, hipStream_t s) {
+  return g.bits == 4 ? gateup_bits<4>(g, src, shared_rec, b, s) : gateup_bits<8>(g, src, shared_rec, b, s);
+}
+
+hipError_t launch_down(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                       const ResidualArgs& r, hipStream_t s) {
+  return g.bits == 4 ? down_bits<4>(g, src, shared_rec, b, r, s) : down_bits<8>(g, src, shared_rec, b, r, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,66 @@
+// Launchers of the HIP kernels (defined in decode.hip and prefill.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace moe {
+
+constexpr int kMaxTopK = 16;
+
+// Where the k routed experts of one step are read from.
+struct ExpertSource {
+  const uint8_t* base;   // routed records: resident blob, or the pool's slot arena
+  uint64_t stride;       // bytes between records
+  int64_t gid_base;      // resident: record index = gid_base + expert id
+  int32_t use_table;     // 1: record index of selection j is table[j] (pool slots)
+  int32_t pad_;
+  int64_t table[kMaxTopK];
+};
+
+struct Geometry {
+  int32_t H, I, E, k, bits, norm_topk;
+  // byte offsets inside a record
+  uint64_t gate_codes, up_codes, down_codes, gate_sc, up_sc, down_sc;
+};
+
+struct StepBuffers {
+  const uint16_t* x;      // bf16 [H] activations of this step
+  float* logits;          // [E+1]; entry E is the shared-gate logit
+  int32_t* route_idx;     // [k] selection of this step
+  float* route_w;         // [k]
+  float* route_gamma;     // [1] sigmoid(x . g_s)
+  float* h;               // [(k+1)][I] SwiGLU activations, slot k = shared expert
+};
+
+struct ResidualArgs {
+  float* out;             // plain layer: out[H]; stack: r_out[H]
+  const float* r_in;      // stack, layer > 0: r_l [H]; NULL otherwise
+  const uint16_t* x_res;  // stack, layer 0: r_0 = x0 (bf16 [H]); NULL otherwise
+  uint16_t* x_next;       // stack: bf16(r_{l+1}) [H], or NULL
+};
+
+// logits[e] = fp32( sum_h x[h] * wr[e][h] + bias[e] ) for e < E, accumulated in
+// fp64; logits[E] = the shared-gate logit (wr row E, no bias).
+hipError_t launch_router(const Geometry& g, const float* wr_rows, const float* bias, const StepBuffers& b,
+                         hipStream_t s);
+
+// Single-wave top-k + routing weights; writes route_idx/w/gamma to the device
+// buffers and, if host_route != NULL, the k indices to that host-visible
+// (pinned, mapped) buffer.
+hipError_t launch_topk(const Geometry& g, const StepBuffers& b, int32_t* host_route, hipStream_t s);
+
+// Gate/up GEMV + SwiGLU for the k routed experts and the shared expert.
+// Without a table, every wave re-derives the top-k from the logits; the first
+// wave also writes the route (idx, w, gamma).
+hipError_t launch_gateup(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec,
+                         const StepBuffers& b, hipStream_t s);
+
+// Down GEMV of the k + 1 experts, weighted combine, optional residual update.
+hipError_t launch_down(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                       const ResidualArgs& r, hipStream_t s);
+
+bool decode_shape_supported(const Geometry& g);
+
+}  // namespace moe

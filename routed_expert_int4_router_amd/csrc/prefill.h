@@ -1,0 +1,34 @@
+// Batched (prefill) path of the routed MoE step: router GEMM, top-k, bucketing
+// of (token, slot) pairs by expert, MFMA grouped GEMMs, combine.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.h"
+#include "moe.h"
+
+namespace moe {
+
+struct PrefillArgs {
+  moe_config cfg;
+  Geometry geo;
+  const uint8_t* experts;   // device, routed records of this layer (E records at stride)
+  uint64_t stride;
+  const uint8_t* shared;    // device, shared-expert record of this layer
+  const float* wr_rows;     // device [E+1][H]
+  const float* bias;        // device [E]
+  const uint16_t* x;        // device bf16 [n_tok][H]
+  int32_t n_tok;
+  float* out;               // device fp32 [n_tok][H]
+  int32_t* route_idx;       // device [n_tok][k]
+  float* route_w;           // device [n_tok][k]
+  float* route_gamma;       // device [n_tok]
+};
+
+bool prefill_supported(const moe_config& cfg);
+moe_status prefill_forward(void** workspace, const PrefillArgs& a, hipStream_t s);
+void prefill_free(void* workspace);
+
+}  // namespace moe

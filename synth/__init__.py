@@ -16,6 +16,7 @@ from .workload import (  # noqa: F401
     router_bias,
     shared_gate,
     tokens,
+    SynthWeights,
     f32_to_bf16_bits,
     bf16_bits_to_f32,
 )

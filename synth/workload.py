@@ -168,3 +168,29 @@ def tokens(seed: int, n_tokens: int, hidden: int, stream: int = 0) -> np.ndarray
         row = _rng(seed, _TOKEN_SLOT, stream, _TOKENS, t).standard_normal(hidden, dtype=np.float32)
         out[t] = f32_to_bf16_bits(row)
     return out
+
+
+class SynthWeights:
+    """The seeded fp32 weights of a config, in the shape a model loader asks for them."""
+
+    def __init__(self, cfg: Config):
+        self.cfg = cfg
+
+    def expert(self, layer: int, e: int):
+        c = self.cfg
+        return expert_weights(c.seed, layer, e, c.hidden, c.inter)
+
+    def shared(self, layer: int):
+        c = self.cfg
+        return shared_expert_weights(c.seed, layer, c.n_experts, c.hidden, c.shared_inter)
+
+    def router(self, layer: int) -> np.ndarray:
+        c = self.cfg
+        return router_weight(c.seed, layer, c.hidden, c.n_experts)
+
+    def bias(self, layer: int) -> Optional[np.ndarray]:
+        return router_bias(self.cfg, layer)
+
+    def shared_gate(self, layer: int) -> np.ndarray:
+        c = self.cfg
+        return shared_gate(c.seed, layer, c.hidden)
