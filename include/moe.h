@@ -54,11 +54,12 @@ typedef enum {
   MOE_ESTATE = -4  /* wrong, destroyed or mismatched handle, or call out of order */
 } moe_status;
 
-/* Shapes of one model. Valid when: bits is 4 or 8; group == 64; hidden,
- * inter and shared_inter are positive multiples of 64 with hidden a multiple
- * of 256 and inter, shared_inter multiples of 64 no larger than 4096;
- * 1 <= top_k <= min(n_experts, 16); 1 <= n_experts <= 4096; n_layers >= 1;
- * norm_topk is 0 or 1 (1: the top-k weights are renormalised to sum to 1). */
+/* Shapes of one model. Valid when: bits is 4 or 8; group == 64; hidden and
+ * inter are powers of two in [64, 4096] with hidden*bits <= 16384 and
+ * inter*bits <= 16384 (a code row holds at most 2048 bytes); shared_inter ==
+ * inter; 1 <= n_experts <= 1024; 1 <= top_k <= min(n_experts, 16);
+ * (top_k + 1) * inter <= 15360; 1 <= n_layers <= 4096; norm_topk is 0 or 1
+ * (1: the top-k weights are renormalised to sum to 1). */
 typedef struct {
   int32_t hidden;       /* H */
   int32_t n_experts;    /* E, routed experts per layer */
@@ -233,6 +234,24 @@ void moe_pool_destroy(moe_pool* p); /* NULL is a no-op */
  * Writes hit [n_steps*k] and victim [n_steps*k]. No GPU involved. */
 moe_status moe_pool_simulate(int64_t n_slots, int32_t k, int64_t n_steps, const int64_t* gids, uint8_t* hit,
                              int64_t* victim);
+
+/* ------------------------------------------------------------- profiling ---*/
+
+typedef struct {
+  char name[32];      /* kernel family: "router", "route", "gateup", "down", "prefill_*" */
+  uint64_t launches;  /* launches recorded */
+  double total_ms;    /* sum of per-launch durations (hipEvent pairs around each launch) */
+} moe_kernel_time_t;
+
+/* enable = 1: from now on record a hipEvent pair on the launch stream around
+ * every kernel this model launches (adds two event records per launch);
+ * enable = 0: stop recording. Errors: MOE_EINVAL, MOE_ESTATE. */
+moe_status moe_profile_enable(moe_model* m, int32_t enable);
+
+/* Wait for the recorded events, then return the per-kernel-family totals
+ * accumulated since profiling was enabled (or last read) and reset them.
+ * Copies min(cap, families) entries; *n receives the number of families. */
+moe_status moe_profile_read(moe_model* m, moe_kernel_time_t* out, size_t cap, size_t* n);
 
 /* --------------------------------------------------------------- errors ---*/
 const char* moe_last_error(void);

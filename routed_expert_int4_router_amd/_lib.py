@@ -26,7 +26,7 @@ EXPORTS = [
     "moe_model_create", "moe_model_set_layer", "moe_model_set_experts", "moe_model_host_blob",
     "moe_model_destroy", "moe_layer_forward", "moe_layer_decode", "moe_stack_decode", "moe_debug_routing",
     "moe_pool_create", "moe_pool_reset", "moe_pool_stats", "moe_pool_trace", "moe_pool_destroy",
-    "moe_pool_simulate", "moe_last_error",
+    "moe_pool_simulate", "moe_profile_enable", "moe_profile_read", "moe_last_error",
 ]
 
 
@@ -39,6 +39,10 @@ class MoeError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in
                 ("hidden", "n_experts", "top_k", "inter", "shared_inter", "bits", "group", "n_layers", "norm_topk")]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_uint64), ("total_ms", ctypes.c_double)]
 
 
 class PoolStats(ctypes.Structure):
@@ -89,6 +93,8 @@ def lib() -> ctypes.CDLL:
             "moe_pool_trace": (I32, [P, P, P, SZ, ctypes.POINTER(SZ)]),
             "moe_pool_destroy": (None, [P]),
             "moe_pool_simulate": (I32, [I64, I32, I64, P, P, P]),
+            "moe_profile_enable": (I32, [P, I32]),
+            "moe_profile_read": (I32, [P, ctypes.POINTER(KernelTime), SZ, ctypes.POINTER(SZ)]),
             "moe_last_error": (ctypes.c_char_p, []),
         }
         for name, (res, args) in sig.items():
@@ -252,6 +258,16 @@ class Model:
         n = x0.shape[0] if n_tok is None else n_tok
         _check(lib().moe_stack_decode(self._h, None if pool is None else pool.handle, _ptr(x0), n, _ptr(out),
                                       _stream(stream)))
+
+    def profile_enable(self, enable: bool = True):
+        _check(lib().moe_profile_enable(self._h, 1 if enable else 0))
+
+    def profile_read(self) -> dict:
+        """{kernel family: (launches, total_ms)} since enable / the last read."""
+        arr = (KernelTime * 32)()
+        n = ctypes.c_size_t()
+        _check(lib().moe_profile_read(self._h, arr, 32, ctypes.byref(n)))
+        return {arr[i].name.decode(): (int(arr[i].launches), float(arr[i].total_ms)) for i in range(min(32, n.value))}
 
     def debug_routing(self, cap: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
         n = ctypes.c_size_t()

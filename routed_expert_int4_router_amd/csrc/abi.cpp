@@ -57,6 +57,74 @@ moe_status hip_fail(hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(e_, what); \
   } while (0)
 
+// Optional per-launch timing: a hipEvent pair around every kernel launch.
+enum KernelKind { K_ROUTER, K_ROUTE, K_GATEUP, K_DOWN, K_PF_ROUTE, K_PF_BUCKET, K_PF_GATEUP, K_PF_DOWN, K_PF_COMBINE,
+                  K_COUNT };
+const char* const kKindName[K_COUNT] = {"router", "route", "gateup", "down", "prefill_route",
+                                        "prefill_bucket", "prefill_gateup", "prefill_down", "prefill_combine"};
+
+struct Profiler {
+  bool on = false;
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> spare;
+  uint64_t launches[K_COUNT] = {};
+  double ms[K_COUNT] = {};
+
+  hipEvent_t get() {
+    if (!spare.empty()) {
+      hipEvent_t e = spare.back();
+      spare.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+  hipError_t harvest() {
+    for (auto& r : pending) {
+      hipError_t e = hipEventSynchronize(r.b);
+      if (e != hipSuccess) return e;
+      float t = 0.f;
+      e = hipEventElapsedTime(&t, r.a, r.b);
+      if (e != hipSuccess) return e;
+      launches[r.kind] += 1;
+      ms[r.kind] += t;
+      spare.push_back(r.a);
+      spare.push_back(r.b);
+    }
+    pending.clear();
+    return hipSuccess;
+  }
+  // Launch `fn` (returning hipError_t) bracketed by events when profiling.
+  template <class F>
+  hipError_t run(int kind, hipStream_t s, F&& fn) {
+    if (!on) return fn();
+    if (pending.size() >= 4096) {
+      hipError_t e = harvest();
+      if (e != hipSuccess) return e;
+    }
+    Rec r{kind, get(), get()};
+    if (!r.a || !r.b) return hipErrorOutOfMemory;
+    hipError_t e = hipEventRecord(r.a, s);
+    if (e != hipSuccess) return e;
+    e = fn();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(r.b, s);
+    if (e != hipSuccess) return e;
+    pending.push_back(r);
+    return hipSuccess;
+  }
+  void release() {
+    harvest();
+    for (auto e : spare) hipEventDestroy(e);
+    spare.clear();
+  }
+};
+
 }  // namespace
 
 struct moe_model {
@@ -82,6 +150,19 @@ struct moe_model {
   size_t route_steps = 0;           // steps recorded by the last call
   std::vector<uint8_t> layer_set;
   void* prefill = nullptr;          // prefill workspace (prefill.hip)
+  Profiler prof;
+  // captured decode sequences, replayed with hipGraphLaunch (kernel arguments
+  // are baked in, so an entry is keyed by every pointer and size it used)
+  struct GraphEntry {
+    int kind, layer, n;
+    const void* x;
+    void* out;
+    hipGraphExec_t exec;
+    uint64_t stamp;
+  };
+  std::vector<GraphEntry> graphs;
+  hipStream_t cap_stream = nullptr;
+  uint64_t graph_clock = 0;
 };
 
 struct moe_pool {
@@ -111,10 +192,16 @@ moe_status check_pool(const moe_pool* p, const char* fn) {
   return MOE_OK;
 }
 
+void drop_graphs(moe_model* m) {
+  for (auto& g : m->graphs) hipGraphExecDestroy(g.exec);
+  m->graphs.clear();
+}
+
 moe_status ensure_route_cap(moe_model* m, size_t steps) {
   if (steps <= m->route_cap) return MOE_OK;
   size_t cap = std::max<size_t>(steps, 2 * m->route_cap);
   HIP_TRY(hipDeviceSynchronize(), "route log resize");
+  drop_graphs(m);  // captured kernels point at the old buffers
   hipFree(m->route_idx);
   hipFree(m->route_w);
   hipFree(m->route_gamma);
@@ -160,9 +247,12 @@ const uint8_t* layer_shared(moe_model* m, int layer) { return m->shared + (size_
 // One token through one layer on the decode kernels.
 moe_status decode_step(moe_model* m, int layer, const StepBuffers& b, const ExpertSource& src,
                        const ResidualArgs& r, hipStream_t s) {
-  HIP_TRY(launch_router(m->geo, layer_wr(m, layer), layer_bias(m, layer), b, s), "router launch");
-  HIP_TRY(launch_gateup(m->geo, src, layer_shared(m, layer), b, s), "gate/up launch");
-  HIP_TRY(launch_down(m->geo, src, layer_shared(m, layer), b, r, s), "down launch");
+  HIP_TRY(m->prof.run(K_ROUTER, s, [&] { return launch_router(m->geo, layer_wr(m, layer), layer_bias(m, layer), b, s); }),
+          "router launch");
+  HIP_TRY(m->prof.run(K_GATEUP, s, [&] { return launch_gateup(m->geo, src, layer_shared(m, layer), b, s); }),
+          "gate/up launch");
+  HIP_TRY(m->prof.run(K_DOWN, s, [&] { return launch_down(m->geo, src, layer_shared(m, layer), b, r, s); }),
+          "down launch");
   return MOE_OK;
 }
 
@@ -177,6 +267,48 @@ moe_status check_forward_args(moe_model* m, int32_t layer, const void* x, int32_
     return fail(MOE_ESTATE, std::string(fn) + ": experts are in host storage; use moe_stack_decode with a pool");
   if (n_tok > 0 && !m->layer_set[(size_t)layer])
     return fail(MOE_ESTATE, std::string(fn) + ": moe_model_set_layer was not called for this layer");
+  return MOE_OK;
+}
+
+// Token sequences at least this long are captured once into a HIP graph and
+// replayed (host launch work drops out of the per-token chain).
+constexpr int kGraphMinTokens = 64;
+constexpr size_t kGraphCacheSize = 8;
+
+template <class F>
+moe_status run_graph(moe_model* m, int kind, int layer, const void* x, void* out, int n, hipStream_t user,
+                     F&& enqueue) {
+  moe_model::GraphEntry* hit = nullptr;
+  for (auto& g : m->graphs)
+    if (g.kind == kind && g.layer == layer && g.n == n && g.x == x && g.out == out) hit = &g;
+  if (!hit) {
+    if (!m->cap_stream) HIP_TRY(hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking), "capture stream");
+    HIP_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal), "graph capture begin");
+    moe_status st = enqueue(m->cap_stream);
+    hipGraph_t graph = nullptr;
+    hipError_t e = hipStreamEndCapture(m->cap_stream, &graph);
+    if (st) {
+      if (graph) hipGraphDestroy(graph);
+      return st;
+    }
+    if (e != hipSuccess) return hip_fail(e, "graph capture end");
+    hipGraphExec_t exec = nullptr;
+    e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+    hipGraphDestroy(graph);
+    if (e != hipSuccess) return hip_fail(e, "graph instantiate");
+    if (m->graphs.size() >= kGraphCacheSize) {
+      auto lru = std::min_element(m->graphs.begin(), m->graphs.end(),
+                                  [](const moe_model::GraphEntry& a, const moe_model::GraphEntry& b) {
+                                    return a.stamp < b.stamp;
+                                  });
+      hipGraphExecDestroy(lru->exec);
+      m->graphs.erase(lru);
+    }
+    m->graphs.push_back({kind, layer, n, x, out, exec, 0});
+    hit = &m->graphs.back();
+  }
+  hit->stamp = ++m->graph_clock;
+  HIP_TRY(hipGraphLaunch(hit->exec, user), "graph launch");
   return MOE_OK;
 }
 
@@ -330,6 +462,9 @@ void moe_model_destroy(moe_model* m) {
   hipFree(m->route_w);
   hipFree(m->route_gamma);
   prefill_free(m->prefill);
+  m->prof.release();
+  drop_graphs(m);
+  if (m->cap_stream) hipStreamDestroy(m->cap_stream);
   m->magic = 0;
   live_del(m);
   delete m;
@@ -344,14 +479,19 @@ moe_status moe_layer_decode(moe_model* m, int32_t layer, const uint16_t* x, int3
   st = ensure_route_cap(m, (size_t)n_tok);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const size_t H = m->cfg.hidden;
-  const ExpertSource src = resident_source(m, layer);
-  for (int t = 0; t < n_tok; ++t) {
-    StepBuffers b = step_buffers(m, x + (size_t)t * H, (size_t)t);
-    ResidualArgs r{out + (size_t)t * H, nullptr, nullptr, nullptr};
-    st = decode_step(m, layer, b, src, r, s);
-    if (st) return st;
-  }
+  auto enqueue = [&](hipStream_t q) -> moe_status {
+    const size_t H = m->cfg.hidden;
+    const ExpertSource src = resident_source(m, layer);
+    for (int t = 0; t < n_tok; ++t) {
+      StepBuffers b = step_buffers(m, x + (size_t)t * H, (size_t)t);
+      ResidualArgs r{out + (size_t)t * H, nullptr, nullptr, nullptr};
+      moe_status e = decode_step(m, layer, b, src, r, q);
+      if (e) return e;
+    }
+    return MOE_OK;
+  };
+  st = (n_tok >= kGraphMinTokens && !m->prof.on) ? run_graph(m, 1, layer, x, out, n_tok, s, enqueue) : enqueue(s);
+  if (st) return st;
   m->route_steps = (size_t)n_tok;
   return MOE_OK;
 }
@@ -427,8 +567,14 @@ moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, in
         continue;
       }
       // pool: top-k on the device, then the host decides hits, misses and victims
-      HIP_TRY(launch_router(m->geo, layer_wr(m, l), layer_bias(m, l), b, s), "router launch");
-      HIP_TRY(launch_topk(m->geo, b, pool->host_route_dev, s), "top-k launch");
+      HIP_TRY(m->prof.run(K_ROUTER, s, [&] { return launch_router(m->geo, layer_wr(m, l), layer_bias(m, l), b, s); }),
+              "router launch");
+      HIP_TRY(m->prof.run(K_ROUTE, s,
+                          [&] {
+                            return launch_route(m->geo, b.logits, 0, 1, b.route_idx, b.route_w, b.route_gamma,
+                                                pool->host_route_dev, s);
+                          }),
+              "route launch");
       HIP_TRY(hipEventRecord(pool->route_ready, s), "event record");
       HIP_TRY(hipEventSynchronize(pool->route_ready), "route sync");
       for (int j = 0; j < k; ++j) gids[(size_t)j] = (int64_t)l * E + pool->host_route[j];
@@ -452,8 +598,10 @@ moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, in
         HIP_TRY(hipEventRecord(pool->copies_done, pool->copy_stream), "event record");
         HIP_TRY(hipStreamWaitEvent(s, pool->copies_done, 0), "stream wait");
       }
-      HIP_TRY(launch_gateup(m->geo, src, layer_shared(m, l), b, s), "gate/up launch");
-      HIP_TRY(launch_down(m->geo, src, layer_shared(m, l), b, r, s), "down launch");
+      HIP_TRY(m->prof.run(K_GATEUP, s, [&] { return launch_gateup(m->geo, src, layer_shared(m, l), b, s); }),
+              "gate/up launch");
+      HIP_TRY(m->prof.run(K_DOWN, s, [&] { return launch_down(m->geo, src, layer_shared(m, l), b, r, s); }),
+              "down launch");
     }
   }
   if (pool) HIP_TRY(hipStreamSynchronize(s), "moe_stack_decode: final sync");
@@ -472,6 +620,35 @@ moe_status moe_debug_routing(moe_model* m, int32_t* idx, float* w, size_t cap, s
   const size_t k = (size_t)m->cfg.top_k;
   if (n && idx) HIP_TRY(hipMemcpy(idx, m->route_idx, n * k * sizeof(int32_t), hipMemcpyDeviceToHost), "copy idx");
   if (n && w) HIP_TRY(hipMemcpy(w, m->route_w, n * k * sizeof(float), hipMemcpyDeviceToHost), "copy w");
+  return MOE_OK;
+}
+
+moe_status moe_profile_enable(moe_model* m, int32_t enable) {
+  clear_error();
+  moe_status st = check_model(m, "moe_profile_enable");
+  if (st) return st;
+  if (enable != 0 && enable != 1) return fail(MOE_EINVAL, "moe_profile_enable: enable must be 0 or 1");
+  m->prof.on = enable != 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_read(moe_model* m, moe_kernel_time_t* out, size_t cap, size_t* n) {
+  clear_error();
+  moe_status st = check_model(m, "moe_profile_read");
+  if (st) return st;
+  if (!n) return fail(MOE_EINVAL, "moe_profile_read: n is NULL");
+  HIP_TRY(m->prof.harvest(), "moe_profile_read: event wait");
+  *n = K_COUNT;
+  for (size_t i = 0; i < K_COUNT && i < cap && out; ++i) {
+    std::memset(out[i].name, 0, sizeof(out[i].name));
+    std::strncpy(out[i].name, kKindName[i], sizeof(out[i].name) - 1);
+    out[i].launches = m->prof.launches[i];
+    out[i].total_ms = m->prof.ms[i];
+  }
+  for (int i = 0; i < K_COUNT; ++i) {
+    m->prof.launches[i] = 0;
+    m->prof.ms[i] = 0.0;
+  }
   return MOE_OK;
 }
 

@@ -24,7 +24,9 @@
 
 #include <cstdint>
 
+#include "dpp.h"
 #include "kernels.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
@@ -87,106 +89,7 @@ __device__ __forceinline__ float chunk_dot(const uint4 c, const float* x) {
 
 template <int LPR>
 __device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
-__device__ __forceinline__ double wave_sum_f64(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
-// Total order key of a logit: larger key = larger logit; NaN ranks with -inf;
-// -0 ranks with +0. Key 0 is below every real logit (used for "removed").
-__device__ __forceinline__ uint32_t order_key(float v) {
-  if (v != v) v = -INFINITY;
-  if (v == 0.0f) v = 0.0f;
-  const uint32_t u = __float_as_uint(v);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float key_value(uint32_t k) {
-  const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
-  return __uint_as_float(u);
-}
-
-// Wave-wide top-k: every lane returns the same sel_e[j] / sel_l[j] for j < k,
-// ordered by (logit descending, index ascending).
-template <int NPL>
-__device__ __forceinline__ void wave_topk(const float* __restrict__ logits, int E, int k, int* sel_e,
-                                          float* sel_l) {
-  const int lane = threadIdx.x & (kWave - 1);
-  uint32_t key[NPL];
-#pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int e = lane + kWave * i;
-    key[i] = (e < E) ? order_key(logits[e]) : 0u;
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j < k) {
-      uint32_t bu = 0u;
-      uint32_t be = 0xFFFFFFFFu;
-#pragma unroll
-      for (int i = 0; i < NPL; ++i) {
-        if (key[i] > bu) {
-          bu = key[i];
-          be = (uint32_t)(lane + kWave * i);
-        }
-      }
-      uint32_t hi = bu, lo = ~be;  // max over (key, -index)
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t ohi = __shfl_xor(hi, off, kWave);
-        const uint32_t olo = __shfl_xor(lo, off, kWave);
-        if (ohi > hi || (ohi == hi && olo > lo)) {
-          hi = ohi;
-          lo = olo;
-        }
-      }
-      const int e = (int)(~lo);
-      sel_e[j] = e;
-      sel_l[j] = key_value(hi);
-#pragma unroll
-      for (int i = 0; i < NPL; ++i)
-        if (lane + kWave * i == e) key[i] = 0u;
-    }
-  }
-}
-
-// Routing weights of the selection: renormalised softmax over the k selected
-// logits (norm_topk = 1) or the plain softmax probabilities (norm_topk = 0).
-template <int NPL>
-__device__ __forceinline__ void route_weights(const float* __restrict__ logits, int E, int k, int norm_topk,
-                                              const float* sel_l, float* w) {
-  const float m = sel_l[0];
-  float z[kMaxTopK];
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    z[j] = (j < k) ? expf(sel_l[j] - m) : 0.f;
-    s += z[j];
-  }
-  if (!norm_topk) {
-    const int lane = threadIdx.x & (kWave - 1);
-    float part = 0.f;
-#pragma unroll
-    for (int i = 0; i < NPL; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E) part += expf(logits[e] - m);
-    }
-    s = wave_sum_f32(part);
-  }
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) w[j] = z[j] / s;
+  return dpp::group_sum<LPR>(v);
 }
 
 // ------------------------------------------------------------------ router ---
@@ -194,6 +97,7 @@ __device__ __forceinline__ void route_weights(const float* __restrict__ logits, 
 // 4 x bf16 steps. Products of a bf16 and an fp32 are exact in fp64, so the
 // fp64 sum rounded once to fp32 is the exactly rounded logit except in
 // vanishingly rare near-ties.
+template <int NIT>
 __global__ void __launch_bounds__(256) router_kernel(Geometry g, const float* __restrict__ wr,
                                                      const float* __restrict__ bias, StepBuffers b) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -201,43 +105,63 @@ __global__ void __launch_bounds__(256) router_kernel(Geometry g, const float* __
   if (row > g.E) return;
   const float4* w4 = reinterpret_cast<const float4*>(wr + (size_t)row * g.H);
   const uint2* x4 = reinterpret_cast<const uint2*>(b.x);
-  double acc = 0.0;
-  for (int i = lane; i < g.H / 4; i += kWave) {
-    const float4 w = w4[i];
-    const uint2 xv = x4[i];
-    acc += (double)bf16f(xv.x & 0xFFFFu) * (double)w.x;
-    acc += (double)bf16f(xv.x >> 16) * (double)w.y;
-    acc += (double)bf16f(xv.y & 0xFFFFu) * (double)w.z;
-    acc += (double)bf16f(xv.y >> 16) * (double)w.w;
+  const int n4 = g.H / 4;
+  float4 w[NIT];
+  uint2 xv[NIT];
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    const int i = min(lane + kWave * it, n4 - 1);  // clamped: every load issues unconditionally
+    w[it] = w4[i];
+    xv[it] = x4[i];
   }
-  acc = wave_sum_f64(acc);
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    if (lane + kWave * it >= n4) {
+      w[it] = make_float4(0.f, 0.f, 0.f, 0.f);
+      xv[it] = make_uint2(0u, 0u);
+    }
+  }
+  double acc = 0.0;
+#pragma unroll
+  for (int it = 0; it < NIT; ++it) {
+    acc += (double)bf16f(xv[it].x & 0xFFFFu) * (double)w[it].x;
+    acc += (double)bf16f(xv[it].x >> 16) * (double)w[it].y;
+    acc += (double)bf16f(xv[it].y & 0xFFFFu) * (double)w[it].z;
+    acc += (double)bf16f(xv[it].y >> 16) * (double)w[it].w;
+  }
+  acc = dpp::wave_sum(acc);
   if (lane == 0) {
     if (row < g.E && bias) acc += (double)bias[row];
     b.logits[row] = (float)acc;
   }
 }
 
-// -------------------------------------------------------------------- topk ---
+// ---------------------------------------------------------------- routing ---
+// One wave per token: top-k + weights + shared gate (route_* at token offsets).
+// Used where the route must exist before the expert kernels are launched: the
+// pool (the host reads the picks through host_route) and batched prefill.
 template <int NPL>
-__global__ void __launch_bounds__(64) topk_kernel(Geometry g, StepBuffers b, int32_t* host_route) {
-  int sel_e[kMaxTopK];
-  float sel_l[kMaxTopK], w[kMaxTopK];
-  wave_topk<NPL>(b.logits, g.E, g.k, sel_e, sel_l);
-  route_weights<NPL>(b.logits, g.E, g.k, g.norm_topk, sel_l, w);
-  const int lane = threadIdx.x;
-#pragma unroll
-  for (int j = 0; j < kMaxTopK; ++j) {
-    if (j < g.k && lane == j) {
-      b.route_idx[j] = sel_e[j];
-      b.route_w[j] = w[j];
-      if (host_route) host_route[j] = sel_e[j];
-    }
-  }
-  if (lane == 0) b.route_gamma[0] = 1.0f / (1.0f + expf(-b.logits[g.E]));
+__global__ void __launch_bounds__(64) route_kernel(Geometry g, const float* __restrict__ logits, int ld_logits,
+                                                   int32_t* route_idx, float* route_w, float* route_gamma,
+                                                   int32_t* host_route) {
+  __shared__ __align__(16) uint32_t lds[kRouteLds];
+  const int t = blockIdx.x;
+  const float* lg = logits + (size_t)t * ld_logits;
+  wave_route<NPL>(lg, g.E, g.k, g.norm_topk, lds, route_idx + (size_t)t * g.k, route_w + (size_t)t * g.k,
+                  host_route ? host_route + (size_t)t * g.k : nullptr);
+  if (threadIdx.x == 0) route_gamma[t] = 1.0f / (1.0f + expf(-lg[g.E]));
 }
 
+// Record of selection slot j: table[j] (pool slots) or gid_base + e (resident).
+// The table is read with static indices only (kernel-argument scalar loads);
+// a dynamic index would turn it into a dependent vector load.
 __device__ __forceinline__ const uint8_t* expert_record(const ExpertSource& src, int j, int e) {
-  const int64_t r = src.use_table ? src.table[j] : (src.gid_base + e);
+  int64_t r = src.gid_base + e;
+  if (src.use_table) {
+#pragma unroll
+    for (int q = 0; q < kMaxTopK; ++q)
+      if (q == j) r = src.table[q];
+  }
   return src.base + (uint64_t)r * src.stride;
 }
 
@@ -250,44 +174,52 @@ __global__ void __launch_bounds__(256) gateup_kernel(Geometry g, ExpertSource sr
                                                      StepBuffers b, int waves_per_expert, int total_waves) {
   constexpr int EPC = 128 / BITS;  // elements per 16-byte chunk
   constexpr int RPW = kWave / LPR;
-  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (wave >= total_waves) return;
+  __shared__ __align__(16) uint32_t lds_route[kRouteLds];
+  const int wave_raw = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  const bool idle = wave_raw >= total_waves;  // padding waves: join the barrier, then leave
+  const int wave = min(wave_raw, total_waves - 1);
   const int lane = threadIdx.x & 63;
-  const int j = wave / waves_per_expert;
+  const int j = __builtin_amdgcn_readfirstlane(wave / waves_per_expert);
   const int row0 = (wave % waves_per_expert) * (RPW * RW);
   const int rsub = lane / LPR, c0 = lane % LPR;
 
+  // Activations first: they do not depend on the routing, and loads issued
+  // before the weight loads can be waited on without waiting for the weights.
+  uint4 xraw[IT][EPC / 8];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const uint4* xp = reinterpret_cast<const uint4*>(b.x + (size_t)(c0 + LPR * it) * EPC);
+#pragma unroll
+    for (int q = 0; q < EPC / 8; ++q) xraw[it][q] = xp[q];
+  }
+
+  // Resident routing: wave 0 of the block computes the token's top-k and the
+  // block shares the picks through LDS (block 0 also publishes the route for
+  // the down kernel). Slots only grow with the wave index and slot k (the
+  // shared expert) is last, so "the block's first slot is routed" is uniform
+  // over the block and every wave reaches the barrier.
+  const int j_first = (blockIdx.x * 4) / waves_per_expert;
+  if (!src.use_table && j_first < g.k) {
+    if (threadIdx.x < 64) {
+      const bool pub = blockIdx.x == 0;
+      wave_route<NPL>(b.logits, g.E, g.k, g.norm_topk, lds_route, pub ? b.route_idx : nullptr,
+                      pub ? b.route_w : nullptr, nullptr);
+      if (pub && threadIdx.x == 0) b.route_gamma[0] = 1.0f / (1.0f + expf(-b.logits[g.E]));
+    }
+    __syncthreads();
+  }
+  if (idle) return;
   const uint8_t* rec;
   if (j == g.k) {
     rec = shared_rec;
   } else if (src.use_table) {
     rec = expert_record(src, j, 0);
   } else {
-    int sel_e[kMaxTopK];
-    float sel_l[kMaxTopK];
-    wave_topk<NPL>(b.logits, g.E, g.k, sel_e, sel_l);
-    int e = 0;
-#pragma unroll
-    for (int q = 0; q < kMaxTopK; ++q)
-      if (q == j) e = sel_e[q];
-    rec = expert_record(src, j, e);
-    if (wave == 0) {
-      float w[kMaxTopK];
-      route_weights<NPL>(b.logits, g.E, g.k, g.norm_topk, sel_l, w);
-#pragma unroll
-      for (int q = 0; q < kMaxTopK; ++q) {
-        if (q < g.k && lane == q) {
-          b.route_idx[q] = sel_e[q];
-          b.route_w[q] = w[q];
-        }
-      }
-      if (lane == 0) b.route_gamma[0] = 1.0f / (1.0f + expf(-b.logits[g.E]));
-    }
+    rec = expert_record(src, j, __builtin_amdgcn_readfirstlane((int)lds_route[kRouteOrdered + 2 * j + 1]));
   }
 
   const size_t row_bytes = (size_t)g.H * BITS / 8;
   const int groups = g.H / 64;
-  // issue all weight loads first
   uint4 cg[RW][IT], cu[RW][IT];
   uint32_t sg[RW][IT], su[RW][IT];
 #pragma unroll
@@ -305,24 +237,20 @@ __global__ void __launch_bounds__(256) gateup_kernel(Geometry g, ExpertSource sr
       su[rr][it] = *reinterpret_cast<const uint32_t*>(rec + g.up_sc + ((size_t)i * groups + grp) * 4);
     }
   }
-  // activations of this lane's chunks
   float xv[IT][EPC];
   float xs[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int ch = c0 + LPR * it;
-    const uint4* xp = reinterpret_cast<const uint4*>(b.x + (size_t)ch * EPC);
-    float s = 0.f;
 #pragma unroll
     for (int q = 0; q < EPC / 8; ++q) {
-      const uint4 v = xp[q];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t w[4] = {xraw[it][q].x, xraw[it][q].y, xraw[it][q].z, xraw[it][q].w};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         xv[it][8 * q + 2 * t] = bf16f(w[t] & 0xFFFFu);
         xv[it][8 * q + 2 * t + 1] = bf16f(w[t] >> 16);
       }
     }
+    float s = 0.f;
 #pragma unroll
     for (int q = 0; q < EPC; ++q) s += xv[it][q];
     xs[it] = s;
@@ -339,7 +267,7 @@ __global__ void __launch_bounds__(256) gateup_kernel(Geometry g, ExpertSource sr
     }
     ag = group_sum<LPR>(ag);
     au = group_sum<LPR>(au);
-    if (c0 == 0) {
+    if (c0 == LPR - 1) {
       const int i = row0 + rsub + RPW * rr;
       const float silu = ag / (1.0f + expf(-ag));
       b.h[(size_t)j * g.I + i] = silu * au;
@@ -350,40 +278,70 @@ __global__ void __launch_bounds__(256) gateup_kernel(Geometry g, ExpertSource sr
 // -------------------------------------------------------------------- down ---
 // Block: RPW * R output rows, 4 waves; wave w handles expert slots j = w, w+4, ...
 // (slot k = shared expert, weight gamma). Lane (r, c) owns chunks c + LPR * it of
-// rows r + RPW * rr. h of all k+1 slots is staged in LDS once per block.
+// rows r + RPW * rr. Each wave stages the h of its own slots in LDS.
 template <int BITS, int LPR, int IT, int R>
 __global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src, const uint8_t* __restrict__ shared_rec,
                                                    StepBuffers b, ResidualArgs res) {
   constexpr int EPC = 128 / BITS;
   constexpr int RPW = kWave / LPR;
   constexpr int RB = RPW * R;
+  constexpr int I = LPR * IT * EPC;                 // down rows hold I codes: LPR * IT chunks
+  constexpr int HU = I / 4 >= kWave ? I / 4 / kWave : 1;  // 1 KiB wave loads per slot's h
+  constexpr int RS = I >= 256 ? I : 256;            // LDS floats per slot (a wave load fills 1 KiB)
+  constexpr int MS = (kMaxTopK + 1 + 3) / 4;        // slots per wave at most (k <= 16)
   extern __shared__ __align__(16) float smem[];
-  float* sh_h = smem;                                 // [(k+1)][I]
-  float* sh_part = smem + (size_t)(g.k + 1) * g.I;    // [4][RB]
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int rsub = lane / LPR, c0 = lane % LPR;
   const int hrow0 = blockIdx.x * RB;
-  const size_t row_bytes = (size_t)g.I * BITS / 8;
-  const int groups = g.I / 64;
   const int nslots = g.k + 1;
+  const int msw = (nslots + 3) / 4;                 // slots per wave in use
+  float* sh_h = smem + (size_t)wv * msw * RS;       // this wave's slots: [msw][RS]
+  float* sh_part = smem + (size_t)4 * msw * RS;     // [4][RB]
+  const size_t row_bytes = (size_t)I * BITS / 8;
+  constexpr int groups = I / 64;
 
-  // issue weight loads of this wave's experts (up to 4 slots per wave: k <= 15)
-  constexpr int MS = (kMaxTopK + 1 + 3) / 4;  // 5
-  uint4 cd[MS][R][IT];
-  uint32_t sd[MS][R][IT];
+  // 1. the step's route (lane q < k holds slot q), one vector load per array
+  const int qk = min(lane, g.k - 1);
+  const int r_idx = src.use_table ? 0 : b.route_idx[qk];
+  const float r_w = b.route_w[qk];
+  const float r_gamma = b.route_gamma[0];
+  // 2. h of this wave's slots straight into LDS (global_load_lds: no registers,
+  //    in flight together with the weight loads below)
+#pragma unroll
+  for (int m = 0; m < MS; ++m) {
+    if (m < msw) {
+      const int j = min(wv + 4 * m, nslots - 1);
+#pragma unroll
+      for (int u = 0; u < HU; ++u) {
+        const float* gsrc = b.h + (size_t)j * I + 4 * min(lane + kWave * u, I / 4 - 1);
+        __builtin_amdgcn_global_load_lds(gsrc, (__attribute__((address_space(3))) void*)(sh_h + (size_t)m * RS + 256 * u),
+                                         16, 0, 0);
+      }
+    }
+  }
+  // 3. expert ids of this wave's slots, all read out before the first weight
+  //    load (the empty asm pins each id in an SGPR here, so the wait for the
+  //    route happens once instead of before every slot's loads)
   int e_of[MS];
 #pragma unroll
   for (int m = 0; m < MS; ++m) {
+    const int j = min(wv + 4 * m, g.k - 1);
+    e_of[m] = __builtin_amdgcn_readlane(r_idx, j);
+    asm volatile("" ::"s"(e_of[m]));
+  }
+  const uint8_t* recs[MS];
+#pragma unroll
+  for (int m = 0; m < MS; ++m) {
     const int j = wv + 4 * m;
-    e_of[m] = 0;
+    recs[m] = (j >= g.k) ? shared_rec : expert_record(src, j, e_of[m]);
+  }
+  uint4 cd[MS][R][IT];
+  uint32_t sd[MS][R][IT];
+#pragma unroll
+  for (int m = 0; m < MS; ++m) {
+    const int j = wv + 4 * m;
     if (j < nslots) {
-      const uint8_t* rec;
-      if (j == g.k) {
-        rec = shared_rec;
-      } else {
-        const int e = src.use_table ? 0 : b.route_idx[j];
-        rec = expert_record(src, j, e);
-      }
+      const uint8_t* rec = recs[m];
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
         const int hr = hrow0 + rsub + RPW * rr;
@@ -397,14 +355,9 @@ __global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src,
       }
     }
   }
-  // stage h
-  {
-    const int n4 = nslots * g.I / 4;
-    const float4* src4 = reinterpret_cast<const float4*>(b.h);
-    float4* dst4 = reinterpret_cast<float4*>(sh_h);
-    for (int q = threadIdx.x; q < n4; q += 256) dst4[q] = src4[q];
-  }
-  __syncthreads();
+  // 4. the LDS copies land through the vector-memory counter: wait for all loads
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_wave_barrier();
 
   float acc[R];
 #pragma unroll
@@ -413,12 +366,12 @@ __global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src,
   for (int m = 0; m < MS; ++m) {
     const int j = wv + 4 * m;
     if (j < nslots) {
-      const float wj = (j == g.k) ? b.route_gamma[0] : b.route_w[j];
+      const float wj = (j == g.k) ? r_gamma : __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(r_w), min(j, g.k - 1)));
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
         const int ch = c0 + LPR * it;
         float hv[EPC];
-        const float4* hp = reinterpret_cast<const float4*>(sh_h + (size_t)j * g.I + ch * EPC);
+        const float4* hp = reinterpret_cast<const float4*>(sh_h + (size_t)m * RS + ch * EPC);
 #pragma unroll
         for (int q = 0; q < EPC / 4; ++q) {
           const float4 v = hp[q];
@@ -442,7 +395,7 @@ __global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src,
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     const float v = group_sum<LPR>(acc[rr]);
-    if (c0 == 0) sh_part[wv * RB + rsub + RPW * rr] = v;
+    if (c0 == LPR - 1) sh_part[wv * RB + rsub + RPW * rr] = v;
   }
   __syncthreads();
   if (threadIdx.x < RB) {
@@ -461,18 +414,11 @@ __global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src,
 
 // ------------------------------------------------------------- dispatchers ---
 
-int npl_for(int E) {
-  int n = (E + 63) / 64;
-  int p = 1;
-  while (p < n) p <<= 1;
-  return p;
-}
-
 int lpr_for(int chunks) { return chunks < 64 ? chunks : 64; }
 
 template <int BITS, int LPR, int IT, int NPL>
-hipError_t gateup_rw(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
-                     hipStream_t s) {
+hipError_t gateup_rwn(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                      hipStream_t s) {
   constexpr int RPW = kWave / LPR;
   int rw = g.I / RPW;
   rw = rw >= 4 ? 4 : (rw >= 2 ? 2 : 1);
@@ -486,14 +432,14 @@ hipError_t gateup_rw(const Geometry& g, const ExpertSource& src, const uint8_t* 
 }
 
 template <int BITS, int LPR, int IT>
-hipError_t gateup_npl(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
-                      hipStream_t s) {
-  switch (npl_for(g.E)) {
-    case 1: return gateup_rw<BITS, LPR, IT, 1>(g, src, shared_rec, b, s);
-    case 2: return gateup_rw<BITS, LPR, IT, 2>(g, src, shared_rec, b, s);
-    case 4: return gateup_rw<BITS, LPR, IT, 4>(g, src, shared_rec, b, s);
-    case 8: return gateup_rw<BITS, LPR, IT, 8>(g, src, shared_rec, b, s);
-    case 16: return gateup_rw<BITS, LPR, IT, 16>(g, src, shared_rec, b, s);
+hipError_t gateup_rw(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                     hipStream_t s) {
+  switch (topk_npl(g.E)) {
+    case 1: return gateup_rwn<BITS, LPR, IT, 1>(g, src, shared_rec, b, s);
+    case 2: return gateup_rwn<BITS, LPR, IT, 2>(g, src, shared_rec, b, s);
+    case 4: return gateup_rwn<BITS, LPR, IT, 4>(g, src, shared_rec, b, s);
+    case 8: return gateup_rwn<BITS, LPR, IT, 8>(g, src, shared_rec, b, s);
+    case 16: return gateup_rwn<BITS, LPR, IT, 16>(g, src, shared_rec, b, s);
   }
   return hipErrorInvalidValue;
 }
@@ -505,15 +451,15 @@ hipError_t gateup_bits(const Geometry& g, const ExpertSource& src, const uint8_t
   const int lpr = lpr_for(chunks), it = chunks / lpr;
   if (it == 1) {
     switch (lpr) {
-      case 2: return gateup_npl<BITS, 2, 1>(g, src, shared_rec, b, s);
-      case 4: return gateup_npl<BITS, 4, 1>(g, src, shared_rec, b, s);
-      case 8: return gateup_npl<BITS, 8, 1>(g, src, shared_rec, b, s);
-      case 16: return gateup_npl<BITS, 16, 1>(g, src, shared_rec, b, s);
-      case 32: return gateup_npl<BITS, 32, 1>(g, src, shared_rec, b, s);
-      case 64: return gateup_npl<BITS, 64, 1>(g, src, shared_rec, b, s);
+      case 2: return gateup_rw<BITS, 2, 1>(g, src, shared_rec, b, s);
+      case 4: return gateup_rw<BITS, 4, 1>(g, src, shared_rec, b, s);
+      case 8: return gateup_rw<BITS, 8, 1>(g, src, shared_rec, b, s);
+      case 16: return gateup_rw<BITS, 16, 1>(g, src, shared_rec, b, s);
+      case 32: return gateup_rw<BITS, 32, 1>(g, src, shared_rec, b, s);
+      case 64: return gateup_rw<BITS, 64, 1>(g, src, shared_rec, b, s);
     }
   } else if (it == 2) {
-    return gateup_npl<BITS, 64, 2>(g, src, shared_rec, b, s);
+    return gateup_rw<BITS, 64, 2>(g, src, shared_rec, b, s);
   }
   return hipErrorInvalidValue;
 }
@@ -527,7 +473,8 @@ hipError_t down_r(const Geometry& g, const ExpertSource& src, const uint8_t* sha
   while (R > 1 && g.H % (RPW * R)) R >>= 1;
   const int RB = RPW * R;
   if (g.H % RB) return hipErrorInvalidValue;
-  const size_t lds = ((size_t)(g.k + 1) * g.I + 4 * RB) * sizeof(float);
+  const size_t rs = g.I >= 256 ? g.I : 256;
+  const size_t lds = ((size_t)4 * ((g.k + 1 + 3) / 4) * rs + 4 * RB) * sizeof(float);
   const dim3 grid(g.H / RB), block(256);
   if (R == 4) hipLaunchKernelGGL((down_kernel<BITS, LPR, IT, 4>), grid, block, lds, s, g, src, shared_rec, b, r);
   else if (R == 2) hipLaunchKernelGGL((down_kernel<BITS, LPR, IT, 2>), grid, block, lds, s, g, src, shared_rec, b, r);
@@ -569,17 +516,27 @@ bool decode_shape_supported(const Geometry& g) {
 hipError_t launch_router(const Geometry& g, const float* wr_rows, const float* bias, const StepBuffers& b,
                          hipStream_t s) {
   const dim3 grid((g.E + 1 + 3) / 4), block(256);
-  hipLaunchKernelGGL(router_kernel, grid, block, 0, s, g, wr_rows, bias, b);
+  const int nit = (g.H / 4 + kWave - 1) / kWave;  // float4 loads per lane
+  switch (nit) {
+    case 1: hipLaunchKernelGGL(router_kernel<1>, grid, block, 0, s, g, wr_rows, bias, b); break;
+    case 2: hipLaunchKernelGGL(router_kernel<2>, grid, block, 0, s, g, wr_rows, bias, b); break;
+    case 4: hipLaunchKernelGGL(router_kernel<4>, grid, block, 0, s, g, wr_rows, bias, b); break;
+    case 8: hipLaunchKernelGGL(router_kernel<8>, grid, block, 0, s, g, wr_rows, bias, b); break;
+    case 16: hipLaunchKernelGGL(router_kernel<16>, grid, block, 0, s, g, wr_rows, bias, b); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_topk(const Geometry& g, const StepBuffers& b, int32_t* host_route, hipStream_t s) {
-  switch (npl_for(g.E)) {
-    case 1: hipLaunchKernelGGL(topk_kernel<1>, dim3(1), dim3(64), 0, s, g, b, host_route); break;
-    case 2: hipLaunchKernelGGL(topk_kernel<2>, dim3(1), dim3(64), 0, s, g, b, host_route); break;
-    case 4: hipLaunchKernelGGL(topk_kernel<4>, dim3(1), dim3(64), 0, s, g, b, host_route); break;
-    case 8: hipLaunchKernelGGL(topk_kernel<8>, dim3(1), dim3(64), 0, s, g, b, host_route); break;
-    case 16: hipLaunchKernelGGL(topk_kernel<16>, dim3(1), dim3(64), 0, s, g, b, host_route); break;
+hipError_t launch_route(const Geometry& g, const float* logits, int ld_logits, int n_tok, int32_t* route_idx,
+                        float* route_w, float* route_gamma, int32_t* host_route, hipStream_t s) {
+  const dim3 grid(n_tok), block(64);
+  switch (topk_npl(g.E)) {
+    case 1: hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
+    case 2: hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
+    case 4: hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
+    case 8: hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
+    case 16: hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -46,14 +46,18 @@ struct ResidualArgs {
 hipError_t launch_router(const Geometry& g, const float* wr_rows, const float* bias, const StepBuffers& b,
                          hipStream_t s);
 
-// Single-wave top-k + routing weights; writes route_idx/w/gamma to the device
-// buffers and, if host_route != NULL, the k indices to that host-visible
-// (pinned, mapped) buffer.
-hipError_t launch_topk(const Geometry& g, const StepBuffers& b, int32_t* host_route, hipStream_t s);
+// Top-k routing of n_tok tokens, one wave each: logits row t at
+// logits + t * ld_logits (E + 1 entries, the last being the shared-gate logit);
+// writes route_idx/route_w [t][k] in selection order, route_gamma[t] =
+// sigmoid(shared-gate logit), and, when host_route is non-NULL (pinned,
+// device-visible), the picks there too.
+hipError_t launch_route(const Geometry& g, const float* logits, int ld_logits, int n_tok, int32_t* route_idx,
+                        float* route_w, float* route_gamma, int32_t* host_route, hipStream_t s);
 
-// Gate/up GEMV + SwiGLU for the k routed experts and the shared expert.
-// Without a table, every wave re-derives the top-k from the logits; the first
-// wave also writes the route (idx, w, gamma).
+// Gate/up GEMV + SwiGLU for the k routed experts and the shared expert -> h.
+// Resident source: each block routes the token from the logits itself (block 0
+// also writes route_idx/w/gamma for the down kernel). Table source (pool): the
+// records are the table's slots and the route must already be written.
 hipError_t launch_gateup(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec,
                          const StepBuffers& b, hipStream_t s);
 

@@ -37,9 +37,10 @@ std::string check_config(const moe_config* c) {
   if (c->shared_inter != c->inter) return "shared_inter must equal inter";
   if (c->hidden * c->bits > 16384 || c->inter * c->bits > 16384)
     return "a code row may hold at most 2048 bytes (hidden*bits and inter*bits <= 16384)";
-  if (c->n_experts < 1 || c->n_experts > 4096) return "n_experts must be in [1, 4096]";
+  if (c->n_experts < 1 || c->n_experts > 1024) return "n_experts must be in [1, 1024]";
   if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return "top_k must be in [1, min(n_experts, 16)]";
   if (c->n_layers < 1 || c->n_layers > 4096) return "n_layers must be in [1, 4096]";
+  if ((c->top_k + 1) * c->inter > 15360) return "(top_k + 1) * inter must be <= 15360";
   if (c->norm_topk != 0 && c->norm_topk != 1) return "norm_topk must be 0 or 1";
   return "";
 }
