@@ -519,8 +519,15 @@ moe_status moe_layer_forward(moe_model* m, int32_t layer, const uint16_t* x, int
     a.route_idx = m->route_idx;
     a.route_w = m->route_w;
     a.route_gamma = m->route_gamma;
-    st = prefill_forward(&m->prefill, a, static_cast<hipStream_t>(stream));
-    if (st) return st;
+    st = prefill_reserve(&m->prefill, m->cfg, n_tok);
+    if (st) return fail(st, "moe_layer_forward: prefill workspace allocation failed");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    void* ws = m->prefill;
+    HIP_TRY(m->prof.run(K_PF_ROUTE, s, [&] { return prefill_route(ws, a, s); }), "moe_layer_forward: route");
+    HIP_TRY(m->prof.run(K_PF_BUCKET, s, [&] { return prefill_bucket(ws, a, s); }), "moe_layer_forward: bucket");
+    HIP_TRY(m->prof.run(K_PF_GATEUP, s, [&] { return prefill_gateup(ws, a, s); }), "moe_layer_forward: gate/up");
+    HIP_TRY(m->prof.run(K_PF_DOWN, s, [&] { return prefill_down(ws, a, s); }), "moe_layer_forward: down");
+    HIP_TRY(m->prof.run(K_PF_COMBINE, s, [&] { return prefill_combine(ws, a, s); }), "moe_layer_forward: combine");
     m->route_steps = (size_t)n_tok;
     return MOE_OK;
   }

@@ -28,7 +28,17 @@ struct PrefillArgs {
 };
 
 bool prefill_supported(const moe_config& cfg);
-moe_status prefill_forward(void** workspace, const PrefillArgs& a, hipStream_t s);
+
+// Workspace for batches of up to n_tok tokens (grown on demand; synchronises
+// the device when it has to reallocate).
+moe_status prefill_reserve(void** workspace, const moe_config& cfg, int n_tok);
 void prefill_free(void* workspace);
+
+// The five stages, in order, on one stream.
+hipError_t prefill_route(void* workspace, const PrefillArgs& a, hipStream_t s);    // xsum, router GEMM, top-k
+hipError_t prefill_bucket(void* workspace, const PrefillArgs& a, hipStream_t s);   // stable sort of pairs by expert
+hipError_t prefill_gateup(void* workspace, const PrefillArgs& a, hipStream_t s);   // grouped gate/up GEMM + SwiGLU
+hipError_t prefill_down(void* workspace, const PrefillArgs& a, hipStream_t s);     // grouped down GEMM x weight
+hipError_t prefill_combine(void* workspace, const PrefillArgs& a, hipStream_t s);  // per-token sum
 
 }  // namespace moe

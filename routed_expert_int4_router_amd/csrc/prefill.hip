@@ -1,9 +1,707 @@
+// Batched (prefill) path of the routed MoE step for gfx950.
+//
+// The pages' runtime has no batched prefill: long prompts run token by token
+// (alphalab.site field test, FAQ item 4, and the method section on prompt
+// length). Here a batch of T tokens takes the layer in nine launches:
+//   xsum        per-token sums of x over each 64-group (bias term of the grid)
+//   router      logits [T][E+1] = x . W_r^T with bf16 MFMA on an exact
+//               three-way bf16 split of the fp32 router rows, fp32 accumulate
+//   route       top-k + weights + shared gate per token (one wave each)
+//   bucket x3   stable counting sort of the T*k (token, slot) pairs by expert
+//               (per-chunk counts, scan + tile list, scatter), deterministic
+//   gateup      grouped GEMM per (expert, 64-row tile, 64-column tile):
+//               int4 codes -> exact bf16 values 16 + q, bf16 MFMA, fp32
+//               per-group scaling acc += s * P + (c - 16 s) * xsum, SwiGLU in
+//               the epilogue, h stored as a bf16 hi/lo pair (+ per-group sums)
+//   down        grouped GEMM on h (hi and lo MFMA passes), router weight in
+//               the epilogue, one fp32 row per (token, slot) and per token
+//   combine     out[t] = sum_j y[t,j] + y_shared[t] in fixed order
+// Pages for the method itself: top-k routing, resident router and shared
+// expert, int4/int8 group quantisation (cheshm.ai news article, paragraphs on
+// how it works and on the code base).
 #include "prefill.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "dpp.h"
+#include "topk.h"
 
 namespace moe {
 
-bool prefill_supported(const moe_config&) { return false; }
-moe_status prefill_forward(void**, const PrefillArgs&, hipStream_t) { return MOE_EINVAL; }
-void prefill_free(void*) {}
+hipError_t launch_route(const Geometry& g, const float* logits, int ld_logits, int n_tok, int32_t* route_idx,
+                        float* route_w, float* route_gamma, int32_t* host_route, hipStream_t s);
+
+namespace {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int BM = 64;        // tile rows (tokens or pairs)
+constexpr int CHUNK = 256;    // pairs per bucketing chunk
+
+struct Workspace {
+  int T = 0, E = 0, k = 0, H = 0, I = 0;
+  float* logits = nullptr;      // [T][E+1]
+  float* xsum = nullptr;        // [T][H/64]
+  int32_t* cnt = nullptr;       // [nchunk][E]
+  int32_t* chunk_off = nullptr; // [nchunk][E]
+  int32_t* e_off = nullptr;     // [E+2]: start of each expert's rows; [E] = T*k (shared rows), [E+1] = T*k + T
+  int32_t* perm = nullptr;      // [T*k] sorted position -> pair id
+  int32_t* tiles = nullptr;     // [1 + max_tiles * 2]: count, then (expert, row0) per tile
+  uint16_t* h_hi = nullptr;     // [T*k + T][I]
+  uint16_t* h_lo = nullptr;
+  float* hsum = nullptr;        // [T*k + T][I/64]
+  float* y = nullptr;           // [T*k + T][H]
+  int max_tiles = 0;
+};
+
+__device__ __forceinline__ float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float f16f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+
+// Reorder the 8 bf16 of a 16-byte chunk (0,1,...,7) -> (0,4,1,5,2,6,3,7): the
+// k-order in which the nibble conversion below emits the codes of a dword.
+__device__ __forceinline__ uint4 perm8(uint4 v) {
+  uint4 o;
+  o.x = (v.x & 0xFFFFu) | (v.z << 16);                 // 0, 4
+  o.y = (v.x >> 16) | (v.z & 0xFFFF0000u);             // 1, 5
+  o.z = (v.y & 0xFFFFu) | (v.w << 16);                 // 2, 6
+  o.w = (v.y >> 16) | (v.w & 0xFFFF0000u);             // 3, 7
+  return o;
+}
+
+// 8 int4 codes of a dword -> bf16 values 16 + q in the order (0,4,1,5,2,6,3,7).
+__device__ __forceinline__ bf16x8 nib_to_bf16(uint32_t w) {
+  const uint32_t m = 0x00780078u, mag = 0x41804180u;
+  uint32_t d[4];
+  d[0] = ((w << 3) & m) | mag;
+  d[1] = ((w >> 1) & m) | mag;
+  d[2] = ((w >> 5) & m) | mag;
+  d[3] = ((w >> 9) & m) | mag;
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<uint4*>(d));
+}
+
+// ------------------------------------------------------------------- xsum ---
+__global__ void __launch_bounds__(256) xsum_kernel(const uint16_t* __restrict__ x, int T, int H, float* xsum) {
+  const int G = H / 64;
+  const int idx = blockIdx.x * 256 + threadIdx.x;  // one (token, group)
+  if (idx >= T * G) return;
+  const int t = idx / G, g = idx % G;
+  const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * H + 64 * g);
+  float s = 0.f;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const uint4 v = p[q];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s += bf16f(w[i] & 0xFFFFu) + bf16f(w[i] >> 16);
+  }
+  xsum[idx] = s;
+}
+
+// ------------------------------------------------------- router (MFMA) ---
+// fp32 value -> three bf16 whose exact sum is the value: the leading 8
+// significand bits, then those of the two rounding residuals (3 x 8 >= 24).
+__device__ __forceinline__ void split3(float v, uint16_t& a, uint16_t& b, uint16_t& c) {
+  a = to_bf16_rne(v);
+  const float r1 = v - bf16f(a);
+  b = to_bf16_rne(r1);
+  c = to_bf16_rne(r1 - bf16f(b));
+}
+
+// logits[t][e] = sum_h x[t][h] * w[e][h] (+ bias[e] for e < E), rows e <= E of
+// the fp32 router matrix (row E = shared gate). Each bf16 x fp32 product is
+// taken exactly as three bf16 x bf16 MFMA products; accumulation is fp32.
+// Block: 64 tokens x 64 rows, 4 waves of 32 x 32 (32x32x16 MFMA).
+__global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
+                                                          const float* __restrict__ bias, int T, int H, int E,
+                                                          float* logits) {
+  __shared__ __align__(16) uint16_t sa[64][72];
+  __shared__ __align__(16) uint16_t sb[3][64][72];
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = (wv >> 1) * 32, wn = (wv & 1) * 32;
+  const int R = E + 1;
+  f32x16 acc = {};
+  const int lr = threadIdx.x >> 2, lq = threadIdx.x & 3;  // staging: row, 16-element quarter
+  const int ta = min(t0 + lr, T - 1), eb = min(e0 + lr, R - 1);
+  const uint4* ga = reinterpret_cast<const uint4*>(x + (size_t)ta * H + 16 * lq);
+  const float4* gb = reinterpret_cast<const float4*>(w + (size_t)eb * H + 16 * lq);
+  for (int k0 = 0; k0 < H; k0 += 64) {
+    const uint4 a0 = ga[k0 / 8], a1 = ga[k0 / 8 + 1];
+    float4 b[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[q] = gb[k0 / 4 + q];
+    __syncthreads();
+    *reinterpret_cast<uint4*>(&sa[lr][16 * lq]) = a0;
+    *reinterpret_cast<uint4*>(&sa[lr][16 * lq + 8]) = a1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float v[4] = {b[q].x, b[q].y, b[q].z, b[q].w};
+      uint16_t hi[4], mid[4], lo[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) split3(v[i], hi[i], mid[i], lo[i]);
+      *reinterpret_cast<uint2*>(&sb[0][lr][16 * lq + 4 * q]) =
+          make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
+      *reinterpret_cast<uint2*>(&sb[1][lr][16 * lq + 4 * q]) =
+          make_uint2(mid[0] | ((uint32_t)mid[1] << 16), mid[2] | ((uint32_t)mid[3] << 16));
+      *reinterpret_cast<uint2*>(&sb[2][lr][16 * lq + 4 * q]) =
+          make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kk = 16 * s + 8 * (lane >> 5);
+      const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sa[wm + (lane & 31)][kk]);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&sb[p][wn + (lane & 31)][kk]);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+      }
+    }
+  }
+  const int n = e0 + wn + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = t0 + wm + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+    if (m < T && n < R) logits[(size_t)m * R + n] = acc[r] + ((n < E && bias) ? bias[n] : 0.f);
+  }
+}
+
+// ------------------------------------------------------------- bucketing ---
+__global__ void __launch_bounds__(CHUNK) bucket_count_kernel(const int32_t* __restrict__ idx, int P, int E, int32_t* cnt) {
+  extern __shared__ int32_t hist[];
+  for (int e = threadIdx.x; e < E; e += CHUNK) hist[e] = 0;
+  __syncthreads();
+  const int p = blockIdx.x * CHUNK + threadIdx.x;
+  if (p < P) atomicAdd(&hist[idx[p]], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += CHUNK) cnt[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+// One block: per-expert totals, expert offsets, per-chunk offsets and the tile
+// list (routed experts, then the shared expert over all T tokens).
+__global__ void __launch_bounds__(1024) bucket_scan_kernel(const int32_t* __restrict__ cnt, int nchunk, int E, int T,
+                                                           int k, int32_t* chunk_off, int32_t* e_off, int32_t* tiles,
+                                                           int max_tiles) {
+  __shared__ int32_t s_tot[1024], s_tiles[1024];
+  __shared__ int32_t s_base, s_tbase;
+  const int e = threadIdx.x;
+  int tot = 0;
+  if (e < E)
+    for (int c = 0; c < nchunk; ++c) tot += cnt[(size_t)c * E + e];
+  const int ntile = (tot + BM - 1) / BM;
+  // block-wide exclusive scans (sequential over waves, DPP within a wave)
+  const uint32_t inc_t = dpp::wave_prefix_u32((uint32_t)tot);
+  const uint32_t inc_n = dpp::wave_prefix_u32((uint32_t)ntile);
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 63) {
+    s_tot[wv] = (int)inc_t;
+    s_tiles[wv] = (int)inc_n;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int a = 0, b = 0;
+    for (int w = 0; w < 16; ++w) {
+      const int ta = s_tot[w], tb = s_tiles[w];
+      s_tot[w] = a;
+      s_tiles[w] = b;
+      a += ta;
+      b += tb;
+    }
+    s_base = a;
+    s_tbase = b;
+  }
+  __syncthreads();
+  const int off = s_tot[wv] + (int)inc_t - tot;
+  const int toff = s_tiles[wv] + (int)inc_n - ntile;
+  if (e < E) {
+    e_off[e] = off;
+    int run = off;
+    for (int c = 0; c < nchunk; ++c) {
+      chunk_off[(size_t)c * E + e] = run;
+      run += cnt[(size_t)c * E + e];
+    }
+    for (int i = 0; i < ntile; ++i) {
+      tiles[1 + 2 * (toff + i)] = e;
+      tiles[2 + 2 * (toff + i)] = i * BM;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    e_off[E] = s_base;         // == T * k
+    e_off[E + 1] = s_base + T;
+    const int nsh = (T + BM - 1) / BM;
+    for (int i = 0; i < nsh; ++i) {
+      tiles[1 + 2 * (s_tbase + i)] = E;
+      tiles[2 + 2 * (s_tbase + i)] = i * BM;
+    }
+    tiles[0] = min(s_tbase + nsh, max_tiles);
+  }
+}
+
+// Stable scatter: a pair's position is its chunk's offset for its expert plus
+// the number of earlier pairs of the same expert in the chunk.
+__global__ void __launch_bounds__(CHUNK) bucket_scatter_kernel(const int32_t* __restrict__ idx, int P, int E,
+                                                               const int32_t* __restrict__ chunk_off, int32_t* perm) {
+  __shared__ int32_t s_e[CHUNK];
+  const int p = blockIdx.x * CHUNK + threadIdx.x;
+  const int e = p < P ? idx[p] : -1;
+  s_e[threadIdx.x] = e;
+  __syncthreads();
+  if (p >= P) return;
+  int rank = 0;
+  for (int q = 0; q < (int)threadIdx.x; ++q) rank += (s_e[q] == e) ? 1 : 0;
+  perm[chunk_off[(size_t)blockIdx.x * E + e] + rank] = p;
+}
+
+// ------------------------------------------------------- grouped GEMM 1 ---
+// Block (tile, n-tile): 64 rows of one expert (pairs in sorted order, or tokens
+// for the shared expert) x 64 intermediate columns, gate and up. Waves 0,1:
+// gate columns [n0, n0+32), [n0+32, n0+64); waves 2,3: up. Each wave computes
+// 64 x 32 with 32x32x16 MFMAs; K runs over the 64-groups of H.
+struct GemmArgs {
+  const uint16_t* x;          // [T][H]
+  const float* xsum;          // [T][H/64]
+  const uint8_t* experts;     // routed records of the layer
+  const uint8_t* shared;      // shared record
+  uint64_t stride;
+  uint64_t gate_codes, up_codes, down_codes, gate_sc, up_sc, down_sc;
+  const int32_t* e_off;       // [E+2]
+  const int32_t* perm;        // [T*k]
+  const int32_t* tiles;
+  const float* route_w;       // [T*k]
+  const float* route_gamma;   // [T]
+  uint16_t* h_hi;
+  uint16_t* h_lo;
+  float* hsum;
+  float* y;
+  int T, H, I, E, k;
+};
+
+__global__ void __launch_bounds__(256) gemm_gateup_kernel(GemmArgs a) {
+  __shared__ __align__(16) uint16_t sx[2][BM][72];     // A tiles (k-permuted), double buffered
+  __shared__ __align__(16) float sxs[64][BM];           // xsum of the tile rows per group (G <= 64)
+  __shared__ __align__(16) float sg[BM][65];            // gate results for the SwiGLU exchange
+  __shared__ int32_t s_tok[BM];
+  const int ntiles = a.tiles[0];
+  if ((int)blockIdx.x >= ntiles) return;
+  const int e = a.tiles[1 + 2 * blockIdx.x], r0 = a.tiles[2 + 2 * blockIdx.x];
+  const int n0 = blockIdx.y * 64;
+  const int rows = a.e_off[e + 1] - a.e_off[e];
+  const int G = a.H / 64;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
+
+  if (threadIdx.x < BM) {
+    const int r = r0 + threadIdx.x;
+    int tok = -1;
+    if (r < rows) tok = e < a.E ? a.perm[a.e_off[e] + r] / a.k : r;
+    s_tok[threadIdx.x] = tok;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < G * BM; q += 256) {
+    const int g = q / BM, m = q % BM;
+    const int tok = s_tok[m];
+    sxs[g][m] = tok >= 0 ? a.xsum[(size_t)tok * G + g] : 0.f;
+  }
+  // staging map: thread -> row lr, 16-element quarter lq of the 64-wide K slice
+  const int lr = threadIdx.x >> 2, lq = threadIdx.x & 3;
+  const int stok = s_tok[lr];
+  const uint4* xrow = reinterpret_cast<const uint4*>(a.x + (size_t)max(stok, 0) * a.H + 16 * lq);
+  auto load_a = [&](int g, uint4& v0, uint4& v1) {
+    if (stok >= 0) {
+      v0 = xrow[8 * g];
+      v1 = xrow[8 * g + 1];
+    } else {
+      v0 = make_uint4(0, 0, 0, 0);
+      v1 = v0;
+    }
+  };
+  // B: this wave's matrix and column
+  const int mat = wv >> 1;
+  const int n = n0 + 32 * (wv & 1) + (lane & 31);
+  const int hh = lane >> 5;
+  const size_t row_bytes = (size_t)a.H / 2;
+  const uint8_t* crow = rec + (mat ? a.up_codes : a.gate_codes) + (size_t)n * row_bytes + 16 * hh;
+  const uint32_t* scrow = reinterpret_cast<const uint32_t*>(rec + (mat ? a.up_sc : a.gate_sc)) + (size_t)n * G;
+
+  f32x16 acc0 = {}, acc1 = {};
+  uint4 av0, av1;
+  load_a(0, av0, av1);
+  uint4 cb = *reinterpret_cast<const uint4*>(crow);
+  uint32_t scv = scrow[0];
+  *reinterpret_cast<uint4*>(&sx[0][lr][16 * lq]) = perm8(av0);
+  *reinterpret_cast<uint4*>(&sx[0][lr][16 * lq + 8]) = perm8(av1);
+  __syncthreads();
+  for (int g = 0; g < G; ++g) {
+    const int buf = g & 1;
+    uint4 nv0, nv1, ncb;
+    uint32_t nsc = 0;
+    if (g + 1 < G) {
+      load_a(g + 1, nv0, nv1);
+      ncb = *reinterpret_cast<const uint4*>(crow + 32 * (g + 1));
+      nsc = scrow[g + 1];
+    }
+    const bf16x8 b0 = nib_to_bf16(cb.x), b1 = nib_to_bf16(cb.y), b2 = nib_to_bf16(cb.z), b3 = nib_to_bf16(cb.w);
+    f32x16 p0 = {}, p1 = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kk = 32 * hh + 8 * s;
+      const bf16x8 bv = s == 0 ? b0 : (s == 1 ? b1 : (s == 2 ? b2 : b3));
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sx[buf][(lane & 31)][kk]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sx[buf][32 + (lane & 31)][kk]);
+      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bv, p0, 0, 0, 0);
+      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bv, p1, 0, 0, 0);
+    }
+    const float sv = f16f(scv & 0xFFFFu), cv = f16f(scv >> 16) - 16.0f * f16f(scv & 0xFFFFu);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
+      acc0[r] += sv * p0[r] + cv * sxs[g][m];
+      acc1[r] += sv * p1[r] + cv * sxs[g][32 + m];
+    }
+    if (g + 1 < G) {
+      *reinterpret_cast<uint4*>(&sx[buf ^ 1][lr][16 * lq]) = perm8(nv0);
+      *reinterpret_cast<uint4*>(&sx[buf ^ 1][lr][16 * lq + 8]) = perm8(nv1);
+      cb = ncb;
+      scv = nsc;
+    }
+    __syncthreads();
+  }
+  // SwiGLU: gate waves publish, up waves combine and store
+  const int nl = 32 * (wv & 1) + (lane & 31);
+  if (mat == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
+      sg[m][nl] = acc0[r];
+      sg[32 + m][nl] = acc1[r];
+    }
+  }
+  __syncthreads();
+  const int base = a.e_off[e] + r0;
+  if (mat == 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m0 = (r >> 2) * 8 + hh * 4 + (r & 3);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int m = m0 + 32 * half;
+        if (r0 + m < rows) {
+          const float gt = sg[m][nl];
+          const float u = half ? acc1[r] : acc0[r];
+          const float hv = gt / (1.0f + expf(-gt)) * u;
+          const uint16_t hi = to_bf16_rne(hv);
+          const uint16_t lo = to_bf16_rne(hv - bf16f(hi));
+          const size_t o = (size_t)(base + m) * a.I + n0 + nl;
+          a.h_hi[o] = hi;
+          a.h_lo[o] = lo;
+          sg[m][nl] = bf16f(hi) + bf16f(lo);  // what the down GEMM multiplies
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // per-row sum of this 64-column group of h (the down matrix's quant group)
+  if (threadIdx.x < BM) {
+    const int m = threadIdx.x;
+    if (r0 + m < rows) {
+      float s = 0.f;
+      for (int c = 0; c < 64; ++c) s += sg[m][c];
+      a.hsum[(size_t)(base + m) * (a.I / 64) + n0 / 64] = s;
+    }
+  }
+}
+
+// ------------------------------------------------------- grouped GEMM 2 ---
+// Block (tile, n-tile): 64 rows x 128 output columns; wave w owns columns
+// [n0 + 32w, n0 + 32w + 32). A = h (hi and lo passes), K over the 64-groups of I.
+__global__ void __launch_bounds__(256) gemm_down_kernel(GemmArgs a) {
+  __shared__ __align__(16) uint16_t shi[2][BM][72];
+  __shared__ __align__(16) uint16_t slo[2][BM][72];
+  __shared__ __align__(16) float shs[64][BM];
+  __shared__ int32_t s_dst[BM];
+  __shared__ float s_w[BM];
+  const int ntiles = a.tiles[0];
+  if ((int)blockIdx.x >= ntiles) return;
+  const int e = a.tiles[1 + 2 * blockIdx.x], r0 = a.tiles[2 + 2 * blockIdx.x];
+  const int n0 = blockIdx.y * 128;
+  const int rows = a.e_off[e + 1] - a.e_off[e];
+  const int base = a.e_off[e] + r0;
+  const int G = a.I / 64;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
+  if (threadIdx.x < BM) {
+    const int r = r0 + threadIdx.x;
+    int dst = -1;
+    float w = 0.f;
+    if (r < rows) {
+      if (e < a.E) {
+        const int p = a.perm[a.e_off[e] + r];
+        dst = p;
+        w = a.route_w[p];
+      } else {
+        dst = a.T * a.k + r;
+        w = a.route_gamma[r];
+      }
+    }
+    s_dst[threadIdx.x] = dst;
+    s_w[threadIdx.x] = w;
+  }
+  for (int q = threadIdx.x; q < G * BM; q += 256) {
+    const int g = q / BM, m = q % BM;
+    shs[g][m] = (r0 + m < rows) ? a.hsum[(size_t)(base + m) * G + g] : 0.f;
+  }
+  const int lr = threadIdx.x >> 2, lq = threadIdx.x & 3;
+  const bool rv = r0 + lr < rows;
+  const uint4* hrow = reinterpret_cast<const uint4*>(a.h_hi + (size_t)(rv ? base + lr : 0) * a.I + 16 * lq);
+  const uint4* lrow = reinterpret_cast<const uint4*>(a.h_lo + (size_t)(rv ? base + lr : 0) * a.I + 16 * lq);
+  auto load_a = [&](int g, uint4& h0, uint4& h1, uint4& l0, uint4& l1) {
+    if (rv) {
+      h0 = hrow[8 * g];
+      h1 = hrow[8 * g + 1];
+      l0 = lrow[8 * g];
+      l1 = lrow[8 * g + 1];
+    } else {
+      h0 = h1 = l0 = l1 = make_uint4(0, 0, 0, 0);
+    }
+  };
+  const int n = n0 + 32 * wv + (lane & 31);
+  const int hh = lane >> 5;
+  const size_t row_bytes = (size_t)a.I / 2;
+  const uint8_t* crow = rec + a.down_codes + (size_t)n * row_bytes + 16 * hh;
+  const uint32_t* scrow = reinterpret_cast<const uint32_t*>(rec + a.down_sc) + (size_t)n * G;
+
+  f32x16 acc0 = {}, acc1 = {};
+  uint4 h0, h1, l0, l1;
+  load_a(0, h0, h1, l0, l1);
+  uint4 cb = *reinterpret_cast<const uint4*>(crow);
+  uint32_t scv = scrow[0];
+  *reinterpret_cast<uint4*>(&shi[0][lr][16 * lq]) = perm8(h0);
+  *reinterpret_cast<uint4*>(&shi[0][lr][16 * lq + 8]) = perm8(h1);
+  *reinterpret_cast<uint4*>(&slo[0][lr][16 * lq]) = perm8(l0);
+  *reinterpret_cast<uint4*>(&slo[0][lr][16 * lq + 8]) = perm8(l1);
+  __syncthreads();
+  for (int g = 0; g < G; ++g) {
+    const int buf = g & 1;
+    uint4 nh0, nh1, nl0, nl1, ncb;
+    uint32_t nsc = 0;
+    if (g + 1 < G) {
+      load_a(g + 1, nh0, nh1, nl0, nl1);
+      ncb = *reinterpret_cast<const uint4*>(crow + 32 * (g + 1));
+      nsc = scrow[g + 1];
+    }
+    const bf16x8 b0 = nib_to_bf16(cb.x), b1 = nib_to_bf16(cb.y), b2 = nib_to_bf16(cb.z), b3 = nib_to_bf16(cb.w);
+    f32x16 p0 = {}, p1 = {};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int kk = 32 * hh + 8 * s;
+      const bf16x8 bv = s == 0 ? b0 : (s == 1 ? b1 : (s == 2 ? b2 : b3));
+      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&shi[buf][(lane & 31)][kk]);
+      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&shi[buf][32 + (lane & 31)][kk]);
+      const bf16x8 c0 = *reinterpret_cast<const bf16x8*>(&slo[buf][(lane & 31)][kk]);
+      const bf16x8 c1 = *reinterpret_cast<const bf16x8*>(&slo[buf][32 + (lane & 31)][kk]);
+      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bv, p0, 0, 0, 0);
+      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bv, p1, 0, 0, 0);
+      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c0, bv, p0, 0, 0, 0);
+      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1, bv, p1, 0, 0, 0);
+    }
+    const float sv = f16f(scv & 0xFFFFu), cv = f16f(scv >> 16) - 16.0f * f16f(scv & 0xFFFFu);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
+      acc0[r] += sv * p0[r] + cv * shs[g][m];
+      acc1[r] += sv * p1[r] + cv * shs[g][32 + m];
+    }
+    if (g + 1 < G) {
+      *reinterpret_cast<uint4*>(&shi[buf ^ 1][lr][16 * lq]) = perm8(nh0);
+      *reinterpret_cast<uint4*>(&shi[buf ^ 1][lr][16 * lq + 8]) = perm8(nh1);
+      *reinterpret_cast<uint4*>(&slo[buf ^ 1][lr][16 * lq]) = perm8(nl0);
+      *reinterpret_cast<uint4*>(&slo[buf ^ 1][lr][16 * lq + 8]) = perm8(nl1);
+      cb = ncb;
+      scv = nsc;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m0 = (r >> 2) * 8 + hh * 4 + (r & 3);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int m = m0 + 32 * half;
+      const int dst = s_dst[m];
+      if (dst >= 0) a.y[(size_t)dst * a.H + n] = s_w[m] * (half ? acc1[r] : acc0[r]);
+    }
+  }
+}
+
+// ------------------------------------------------------------------ combine ---
+__global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ y, int T, int k, int H, float* out) {
+  const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;  // one float4 of one token
+  const size_t per = (size_t)H / 4;
+  if (q >= (size_t)T * per) return;
+  const size_t t = q / per, c = q % per;
+  const float4* y4 = reinterpret_cast<const float4*>(y);
+  float4 s = y4[(t * k) * per + c];
+  for (int j = 1; j < k; ++j) {
+    const float4 v = y4[(t * k + j) * per + c];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  const float4 v = y4[((size_t)T * k + t) * per + c];
+  s.x += v.x;
+  s.y += v.y;
+  s.z += v.z;
+  s.w += v.w;
+  reinterpret_cast<float4*>(out)[q] = s;
+}
+
+template <class T>
+bool grow(T*& p, size_t n) {
+  hipFree(p);
+  p = nullptr;
+  return hipMalloc(&p, (n ? n : 1) * sizeof(T)) == hipSuccess;
+}
+
+Workspace* ws_of(void* p) { return static_cast<Workspace*>(p); }
+
+GemmArgs gemm_args(const Workspace* w, const PrefillArgs& pa) {
+  GemmArgs ga{};
+  ga.x = pa.x;
+  ga.xsum = w->xsum;
+  ga.experts = pa.experts;
+  ga.shared = pa.shared;
+  ga.stride = pa.stride;
+  ga.gate_codes = pa.geo.gate_codes;
+  ga.up_codes = pa.geo.up_codes;
+  ga.down_codes = pa.geo.down_codes;
+  ga.gate_sc = pa.geo.gate_sc;
+  ga.up_sc = pa.geo.up_sc;
+  ga.down_sc = pa.geo.down_sc;
+  ga.e_off = w->e_off;
+  ga.perm = w->perm;
+  ga.tiles = w->tiles;
+  ga.route_w = pa.route_w;
+  ga.route_gamma = pa.route_gamma;
+  ga.h_hi = w->h_hi;
+  ga.h_lo = w->h_lo;
+  ga.hsum = w->hsum;
+  ga.y = w->y;
+  ga.T = pa.n_tok;
+  ga.H = pa.cfg.hidden;
+  ga.I = pa.cfg.inter;
+  ga.E = pa.cfg.n_experts;
+  ga.k = pa.cfg.top_k;
+  return ga;
+}
+
+int n_chunks(const PrefillArgs& pa) { return (pa.n_tok * pa.cfg.top_k + CHUNK - 1) / CHUNK; }
+
+}  // namespace
+
+bool prefill_supported(const moe_config& cfg) {
+  return cfg.bits == 4 && cfg.hidden % 128 == 0 && cfg.inter % 64 == 0 && cfg.hidden / 64 <= 64 &&
+         cfg.inter / 64 <= 64 && cfg.n_experts <= 1024 && cfg.top_k <= kTopkMax;
+}
+
+void prefill_free(void* ws) {
+  if (!ws) return;
+  Workspace* w = ws_of(ws);
+  hipFree(w->logits);
+  hipFree(w->xsum);
+  hipFree(w->cnt);
+  hipFree(w->chunk_off);
+  hipFree(w->e_off);
+  hipFree(w->perm);
+  hipFree(w->tiles);
+  hipFree(w->h_hi);
+  hipFree(w->h_lo);
+  hipFree(w->hsum);
+  hipFree(w->y);
+  delete w;
+}
+
+moe_status prefill_reserve(void** wsp, const moe_config& c, int T) {
+  Workspace* w = ws_of(*wsp);
+  if (!w) {
+    w = new Workspace();
+    *wsp = w;
+  }
+  const int E = c.n_experts, k = c.top_k, H = c.hidden, I = c.inter;
+  if (w->T >= T && w->E == E && w->k == k && w->H == H && w->I == I) return MOE_OK;
+  if (hipDeviceSynchronize() != hipSuccess) return MOE_EHIP;
+  const size_t P = (size_t)T * k, rows = P + T;
+  const int nchunk = (int)((P + CHUNK - 1) / CHUNK);
+  const int max_tiles = (int)((P + BM - 1) / BM) + E + (T + BM - 1) / BM;
+  w->T = 0;  // invalid until every buffer is in place
+  const bool ok = grow(w->logits, (size_t)T * (E + 1)) && grow(w->xsum, (size_t)T * (H / 64)) &&
+                  grow(w->cnt, (size_t)nchunk * E) && grow(w->chunk_off, (size_t)nchunk * E) &&
+                  grow(w->e_off, (size_t)E + 2) && grow(w->perm, P) && grow(w->tiles, (size_t)1 + 2 * max_tiles) &&
+                  grow(w->h_hi, rows * I) && grow(w->h_lo, rows * I) && grow(w->hsum, rows * (I / 64)) &&
+                  grow(w->y, rows * H);
+  if (!ok) return MOE_ENOMEM;
+  w->T = T;
+  w->E = E;
+  w->k = k;
+  w->H = H;
+  w->I = I;
+  w->max_tiles = max_tiles;
+  return MOE_OK;
+}
+
+hipError_t prefill_route(void* ws, const PrefillArgs& pa, hipStream_t s) {
+  Workspace* w = ws_of(ws);
+  const int T = pa.n_tok, H = pa.cfg.hidden, E = pa.cfg.n_experts;
+  hipLaunchKernelGGL(xsum_kernel, dim3((T * (H / 64) + 255) / 256), dim3(256), 0, s, pa.x, T, H, w->xsum);
+  hipLaunchKernelGGL(router_gemm_kernel, dim3((T + 63) / 64, (E + 1 + 63) / 64), dim3(256), 0, s, pa.x, pa.wr_rows,
+                     pa.bias, T, H, E, w->logits);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_route(pa.geo, w->logits, E + 1, T, pa.route_idx, pa.route_w, pa.route_gamma, nullptr, s);
+}
+
+hipError_t prefill_bucket(void* ws, const PrefillArgs& pa, hipStream_t s) {
+  Workspace* w = ws_of(ws);
+  const int T = pa.n_tok, E = pa.cfg.n_experts, k = pa.cfg.top_k, P = T * k, nchunk = n_chunks(pa);
+  hipLaunchKernelGGL(bucket_count_kernel, dim3(nchunk), dim3(CHUNK), E * sizeof(int32_t), s, pa.route_idx, P, E,
+                     w->cnt);
+  hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, w->cnt, nchunk, E, T, k, w->chunk_off, w->e_off,
+                     w->tiles, w->max_tiles);
+  hipLaunchKernelGGL(bucket_scatter_kernel, dim3(nchunk), dim3(CHUNK), 0, s, pa.route_idx, P, E, w->chunk_off,
+                     w->perm);
+  return hipGetLastError();
+}
+
+hipError_t prefill_gateup(void* ws, const PrefillArgs& pa, hipStream_t s) {
+  Workspace* w = ws_of(ws);
+  hipLaunchKernelGGL(gemm_gateup_kernel, dim3(w->max_tiles, pa.cfg.inter / 64), dim3(256), 0, s, gemm_args(w, pa));
+  return hipGetLastError();
+}
+
+hipError_t prefill_down(void* ws, const PrefillArgs& pa, hipStream_t s) {
+  Workspace* w = ws_of(ws);
+  hipLaunchKernelGGL(gemm_down_kernel, dim3(w->max_tiles, pa.cfg.hidden / 128), dim3(256), 0, s, gemm_args(w, pa));
+  return hipGetLastError();
+}
+
+hipError_t prefill_combine(void* ws, const PrefillArgs& pa, hipStream_t s) {
+  Workspace* w = ws_of(ws);
+  const size_t n4 = (size_t)pa.n_tok * pa.cfg.hidden / 4;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, w->y, pa.n_tok,
+                     pa.cfg.top_k, pa.cfg.hidden, pa.out);
+  return hipGetLastError();
+}
 
 }  // namespace moe

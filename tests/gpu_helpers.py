@@ -4,9 +4,11 @@ the comparison rules against the oracle.
 Matching rules:
 * top-k selections are bit-exact, except where the oracle's exactly rounded
   logits of the two differing experts lie within
-  eps = 2^-16 * sum_h |x_h * W_r[h, e]| of each other (an fp32-vs-exact
+  eps = eps_rel * sum_h |x_h * W_r[h, e]| of each other (an fp32-vs-exact
   near-tie); such tokens are re-evaluated by the oracle with the GPU's
-  selection and counted;
+  selection and counted. eps_rel is 2^-16 for the decode router (fp64
+  accumulation, one fp32 rounding) and prefill_eps_rel(H) for the batched
+  router (3H exact bf16 products, each summed with at most one fp32 rounding);
 * outputs: per-token relative L2 error <= 2e-3 against the float64 oracle.
 """
 from __future__ import annotations
@@ -43,13 +45,23 @@ def build(cfg: synth.Config, storage=moe.STORE_DEVICE):
     return loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage)
 
 
-def selection_ok(gpu_sel, oracle_logits, x_row, w_r, k):
+DECODE_EPS_REL = 2.0 ** -16
+
+
+def prefill_eps_rel(hidden: int) -> float:
+    """Bound on |fp32 MFMA logit - exact| / sum|x w| for the batched router:
+    3 * hidden exact products (three bf16 parts per fp32 weight) accumulated
+    in fp32, one rounding of at most 2^-24 relative each, plus the bias add."""
+    return (3 * hidden + 2) * 2.0 ** -24
+
+
+def selection_ok(gpu_sel, oracle_logits, x_row, w_r, k, eps_rel=DECODE_EPS_REL):
     """True when gpu_sel equals the oracle's top-k, or differs only at near-ties."""
     want = omoe.topk_order(oracle_logits, k)
     if np.array_equal(np.asarray(gpu_sel), want):
         return True, 0
     mass = omoe.route_abs_mass(x_row[None, :], w_r)[0]
-    eps = 2.0 ** -16 * mass
+    eps = eps_rel * mass
     l = oracle_logits.astype(np.float64)
     for a, b in zip(want, gpu_sel):
         if a != b and abs(l[a] - l[b]) > max(eps[a], eps[b]):
@@ -57,15 +69,16 @@ def selection_ok(gpu_sel, oracle_logits, x_row, w_r, k):
     return True, 1
 
 
-def check_layer(cfg, om, layer, x_bits, gpu_out, gpu_idx, tokens):
-    """Compare GPU outputs/selections of one layer with the oracle on the sampled tokens."""
-    lw = om.layer(layer)
+def check_layer(cfg, om, layer, x_bits, gpu_out, gpu_idx, tokens, eps_rel=DECODE_EPS_REL, lw=None):
+    """Compare GPU outputs/selections of one layer with the oracle on the sampled tokens
+    (lw overrides the oracle's weights of that layer)."""
+    lw = om.layer(layer) if lw is None else lw
     x = quant.f64_from_bf16_bits(x_bits[tokens])
     res = omoe.layer_forward(x, lw, cfg.top_k, cfg.norm_topk)
     ties = 0
     sel = res.route.idx.copy()
     for i, t in enumerate(tokens):
-        ok, tie = selection_ok(gpu_idx[t], res.route.logits[i], x[i], lw.w_r, cfg.top_k)
+        ok, tie = selection_ok(gpu_idx[t], res.route.logits[i], x[i], lw.w_r, cfg.top_k, eps_rel)
         assert ok, f"token {t}: GPU selection {list(gpu_idx[t])} vs oracle {list(res.route.idx[i])}"
         if tie:
             ties += 1
@@ -76,7 +89,7 @@ def check_layer(cfg, om, layer, x_bits, gpu_out, gpu_idx, tokens):
     return float(err.max()), ties
 
 
-def check_routing_only(cfg, layer, x_bits, gpu_idx):
+def check_routing_only(cfg, layer, x_bits, gpu_idx, eps_rel=DECODE_EPS_REL):
     """Top-k of every token against the oracle's exactly rounded logits (no expert math)."""
     w_r = synth.router_weight(cfg.seed, layer, cfg.hidden, cfg.n_experts)
     rho = synth.router_bias(cfg, layer)
@@ -84,7 +97,7 @@ def check_routing_only(cfg, layer, x_bits, gpu_idx):
     logits = omoe.router_logits(x, w_r, rho)
     ties = 0
     for t in range(x.shape[0]):
-        ok, tie = selection_ok(gpu_idx[t], logits[t], x[t], w_r, cfg.top_k)
+        ok, tie = selection_ok(gpu_idx[t], logits[t], x[t], w_r, cfg.top_k, eps_rel)
         assert ok, f"token {t}: selection {list(gpu_idx[t])} vs {list(omoe.topk_order(logits[t], cfg.top_k))}"
         ties += tie
     return ties
