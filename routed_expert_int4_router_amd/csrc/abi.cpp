@@ -21,6 +21,7 @@
 
 #include "common.h"
 #include "kernels.h"
+#include "launch.h"
 #include "pool_policy.h"
 #include "prefill.h"
 
@@ -58,10 +59,24 @@ moe_status hip_fail(hipError_t e, const char* what) {
   } while (0)
 
 // Optional per-launch timing: a hipEvent pair around every kernel launch.
-enum KernelKind { K_ROUTER, K_ROUTE, K_GATEUP, K_DOWN, K_PF_ROUTE, K_PF_BUCKET, K_PF_GATEUP, K_PF_DOWN, K_PF_COMBINE,
-                  K_COUNT };
-const char* const kKindName[K_COUNT] = {"router", "route", "gateup", "down", "prefill_route",
-                                        "prefill_bucket", "prefill_gateup", "prefill_down", "prefill_combine"};
+}  // namespace
+
+LaunchEvents& moe::launch_events() {
+  thread_local LaunchEvents ev{nullptr, nullptr};
+  return ev;
+}
+
+namespace {
+
+enum KernelKind {
+  K_ROUTER, K_ROUTE, K_GATEUP, K_DOWN,
+  K_PF_XSUM, K_PF_ROUTER, K_PF_ROUTE, K_PF_COUNT, K_PF_SCAN, K_PF_SCATTER, K_PF_GATEUP, K_PF_DOWN, K_PF_COMBINE,
+  K_COUNT
+};
+const char* const kKindName[K_COUNT] = {"router",         "route",          "gateup",         "down",
+                                        "prefill_xsum",   "prefill_router", "prefill_route",  "prefill_count",
+                                        "prefill_scan",   "prefill_scatter", "prefill_gateup", "prefill_down",
+                                        "prefill_combine"};
 
 struct Profiler {
   bool on = false;
@@ -109,12 +124,17 @@ struct Profiler {
     }
     Rec r{kind, get(), get()};
     if (!r.a || !r.b) return hipErrorOutOfMemory;
-    hipError_t e = hipEventRecord(r.a, s);
-    if (e != hipSuccess) return e;
-    e = fn();
-    if (e != hipSuccess) return e;
-    e = hipEventRecord(r.b, s);
-    if (e != hipSuccess) return e;
+    // fn launches exactly one kernel; that launch takes the kernel's own
+    // begin/end timestamps into the pair (see launch.h).
+    launch_events() = LaunchEvents{r.a, r.b};
+    const hipError_t e = fn();
+    const bool consumed = launch_events().start == nullptr;
+    launch_events() = LaunchEvents{};
+    if (e != hipSuccess || !consumed) {
+      spare.push_back(r.a);
+      spare.push_back(r.b);
+      return e;
+    }
     pending.push_back(r);
     return hipSuccess;
   }
@@ -523,11 +543,11 @@ moe_status moe_layer_forward(moe_model* m, int32_t layer, const uint16_t* x, int
     if (st) return fail(st, "moe_layer_forward: prefill workspace allocation failed");
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* ws = m->prefill;
-    HIP_TRY(m->prof.run(K_PF_ROUTE, s, [&] { return prefill_route(ws, a, s); }), "moe_layer_forward: route");
-    HIP_TRY(m->prof.run(K_PF_BUCKET, s, [&] { return prefill_bucket(ws, a, s); }), "moe_layer_forward: bucket");
-    HIP_TRY(m->prof.run(K_PF_GATEUP, s, [&] { return prefill_gateup(ws, a, s); }), "moe_layer_forward: gate/up");
-    HIP_TRY(m->prof.run(K_PF_DOWN, s, [&] { return prefill_down(ws, a, s); }), "moe_layer_forward: down");
-    HIP_TRY(m->prof.run(K_PF_COMBINE, s, [&] { return prefill_combine(ws, a, s); }), "moe_layer_forward: combine");
+    using Stage = hipError_t (*)(void*, const PrefillArgs&, hipStream_t);
+    static const Stage kStages[] = {prefill_xsum,  prefill_router,  prefill_route,  prefill_count,  prefill_scan,
+                                    prefill_scatter, prefill_gateup, prefill_down, prefill_combine};
+    for (int i = 0; i < 9; ++i)
+      HIP_TRY(m->prof.run(K_PF_XSUM + i, s, [&] { return kStages[i](ws, a, s); }), "moe_layer_forward: prefill stage");
     m->route_steps = (size_t)n_tok;
     return MOE_OK;
   }

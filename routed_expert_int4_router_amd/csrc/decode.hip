@@ -26,6 +26,7 @@
 
 #include "dpp.h"
 #include "kernels.h"
+#include "launch.h"
 #include "topk.h"
 
 namespace moe {
@@ -425,9 +426,9 @@ hipError_t gateup_rwn(const Geometry& g, const ExpertSource& src, const uint8_t*
   const int wpe = g.I / (RPW * rw);
   const int total = (g.k + 1) * wpe;
   const dim3 grid((total + 3) / 4), block(256);
-  if (rw == 4) hipLaunchKernelGGL((gateup_kernel<BITS, LPR, IT, 4, NPL>), grid, block, 0, s, g, src, shared_rec, b, wpe, total);
-  else if (rw == 2) hipLaunchKernelGGL((gateup_kernel<BITS, LPR, IT, 2, NPL>), grid, block, 0, s, g, src, shared_rec, b, wpe, total);
-  else hipLaunchKernelGGL((gateup_kernel<BITS, LPR, IT, 1, NPL>), grid, block, 0, s, g, src, shared_rec, b, wpe, total);
+  if (rw == 4) launch((gateup_kernel<BITS, LPR, IT, 4, NPL>), grid, block, 0, s, g, src, shared_rec, b, wpe, total);
+  else if (rw == 2) launch((gateup_kernel<BITS, LPR, IT, 2, NPL>), grid, block, 0, s, g, src, shared_rec, b, wpe, total);
+  else launch((gateup_kernel<BITS, LPR, IT, 1, NPL>), grid, block, 0, s, g, src, shared_rec, b, wpe, total);
   return hipGetLastError();
 }
 
@@ -476,9 +477,9 @@ hipError_t down_r(const Geometry& g, const ExpertSource& src, const uint8_t* sha
   const size_t rs = g.I >= 256 ? g.I : 256;
   const size_t lds = ((size_t)4 * ((g.k + 1 + 3) / 4) * rs + 4 * RB) * sizeof(float);
   const dim3 grid(g.H / RB), block(256);
-  if (R == 4) hipLaunchKernelGGL((down_kernel<BITS, LPR, IT, 4>), grid, block, lds, s, g, src, shared_rec, b, r);
-  else if (R == 2) hipLaunchKernelGGL((down_kernel<BITS, LPR, IT, 2>), grid, block, lds, s, g, src, shared_rec, b, r);
-  else hipLaunchKernelGGL((down_kernel<BITS, LPR, IT, 1>), grid, block, lds, s, g, src, shared_rec, b, r);
+  if (R == 4) launch((down_kernel<BITS, LPR, IT, 4>), grid, block, lds, s, g, src, shared_rec, b, r);
+  else if (R == 2) launch((down_kernel<BITS, LPR, IT, 2>), grid, block, lds, s, g, src, shared_rec, b, r);
+  else launch((down_kernel<BITS, LPR, IT, 1>), grid, block, lds, s, g, src, shared_rec, b, r);
   return hipGetLastError();
 }
 
@@ -518,11 +519,11 @@ hipError_t launch_router(const Geometry& g, const float* wr_rows, const float* b
   const dim3 grid((g.E + 1 + 3) / 4), block(256);
   const int nit = (g.H / 4 + kWave - 1) / kWave;  // float4 loads per lane
   switch (nit) {
-    case 1: hipLaunchKernelGGL(router_kernel<1>, grid, block, 0, s, g, wr_rows, bias, b); break;
-    case 2: hipLaunchKernelGGL(router_kernel<2>, grid, block, 0, s, g, wr_rows, bias, b); break;
-    case 4: hipLaunchKernelGGL(router_kernel<4>, grid, block, 0, s, g, wr_rows, bias, b); break;
-    case 8: hipLaunchKernelGGL(router_kernel<8>, grid, block, 0, s, g, wr_rows, bias, b); break;
-    case 16: hipLaunchKernelGGL(router_kernel<16>, grid, block, 0, s, g, wr_rows, bias, b); break;
+    case 1: launch(router_kernel<1>, grid, block, 0, s, g, wr_rows, bias, b); break;
+    case 2: launch(router_kernel<2>, grid, block, 0, s, g, wr_rows, bias, b); break;
+    case 4: launch(router_kernel<4>, grid, block, 0, s, g, wr_rows, bias, b); break;
+    case 8: launch(router_kernel<8>, grid, block, 0, s, g, wr_rows, bias, b); break;
+    case 16: launch(router_kernel<16>, grid, block, 0, s, g, wr_rows, bias, b); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -532,11 +533,11 @@ hipError_t launch_route(const Geometry& g, const float* logits, int ld_logits, i
                         float* route_w, float* route_gamma, int32_t* host_route, hipStream_t s) {
   const dim3 grid(n_tok), block(64);
   switch (topk_npl(g.E)) {
-    case 1: hipLaunchKernelGGL(route_kernel<1>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
-    case 2: hipLaunchKernelGGL(route_kernel<2>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
-    case 4: hipLaunchKernelGGL(route_kernel<4>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
-    case 8: hipLaunchKernelGGL(route_kernel<8>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
-    case 16: hipLaunchKernelGGL(route_kernel<16>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
+    case 1: launch(route_kernel<1>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
+    case 2: launch(route_kernel<2>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
+    case 4: launch(route_kernel<4>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
+    case 8: launch(route_kernel<8>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
+    case 16: launch(route_kernel<16>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -34,9 +34,13 @@ bool prefill_supported(const moe_config& cfg);
 moe_status prefill_reserve(void** workspace, const moe_config& cfg, int n_tok);
 void prefill_free(void* workspace);
 
-// The five stages, in order, on one stream.
-hipError_t prefill_route(void* workspace, const PrefillArgs& a, hipStream_t s);    // xsum, router GEMM, top-k
-hipError_t prefill_bucket(void* workspace, const PrefillArgs& a, hipStream_t s);   // stable sort of pairs by expert
+// The stages, one kernel each, in this order on one stream.
+hipError_t prefill_xsum(void* workspace, const PrefillArgs& a, hipStream_t s);     // per-token 64-group sums of x
+hipError_t prefill_router(void* workspace, const PrefillArgs& a, hipStream_t s);   // logits [T][E+1] (MFMA)
+hipError_t prefill_route(void* workspace, const PrefillArgs& a, hipStream_t s);    // top-k, weights, shared gate
+hipError_t prefill_count(void* workspace, const PrefillArgs& a, hipStream_t s);    // pairs per (chunk, expert)
+hipError_t prefill_scan(void* workspace, const PrefillArgs& a, hipStream_t s);     // offsets and the tile list
+hipError_t prefill_scatter(void* workspace, const PrefillArgs& a, hipStream_t s);  // stable placement of pairs
 hipError_t prefill_gateup(void* workspace, const PrefillArgs& a, hipStream_t s);   // grouped gate/up GEMM + SwiGLU
 hipError_t prefill_down(void* workspace, const PrefillArgs& a, hipStream_t s);     // grouped down GEMM x weight
 hipError_t prefill_combine(void* workspace, const PrefillArgs& a, hipStream_t s);  // per-token sum

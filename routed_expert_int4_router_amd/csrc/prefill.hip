@@ -27,6 +27,7 @@
 #include <vector>
 
 #include "dpp.h"
+#include "launch.h"
 #include "topk.h"
 
 namespace moe {
@@ -661,45 +662,65 @@ moe_status prefill_reserve(void** wsp, const moe_config& c, int T) {
   return MOE_OK;
 }
 
-hipError_t prefill_route(void* ws, const PrefillArgs& pa, hipStream_t s) {
+hipError_t prefill_xsum(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
-  const int T = pa.n_tok, H = pa.cfg.hidden, E = pa.cfg.n_experts;
-  hipLaunchKernelGGL(xsum_kernel, dim3((T * (H / 64) + 255) / 256), dim3(256), 0, s, pa.x, T, H, w->xsum);
-  hipLaunchKernelGGL(router_gemm_kernel, dim3((T + 63) / 64, (E + 1 + 63) / 64), dim3(256), 0, s, pa.x, pa.wr_rows,
-                     pa.bias, T, H, E, w->logits);
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  return launch_route(pa.geo, w->logits, E + 1, T, pa.route_idx, pa.route_w, pa.route_gamma, nullptr, s);
+  const int T = pa.n_tok, H = pa.cfg.hidden;
+  launch(xsum_kernel, dim3((T * (H / 64) + 255) / 256), dim3(256), 0, s, pa.x, T, H, w->xsum);
+  return hipGetLastError();
 }
 
-hipError_t prefill_bucket(void* ws, const PrefillArgs& pa, hipStream_t s) {
+hipError_t prefill_router(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
-  const int T = pa.n_tok, E = pa.cfg.n_experts, k = pa.cfg.top_k, P = T * k, nchunk = n_chunks(pa);
-  hipLaunchKernelGGL(bucket_count_kernel, dim3(nchunk), dim3(CHUNK), E * sizeof(int32_t), s, pa.route_idx, P, E,
-                     w->cnt);
-  hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, w->cnt, nchunk, E, T, k, w->chunk_off, w->e_off,
-                     w->tiles, w->max_tiles);
-  hipLaunchKernelGGL(bucket_scatter_kernel, dim3(nchunk), dim3(CHUNK), 0, s, pa.route_idx, P, E, w->chunk_off,
-                     w->perm);
+  const int T = pa.n_tok, H = pa.cfg.hidden, E = pa.cfg.n_experts;
+  launch(router_gemm_kernel, dim3((T + 63) / 64, (E + 1 + 63) / 64), dim3(256), 0, s, pa.x, pa.wr_rows, pa.bias, T, H,
+         E, w->logits);
+  return hipGetLastError();
+}
+
+hipError_t prefill_route(void* ws, const PrefillArgs& pa, hipStream_t s) {
+  Workspace* w = ws_of(ws);
+  return launch_route(pa.geo, w->logits, pa.cfg.n_experts + 1, pa.n_tok, pa.route_idx, pa.route_w, pa.route_gamma,
+                      nullptr, s);
+}
+
+hipError_t prefill_count(void* ws, const PrefillArgs& pa, hipStream_t s) {
+  Workspace* w = ws_of(ws);
+  const int E = pa.cfg.n_experts, P = pa.n_tok * pa.cfg.top_k;
+  launch(bucket_count_kernel, dim3(n_chunks(pa)), dim3(CHUNK), (uint32_t)(E * sizeof(int32_t)), s, pa.route_idx, P, E,
+         w->cnt);
+  return hipGetLastError();
+}
+
+hipError_t prefill_scan(void* ws, const PrefillArgs& pa, hipStream_t s) {
+  Workspace* w = ws_of(ws);
+  launch(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, w->cnt, n_chunks(pa), pa.cfg.n_experts, pa.n_tok,
+         pa.cfg.top_k, w->chunk_off, w->e_off, w->tiles, w->max_tiles);
+  return hipGetLastError();
+}
+
+hipError_t prefill_scatter(void* ws, const PrefillArgs& pa, hipStream_t s) {
+  Workspace* w = ws_of(ws);
+  const int E = pa.cfg.n_experts, P = pa.n_tok * pa.cfg.top_k;
+  launch(bucket_scatter_kernel, dim3(n_chunks(pa)), dim3(CHUNK), 0, s, pa.route_idx, P, E, w->chunk_off, w->perm);
   return hipGetLastError();
 }
 
 hipError_t prefill_gateup(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
-  hipLaunchKernelGGL(gemm_gateup_kernel, dim3(w->max_tiles, pa.cfg.inter / 64), dim3(256), 0, s, gemm_args(w, pa));
+  launch(gemm_gateup_kernel, dim3(w->max_tiles, pa.cfg.inter / 64), dim3(256), 0, s, gemm_args(w, pa));
   return hipGetLastError();
 }
 
 hipError_t prefill_down(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
-  hipLaunchKernelGGL(gemm_down_kernel, dim3(w->max_tiles, pa.cfg.hidden / 128), dim3(256), 0, s, gemm_args(w, pa));
+  launch(gemm_down_kernel, dim3(w->max_tiles, pa.cfg.hidden / 128), dim3(256), 0, s, gemm_args(w, pa));
   return hipGetLastError();
 }
 
 hipError_t prefill_combine(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
   const size_t n4 = (size_t)pa.n_tok * pa.cfg.hidden / 4;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, w->y, pa.n_tok,
+  launch(combine_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, w->y, pa.n_tok,
                      pa.cfg.top_k, pa.cfg.hidden, pa.out);
   return hipGetLastError();
 }
