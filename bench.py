@@ -17,9 +17,10 @@ Workloads (synthetic, seeded, weights ~N(0, 0.02) packed to int4/int8 g64):
 A step is one pass of the workload's tokens through the whole path (router,
 top-k, expert GEMV/GEMM, combine, stack glue, pool). W untimed steps, then K
 timed steps bracketed by device synchronisation; value = tokens / second.
-A second, instrumented pass of the same steps records a hipEvent pair around
-every kernel launch; the dominant kernel's average duration and its
-algorithmic bytes (or flops) give the roofline entry. The CPU oracle is timed
+A second, instrumented pass of the same steps hands every kernel launch a
+hipEvent pair that the launch fills with the kernel's own begin/end
+timestamps; the dominant kernel's average duration and its algorithmic bytes
+(or flops) give the roofline entry. The CPU oracle is timed
 on a bounded sample of the same workload, single-threaded.
 """
 from __future__ import annotations
