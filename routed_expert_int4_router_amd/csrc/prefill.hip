@@ -47,6 +47,7 @@ struct Workspace {
   int T = 0, E = 0, k = 0, H = 0, I = 0;
   float* logits = nullptr;      // [T][E+1]
   float* xsum = nullptr;        // [T][H/64]
+  uint16_t* xp = nullptr;       // [T][H] k-permuted copy of x
   int32_t* cnt = nullptr;       // [nchunk][E]
   int32_t* chunk_off = nullptr; // [nchunk][E]
   int32_t* e_off = nullptr;     // [E+2]: start of each expert's rows; [E] = T*k (shared rows), [E+1] = T*k + T
@@ -92,19 +93,26 @@ __device__ __forceinline__ bf16x8 nib_to_bf16(uint32_t w) {
 }
 
 // ------------------------------------------------------------------- xsum ---
-__global__ void __launch_bounds__(256) xsum_kernel(const uint16_t* __restrict__ x, int T, int H, float* xsum) {
+// Per (token, 64-group): the group sum of x (the bias term of the grid) and a
+// copy of the 64 values with every 8-chunk in the order (0,4,1,5,2,6,3,7), the
+// order in which nib_to_bf16 emits the codes of a dword. The grouped GEMM
+// streams that copy into LDS unchanged.
+__global__ void __launch_bounds__(256) xsum_kernel(const uint16_t* __restrict__ x, int T, int H, float* xsum,
+                                                   uint16_t* xp) {
   const int G = H / 64;
   const int idx = blockIdx.x * 256 + threadIdx.x;  // one (token, group)
   if (idx >= T * G) return;
   const int t = idx / G, g = idx % G;
   const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * H + 64 * g);
+  uint4* q = reinterpret_cast<uint4*>(xp + (size_t)t * H + 64 * g);
   float s = 0.f;
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const uint4 v = p[q];
+  for (int c = 0; c < 8; ++c) {
+    const uint4 v = p[c];
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) s += bf16f(w[i] & 0xFFFFu) + bf16f(w[i] >> 16);
+    q[c] = perm8(v);
   }
   xsum[idx] = s;
 }
@@ -266,12 +274,26 @@ __global__ void __launch_bounds__(CHUNK) bucket_scatter_kernel(const int32_t* __
 }
 
 // ------------------------------------------------------- grouped GEMM 1 ---
-// Block (tile, n-tile): 64 rows of one expert (pairs in sorted order, or tokens
-// for the shared expert) x 64 intermediate columns, gate and up. Waves 0,1:
-// gate columns [n0, n0+32), [n0+32, n0+64); waves 2,3: up. Each wave computes
-// 64 x 32 with 32x32x16 MFMAs; K runs over the 64-groups of H.
+// Block = (tile, 128 columns of I), 8 waves: 64 rows of one expert (sorted
+// pairs, or tokens for the shared expert) x 128 gate + 128 up columns. Waves
+// 0-3 compute gate columns [32w, 32w + 32), waves 4-7 the same up columns;
+// each wave is 64 x 32 (two 32x32x16 MFMA tiles). K runs over the 64-groups
+// of H.
+//
+// Operands reach LDS by direct global->LDS DMA (no registers): per group the
+// A rows (the k-permuted x of the tile's tokens, 8 KB) and the code rows
+// (8 KB) go into NST-stage rings, NST - 1 groups ahead; the (s, c) words of
+// all groups and the tile rows' x sums are loaded once up front. Every wave
+// issues one A and one B DMA per group (a group past the end reloads the last
+// one into a free stage), so waiting for "all but the newest 2 (NST - 2)" DMAs
+// plus one barrier per group makes group g's stages visible to every wave.
+//
+// Per group: P = A . (16 + q) on the matrix cores (exact integer operands,
+// fp32 accumulate) and acc += s * P. The affine term sum_g (c - 16 s) * sum_k x
+// is a K = G contraction done at the end with fp32 MFMAs.
 struct GemmArgs {
   const uint16_t* x;          // [T][H]
+  const uint16_t* xp;         // [T][H], 8-chunks in nib_to_bf16 order
   const float* xsum;          // [T][H/64]
   const uint8_t* experts;     // routed records of the layer
   const uint8_t* shared;      // shared record
@@ -289,109 +311,240 @@ struct GemmArgs {
   int T, H, I, E, k;
 };
 
-__global__ void __launch_bounds__(256) gemm_gateup_kernel(GemmArgs a) {
-  __shared__ __align__(16) uint16_t sx[2][BM][72];     // A tiles (k-permuted), double buffered
-  __shared__ __align__(16) float sxs[64][BM];           // xsum of the tile rows per group (G <= 64)
-  __shared__ __align__(16) float sg[BM][65];            // gate results for the SwiGLU exchange
-  __shared__ int32_t s_tok[BM];
-  const int ntiles = a.tiles[0];
-  if ((int)blockIdx.x >= ntiles) return;
-  const int e = a.tiles[1 + 2 * blockIdx.x], r0 = a.tiles[2 + 2 * blockIdx.x];
-  const int n0 = blockIdx.y * 64;
-  const int rows = a.e_off[e + 1] - a.e_off[e];
-  const int G = a.H / 64;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
+constexpr int GU_BN = 128;            // I columns per block
+constexpr int A_STAGE = BM * 64 * 2;  // 64 rows x 64 bf16
+constexpr int B_STAGE = 2 * GU_BN * 32;  // 256 code rows x 64 int4
 
-  if (threadIdx.x < BM) {
-    const int r = r0 + threadIdx.x;
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 4, 0, 0);
+}
+
+// Logical block index. The 8 XCDs take blocks round-robin, so XCD x gets the
+// contiguous logical range [x * per, (x + 1) * per) of the n_real blocks that
+// have work (the grid is sized for the worst case; n_real is known only on the
+// device): the column tiles of one row tile, and neighbouring row tiles of one
+// expert, share that XCD's L2. Returns -1 for a block with nothing to do.
+__device__ __forceinline__ int xcd_block(int n_real) {
+  const int per = (n_real + 7) / 8;
+  const int x = (int)(blockIdx.x % 8), i = (int)(blockIdx.x / 8);
+  const int l = x * per + i;
+  return (i < per && l < n_real) ? l : -1;
+}
+
+// Code-row and scale sources of a quad (4 groups) for this lane's DMAs.
+struct QuadSources {
+  const uint8_t* b[4];  // code-row chunks of DMA instructions t = 0..3 (quad 0)
+  const uint8_t* s;     // scale words (quad 0), lanes 0..31
+};
+
+// Operands of one K group, read from LDS into registers one step ahead of
+// their use.
+struct GroupFrag {
+  bf16x8 a0[4], a1[4];  // A rows mrow and 32 + mrow for the 4 MFMA steps
+  uint4 codes;          // 32 codes of column brow (k half hh)
+  uint32_t sc;          // (s, c) of column brow
+};
+// Affine-term operands of one quad (read with its last group).
+struct AffineFrag {
+  float cp[2], x0[2], x1[2];
+};
+
+// Step for group g = 4Q + J: issue the DMA of A(g + PF) into the free A stage
+// (wrA) and, for J == 0, first the next quad's code rows and scale words
+// (wrB, wrS); then read group g's operands from LDS. The restrict qualifiers
+// tell the compiler that the stages read here are not the ones being
+// written, so it adds no wait of its own between the DMAs and the LDS reads;
+// the caller's vmcnt wait + barrier orders them.
+template <int J>
+__device__ __forceinline__ void gateup_fetch(const uint8_t* __restrict__ rdA, const uint8_t* __restrict__ rdB,
+                                             const uint8_t* __restrict__ rdS, uint8_t* __restrict__ wrA,
+                                             uint8_t* __restrict__ wrB, uint8_t* __restrict__ wrS,
+                                             const float* __restrict__ sX, const uint16_t* srcA,
+                                             const QuadSources& qs, int qnext, int Q, int wv, int lane, int brow,
+                                             int hh, int mrow, GroupFrag& f, AffineFrag& af) {
+  if constexpr (J == 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma16(qs.b[t] + 128 * qnext, wrB + (4 * wv + t) * 1024);
+    if (lane < 32) dma16(qs.s + 16 * qnext, wrS + wv * 512);
+  }
+  dma16(srcA, wrA + wv * 1024);
+  const int slot = (2 * J + hh) ^ (brow & 7);
+  f.codes = *reinterpret_cast<const uint4*>(rdB + brow * 128 + slot * 16);
+  f.sc = *reinterpret_cast<const uint32_t*>(rdS + brow * 16 + J * 4);
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int off = ((4 * hh + st) ^ (mrow & 7)) * 16;
+    f.a0[st] = *reinterpret_cast<const bf16x8*>(rdA + mrow * 128 + off);
+    f.a1[st] = *reinterpret_cast<const bf16x8*>(rdA + (32 + mrow) * 128 + off);
+  }
+  if constexpr (J == 3) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = 2 * u + hh, g = 4 * Q + j;
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(rdS + brow * 16 + j * 4);
+      af.cp[u] = f16f(w >> 16) - 16.0f * f16f(w & 0xFFFFu);
+      af.x0[u] = sX[g * 64 + mrow];
+      af.x1[u] = sX[g * 64 + 32 + mrow];
+    }
+  }
+}
+
+// P = A . (16 + q) for one group (exact operands, fp32 accumulate), acc += s * P.
+__device__ __forceinline__ void gateup_compute(const GroupFrag& f, f32x16& acc0, f32x16& acc1) {
+  const bf16x8 b[4] = {nib_to_bf16(f.codes.x), nib_to_bf16(f.codes.y), nib_to_bf16(f.codes.z),
+                       nib_to_bf16(f.codes.w)};
+  f32x16 p0 = {}, p1 = {};
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0[st], b[st], p0, 0, 0, 0);
+    p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1[st], b[st], p1, 0, 0, 0);
+  }
+  const float sv = f16f(f.sc & 0xFFFFu);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    acc0[r] += sv * p0[r];
+    acc1[r] += sv * p1[r];
+  }
+}
+
+// Affine term of one quad: acc[m][n] += sum_{g in quad} xs[m][g] * (c - 16 s)[n][g]
+// as two fp32 MFMAs (K = 2) per 32-row tile.
+__device__ __forceinline__ void gateup_affine(const AffineFrag& af, f32x16& acc0, f32x16& acc1) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(af.x0[u], af.cp[u], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(af.x1[u], af.cp[u], acc1, 0, 0, 0);
+  }
+}
+
+constexpr int GU_NA = 6;                     // A ring stages (one group each)
+constexpr int GU_PF = GU_NA - 1;             // A prefetch distance in groups
+constexpr int BQ_STAGE = 2 * GU_BN * 128;    // 256 code rows x 4 groups
+constexpr int SQ_STAGE = 2 * GU_BN * 16;     // 256 rows x 4 (s, c) words
+
+size_t gateup_lds_bytes(int G) {
+  return (size_t)GU_NA * A_STAGE + 2 * (size_t)BQ_STAGE + 2 * (size_t)SQ_STAGE + (size_t)256 * G;
+}
+
+__global__ void __launch_bounds__(512, 2) gemm_gateup_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int32_t s_tok[BM];
+  const int G = a.H / 64, NQ = G / 4, NT = (a.I + GU_BN - 1) / GU_BN;
+  const int L = xcd_block(a.tiles[0] * NT);
+  if (L < 0) return;
+  const int tile = L / NT, nt = L % NT;
+  const int e = a.tiles[1 + 2 * tile], r0 = a.tiles[2 + 2 * tile];
+  const int n0 = nt * GU_BN;
+  const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  uint8_t* sA = smem;                                       // [NA][64 rows][8 slots of 16 B]
+  uint8_t* sB = sA + GU_NA * A_STAGE;                       // [2][256 rows][8 slots of 16 B] (4 groups)
+  uint8_t* sS = sB + 2 * BQ_STAGE;                          // [2][256 rows][4 words]
+  float* sX = reinterpret_cast<float*>(sS + 2 * SQ_STAGE);  // [G][64 rows]
+
+  // Code rows of a quad: DMA instruction t of wave w covers rows 32w + 8t ..
+  // +8 (full 128-byte lines); lane -> (row, slot), slot = chunk ^ (row & 7).
+  QuadSources qs;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int row = 32 * wv + 8 * t + (lane >> 3), chunk = (lane & 7) ^ (row & 7);
+    const int n = min(n0 + (row & (GU_BN - 1)), a.I - 1);
+    qs.b[t] = rec + (row < GU_BN ? a.gate_codes : a.up_codes) + (size_t)n * (a.H / 2) + 16 * chunk;
+  }
+  {
+    const int row = 32 * wv + (lane & 31);
+    const int n = min(n0 + (row & (GU_BN - 1)), a.I - 1);
+    qs.s = rec + (row < GU_BN ? a.gate_sc : a.up_sc) + (size_t)n * G * 4;
+  }
+  // quad 0 of B and S first: they do not depend on the tile's tokens
+#pragma unroll
+  for (int t = 0; t < 4; ++t) dma16(qs.b[t], sB + (4 * wv + t) * 1024);
+  if (lane < 32) dma16(qs.s, sS + wv * 512);
+
+  const int rows = a.e_off[e + 1] - a.e_off[e];
+  if (tid < BM) {
+    const int r = r0 + tid;
     int tok = -1;
     if (r < rows) tok = e < a.E ? a.perm[a.e_off[e] + r] / a.k : r;
-    s_tok[threadIdx.x] = tok;
+    s_tok[tid] = tok;
   }
   __syncthreads();
-  for (int q = threadIdx.x; q < G * BM; q += 256) {
-    const int g = q / BM, m = q % BM;
-    const int tok = s_tok[m];
-    sxs[g][m] = tok >= 0 ? a.xsum[(size_t)tok * G + g] : 0.f;
+  // x sums: instruction g loads group g of the 64 rows
+  {
+    const int tok = max(s_tok[lane], 0);
+    for (int g = wv; g < G; g += 8) dma4(a.xsum + (size_t)tok * G + g, reinterpret_cast<uint8_t*>(sX) + g * 256);
   }
-  // staging map: thread -> row lr, 16-element quarter lq of the 64-wide K slice
-  const int lr = threadIdx.x >> 2, lq = threadIdx.x & 3;
-  const int stok = s_tok[lr];
-  const uint4* xrow = reinterpret_cast<const uint4*>(a.x + (size_t)max(stok, 0) * a.H + 16 * lq);
-  auto load_a = [&](int g, uint4& v0, uint4& v1) {
-    if (stok >= 0) {
-      v0 = xrow[8 * g];
-      v1 = xrow[8 * g + 1];
-    } else {
-      v0 = make_uint4(0, 0, 0, 0);
-      v1 = v0;
-    }
-  };
-  // B: this wave's matrix and column
-  const int mat = wv >> 1;
-  const int n = n0 + 32 * (wv & 1) + (lane & 31);
-  const int hh = lane >> 5;
-  const size_t row_bytes = (size_t)a.H / 2;
-  const uint8_t* crow = rec + (mat ? a.up_codes : a.gate_codes) + (size_t)n * row_bytes + 16 * hh;
-  const uint32_t* scrow = reinterpret_cast<const uint32_t*>(rec + (mat ? a.up_sc : a.gate_sc)) + (size_t)n * G;
+  const uint16_t* asrc;
+  {
+    const int row = 8 * wv + (lane >> 3), chunk = (lane & 7) ^ (row & 7);
+    asrc = a.xp + (size_t)max(s_tok[row], 0) * a.H + 8 * chunk;
+  }
+  // Prologue A(0..PF-1). From here on every group iteration issues one A DMA,
+  // and the first group of each quad first the next quad's 4 B + 1 S DMAs, so
+  // the number of DMAs issued after the newest one a wait needs is fixed:
+  // 4 at a quad's first group (B/S of this quad), 9 at the others (A(g)).
+  for (int g = 0; g < GU_PF; ++g) dma16(asrc + 64 * min(g, G - 1), sA + g * A_STAGE + wv * 1024);
 
+  const int mat = wv >> 2;
+  const int nl = 32 * (wv & 3) + (lane & 31);  // column within the block
+  const int brow = GU_BN * mat + nl;           // code / scale row within the block
+  const int hh = lane >> 5;
+  const int mrow = lane & 31;
   f32x16 acc0 = {}, acc1 = {};
-  uint4 av0, av1;
-  load_a(0, av0, av1);
-  uint4 cb = *reinterpret_cast<const uint4*>(crow);
-  uint32_t scv = scrow[0];
-  *reinterpret_cast<uint4*>(&sx[0][lr][16 * lq]) = perm8(av0);
-  *reinterpret_cast<uint4*>(&sx[0][lr][16 * lq + 8]) = perm8(av1);
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    uint4 nv0, nv1, ncb;
-    uint32_t nsc = 0;
-    if (g + 1 < G) {
-      load_a(g + 1, nv0, nv1);
-      ncb = *reinterpret_cast<const uint4*>(crow + 32 * (g + 1));
-      nsc = scrow[g + 1];
-    }
-    const bf16x8 b0 = nib_to_bf16(cb.x), b1 = nib_to_bf16(cb.y), b2 = nib_to_bf16(cb.z), b3 = nib_to_bf16(cb.w);
-    f32x16 p0 = {}, p1 = {};
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kk = 32 * hh + 8 * s;
-      const bf16x8 bv = s == 0 ? b0 : (s == 1 ? b1 : (s == 2 ? b2 : b3));
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&sx[buf][(lane & 31)][kk]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&sx[buf][32 + (lane & 31)][kk]);
-      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bv, p0, 0, 0, 0);
-      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bv, p1, 0, 0, 0);
-    }
-    const float sv = f16f(scv & 0xFFFFu), cv = f16f(scv >> 16) - 16.0f * f16f(scv & 0xFFFFu);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
-      acc0[r] += sv * p0[r] + cv * sxs[g][m];
-      acc1[r] += sv * p1[r] + cv * sxs[g][32 + m];
-    }
-    if (g + 1 < G) {
-      *reinterpret_cast<uint4*>(&sx[buf ^ 1][lr][16 * lq]) = perm8(nv0);
-      *reinterpret_cast<uint4*>(&sx[buf ^ 1][lr][16 * lq + 8]) = perm8(nv1);
-      cb = ncb;
-      scv = nsc;
-    }
-    __syncthreads();
+  GroupFrag fa, fb;
+  AffineFrag af;
+  // Step g (wait for group g's stages, barrier, DMAs, LDS -> registers) runs
+  // one group ahead of compute g. The lgkmcnt(0) in each wait makes sure this
+  // wave's reads of the stages the DMAs after the barrier will overwrite are
+  // complete. Waits: vmcnt(4) at a quad's first group (B/S of the quad),
+  // vmcnt(9) otherwise (A(g)).
+#define GU_STEP(Q, J, WAIT, F)                                                                                  \
+  {                                                                                                             \
+    const int g = 4 * (Q) + (J);                                                                                \
+    __builtin_amdgcn_s_waitcnt(WAIT);                                                                           \
+    __builtin_amdgcn_s_barrier();                                                                               \
+    gateup_fetch<J>(sA + (g % GU_NA) * A_STAGE, sB + ((Q) & 1) * BQ_STAGE, sS + ((Q) & 1) * SQ_STAGE,          \
+                    sA + ((g + GU_PF) % GU_NA) * A_STAGE, sB + (((Q) + 1) & 1) * BQ_STAGE,                      \
+                    sS + (((Q) + 1) & 1) * SQ_STAGE, sX, asrc + 64 * min(g + GU_PF, G - 1), qs,                 \
+                    min((Q) + 1, NQ - 1), (Q), wv, lane, brow, hh, mrow, F, af);                                \
   }
-  // SwiGLU: gate waves publish, up waves combine and store
-  const int nl = 32 * (wv & 1) + (lane & 31);
+  GU_STEP(0, 0, 0x0074, fa)
+  for (int Q = 0; Q < NQ; ++Q) {
+    GU_STEP(Q, 1, 0x0079, fb)
+    gateup_compute(fa, acc0, acc1);
+    GU_STEP(Q, 2, 0x0079, fa)
+    gateup_compute(fb, acc0, acc1);
+    GU_STEP(Q, 3, 0x0079, fb)
+    gateup_compute(fa, acc0, acc1);
+    if (Q + 1 < NQ) GU_STEP(Q + 1, 0, 0x0074, fa)
+    gateup_compute(fb, acc0, acc1);
+    gateup_affine(af, acc0, acc1);
+  }
+#undef GU_STEP
+  // SwiGLU: gate waves publish through LDS (the A ring, once no DMA is in flight)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  constexpr int SGS = GU_BN + 1;
+  float* sg = reinterpret_cast<float*>(sA);  // [64][GU_BN + 1]
   if (mat == 0) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
-      sg[m][nl] = acc0[r];
-      sg[32 + m][nl] = acc1[r];
+      sg[m * SGS + nl] = acc0[r];
+      sg[(32 + m) * SGS + nl] = acc1[r];
     }
   }
   __syncthreads();
   const int base = a.e_off[e] + r0;
-  if (mat == 1) {
+  // h is stored with each 8-chunk in nib_to_bf16 order, ready for the down GEMM's DMA
+  const int p = nl & 7;
+  const int col = n0 + (nl & ~7) + (p < 4 ? 2 * p : 2 * (p - 4) + 1);
+  if (mat == 1 && n0 + nl < a.I) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m0 = (r >> 2) * 8 + hh * 4 + (r & 3);
@@ -399,27 +552,27 @@ __global__ void __launch_bounds__(256) gemm_gateup_kernel(GemmArgs a) {
       for (int half = 0; half < 2; ++half) {
         const int m = m0 + 32 * half;
         if (r0 + m < rows) {
-          const float gt = sg[m][nl];
+          const float gt = sg[m * SGS + nl];
           const float u = half ? acc1[r] : acc0[r];
           const float hv = gt / (1.0f + expf(-gt)) * u;
           const uint16_t hi = to_bf16_rne(hv);
           const uint16_t lo = to_bf16_rne(hv - bf16f(hi));
-          const size_t o = (size_t)(base + m) * a.I + n0 + nl;
+          const size_t o = (size_t)(base + m) * a.I + col;
           a.h_hi[o] = hi;
           a.h_lo[o] = lo;
-          sg[m][nl] = bf16f(hi) + bf16f(lo);  // what the down GEMM multiplies
+          sg[m * SGS + nl] = bf16f(hi) + bf16f(lo);  // what the down GEMM multiplies
         }
       }
     }
   }
   __syncthreads();
-  // per-row sum of this 64-column group of h (the down matrix's quant group)
-  if (threadIdx.x < BM) {
-    const int m = threadIdx.x;
-    if (r0 + m < rows) {
-      float s = 0.f;
-      for (int c = 0; c < 64; ++c) s += sg[m][c];
-      a.hsum[(size_t)(base + m) * (a.I / 64) + n0 / 64] = s;
+  // per-row sums of each 64-column group of h (the down matrix's quant groups)
+  if (tid < 2 * BM) {
+    const int m = tid & (BM - 1), part = tid >> 6;
+    if (r0 + m < rows && n0 + 64 * part < a.I) {
+      float sum = 0.f;
+      for (int c = 0; c < 64; ++c) sum += sg[m * SGS + 64 * part + c];
+      a.hsum[(size_t)(base + m) * (a.I / 64) + n0 / 64 + part] = sum;
     }
   }
 }
@@ -488,10 +641,10 @@ __global__ void __launch_bounds__(256) gemm_down_kernel(GemmArgs a) {
   load_a(0, h0, h1, l0, l1);
   uint4 cb = *reinterpret_cast<const uint4*>(crow);
   uint32_t scv = scrow[0];
-  *reinterpret_cast<uint4*>(&shi[0][lr][16 * lq]) = perm8(h0);
-  *reinterpret_cast<uint4*>(&shi[0][lr][16 * lq + 8]) = perm8(h1);
-  *reinterpret_cast<uint4*>(&slo[0][lr][16 * lq]) = perm8(l0);
-  *reinterpret_cast<uint4*>(&slo[0][lr][16 * lq + 8]) = perm8(l1);
+  *reinterpret_cast<uint4*>(&shi[0][lr][16 * lq]) = h0;
+  *reinterpret_cast<uint4*>(&shi[0][lr][16 * lq + 8]) = h1;
+  *reinterpret_cast<uint4*>(&slo[0][lr][16 * lq]) = l0;
+  *reinterpret_cast<uint4*>(&slo[0][lr][16 * lq + 8]) = l1;
   __syncthreads();
   for (int g = 0; g < G; ++g) {
     const int buf = g & 1;
@@ -525,10 +678,10 @@ __global__ void __launch_bounds__(256) gemm_down_kernel(GemmArgs a) {
       acc1[r] += sv * p1[r] + cv * shs[g][32 + m];
     }
     if (g + 1 < G) {
-      *reinterpret_cast<uint4*>(&shi[buf ^ 1][lr][16 * lq]) = perm8(nh0);
-      *reinterpret_cast<uint4*>(&shi[buf ^ 1][lr][16 * lq + 8]) = perm8(nh1);
-      *reinterpret_cast<uint4*>(&slo[buf ^ 1][lr][16 * lq]) = perm8(nl0);
-      *reinterpret_cast<uint4*>(&slo[buf ^ 1][lr][16 * lq + 8]) = perm8(nl1);
+      *reinterpret_cast<uint4*>(&shi[buf ^ 1][lr][16 * lq]) = nh0;
+      *reinterpret_cast<uint4*>(&shi[buf ^ 1][lr][16 * lq + 8]) = nh1;
+      *reinterpret_cast<uint4*>(&slo[buf ^ 1][lr][16 * lq]) = nl0;
+      *reinterpret_cast<uint4*>(&slo[buf ^ 1][lr][16 * lq + 8]) = nl1;
       cb = ncb;
       scv = nsc;
     }
@@ -582,6 +735,7 @@ GemmArgs gemm_args(const Workspace* w, const PrefillArgs& pa) {
   GemmArgs ga{};
   ga.x = pa.x;
   ga.xsum = w->xsum;
+  ga.xp = w->xp;
   ga.experts = pa.experts;
   ga.shared = pa.shared;
   ga.stride = pa.stride;
@@ -613,7 +767,8 @@ int n_chunks(const PrefillArgs& pa) { return (pa.n_tok * pa.cfg.top_k + CHUNK - 
 }  // namespace
 
 bool prefill_supported(const moe_config& cfg) {
-  return cfg.bits == 4 && cfg.hidden % 128 == 0 && cfg.inter % 64 == 0 && cfg.hidden / 64 <= 64 &&
+  // the gate/up block loads the scale words 4 groups (16 bytes) at a time: H % 256 == 0
+  return cfg.bits == 4 && cfg.hidden % 256 == 0 && cfg.inter % 64 == 0 && cfg.hidden / 64 <= 64 &&
          cfg.inter / 64 <= 64 && cfg.n_experts <= 1024 && cfg.top_k <= kTopkMax;
 }
 
@@ -622,6 +777,7 @@ void prefill_free(void* ws) {
   Workspace* w = ws_of(ws);
   hipFree(w->logits);
   hipFree(w->xsum);
+  hipFree(w->xp);
   hipFree(w->cnt);
   hipFree(w->chunk_off);
   hipFree(w->e_off);
@@ -647,7 +803,7 @@ moe_status prefill_reserve(void** wsp, const moe_config& c, int T) {
   const int nchunk = (int)((P + CHUNK - 1) / CHUNK);
   const int max_tiles = (int)((P + BM - 1) / BM) + E + (T + BM - 1) / BM;
   w->T = 0;  // invalid until every buffer is in place
-  const bool ok = grow(w->logits, (size_t)T * (E + 1)) && grow(w->xsum, (size_t)T * (H / 64)) &&
+  const bool ok = grow(w->logits, (size_t)T * (E + 1)) && grow(w->xsum, (size_t)T * (H / 64)) && grow(w->xp, (size_t)T * H) &&
                   grow(w->cnt, (size_t)nchunk * E) && grow(w->chunk_off, (size_t)nchunk * E) &&
                   grow(w->e_off, (size_t)E + 2) && grow(w->perm, P) && grow(w->tiles, (size_t)1 + 2 * max_tiles) &&
                   grow(w->h_hi, rows * I) && grow(w->h_lo, rows * I) && grow(w->hsum, rows * (I / 64)) &&
@@ -665,7 +821,7 @@ moe_status prefill_reserve(void** wsp, const moe_config& c, int T) {
 hipError_t prefill_xsum(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
   const int T = pa.n_tok, H = pa.cfg.hidden;
-  launch(xsum_kernel, dim3((T * (H / 64) + 255) / 256), dim3(256), 0, s, pa.x, T, H, w->xsum);
+  launch(xsum_kernel, dim3((T * (H / 64) + 255) / 256), dim3(256), 0, s, pa.x, T, H, w->xsum, w->xp);
   return hipGetLastError();
 }
 
@@ -707,7 +863,18 @@ hipError_t prefill_scatter(void* ws, const PrefillArgs& pa, hipStream_t s) {
 
 hipError_t prefill_gateup(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
-  launch(gemm_gateup_kernel, dim3(w->max_tiles, pa.cfg.inter / 64), dim3(256), 0, s, gemm_args(w, pa));
+  const int G = pa.cfg.hidden / 64;
+  const size_t lds = gateup_lds_bytes(G);
+  // dynamic LDS above 64 KB has to be allowed per kernel (LDS is 160 KB per CU)
+  static size_t attr_bytes = 0;
+  if (attr_bytes < lds) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_gateup_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_bytes = lds;
+  }
+  const int nblk = w->max_tiles * ((pa.cfg.inter + GU_BN - 1) / GU_BN);
+  launch(gemm_gateup_kernel, dim3((unsigned)(8 * ((nblk + 7) / 8))), dim3(512), (uint32_t)lds, s, gemm_args(w, pa));
   return hipGetLastError();
 }
 

@@ -25,17 +25,17 @@ def _forward(model, cfg, xb):
 
 
 def _takes_prefill(cfg, n):
-    return n * cfg.top_k >= 4 * cfg.n_experts
+    return n * cfg.top_k >= 4 * cfg.n_experts and cfg.hidden % 256 == 0 and cfg.bits == 4
 
 
 # Shapes chosen to hit the tile edges: several 64-row tiles per expert with a
 # ragged last tile, experts that receive no token, a shared-expert tile count
-# that is not a multiple of anything, K = H from 128 to 1024 and I from 64.
+# that is not a multiple of anything, K = H from 256 to 2048 and I from 64.
 PREFILL_CASES = [
     (dict(), 37),
     (dict(n_experts=4, top_k=2, hidden=512, inter=256, shared_inter=256), 200),
     (dict(n_experts=100, top_k=7, hidden=1024, inter=64, shared_inter=64, norm_topk=0), 131),
-    (dict(n_experts=33, top_k=5, hidden=128, inter=64, shared_inter=64, bias="normal"), 65),
+    (dict(n_experts=33, top_k=5, hidden=256, inter=64, shared_inter=64, bias="normal"), 65),
     (dict(n_experts=8, top_k=8, hidden=256, inter=128, shared_inter=128), 129),
     (dict(n_experts=64, top_k=4, hidden=2048, inter=512, shared_inter=512, bias="normal"), 64),
 ]
