@@ -585,25 +585,139 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
 }
 
 // ------------------------------------------------------- grouped GEMM 2 ---
-// Block (tile, n-tile): 64 rows x 128 output columns; wave w owns columns
-// [n0 + 32w, n0 + 32w + 32). A = h (hi and lo passes), K over the 64-groups of I.
-__global__ void __launch_bounds__(256) gemm_down_kernel(GemmArgs a) {
-  __shared__ __align__(16) uint16_t shi[2][BM][72];
-  __shared__ __align__(16) uint16_t slo[2][BM][72];
-  __shared__ __align__(16) float shs[64][BM];
+// Block = (tile, 256 output columns of H), 4 waves, two blocks per CU: 64
+// rows of one expert x 256 columns; wave w computes columns [64w, 64w + 64)
+// as 2 x 2 tiles of 32x32x16 MFMA. A = h as a bf16 (hi, lo) pair (two MFMAs
+// per step, together exact to about 16 significant bits), K over the
+// 64-groups of I. Operands move by global->LDS DMA into DN_NS-stage rings,
+// DN_PF groups ahead, 7 DMAs per wave per group (hi 2, lo 2, codes 2, scales
+// 1); the affine term uses the per-group sums of h written by the gate/up
+// kernel. Output: y[pair][n] = weight * acc (one fp32 row per (token, slot),
+// the shared expert's rows after them).
+constexpr int DN_BN = 256;                 // H columns per block
+constexpr int DN_NS = 3;                   // ring stages
+constexpr int DN_PF = DN_NS - 1;           // prefetch distance in groups
+constexpr int DA_STAGE = BM * 64 * 2;      // 64 rows x 64 bf16, for each of hi and lo
+constexpr int DB_STAGE = DN_BN * 32;       // 256 code rows x 64 int4
+constexpr int DS_STAGE = DN_BN * 4;        // 256 (s, c) words
+
+size_t down_lds_bytes(int GI) { return (size_t)DN_NS * (2 * DA_STAGE + DB_STAGE + DS_STAGE) + (size_t)256 * GI; }
+
+struct DownSources {
+  const uint16_t* hi[2];  // A (instruction t): row 8 (2w + t) + lane / 8, chunk (lane % 8) ^ (row % 8)
+  const uint16_t* lo[2];
+  bool live[2];
+  const uint8_t* b[2];    // code rows: instruction t covers rows 64w + 32t + lane / 2, half lane % 2
+  const uint8_t* s;       // scale word of row 64w + lane
+};
+
+// DMAs of group gn into the free stages; the restrict qualifiers keep the
+// compiler from ordering them against this group's LDS reads (the caller's
+// wait + barrier does).
+__device__ __forceinline__ void down_issue(uint8_t* __restrict__ wrH, uint8_t* __restrict__ wrL,
+                                           uint8_t* __restrict__ wrB, uint8_t* __restrict__ wrS,
+                                           const DownSources& src, int gn, int wv) {
+  dma16(src.b[0] + 32 * gn, wrB + (2 * wv) * 1024);
+  dma16(src.b[1] + 32 * gn, wrB + (2 * wv + 1) * 1024);
+  dma4(src.s + 4 * gn, wrS + wv * 256);
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (src.live[t]) dma16(src.hi[t] + 64 * gn, wrH + (2 * wv + t) * 1024);
+    if (src.live[t]) dma16(src.lo[t] + 64 * gn, wrL + (2 * wv + t) * 1024);
+  }
+}
+
+// One group: acc += s * (A_hi + A_lo) . (16 + q); for an odd group also the
+// affine term of the pair (g - 1, g) (lanes of k-half hh take group g-1+hh).
+__device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, const uint8_t* __restrict__ rdL,
+                                           const uint8_t* __restrict__ rdB, const uint8_t* __restrict__ rdS,
+                                           const float* __restrict__ sHs, uint8_t* __restrict__ wrH,
+                                           uint8_t* __restrict__ wrL, uint8_t* __restrict__ wrB,
+                                           uint8_t* __restrict__ wrS, const DownSources& src, int gn, int g,
+                                           int wv, int brow, int hh, int mrow, float (&cprev)[2], f32x16 (&acc)[4]) {
+  down_issue(wrH, wrL, wrB, wrS, src, gn, wv);
+  bf16x8 ah[2][4], al[2][4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int off = ((4 * hh + st) ^ (mrow & 7)) * 16;
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      ah[mm][st] = *reinterpret_cast<const bf16x8*>(rdH + (32 * mm + mrow) * 128 + off);
+      al[mm][st] = *reinterpret_cast<const bf16x8*>(rdL + (32 * mm + mrow) * 128 + off);
+    }
+  }
+  float cval[2];
+#pragma unroll
+  for (int nn = 0; nn < 2; ++nn) {
+    const uint4 cw = *reinterpret_cast<const uint4*>(rdB + (brow + 32 * nn) * 32 + hh * 16);
+    const uint32_t sw = *reinterpret_cast<const uint32_t*>(rdS + (brow + 32 * nn) * 4);
+    const bf16x8 b[4] = {nib_to_bf16(cw.x), nib_to_bf16(cw.y), nib_to_bf16(cw.z), nib_to_bf16(cw.w)};
+    f32x16 p0 = {}, p1 = {};
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[0][st], b[st], p0, 0, 0, 0);
+      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[1][st], b[st], p1, 0, 0, 0);
+      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[0][st], b[st], p0, 0, 0, 0);
+      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[1][st], b[st], p1, 0, 0, 0);
+    }
+    const float sv = f16f(sw & 0xFFFFu);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      acc[2 * nn][r] += sv * p0[r];
+      acc[2 * nn + 1][r] += sv * p1[r];
+    }
+    cval[nn] = f16f(sw >> 16) - 16.0f * sv;
+  }
+  if (g & 1) {
+    const int gx = g - 1 + hh;
+    const float x0 = sHs[gx * 64 + mrow], x1 = sHs[gx * 64 + 32 + mrow];
+#pragma unroll
+    for (int nn = 0; nn < 2; ++nn) {
+      const float cp = hh ? cval[nn] : cprev[nn];
+      acc[2 * nn] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, cp, acc[2 * nn], 0, 0, 0);
+      acc[2 * nn + 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, cp, acc[2 * nn + 1], 0, 0, 0);
+    }
+  } else {
+    cprev[0] = cval[0];
+    cprev[1] = cval[1];
+  }
+}
+
+__global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int32_t s_dst[BM];
   __shared__ float s_w[BM];
-  const int ntiles = a.tiles[0];
-  if ((int)blockIdx.x >= ntiles) return;
-  const int e = a.tiles[1 + 2 * blockIdx.x], r0 = a.tiles[2 + 2 * blockIdx.x];
-  const int n0 = blockIdx.y * 128;
+  const int GI = a.I / 64, NT = a.H / DN_BN;
+  const int L = xcd_block(a.tiles[0] * NT);
+  if (L < 0) return;
+  const int tile = L / NT, nt = L % NT;
+  const int e = a.tiles[1 + 2 * tile], r0 = a.tiles[2 + 2 * tile];
+  const int n0 = nt * DN_BN;
+  const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  uint8_t* sH = smem;                                               // [NS][64][8 slots of 16 B]
+  uint8_t* sL = sH + DN_NS * DA_STAGE;
+  uint8_t* sB = sL + DN_NS * DA_STAGE;                              // [NS][256 rows][32 B]
+  uint8_t* sS = sB + DN_NS * DB_STAGE;                              // [NS][256 rows] words
+  float* sHs = reinterpret_cast<float*>(sS + DN_NS * DS_STAGE);     // [GI][64 rows]
+
+  DownSources src;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int q = (2 * wv + t) * 64 + lane, row = q >> 1;
+    src.b[t] = rec + a.down_codes + (size_t)(n0 + row) * (a.I / 2) + 16 * (q & 1);
+  }
+  src.s = rec + a.down_sc + (size_t)(n0 + 64 * wv + lane) * GI * 4;
+  for (int g = 0; g < DN_PF; ++g) {
+    const int gc = min(g, GI - 1);
+    dma16(src.b[0] + 32 * gc, sB + g * DB_STAGE + (2 * wv) * 1024);
+    dma16(src.b[1] + 32 * gc, sB + g * DB_STAGE + (2 * wv + 1) * 1024);
+    dma4(src.s + 4 * gc, sS + g * DS_STAGE + wv * 256);
+  }
   const int rows = a.e_off[e + 1] - a.e_off[e];
   const int base = a.e_off[e] + r0;
-  const int G = a.I / 64;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
-  if (threadIdx.x < BM) {
-    const int r = r0 + threadIdx.x;
+  if (tid < BM) {
+    const int r = r0 + tid;
     int dst = -1;
     float w = 0.f;
     if (r < rows) {
@@ -616,92 +730,73 @@ __global__ void __launch_bounds__(256) gemm_down_kernel(GemmArgs a) {
         w = a.route_gamma[r];
       }
     }
-    s_dst[threadIdx.x] = dst;
-    s_w[threadIdx.x] = w;
+    s_dst[tid] = dst;
+    s_w[tid] = w;
   }
-  for (int q = threadIdx.x; q < G * BM; q += 256) {
-    const int g = q / BM, m = q % BM;
-    shs[g][m] = (r0 + m < rows) ? a.hsum[(size_t)(base + m) * G + g] : 0.f;
+  const int nrow = min(rows - r0, BM);  // rows of this tile (>= 1)
+  // h group sums: instruction g loads group g of the 64 rows
+  {
+    const size_t hrow = (size_t)base + min(lane, nrow - 1);
+    for (int g = wv; g < GI; g += 4) dma4(a.hsum + hrow * GI + g, reinterpret_cast<uint8_t*>(sHs) + g * 256);
   }
-  const int lr = threadIdx.x >> 2, lq = threadIdx.x & 3;
-  const bool rv = r0 + lr < rows;
-  const uint4* hrow = reinterpret_cast<const uint4*>(a.h_hi + (size_t)(rv ? base + lr : 0) * a.I + 16 * lq);
-  const uint4* lrow = reinterpret_cast<const uint4*>(a.h_lo + (size_t)(rv ? base + lr : 0) * a.I + 16 * lq);
-  auto load_a = [&](int g, uint4& h0, uint4& h1, uint4& l0, uint4& l1) {
-    if (rv) {
-      h0 = hrow[8 * g];
-      h1 = hrow[8 * g + 1];
-      l0 = lrow[8 * g];
-      l1 = lrow[8 * g + 1];
-    } else {
-      h0 = h1 = l0 = l1 = make_uint4(0, 0, 0, 0);
-    }
-  };
-  const int n = n0 + 32 * wv + (lane & 31);
-  const int hh = lane >> 5;
-  const size_t row_bytes = (size_t)a.I / 2;
-  const uint8_t* crow = rec + a.down_codes + (size_t)n * row_bytes + 16 * hh;
-  const uint32_t* scrow = reinterpret_cast<const uint32_t*>(rec + a.down_sc) + (size_t)n * G;
-
-  f32x16 acc0 = {}, acc1 = {};
-  uint4 h0, h1, l0, l1;
-  load_a(0, h0, h1, l0, l1);
-  uint4 cb = *reinterpret_cast<const uint4*>(crow);
-  uint32_t scv = scrow[0];
-  *reinterpret_cast<uint4*>(&shi[0][lr][16 * lq]) = h0;
-  *reinterpret_cast<uint4*>(&shi[0][lr][16 * lq + 8]) = h1;
-  *reinterpret_cast<uint4*>(&slo[0][lr][16 * lq]) = l0;
-  *reinterpret_cast<uint4*>(&slo[0][lr][16 * lq + 8]) = l1;
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const int buf = g & 1;
-    uint4 nh0, nh1, nl0, nl1, ncb;
-    uint32_t nsc = 0;
-    if (g + 1 < G) {
-      load_a(g + 1, nh0, nh1, nl0, nl1);
-      ncb = *reinterpret_cast<const uint4*>(crow + 32 * (g + 1));
-      nsc = scrow[g + 1];
-    }
-    const bf16x8 b0 = nib_to_bf16(cb.x), b1 = nib_to_bf16(cb.y), b2 = nib_to_bf16(cb.z), b3 = nib_to_bf16(cb.w);
-    f32x16 p0 = {}, p1 = {};
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kk = 32 * hh + 8 * s;
-      const bf16x8 bv = s == 0 ? b0 : (s == 1 ? b1 : (s == 2 ? b2 : b3));
-      const bf16x8 a0 = *reinterpret_cast<const bf16x8*>(&shi[buf][(lane & 31)][kk]);
-      const bf16x8 a1 = *reinterpret_cast<const bf16x8*>(&shi[buf][32 + (lane & 31)][kk]);
-      const bf16x8 c0 = *reinterpret_cast<const bf16x8*>(&slo[buf][(lane & 31)][kk]);
-      const bf16x8 c1 = *reinterpret_cast<const bf16x8*>(&slo[buf][32 + (lane & 31)][kk]);
-      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bv, p0, 0, 0, 0);
-      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bv, p1, 0, 0, 0);
-      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c0, bv, p0, 0, 0, 0);
-      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c1, bv, p1, 0, 0, 0);
+  for (int t = 0; t < 2; ++t) {
+    const int row = 8 * (2 * wv + t) + (lane >> 3), chunk = (lane & 7) ^ (row & 7);
+    const size_t hrow = (size_t)base + min(row, nrow - 1);
+    src.hi[t] = a.h_hi + hrow * a.I + 8 * chunk;
+    src.lo[t] = a.h_lo + hrow * a.I + 8 * chunk;
+    src.live[t] = row < nrow || lane == 0;
+  }
+  for (int g = 0; g < DN_PF; ++g) {
+    const int gc = min(g, GI - 1);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      if (src.live[t]) dma16(src.hi[t] + 64 * gc, sH + g * DA_STAGE + (2 * wv + t) * 1024);
+      if (src.live[t]) dma16(src.lo[t] + 64 * gc, sL + g * DA_STAGE + (2 * wv + t) * 1024);
     }
-    const float sv = f16f(scv & 0xFFFFu), cv = f16f(scv >> 16) - 16.0f * f16f(scv & 0xFFFFu);
+  }
+  const int nl = 64 * wv + (lane & 31);  // first column of this lane (second: + 32)
+  const int brow = nl;
+  const int hh = lane >> 5;
+  const int mrow = lane & 31;
+  f32x16 acc[4] = {};
+  float cprev[2] = {0.f, 0.f};
+  // Waits (PF = 2): step 0 needs A(0), after which only A(1) (4 DMAs) was
+  // issued; step g >= 1 needs group g, issued one step (7 DMAs) earlier.
+  static_assert(DN_PF == 2, "wait counts below are written for PF = 2");
+  for (int g = 0; g < GI; ++g) {
+    if (g == 0)
+      __builtin_amdgcn_s_waitcnt(0x0070 | 4);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070 | 7);
+    __builtin_amdgcn_s_barrier();
+    const int rd = g % DN_NS, wr = (g + DN_PF) % DN_NS;
+    down_group(sH + rd * DA_STAGE, sL + rd * DA_STAGE, sB + rd * DB_STAGE, sS + rd * DS_STAGE, sHs,
+               sH + wr * DA_STAGE, sL + wr * DA_STAGE, sB + wr * DB_STAGE, sS + wr * DS_STAGE, src,
+               min(g + DN_PF, GI - 1), g, wv, brow, hh, mrow, cprev, acc);
+  }
+  if (GI & 1) {  // odd group count: the last group's affine term, paired with zeros
+    const float x0 = hh ? 0.f : sHs[(GI - 1) * 64 + mrow], x1 = hh ? 0.f : sHs[(GI - 1) * 64 + 32 + mrow];
+#pragma unroll
+    for (int nn = 0; nn < 2; ++nn) {
+      const float cp = hh ? 0.f : cprev[nn];
+      acc[2 * nn] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, cp, acc[2 * nn], 0, 0, 0);
+      acc[2 * nn + 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, cp, acc[2 * nn + 1], 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA in flight at exit
+#pragma unroll
+  for (int nn = 0; nn < 2; ++nn) {
+    const int n = n0 + nl + 32 * nn;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
-      acc0[r] += sv * p0[r] + cv * shs[g][m];
-      acc1[r] += sv * p1[r] + cv * shs[g][32 + m];
-    }
-    if (g + 1 < G) {
-      *reinterpret_cast<uint4*>(&shi[buf ^ 1][lr][16 * lq]) = nh0;
-      *reinterpret_cast<uint4*>(&shi[buf ^ 1][lr][16 * lq + 8]) = nh1;
-      *reinterpret_cast<uint4*>(&slo[buf ^ 1][lr][16 * lq]) = nl0;
-      *reinterpret_cast<uint4*>(&slo[buf ^ 1][lr][16 * lq + 8]) = nl1;
-      cb = ncb;
-      scv = nsc;
-    }
-    __syncthreads();
-  }
+      const int m0 = (r >> 2) * 8 + hh * 4 + (r & 3);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m0 = (r >> 2) * 8 + hh * 4 + (r & 3);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int m = m0 + 32 * half;
-      const int dst = s_dst[m];
-      if (dst >= 0) a.y[(size_t)dst * a.H + n] = s_w[m] * (half ? acc1[r] : acc0[r]);
+      for (int half = 0; half < 2; ++half) {
+        const int m = m0 + 32 * half;
+        const int dst = s_dst[m];
+        if (dst >= 0) a.y[(size_t)dst * a.H + n] = s_w[m] * acc[2 * nn + half][r];
+      }
     }
   }
 }
@@ -887,7 +982,16 @@ hipError_t prefill_gateup(void* ws, const PrefillArgs& pa, hipStream_t s) {
 
 hipError_t prefill_down(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
-  launch(gemm_down_kernel, dim3(w->max_tiles, pa.cfg.hidden / 128), dim3(256), 0, s, gemm_args(w, pa));
+  const size_t lds = down_lds_bytes(pa.cfg.inter / 64);
+  static size_t attr_bytes = 0;
+  if (attr_bytes < lds) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(gemm_down_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    attr_bytes = lds;
+  }
+  const int nblk = w->max_tiles * (pa.cfg.hidden / DN_BN);
+  launch(gemm_down_kernel, dim3((unsigned)(8 * ((nblk + 7) / 8))), dim3(256), (uint32_t)lds, s, gemm_args(w, pa));
   return hipGetLastError();
 }
 
