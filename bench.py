@@ -148,6 +148,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-pass", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="after the timed steps, copy BYTES of device memory once with a plain copy "
+                         "kernel (a known-size reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU mode",
@@ -205,6 +208,15 @@ def main() -> int:
         st = pool.stats()
         extra["pool"] = {**st, "hit_rate": st["hits"] / max(1, st["accesses"]),
                          "h2d_GBps": st["h2d_bytes"] / (elapsed / args.steps) / 1e9 / 1.0}
+    if args.copy_calibration > 0:
+        n = args.copy_calibration // 4
+        src_t = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst_t = torch.empty_like(src_t)
+        torch.cuda.synchronize()
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {4 * n} bytes")
+        del src_t, dst_t
     roofline = None
     if not args.no_kernel_pass:
         n_prof = max(1, min(args.steps, 5))

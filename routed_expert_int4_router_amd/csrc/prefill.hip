@@ -41,7 +41,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int BM = 64;        // tile rows (tokens or pairs)
-constexpr int CHUNK = 256;    // pairs per bucketing chunk
+constexpr int CHUNK = 512;    // pairs per bucketing chunk
 
 struct Workspace {
   int T = 0, E = 0, k = 0, H = 0, I = 0;
@@ -200,14 +200,17 @@ __global__ void __launch_bounds__(CHUNK) bucket_count_kernel(const int32_t* __re
 // One block: per-expert totals, expert offsets, per-chunk offsets and the tile
 // list (routed experts, then the shared expert over all T tokens).
 __global__ void __launch_bounds__(1024) bucket_scan_kernel(const int32_t* __restrict__ cnt, int nchunk, int E, int T,
-                                                           int k, int32_t* chunk_off, int32_t* e_off, int32_t* tiles,
+                                                           int k, int32_t* __restrict__ chunk_off,
+                                                           int32_t* __restrict__ e_off, int32_t* __restrict__ tiles,
                                                            int max_tiles) {
   __shared__ int32_t s_tot[1024], s_tiles[1024];
   __shared__ int32_t s_base, s_tbase;
   const int e = threadIdx.x;
   int tot = 0;
-  if (e < E)
+  if (e < E) {
+#pragma unroll 8
     for (int c = 0; c < nchunk; ++c) tot += cnt[(size_t)c * E + e];
+  }
   const int ntile = (tot + BM - 1) / BM;
   // block-wide exclusive scans (sequential over waves, DPP within a wave)
   const uint32_t inc_t = dpp::wave_prefix_u32((uint32_t)tot);
@@ -236,6 +239,7 @@ __global__ void __launch_bounds__(1024) bucket_scan_kernel(const int32_t* __rest
   if (e < E) {
     e_off[e] = off;
     int run = off;
+#pragma unroll 8
     for (int c = 0; c < nchunk; ++c) {
       chunk_off[(size_t)c * E + e] = run;
       run += cnt[(size_t)c * E + e];
@@ -274,26 +278,27 @@ __global__ void __launch_bounds__(CHUNK) bucket_scatter_kernel(const int32_t* __
 }
 
 // ------------------------------------------------------- grouped GEMM 1 ---
-// Block = (tile, 128 columns of I), 4 waves: 64 rows of one expert (sorted
-// pairs, or tokens for the shared expert) x 128 gate + 128 up columns. Waves
-// 0,1 compute gate columns [64w, 64w + 64), waves 2,3 the same up columns;
-// each wave is 64 x 64 (2 x 2 tiles of 32x32x16 MFMA). K runs over the
-// 64-groups of H. Two blocks share a CU: their waves are not tied by a common
-// barrier, so one block's VALU work (code conversion, group scaling) overlaps
-// the other's MFMAs on the same SIMD.
+// Block = (tile, 64 columns of I), 4 waves, two blocks per CU: 64 rows of one
+// expert (sorted pairs, or tokens for the shared expert) x 64 gate + 64 up
+// columns. Waves 0,1 compute gate columns [32w, 32w + 32), waves 2,3 the
+// same up columns; each wave is 64 x 32 (two 32x32x16 MFMA tiles). K runs
+// over the 64-groups of H. The two blocks of a CU are not tied by a common
+// barrier, so one block's VALU work (code conversion, group scaling)
+// overlaps the other's MFMAs on the same SIMD.
 //
-// Operands reach LDS by direct global->LDS DMA (no registers), GU_PF groups
-// ahead into GU_NS-stage rings: per group the A rows (the k-permuted x of the
-// tile's tokens, 8 KB; rows past the tile's end are not fetched), the code
-// rows (256 x 32 bytes) and the (s, c) words (256 x 4 bytes). Every wave
-// issues the same 5 DMAs per group (a group past the end reloads the last
-// one into a free stage), so waiting for "all but the newest 5 * (PF - 1)"
-// DMAs plus one barrier makes group g's stages visible to every wave. Each
-// wave reads a group's operands into registers one group ahead of its MFMAs.
+// Operands reach LDS by direct global->LDS DMA (no registers): the A rows
+// (the k-permuted x of the tile's tokens; rows past the tile's end are not
+// fetched) one group (8 KB) at a time, GU_PF groups ahead, into a GU_NA-stage
+// ring; the code rows and (s, c) words a quad of 4 groups at a time (one
+// 128-byte line per code row, 16 bytes of scales per row), one quad ahead,
+// into 2-stage rings. Few, full-line requests matter here: the L2 request
+// rate, not its bandwidth, limits this kernel. Every wave issues the same
+// DMAs in the same order, so fixed "all but the newest n" waits plus one
+// barrier per group make a group's stages visible to every wave.
 //
 // Per group: P = A . (16 + q) on the matrix cores (exact integer operands,
 // fp32 accumulate) and acc += s * P. The affine term sum_g (c - 16 s) * sum_k x
-// runs as fp32 MFMAs (K = 2: two groups per step).
+// runs as fp32 MFMAs (K = 2 per step) once per quad.
 struct GemmArgs {
   const uint16_t* x;          // [T][H]
   const uint16_t* xp;         // [T][H], 8-chunks in nib_to_bf16 order
@@ -335,102 +340,107 @@ __device__ __forceinline__ int xcd_block(int n_real) {
   return (i < per && l < n_real) ? l : -1;
 }
 
-constexpr int GU_BN = 128;                  // I columns per block
-constexpr int GU_NS = 4;                    // ring stages
-constexpr int GU_PF = GU_NS - 1;            // prefetch distance in groups
-constexpr int A_STAGE = BM * 64 * 2;        // 64 rows x 64 bf16 (8 KB)
-constexpr int B_STAGE = 2 * GU_BN * 32;     // 256 code rows x 64 int4 (8 KB)
-constexpr int S_STAGE = 2 * GU_BN * 4;      // 256 (s, c) words (1 KB)
+constexpr int GU_BN = 64;                     // I columns per block
+constexpr int GU_NA = 4;                      // A ring stages (one group each)
+constexpr int GU_PF = GU_NA - 1;              // A prefetch distance in groups
+constexpr int A_STAGE = BM * 64 * 2;          // 64 rows x 64 bf16 (8 KB)
+constexpr int BQ_STAGE = 2 * GU_BN * 128;     // 128 code rows x 4 groups (16 KB)
+constexpr int SQ_STAGE = 2 * GU_BN * 16;      // 128 rows x 4 (s, c) words (2 KB)
 
 size_t gateup_lds_bytes(int G) {
-  return (size_t)GU_NS * (A_STAGE + B_STAGE + S_STAGE) + (size_t)256 * G;
+  return (size_t)GU_NA * A_STAGE + 2 * (size_t)BQ_STAGE + 2 * (size_t)SQ_STAGE + (size_t)256 * G;
 }
+
+// Per-lane DMA sources (group / quad 0).
+struct GateUpSources {
+  const uint16_t* a[2];  // A (instruction t): row 8 (2w + t) + lane / 8, chunk (lane % 8) ^ (row % 8); +64 g
+  bool a_live[2];        // the row exists (lane 0 always fetches, keeping the DMA issued)
+  const uint8_t* b[4];   // code rows, instruction t: row 32w + 8t + lane / 8, chunk (lane % 8) ^ (row % 8); +128 Q
+  const uint8_t* s;      // scale words of row 32w + lane (lanes < 32); +16 Q
+};
 
 // Operands of one K group for one lane, read one group ahead of their use.
 struct GroupFrag {
   bf16x8 a0[4], a1[4];  // A rows mrow and 32 + mrow for the 4 MFMA steps
-  uint4 c0, c1;         // 32 codes of columns n and n + 32 (k half hh)
-  uint32_t s0, s1;      // (s, c) words of those columns
-  float x0, x1;         // x sums of rows mrow, 32 + mrow, group 2 * (g / 2) + hh
+  uint4 codes;          // 32 codes of column brow (k half hh)
+  uint32_t sc;          // (s, c) of column brow
+};
+// Affine-term operands of one quad, read with its last group.
+struct AffineFrag {
+  float cp[2], x0[2], x1[2];
 };
 
-// Per-lane DMA sources (group 0; group g adds 64 g elements for A, 32 g bytes
-// for codes, 4 g bytes for scales).
-struct GateUpSources {
-  const uint16_t* a[2];  // A (instruction t): row 8 (2w + t) + lane / 8, 16-byte chunk (lane % 8) ^ (row % 8)
-  bool a_live[2];        // the row exists (lane 0 always fetches, keeping the DMA issued)
-  const uint8_t* b[2];   // code rows (instruction t: rows 64w + 32t + lane / 2, half lane % 2)
-  const uint8_t* s;      // scale word of row 64w + lane
-};
-
-// Step for group g: issue the DMAs of group g + PF into the free stages (wr*),
-// then read group g's operands from its stages (rd*). The restrict qualifiers
-// tell the compiler that the stages read are not the ones written, so it adds
-// no wait of its own between the DMAs and the LDS reads; the caller's vmcnt
-// wait + barrier orders them.
+// Step for group g = 4Q + J: issue (for J == 0) the next quad's code rows and
+// scale words, then A(g + PF); then read group g's operands from LDS. The
+// restrict qualifiers tell the compiler that the stages read are not the
+// ones written, so it adds no wait of its own between DMAs and LDS reads;
+// the caller's vmcnt wait + barrier orders them.
+template <int J>
 __device__ __forceinline__ void gateup_fetch(const uint8_t* __restrict__ rdA, const uint8_t* __restrict__ rdB,
                                              const uint8_t* __restrict__ rdS, uint8_t* __restrict__ wrA,
                                              uint8_t* __restrict__ wrB, uint8_t* __restrict__ wrS,
-                                             const float* __restrict__ sX, const GateUpSources& src, int gn, int g,
-                                             int wv, int lane, int brow, int hh, int mrow, GroupFrag& f) {
-  dma16(src.b[0] + 32 * gn, wrB + (2 * wv) * 1024);
-  dma16(src.b[1] + 32 * gn, wrB + (2 * wv + 1) * 1024);
-  dma4(src.s + 4 * gn, wrS + wv * 256);
+                                             const float* __restrict__ sX, const GateUpSources& src, int qn, int gn,
+                                             int Q, int wv, int lane, int brow, int hh, int mrow, GroupFrag& f,
+                                             AffineFrag& af) {
+  if constexpr (J == 0) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) dma16(src.b[t] + 128 * qn, wrB + (4 * wv + t) * 1024);
+    if (lane < 32) dma16(src.s + 16 * qn, wrS + wv * 512);
+  }
   if (src.a_live[0]) dma16(src.a[0] + 64 * gn, wrA + (2 * wv) * 1024);
   if (src.a_live[1]) dma16(src.a[1] + 64 * gn, wrA + (2 * wv + 1) * 1024);
-  f.c0 = *reinterpret_cast<const uint4*>(rdB + brow * 32 + hh * 16);
-  f.c1 = *reinterpret_cast<const uint4*>(rdB + (brow + 32) * 32 + hh * 16);
-  f.s0 = *reinterpret_cast<const uint32_t*>(rdS + brow * 4);
-  f.s1 = *reinterpret_cast<const uint32_t*>(rdS + (brow + 32) * 4);
+  const int slot = (2 * J + hh) ^ (brow & 7);
+  f.codes = *reinterpret_cast<const uint4*>(rdB + brow * 128 + slot * 16);
+  f.sc = *reinterpret_cast<const uint32_t*>(rdS + brow * 16 + J * 4);
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     const int off = ((4 * hh + st) ^ (mrow & 7)) * 16;
     f.a0[st] = *reinterpret_cast<const bf16x8*>(rdA + mrow * 128 + off);
     f.a1[st] = *reinterpret_cast<const bf16x8*>(rdA + (32 + mrow) * 128 + off);
   }
-  const int gx = (g & ~1) + hh;
-  f.x0 = sX[gx * 64 + mrow];
-  f.x1 = sX[gx * 64 + 32 + mrow];
-}
-
-// One group: P = A . (16 + q) per 32x32 tile, acc += s * P. For an odd group
-// also the affine term of the pair (g - 1, g): lanes of k-half hh take group
-// g - 1 + hh, with cprev the (c - 16 s) values of group g - 1.
-__device__ __forceinline__ void gateup_compute(const GroupFrag& f, bool odd, int hh, float cprev0, float cprev1,
-                                               f32x16 (&acc)[4]) {
-  const uint4 cw[2] = {f.c0, f.c1};
-  const float sv[2] = {f16f(f.s0 & 0xFFFFu), f16f(f.s1 & 0xFFFFu)};
+  if constexpr (J == 3) {
 #pragma unroll
-  for (int nn = 0; nn < 2; ++nn) {
-    const bf16x8 b[4] = {nib_to_bf16(cw[nn].x), nib_to_bf16(cw[nn].y), nib_to_bf16(cw[nn].z),
-                         nib_to_bf16(cw[nn].w)};
-    f32x16 p0 = {}, p1 = {};
-#pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0[st], b[st], p0, 0, 0, 0);
-      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1[st], b[st], p1, 0, 0, 0);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      acc[2 * nn][r] += sv[nn] * p0[r];
-      acc[2 * nn + 1][r] += sv[nn] * p1[r];
+    for (int u = 0; u < 2; ++u) {
+      const int j = 2 * u + hh, g = 4 * Q + j;
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(rdS + brow * 16 + j * 4);
+      af.cp[u] = f16f(w >> 16) - 16.0f * f16f(w & 0xFFFFu);
+      af.x0[u] = sX[g * 64 + mrow];
+      af.x1[u] = sX[g * 64 + 32 + mrow];
     }
   }
-  if (odd) {
-    const float c0 = f16f(f.s0 >> 16) - 16.0f * f16f(f.s0 & 0xFFFFu);
-    const float c1 = f16f(f.s1 >> 16) - 16.0f * f16f(f.s1 & 0xFFFFu);
-    const float cp0 = hh ? c0 : cprev0, cp1 = hh ? c1 : cprev1;
-    acc[0] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.x0, cp0, acc[0], 0, 0, 0);
-    acc[1] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.x1, cp0, acc[1], 0, 0, 0);
-    acc[2] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.x0, cp1, acc[2], 0, 0, 0);
-    acc[3] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.x1, cp1, acc[3], 0, 0, 0);
+}
+
+// P = A . (16 + q) for one group (exact operands, fp32 accumulate), acc += s * P.
+__device__ __forceinline__ void gateup_compute(const GroupFrag& f, f32x16& acc0, f32x16& acc1) {
+  const bf16x8 b[4] = {nib_to_bf16(f.codes.x), nib_to_bf16(f.codes.y), nib_to_bf16(f.codes.z),
+                       nib_to_bf16(f.codes.w)};
+  f32x16 p0 = {}, p1 = {};
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0[st], b[st], p0, 0, 0, 0);
+    p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1[st], b[st], p1, 0, 0, 0);
+  }
+  const float sv = f16f(f.sc & 0xFFFFu);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    acc0[r] += sv * p0[r];
+    acc1[r] += sv * p1[r];
+  }
+}
+
+// Affine term of one quad: acc[m][n] += sum_{g in quad} xs[m][g] * (c - 16 s)[n][g].
+__device__ __forceinline__ void gateup_affine(const AffineFrag& af, f32x16& acc0, f32x16& acc1) {
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(af.x0[u], af.cp[u], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(af.x1[u], af.cp[u], acc1, 0, 0, 0);
   }
 }
 
 __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int32_t s_tok[BM];
-  const int G = a.H / 64, NT = (a.I + GU_BN - 1) / GU_BN;
+  const int G = a.H / 64, NQ = G / 4, NT = (a.I + GU_BN - 1) / GU_BN;
   const int L = xcd_block(a.tiles[0] * NT);
   if (L < 0) return;
   const int tile = L / NT, nt = L % NT;
@@ -438,30 +448,27 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   const int n0 = nt * GU_BN;
   const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-  uint8_t* sA = smem;                                              // [NS][64 rows][8 slots of 16 B]
-  uint8_t* sB = sA + GU_NS * A_STAGE;                              // [NS][256 rows][32 B]
-  uint8_t* sS = sB + GU_NS * B_STAGE;                              // [NS][256 rows] words
-  float* sX = reinterpret_cast<float*>(sS + GU_NS * S_STAGE);      // [G][64 rows]
+  uint8_t* sA = smem;                                       // [NA][64 rows][8 slots of 16 B]
+  uint8_t* sB = sA + GU_NA * A_STAGE;                       // [2][128 rows][8 slots of 16 B] (4 groups)
+  uint8_t* sS = sB + 2 * BQ_STAGE;                          // [2][128 rows][4 words]
+  float* sX = reinterpret_cast<float*>(sS + 2 * SQ_STAGE);  // [G][64 rows]
 
   GateUpSources src;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int q = (2 * wv + t) * 64 + lane, row = q >> 1;
+  for (int t = 0; t < 4; ++t) {
+    const int row = 32 * wv + 8 * t + (lane >> 3), chunk = (lane & 7) ^ (row & 7);
     const int n = min(n0 + (row & (GU_BN - 1)), a.I - 1);
-    src.b[t] = rec + (row < GU_BN ? a.gate_codes : a.up_codes) + (size_t)n * (a.H / 2) + 16 * (q & 1);
+    src.b[t] = rec + (row < GU_BN ? a.gate_codes : a.up_codes) + (size_t)n * (a.H / 2) + 16 * chunk;
   }
   {
-    const int row = 64 * wv + lane;
+    const int row = 32 * wv + (lane & 31);
     const int n = min(n0 + (row & (GU_BN - 1)), a.I - 1);
     src.s = rec + (row < GU_BN ? a.gate_sc : a.up_sc) + (size_t)n * G * 4;
   }
-  // code rows and scales of groups 0 .. PF-1 first: they do not depend on the tile's tokens
-  for (int g = 0; g < GU_PF; ++g) {
-    const int gc = min(g, G - 1);
-    dma16(src.b[0] + 32 * gc, sB + g * B_STAGE + (2 * wv) * 1024);
-    dma16(src.b[1] + 32 * gc, sB + g * B_STAGE + (2 * wv + 1) * 1024);
-    dma4(src.s + 4 * gc, sS + g * S_STAGE + wv * 256);
-  }
+  // quad 0 of codes and scales first: they do not depend on the tile's tokens
+#pragma unroll
+  for (int t = 0; t < 4; ++t) dma16(src.b[t], sB + (4 * wv + t) * 1024);
+  if (lane < 32) dma16(src.s, sS + wv * 512);
 
   const int rows = a.e_off[e + 1] - a.e_off[e];
   if (tid < BM) {
@@ -489,97 +496,92 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   }
 
   const int mat = wv >> 1;
-  const int nl = 64 * (wv & 1) + (lane & 31);  // first column of this lane within the block (second: + 32)
+  const int nl = 32 * (wv & 1) + (lane & 31);  // column within the block
   const int brow = GU_BN * mat + nl;           // code / scale row within the block
   const int hh = lane >> 5;
   const int mrow = lane & 31;
-  f32x16 acc[4] = {};
+  f32x16 acc0 = {}, acc1 = {};
   GroupFrag fa, fb;
-  float cprev0 = 0.f, cprev1 = 0.f;
-  // Step g (wait for group g's stages, barrier, DMAs of g + PF, LDS ->
-  // registers) runs one group ahead of compute g. Waits: after the prologue
-  // only the A DMAs (2 per group) of groups 0 .. PF-1 follow the code/scale
-  // DMAs of those groups, so step g < PF-1 waits for all but the
-  // 2 (PF-1-g) newer A DMAs plus the 5 g the steps since issued; from step
-  // PF-1 on the count is 5 (PF - 1). lgkmcnt(0) makes this wave's reads of
-  // the stages about to be overwritten complete.
+  AffineFrag af;
+  // Step g (wait, barrier, DMAs, LDS -> registers) runs one group ahead of
+  // compute g. Per step a wave issues A(g + 3) (2 DMAs), preceded at a quad's
+  // first group by the next quad's codes and scales (5 DMAs). Waiting for
+  // A(g) leaves the DMAs of steps g-2 and g-1 in flight: 4 when neither
+  // starts a quad (J = 0, 3), 9 otherwise; the codes and scales of quad Q
+  // were issued before A(4Q) and so are covered at J = 0. lgkmcnt(0) makes
+  // this wave's reads of the stages about to be overwritten complete.
   static_assert(GU_PF == 3, "wait counts below are written for PF = 3");
-  auto step = [&](int g, GroupFrag& f) {
-    switch (g) {
-      case 0: __builtin_amdgcn_s_waitcnt(0x0070 | 4); break;   // A(1), A(2) after A(0)
-      case 1: __builtin_amdgcn_s_waitcnt(0x0070 | 7); break;   // A(2) + step 0
-      default: __builtin_amdgcn_s_waitcnt(0x0070 | 10); break; // steps g-2, g-1
-    }
-    __builtin_amdgcn_s_barrier();
-    gateup_fetch(sA + (g % GU_NS) * A_STAGE, sB + (g % GU_NS) * B_STAGE, sS + (g % GU_NS) * S_STAGE,
-                 sA + ((g + GU_PF) % GU_NS) * A_STAGE, sB + ((g + GU_PF) % GU_NS) * B_STAGE,
-                 sS + ((g + GU_PF) % GU_NS) * S_STAGE, sX, src, min(g + GU_PF, G - 1), g, wv, lane, brow, hh,
-                 mrow, f);
-  };
-  step(0, fa);
-  for (int g = 0; g < G; g += 2) {
-    step(g + 1, fb);
-    gateup_compute(fa, false, hh, 0.f, 0.f, acc);
-    cprev0 = f16f(fa.s0 >> 16) - 16.0f * f16f(fa.s0 & 0xFFFFu);
-    cprev1 = f16f(fa.s1 >> 16) - 16.0f * f16f(fa.s1 & 0xFFFFu);
-    if (g + 2 < G) step(g + 2, fa);
-    gateup_compute(fb, true, hh, cprev0, cprev1, acc);
+#define GU_STEP(Q, J, WAIT, F)                                                                                    \
+  {                                                                                                               \
+    const int g = 4 * (Q) + (J);                                                                                  \
+    __builtin_amdgcn_s_waitcnt(0x0070 | (WAIT));                                                                  \
+    __builtin_amdgcn_s_barrier();                                                                                 \
+    gateup_fetch<J>(sA + (g % GU_NA) * A_STAGE, sB + ((Q) & 1) * BQ_STAGE, sS + ((Q) & 1) * SQ_STAGE,            \
+                    sA + ((g + GU_PF) % GU_NA) * A_STAGE, sB + (((Q) + 1) & 1) * BQ_STAGE,                        \
+                    sS + (((Q) + 1) & 1) * SQ_STAGE, sX, src, min((Q) + 1, NQ - 1), min(g + GU_PF, G - 1), (Q), \
+                    wv, lane, brow, hh, mrow, F, af);                                                             \
   }
-  // SwiGLU: gate waves publish through LDS (the A and code rings, once no DMA is in flight)
+  GU_STEP(0, 0, 4, fa)
+  for (int Q = 0; Q < NQ; ++Q) {
+    GU_STEP(Q, 1, 9, fb)
+    gateup_compute(fa, acc0, acc1);
+    GU_STEP(Q, 2, 9, fa)
+    gateup_compute(fb, acc0, acc1);
+    GU_STEP(Q, 3, 4, fb)
+    gateup_compute(fa, acc0, acc1);
+    if (Q + 1 < NQ) GU_STEP(Q + 1, 0, 4, fa)
+    gateup_compute(fb, acc0, acc1);
+    gateup_affine(af, acc0, acc1);
+  }
+#undef GU_STEP
+  // SwiGLU: gate waves publish through LDS (the A ring, once no DMA is in flight)
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
   constexpr int SGS = GU_BN + 1;
-  static_assert(BM * SGS * 4 <= GU_NS * (A_STAGE + B_STAGE), "SwiGLU exchange must fit the rings");
+  static_assert(BM * SGS * 4 <= GU_NA * A_STAGE, "SwiGLU exchange must fit the A ring");
   float* sg = reinterpret_cast<float*>(sA);  // [64][GU_BN + 1]
   if (mat == 0) {
 #pragma unroll
-    for (int nn = 0; nn < 2; ++nn)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
-        sg[m * SGS + nl + 32 * nn] = acc[2 * nn][r];
-        sg[(32 + m) * SGS + nl + 32 * nn] = acc[2 * nn + 1][r];
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
+      sg[m * SGS + nl] = acc0[r];
+      sg[(32 + m) * SGS + nl] = acc1[r];
+    }
   }
   __syncthreads();
   const int base = a.e_off[e] + r0;
-  if (mat == 1) {
+  // h is stored with each 8-chunk in nib_to_bf16 order, ready for the down GEMM's DMA
+  const int p = nl & 7;
+  const int col = n0 + (nl & ~7) + (p < 4 ? 2 * p : 2 * (p - 4) + 1);
+  if (mat == 1 && n0 + nl < a.I) {
 #pragma unroll
-    for (int nn = 0; nn < 2; ++nn) {
-      const int c = nl + 32 * nn;
-      if (n0 + c >= a.I) continue;
-      // h is stored with each 8-chunk in nib_to_bf16 order, ready for the down GEMM's DMA
-      const int p = c & 7;
-      const int col = n0 + (c & ~7) + (p < 4 ? 2 * p : 2 * (p - 4) + 1);
+    for (int r = 0; r < 16; ++r) {
+      const int m0 = (r >> 2) * 8 + hh * 4 + (r & 3);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m0 = (r >> 2) * 8 + hh * 4 + (r & 3);
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int m = m0 + 32 * half;
-          if (r0 + m < rows) {
-            const float gt = sg[m * SGS + c];
-            const float u = acc[2 * nn + half][r];
-            const float hv = gt / (1.0f + expf(-gt)) * u;
-            const uint16_t hi = to_bf16_rne(hv);
-            const uint16_t lo = to_bf16_rne(hv - bf16f(hi));
-            const size_t o = (size_t)(base + m) * a.I + col;
-            a.h_hi[o] = hi;
-            a.h_lo[o] = lo;
-            sg[m * SGS + c] = bf16f(hi) + bf16f(lo);  // what the down GEMM multiplies
-          }
+      for (int half = 0; half < 2; ++half) {
+        const int m = m0 + 32 * half;
+        if (r0 + m < rows) {
+          const float gt = sg[m * SGS + nl];
+          const float u = half ? acc1[r] : acc0[r];
+          const float hv = gt / (1.0f + expf(-gt)) * u;
+          const uint16_t hi = to_bf16_rne(hv);
+          const uint16_t lo = to_bf16_rne(hv - bf16f(hi));
+          const size_t o = (size_t)(base + m) * a.I + col;
+          a.h_hi[o] = hi;
+          a.h_lo[o] = lo;
+          sg[m * SGS + nl] = bf16f(hi) + bf16f(lo);  // what the down GEMM multiplies
         }
       }
     }
   }
   __syncthreads();
-  // per-row sums of each 64-column group of h (the down matrix's quant groups)
-  if (tid < 2 * BM) {
-    const int m = tid & (BM - 1), part = tid >> 6;
-    if (r0 + m < rows && n0 + 64 * part < a.I) {
+  // per-row sum of this 64-column group of h (a quant group of the down matrix)
+  if (tid < BM) {
+    const int m = tid;
+    if (r0 + m < rows && n0 < a.I) {
       float sum = 0.f;
-      for (int c = 0; c < 64; ++c) sum += sg[m * SGS + 64 * part + c];
-      a.hsum[(size_t)(base + m) * (a.I / 64) + n0 / 64 + part] = sum;
+      for (int c = 0; c < 64; ++c) sum += sg[m * SGS + c];
+      a.hsum[(size_t)(base + m) * (a.I / 64) + nt] = sum;
     }
   }
 }
