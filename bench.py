@@ -137,13 +137,37 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
+def link_probe(torch, chunk: int, n: int = 512) -> float:
+    """Host->device rate of pinned hipMemcpyAsync copies of one expert record
+    (the pool's miss unit), back to back on one stream after a warm-up: the
+    link's practical peak for that transfer size."""
+    slots = 16
+    src = torch.empty(chunk * slots, dtype=torch.uint8).pin_memory()
+    dst = torch.empty(chunk * slots, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+
+    def burst(count):
+        with torch.cuda.stream(s):
+            for i in range(count):
+                j = (i % slots) * chunk
+                dst[j:j + chunk].copy_(src[j:j + chunk], non_blocking=True)
+        s.synchronize()
+
+    burst(2 * slots)
+    t0 = time.perf_counter()
+    burst(n)
+    dt = time.perf_counter() - t0
+    return round(n * chunk / dt / 1e9, 2)
+
+
 # -------------------------------------------------------------------- main ---
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 20 for one layer, 3 for resident stacks, 2 for the pooled stack)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default: 3 for one layer, else 1)")
     ap.add_argument("--workload", default="decode80b")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -167,6 +191,10 @@ def main() -> int:
         return 1
     cfg = synth.get_config(args.workload)
     T = cfg.n_tokens
+    if args.steps is None:
+        args.steps = 20 if cfg.n_layers == 1 else (2 if cfg.pool_budget else 3)
+    if args.warmup is None:
+        args.warmup = 3 if cfg.n_layers == 1 else 1
     log(f"workload {cfg.name}: {cfg.description}")
     t0 = time.perf_counter()
     storage = moe.STORE_HOST if cfg.pool_budget else moe.STORE_DEVICE
@@ -205,9 +233,10 @@ def main() -> int:
 
     extra = {}
     if pool is not None:
-        st = pool.stats()
-        extra["pool"] = {**st, "hit_rate": st["hits"] / max(1, st["accesses"]),
-                         "h2d_GBps": st["h2d_bytes"] / (elapsed / args.steps) / 1e9 / 1.0}
+        st = pool.stats()  # counts of the last timed step (the pool is reset at every step)
+        extra["pool"] = {**st, "hit_rate": round(st["hits"] / max(1, st["accesses"]), 4),
+                         "h2d_GBps": round(st["h2d_bytes"] / (elapsed / args.steps) / 1e9, 2),
+                         "link_probe_GBps": link_probe(torch, moe.expert_bytes(cfg))}
     if args.copy_calibration > 0:
         n = args.copy_calibration // 4
         src_t = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -219,7 +248,7 @@ def main() -> int:
         del src_t, dst_t
     roofline = None
     if not args.no_kernel_pass:
-        n_prof = max(1, min(args.steps, 5))
+        n_prof = max(1, min(args.steps, 5 if cfg.n_layers == 1 else 1))
         model.profile_enable(True)
         for i in range(n_prof):
             step()
