@@ -51,16 +51,28 @@ def log(msg: str) -> None:
 # ------------------------------------------------------- algorithmic bytes ---
 
 def decode_kernel_bytes(cfg, stack: bool) -> dict:
-    """Bytes each decode kernel must move per launch (one token, one layer)."""
+    """Bytes each decode kernel must move per launch (one token, one layer).
+
+    Fused path (expert + reduce): the expert kernel reads the k + 1 records
+    (gate, up, down codes and scales), x and the logits, and writes one fp32
+    partial row of H per (slot, I slice); reduce reads those rows and writes
+    out (a stack also reads the residual and writes the bf16 recast).
+    Two-kernel path (gateup + down, for shapes the fused kernel does not take).
+    """
     H, I, E, k, b = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.bits
     codes = I * H * b // 8          # one matrix
     sc = I * H // 64 * 4
     router = (E + 1) * H * 4 + E * 4 + H * 2 + (E + 1) * 4
+    parts = (k + 1) * (I * b // 128) * H * 4
+    expert = (k + 1) * 3 * (codes + sc) + H * 2 + (E + 1) * 4 + parts
+    reduce = parts + H * 4
     gateup = (k + 1) * 2 * (codes + sc) + H * 2 + (E + 1) * 4 + (k + 1) * I * 4
     down = (k + 1) * (codes + sc) + (k + 1) * I * 4 + (k + 1) * 4 + H * 4
     if stack:
-        down += H * 4 + H * 2       # residual read + bf16 recast write
-    return {"router": router, "gateup": gateup, "down": down, "topk": (E + 1) * 4 + 2 * k * 4}
+        reduce += H * 4 + H * 2     # residual read + bf16 recast write
+        down += H * 4 + H * 2
+    return {"router": router, "expert": expert, "reduce": reduce, "gateup": gateup, "down": down,
+            "topk": (E + 1) * 4 + 2 * k * 4}
 
 
 def step_bytes_per_token(cfg) -> int:

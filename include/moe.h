@@ -85,12 +85,15 @@ typedef struct moe_model moe_model;
 typedef struct moe_pool moe_pool;
 
 /* ---------------------------------------------------------------- layout ---
- * Packed expert record (one expert, inter = I): gate codes [I][H], up codes
- * [I][H], down codes [H][I], row-major; int4 stores element k of a row in
- * byte k>>1 (even k in the low nibble), int8 one unsigned byte per element.
- * Then (scale, bias) fp16 pairs per 64-element group along each row: gate
- * [I][H/64][2], up [I][H/64][2], down [H][I/64][2]. Then zero bytes up to
- * the stride = round_up(record bytes, 4096). The dequantised weight is
+ * Packed expert record (one expert, inter = I): gate codes [I][H] and up
+ * codes [I][H], row-major; then the down matrix [H][I] in 16-byte tiles
+ * [I*bits/128][H][16]: each row is cut into 16-byte tiles (32 int4 or 16 int8
+ * codes) and tile t of every row precedes tile t+1 of any row, so an I-slice
+ * of the whole matrix is contiguous. int4 stores element k of a row in byte
+ * k>>1 (even k in the low nibble), int8 one unsigned byte per element. Then
+ * (scale, bias) fp16 pairs per 64-element group along each row: gate
+ * [I][H/64][2], up [I][H/64][2], and down group-major [I/64][H][2]. Then zero
+ * bytes up to the stride = round_up(record bytes, 4096). The dequantised weight is
  * scale * code + bias. Global expert id gid = layer * E + e; record gid sits
  * at byte offset base + gid * stride (fixed-stride blob, one read of the
  * record bytes per expert: paotong.dev commentary, paragraph on the fetch
@@ -124,8 +127,9 @@ moe_status moe_pack(const moe_config* cfg, int32_t inter, const float* w_gate, c
                     const float* w_down, int64_t n, void* dst, size_t dst_bytes);
 
 /* Decode one record (host) for inspection: codes one byte per element in the
- * order gate [I][H], up [I][H], down [H][I] (3*H*inter bytes into q_out);
- * fp16 bit patterns of the (scale, bias) pairs in record order into sc_out
+ * order gate [I][H], up [I][H], down [H][I] (3*H*inter bytes into q_out, the
+ * down tiles put back into rows); fp16 bit patterns of the (scale, bias)
+ * pairs as gate [I][H/64][2], up [I][H/64][2], down [H][I/64][2] into sc_out
  * (3*H*inter/64*2 uint16). */
 moe_status moe_unpack(const moe_config* cfg, int32_t inter, const void* record, uint8_t* q_out,
                       uint16_t* sc_out);

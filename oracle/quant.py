@@ -15,10 +15,15 @@ unsigned, every rounding to nearest with ties to even, and the codes computed
 from the already-rounded scale and bias.
 
 Record layout (both packers are written from this description):
-  gate codes [I][H], up codes [I][H], down codes [H][I]   row-major;
-      int4: element k of a row sits in byte k>>1, even k in the low nibble;
-      int8: one unsigned byte per element;
-  gate (s,c) [I][H/64][2], up (s,c) [I][H/64][2], down (s,c) [H][I/64][2]  fp16;
+  gate codes [I][H], up codes [I][H]   row-major;
+  down codes [I*bits/128][H][16 bytes]: row n of the down matrix [H][I] is cut
+      into 16-byte tiles (32 int4 / 16 int8 codes) and tile t of every row
+      comes before tile t+1 of any row (so one I-slice of the whole matrix is
+      contiguous);
+      in a row or tile, int4 element k sits in byte k>>1, even k in the low
+      nibble; int8: one unsigned byte per element;
+  gate (s,c) [I][H/64][2], up (s,c) [I][H/64][2]  fp16, row-major;
+  down (s,c) [I/64][H][2]  fp16, group-major;
   zero bytes up to the stride, stride = round_up(record bytes, 4096).
 """
 from __future__ import annotations
@@ -203,6 +208,34 @@ def _sc_from_bytes(b: np.ndarray, rows: int, groups: int) -> Tuple[np.ndarray, n
     return sc[:, :, 0].copy(), sc[:, :, 1].copy()
 
 
+TILE = 16  # bytes of a down-matrix tile
+
+
+def tile_rows(b: np.ndarray, rows: int) -> np.ndarray:
+    """Row-major bytes [rows][row_bytes] -> [row_bytes/16][rows][16]."""
+    b = np.asarray(b, dtype=np.uint8).reshape(rows, -1, TILE)
+    return np.ascontiguousarray(b.transpose(1, 0, 2)).reshape(-1)
+
+
+def untile_rows(b: np.ndarray, rows: int, row_bytes: int) -> np.ndarray:
+    """Inverse of tile_rows."""
+    b = np.asarray(b, dtype=np.uint8)[: rows * row_bytes].reshape(row_bytes // TILE, rows, TILE)
+    return np.ascontiguousarray(b.transpose(1, 0, 2)).reshape(-1)
+
+
+def _sc_bytes_group_major(m: QMatrix) -> np.ndarray:
+    N, G = m.s.shape
+    sc = np.empty((G, N, 2), dtype=np.float16)
+    sc[:, :, 0] = m.s.T
+    sc[:, :, 1] = m.c.T
+    return sc.reshape(-1).view(np.uint8)
+
+
+def _sc_from_bytes_group_major(b: np.ndarray, rows: int, groups: int) -> Tuple[np.ndarray, np.ndarray]:
+    sc = np.ascontiguousarray(b[: rows * groups * 4]).view(np.float16).reshape(groups, rows, 2)
+    return sc[:, :, 0].T.copy(), sc[:, :, 1].T.copy()
+
+
 class Expert(NamedTuple):
     gate: QMatrix   # [I][H]
     up: QMatrix     # [I][H]
@@ -221,10 +254,10 @@ def pack_record(e: Expert, bits: int, pad_to_stride: bool = True) -> np.ndarray:
     out = np.zeros(n, dtype=np.uint8)
     out[lay.gate_codes:lay.up_codes] = encode_codes(e.gate.q, bits)
     out[lay.up_codes:lay.down_codes] = encode_codes(e.up.q, bits)
-    out[lay.down_codes:lay.gate_sc] = encode_codes(e.down.q, bits)
+    out[lay.down_codes:lay.gate_sc] = tile_rows(encode_codes(e.down.q, bits), H)
     out[lay.gate_sc:lay.up_sc] = _sc_bytes(e.gate)
     out[lay.up_sc:lay.down_sc] = _sc_bytes(e.up)
-    out[lay.down_sc:lay.end] = _sc_bytes(e.down)
+    out[lay.down_sc:lay.end] = _sc_bytes_group_major(e.down)
     return out
 
 
@@ -234,10 +267,10 @@ def unpack_record(rec: np.ndarray, hidden: int, inter: int, bits: int) -> Expert
     H, I = hidden, inter
     gq = decode_codes(rec[lay.gate_codes:lay.up_codes], I, H, bits)
     uq = decode_codes(rec[lay.up_codes:lay.down_codes], I, H, bits)
-    dq = decode_codes(rec[lay.down_codes:lay.gate_sc], H, I, bits)
+    dq = decode_codes(untile_rows(rec[lay.down_codes:lay.gate_sc], H, I * bits // 8), H, I, bits)
     gs, gc = _sc_from_bytes(rec[lay.gate_sc:lay.up_sc], I, H // GROUP)
     us, uc = _sc_from_bytes(rec[lay.up_sc:lay.down_sc], I, H // GROUP)
-    ds, dc = _sc_from_bytes(rec[lay.down_sc:lay.end], H, I // GROUP)
+    ds, dc = _sc_from_bytes_group_major(rec[lay.down_sc:lay.end], H, I // GROUP)
     return Expert(QMatrix(gq, gs, gc), QMatrix(uq, us, uc), QMatrix(dq, ds, dc))
 
 

@@ -69,11 +69,12 @@ LaunchEvents& moe::launch_events() {
 namespace {
 
 enum KernelKind {
-  K_ROUTER, K_ROUTE, K_GATEUP, K_DOWN,
+  K_ROUTER, K_ROUTE, K_GATEUP, K_DOWN, K_EXPERT, K_REDUCE,
   K_PF_XSUM, K_PF_ROUTER, K_PF_ROUTE, K_PF_COUNT, K_PF_SCAN, K_PF_SCATTER, K_PF_GATEUP, K_PF_DOWN, K_PF_COMBINE,
   K_COUNT
 };
 const char* const kKindName[K_COUNT] = {"router",         "route",          "gateup",         "down",
+                                        "expert",         "reduce",
                                         "prefill_xsum",   "prefill_router", "prefill_route",  "prefill_count",
                                         "prefill_scan",   "prefill_scatter", "prefill_gateup", "prefill_down",
                                         "prefill_combine"};
@@ -246,6 +247,7 @@ StepBuffers step_buffers(moe_model* m, const uint16_t* x, size_t step) {
   b.route_w = m->route_w + step * (size_t)m->cfg.top_k;
   b.route_gamma = m->route_gamma + step;
   b.h = m->h;
+  b.partial = m->h;  // the fused path's partial rows share the buffer
   return b;
 }
 
@@ -264,16 +266,29 @@ const float* layer_wr(moe_model* m, int layer) {
 const float* layer_bias(moe_model* m, int layer) { return m->bias + (size_t)layer * m->cfg.n_experts; }
 const uint8_t* layer_shared(moe_model* m, int layer) { return m->shared + (size_t)layer * m->shared_stride; }
 
-// One token through one layer on the decode kernels.
-moe_status decode_step(moe_model* m, int layer, const StepBuffers& b, const ExpertSource& src,
-                       const ResidualArgs& r, hipStream_t s) {
-  HIP_TRY(m->prof.run(K_ROUTER, s, [&] { return launch_router(m->geo, layer_wr(m, layer), layer_bias(m, layer), b, s); }),
-          "router launch");
+// The expert kernels of one token-layer (after routing): fused expert +
+// reduce where the shape allows, else gate/up + down.
+moe_status expert_steps(moe_model* m, int layer, const StepBuffers& b, const ExpertSource& src,
+                        const ResidualArgs& r, hipStream_t s) {
+  if (fused_expert_supported(m->geo)) {
+    HIP_TRY(m->prof.run(K_EXPERT, s, [&] { return launch_expert(m->geo, src, layer_shared(m, layer), b, s); }),
+            "expert launch");
+    HIP_TRY(m->prof.run(K_REDUCE, s, [&] { return launch_reduce(m->geo, b, r, s); }), "reduce launch");
+    return MOE_OK;
+  }
   HIP_TRY(m->prof.run(K_GATEUP, s, [&] { return launch_gateup(m->geo, src, layer_shared(m, layer), b, s); }),
           "gate/up launch");
   HIP_TRY(m->prof.run(K_DOWN, s, [&] { return launch_down(m->geo, src, layer_shared(m, layer), b, r, s); }),
           "down launch");
   return MOE_OK;
+}
+
+// One token through one layer on the decode kernels.
+moe_status decode_step(moe_model* m, int layer, const StepBuffers& b, const ExpertSource& src,
+                       const ResidualArgs& r, hipStream_t s) {
+  HIP_TRY(m->prof.run(K_ROUTER, s, [&] { return launch_router(m->geo, layer_wr(m, layer), layer_bias(m, layer), b, s); }),
+          "router launch");
+  return expert_steps(m, layer, b, src, r, s);
 }
 
 moe_status check_forward_args(moe_model* m, int32_t layer, const void* x, int32_t n_tok, const void* out,
@@ -386,7 +401,13 @@ moe_status moe_model_create(const moe_config* cfg, int32_t storage, moe_model** 
   ok = ok && hipMalloc(&m->wr_rows, L * (E + 1) * H * sizeof(float)) == hipSuccess;
   ok = ok && hipMalloc(&m->bias, L * E * sizeof(float)) == hipSuccess;
   ok = ok && hipMalloc(&m->logits, (E + 1) * sizeof(float)) == hipSuccess;
-  ok = ok && hipMalloc(&m->h, (size_t)(cfg->top_k + 1) * cfg->inter * sizeof(float)) == hipSuccess;
+  {
+    // decode scratch: h of the two-kernel path, or the fused path's partial rows
+    const size_t slots = (size_t)cfg->top_k + 1;
+    const size_t n_h = slots * cfg->inter;
+    const size_t n_part = slots * ((size_t)cfg->inter * cfg->bits / 128) * cfg->hidden;
+    ok = ok && hipMalloc(&m->h, std::max(n_h, n_part) * sizeof(float)) == hipSuccess;
+  }
   ok = ok && hipMalloc(&m->rbuf, H * sizeof(float)) == hipSuccess;
   ok = ok && hipMalloc(&m->xbuf, 2 * H * sizeof(uint16_t)) == hipSuccess;
   if (ok) ok = hipMemset(m->bias, 0, L * E * sizeof(float)) == hipSuccess;
@@ -625,10 +646,8 @@ moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, in
         HIP_TRY(hipEventRecord(pool->copies_done, pool->copy_stream), "event record");
         HIP_TRY(hipStreamWaitEvent(s, pool->copies_done, 0), "stream wait");
       }
-      HIP_TRY(m->prof.run(K_GATEUP, s, [&] { return launch_gateup(m->geo, src, layer_shared(m, l), b, s); }),
-              "gate/up launch");
-      HIP_TRY(m->prof.run(K_DOWN, s, [&] { return launch_down(m->geo, src, layer_shared(m, l), b, r, s); }),
-              "down launch");
+      st = expert_steps(m, l, b, src, r, s);
+      if (st) return st;
     }
   }
   if (pool) HIP_TRY(hipStreamSynchronize(s), "moe_stack_decode: final sync");

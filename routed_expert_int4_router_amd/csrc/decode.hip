@@ -298,8 +298,6 @@ __global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src,
   const int msw = (nslots + 3) / 4;                 // slots per wave in use
   float* sh_h = smem + (size_t)wv * msw * RS;       // this wave's slots: [msw][RS]
   float* sh_part = smem + (size_t)4 * msw * RS;     // [4][RB]
-  const size_t row_bytes = (size_t)I * BITS / 8;
-  constexpr int groups = I / 64;
 
   // 1. the step's route (lane q < k holds slot q), one vector load per array
   const int qk = min(lane, g.k - 1);
@@ -346,12 +344,11 @@ __global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src,
 #pragma unroll
       for (int rr = 0; rr < R; ++rr) {
         const int hr = hrow0 + rsub + RPW * rr;
-        const uint8_t* drow = rec + g.down_codes + (size_t)hr * row_bytes;
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
-          const int ch = c0 + LPR * it;
-          cd[m][rr][it] = ld_stream(drow + 16 * ch);
-          sd[m][rr][it] = *reinterpret_cast<const uint32_t*>(rec + g.down_sc + ((size_t)hr * groups + ch * EPC / 64) * 4);
+          const int ch = c0 + LPR * it;  // tile ch of row hr: [I*bits/128][H][16 B]; (s, c) [I/64][H]
+          cd[m][rr][it] = ld_stream(rec + g.down_codes + ((size_t)ch * g.H + hr) * 16);
+          sd[m][rr][it] = *reinterpret_cast<const uint32_t*>(rec + g.down_sc + ((size_t)(ch * EPC / 64) * g.H + hr) * 4);
         }
       }
     }
@@ -409,6 +406,216 @@ __global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src,
       if (res.x_next) res.x_next[hr] = to_bf16_rne(r);
     } else {
       res.out[hr] = o;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ expert ---
+// Fused expert step. Block (slot j, slice sl): I rows [sl * SL, sl * SL + SL)
+// of expert slot j (slot k = the shared expert), 16 waves (enough waves per
+// SIMD to overlap one wave's dequantisation arithmetic with another's
+// loads). The block
+//   1. routes the token (wave 0: top-k of the logits, weights in LDS; a pool
+//      step reads the route and the record table instead),
+//   2. issues the gate/up code rows of its SL rows and the down codes of the
+//      slice (16 bytes of every down row) together, so the weight latency is
+//      paid once,
+//   3. computes h = silu(gate . x) * (up . x) for its rows into LDS,
+//   4. writes w_j * (down[:, slice] . h[slice]) for all H outputs as one
+//      partial row (w_k = gamma for the shared expert).
+// The reduce kernel sums the (k + 1) * (I / SL) partial rows in a fixed
+// order, so results do not depend on scheduling. SL = 128 / BITS, so the down
+// slice of a row is one 16-byte chunk inside one quantisation group.
+constexpr int kExpertWaves = 16;
+
+template <int BITS, int LPR, int IT, int NPL, int DQ>
+__global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, ExpertSource src,
+                                                                  const uint8_t* __restrict__ shared_rec,
+                                                                  StepBuffers b) {
+  constexpr int EPC = 128 / BITS;  // codes per 16-byte chunk
+  constexpr int SL = EPC;          // I rows per block
+  constexpr int NT = 64 * kExpertWaves;
+  constexpr int RPWV = SL / kExpertWaves;  // gate/up rows per wave (2 for int4, 1 for int8)
+  constexpr int RPW = kWave / LPR; // rows per wave pass
+  constexpr int RW = (RPWV + RPW - 1) / RPW;
+  __shared__ __align__(16) uint32_t lds_route[kRouteLds];
+  __shared__ __align__(16) float sh_h[SL];
+  const int nsl = g.I / SL;
+  const int j = __builtin_amdgcn_readfirstlane((int)blockIdx.x / nsl);
+  const int sl = __builtin_amdgcn_readfirstlane((int)blockIdx.x % nsl);
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = threadIdx.x & 63;
+  const int rsub = lane / LPR, c0 = lane % LPR;
+
+  // activations first: they do not depend on the routing
+  uint4 xraw[IT][EPC / 8];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const uint4* xp = reinterpret_cast<const uint4*>(b.x + (size_t)(c0 + LPR * it) * EPC);
+#pragma unroll
+    for (int q = 0; q < EPC / 8; ++q) xraw[it][q] = xp[q];
+  }
+  // 1. route
+  if (j < g.k && !src.use_table) {
+    if (threadIdx.x < 64) {
+      const bool pub = blockIdx.x == 0;
+      wave_route<NPL>(b.logits, g.E, g.k, g.norm_topk, lds_route, pub ? b.route_idx : nullptr,
+                      pub ? b.route_w : nullptr, nullptr);
+    }
+    __syncthreads();
+  }
+  const uint8_t* rec;
+  if (j == g.k) {
+    rec = shared_rec;
+  } else if (src.use_table) {
+    rec = expert_record(src, j, 0);
+  } else {
+    rec = expert_record(src, j, __builtin_amdgcn_readfirstlane((int)lds_route[kRouteOrdered + 2 * j + 1]));
+  }
+
+  // 2. all weight loads of the block
+  const size_t row_bytes = (size_t)g.H * BITS / 8;
+  const int groups = g.H / 64;
+  uint4 cg[RW][IT], cu[RW][IT];
+  uint32_t sg[RW][IT], su[RW][IT];
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr) {
+    const int i = sl * SL + wv * RPWV + min(rsub + RPW * rr, RPWV - 1);  // idle lanes re-read a valid row
+    const uint8_t* grow = rec + g.gate_codes + (size_t)i * row_bytes;
+    const uint8_t* urow = rec + g.up_codes + (size_t)i * row_bytes;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int ch = c0 + LPR * it;
+      cg[rr][it] = ld_stream(grow + 16 * ch);
+      cu[rr][it] = ld_stream(urow + 16 * ch);
+      const int grp = ch * EPC / 64;
+      sg[rr][it] = *reinterpret_cast<const uint32_t*>(rec + g.gate_sc + ((size_t)i * groups + grp) * 4);
+      su[rr][it] = *reinterpret_cast<const uint32_t*>(rec + g.up_sc + ((size_t)i * groups + grp) * 4);
+    }
+  }
+  // down tile sl of every row: contiguous in the record (tiles [I/SL][H][16 B],
+  // (s, c) group-major [I/64][H])
+  const uint8_t* dtile = rec + g.down_codes + (size_t)sl * g.H * 16;
+  const uint32_t* dsc = reinterpret_cast<const uint32_t*>(rec + g.down_sc) + (size_t)(sl * SL / 64) * g.H;
+  uint4 cd[DQ];
+  uint32_t sd[DQ];
+#pragma unroll
+  for (int q = 0; q < DQ; ++q) {
+    const int n = min((int)threadIdx.x + NT * q, g.H - 1);
+    cd[q] = ld_stream(dtile + (size_t)n * 16);
+    sd[q] = dsc[n];
+  }
+  // the slot's weight (and the published shared gate) only after every weight
+  // load is in flight; nothing is scheduled across this point
+  float wjv;
+  if (j == g.k)
+    wjv = src.use_table ? b.route_gamma[0] : 1.0f / (1.0f + expf(-b.logits[g.E]));
+  else if (src.use_table)
+    wjv = b.route_w[j];
+  else
+    wjv = __uint_as_float(lds_route[kRouteOrdered + 2 * j]);
+  if (blockIdx.x == 0 && threadIdx.x == 0 && !src.use_table) b.route_gamma[0] = 1.0f / (1.0f + expf(-b.logits[g.E]));
+  __builtin_amdgcn_sched_barrier(0);
+  const float wj = wjv;
+
+  // 3. gate/up dots, SwiGLU -> h of the slice in LDS
+  float xv[IT][EPC];
+  float xs[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+#pragma unroll
+    for (int q = 0; q < EPC / 8; ++q) {
+      const uint32_t w[4] = {xraw[it][q].x, xraw[it][q].y, xraw[it][q].z, xraw[it][q].w};
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        xv[it][8 * q + 2 * t] = bf16f(w[t] & 0xFFFFu);
+        xv[it][8 * q + 2 * t + 1] = bf16f(w[t] >> 16);
+      }
+    }
+    float sx = 0.f;
+#pragma unroll
+    for (int q = 0; q < EPC; ++q) sx += xv[it][q];
+    xs[it] = sx;
+  }
+#pragma unroll
+  for (int rr = 0; rr < RW; ++rr) {
+    float ag = 0.f, au = 0.f;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const float dg = chunk_dot<BITS>(cg[rr][it], xv[it]);
+      const float du = chunk_dot<BITS>(cu[rr][it], xv[it]);
+      ag += f16f(sg[rr][it] & 0xFFFFu) * dg + f16f(sg[rr][it] >> 16) * xs[it];
+      au += f16f(su[rr][it] & 0xFFFFu) * du + f16f(su[rr][it] >> 16) * xs[it];
+    }
+    ag = group_sum<LPR>(ag);
+    au = group_sum<LPR>(au);
+    const int r = rsub + RPW * rr;
+    if (c0 == LPR - 1 && r < RPWV) sh_h[wv * RPWV + r] = ag / (1.0f + expf(-ag)) * au;
+  }
+  __syncthreads();
+
+  // 4. partial down projection of the slice for every output row
+  float hv[SL];
+#pragma unroll
+  for (int q = 0; q < SL / 4; ++q) {
+    const float4 v = reinterpret_cast<const float4*>(sh_h)[q];
+    hv[4 * q] = v.x;
+    hv[4 * q + 1] = v.y;
+    hv[4 * q + 2] = v.z;
+    hv[4 * q + 3] = v.w;
+  }
+  float hs = 0.f;
+#pragma unroll
+  for (int q = 0; q < SL; ++q) hs += hv[q];
+  float* part = b.partial + ((size_t)j * nsl + sl) * g.H;
+#pragma unroll
+  for (int q = 0; q < DQ; ++q) {
+    const int n = (int)threadIdx.x + NT * q;
+    const float d = chunk_dot<BITS>(cd[q], hv);
+    const float v = f16f(sd[q] & 0xFFFFu) * d + f16f(sd[q] >> 16) * hs;
+    if (n < g.H) part[n] = wj * v;
+  }
+}
+
+// ------------------------------------------------------------------ reduce ---
+// out[n] = sum of the nparts partial rows at column n, in a fixed order, plus
+// the residual update of a layer stack. Block: 64 columns, 16 waves; wave w
+// owns rows p = w, w + 16, ...; it loads up to 16 of them at once (one round
+// of memory latency for up to 256 rows) and adds them in row order; the 16
+// wave sums are then added in wave order.
+constexpr int kReduceWaves = 16;
+constexpr int kReduceBatch = 16;
+__global__ void __launch_bounds__(64 * kReduceWaves) reduce_kernel(int H, int nparts, const float* __restrict__ partial,
+                                                                   ResidualArgs res) {
+  __shared__ float sh[kReduceWaves][64];
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = blockIdx.x * 64 + lane;
+  const float* p = partial + n;
+  constexpr int S = kReduceWaves;
+  float acc = 0.f;
+  for (int q0 = wv; q0 < nparts; q0 += S * kReduceBatch) {
+    float v[kReduceBatch];
+#pragma unroll
+    for (int u = 0; u < kReduceBatch; ++u) {
+      const int q = min(q0 + S * u, nparts - 1);  // clamped: every load issues unconditionally
+      v[u] = p[(size_t)q * H];
+    }
+#pragma unroll
+    for (int u = 0; u < kReduceBatch; ++u)
+      if (q0 + S * u < nparts) acc += v[u];
+  }
+  sh[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0) {
+    float o = sh[0][lane];
+#pragma unroll
+    for (int w = 1; w < S; ++w) o += sh[w][lane];
+    if (res.r_in || res.x_res) {
+      const float r = (res.r_in ? res.r_in[n] : bf16f(res.x_res[n])) + o;
+      res.out[n] = r;
+      if (res.x_next) res.x_next[n] = to_bf16_rne(r);
+    } else {
+      res.out[n] = o;
     }
   }
 }
@@ -503,6 +710,53 @@ hipError_t down_bits(const Geometry& g, const ExpertSource& src, const uint8_t* 
   return hipErrorInvalidValue;
 }
 
+template <int BITS, int LPR, int IT, int NPL>
+hipError_t expert_dq(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                     hipStream_t s) {
+  const dim3 grid((g.k + 1) * (g.I * BITS / 128)), block(64 * kExpertWaves);
+  switch (g.H <= 64 * kExpertWaves ? 1 : g.H / (64 * kExpertWaves)) {
+    case 1: launch((expert_kernel<BITS, LPR, IT, NPL, 1>), grid, block, 0, s, g, src, shared_rec, b); break;
+    case 2: launch((expert_kernel<BITS, LPR, IT, NPL, 2>), grid, block, 0, s, g, src, shared_rec, b); break;
+    case 4: launch((expert_kernel<BITS, LPR, IT, NPL, 4>), grid, block, 0, s, g, src, shared_rec, b); break;
+    case 8: launch((expert_kernel<BITS, LPR, IT, NPL, 8>), grid, block, 0, s, g, src, shared_rec, b); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int BITS, int LPR, int IT>
+hipError_t expert_npl(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                      hipStream_t s) {
+  switch (topk_npl(g.E)) {
+    case 1: return expert_dq<BITS, LPR, IT, 1>(g, src, shared_rec, b, s);
+    case 2: return expert_dq<BITS, LPR, IT, 2>(g, src, shared_rec, b, s);
+    case 4: return expert_dq<BITS, LPR, IT, 4>(g, src, shared_rec, b, s);
+    case 8: return expert_dq<BITS, LPR, IT, 8>(g, src, shared_rec, b, s);
+    case 16: return expert_dq<BITS, LPR, IT, 16>(g, src, shared_rec, b, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int BITS>
+hipError_t expert_bits(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                       hipStream_t s) {
+  const int chunks = g.H * BITS / 128;
+  const int lpr = lpr_for(chunks), it = chunks / lpr;
+  if (it == 1) {
+    switch (lpr) {
+      case 2: return expert_npl<BITS, 2, 1>(g, src, shared_rec, b, s);
+      case 4: return expert_npl<BITS, 4, 1>(g, src, shared_rec, b, s);
+      case 8: return expert_npl<BITS, 8, 1>(g, src, shared_rec, b, s);
+      case 16: return expert_npl<BITS, 16, 1>(g, src, shared_rec, b, s);
+      case 32: return expert_npl<BITS, 32, 1>(g, src, shared_rec, b, s);
+      case 64: return expert_npl<BITS, 64, 1>(g, src, shared_rec, b, s);
+    }
+  } else if (it == 2 && BITS == 8) {
+    return expert_npl<BITS, 64, 2>(g, src, shared_rec, b, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 bool decode_shape_supported(const Geometry& g) {
@@ -540,6 +794,24 @@ hipError_t launch_route(const Geometry& g, const float* logits, int ld_logits, i
     case 16: launch(route_kernel<16>, grid, block, 0, s, g, logits, ld_logits, route_idx, route_w, route_gamma, host_route); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+bool fused_expert_supported(const Geometry& g) {
+  // registers: the int4 gate/up rows of H = 4096 (two chunks per lane, 8 rows
+  // per wave) and the down rows of H > 2048 do not fit; those shapes keep the
+  // two-kernel path
+  return g.H <= 2048 && (g.bits == 8 || g.H * 4 / 128 <= 64) && g.I * g.bits / 128 >= 1;
+}
+
+hipError_t launch_expert(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                         hipStream_t s) {
+  return g.bits == 4 ? expert_bits<4>(g, src, shared_rec, b, s) : expert_bits<8>(g, src, shared_rec, b, s);
+}
+
+hipError_t launch_reduce(const Geometry& g, const StepBuffers& b, const ResidualArgs& r, hipStream_t s) {
+  const int nparts = (g.k + 1) * (g.I * g.bits / 128);
+  launch(reduce_kernel, dim3(g.H / 64), dim3(64 * kReduceWaves), 0, s, g.H, nparts, (const float*)b.partial, r);
   return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@ struct StepBuffers {
   int32_t* route_idx;     // [k] selection of this step
   float* route_w;         // [k]
   float* route_gamma;     // [1] sigmoid(x . g_s)
-  float* h;               // [(k+1)][I] SwiGLU activations, slot k = shared expert
+  float* h;               // two-kernel path: [(k+1)][I] SwiGLU activations, slot k = shared expert
+  float* partial;         // fused path: [(k+1) * I * bits / 128][H] weighted partial down rows
 };
 
 struct ResidualArgs {
@@ -66,5 +67,14 @@ hipError_t launch_down(const Geometry& g, const ExpertSource& src, const uint8_t
                        const ResidualArgs& r, hipStream_t s);
 
 bool decode_shape_supported(const Geometry& g);
+
+// Fused decode path: expert (route + gate/up + SwiGLU + partial down rows of
+// one I slice per block) then reduce (fixed-order sum of the partial rows,
+// residual update). Used for every shape fused_expert_supported accepts; the
+// others run launch_gateup + launch_down.
+bool fused_expert_supported(const Geometry& g);
+hipError_t launch_expert(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
+                         hipStream_t s);
+hipError_t launch_reduce(const Geometry& g, const StepBuffers& b, const ResidualArgs& r, hipStream_t s);
 
 }  // namespace moe

@@ -157,13 +157,34 @@ static void encode_row(const uint8_t* q, int K, int bits, uint8_t* dst) {
   for (int i = 0; i < K / 2; ++i) dst[i] = (uint8_t)(q[2 * i] | (q[2 * i + 1] << 4));
 }
 
-// Pack one matrix [N][K] into its codes region and sc region.
+// Pack one matrix [N][K] into its codes region and sc region: row-major codes
+// and (s, c) pairs [N][K/64][2] (gate, up).
 static bool pack_matrix(const float* w, int N, int K, int bits, uint8_t* codes, uint16_t* sc) {
   std::vector<uint8_t> q((size_t)K);
   size_t row_bytes = (size_t)K * bits / 8;
   for (int n = 0; n < N; ++n) {
     if (!quantize_row(w + (size_t)n * K, K, bits, q.data(), sc + (size_t)n * (K / 64) * 2)) return false;
     encode_row(q.data(), K, bits, codes + (size_t)n * row_bytes);
+  }
+  return true;
+}
+
+// The down matrix [N = H][K = I]: codes in 16-byte tiles [K*bits/128][N][16]
+// (tile t of every row before tile t+1 of any row) and (s, c) pairs
+// group-major [K/64][N][2].
+static bool pack_matrix_tiled(const float* w, int N, int K, int bits, uint8_t* codes, uint16_t* sc) {
+  std::vector<uint8_t> q((size_t)K), row((size_t)K * bits / 8);
+  std::vector<uint16_t> sr((size_t)(K / 64) * 2);
+  const size_t tiles = (size_t)K * bits / 128;
+  const int G = K / 64;
+  for (int n = 0; n < N; ++n) {
+    if (!quantize_row(w + (size_t)n * K, K, bits, q.data(), sr.data())) return false;
+    encode_row(q.data(), K, bits, row.data());
+    for (size_t t = 0; t < tiles; ++t) std::memcpy(codes + (t * N + n) * 16, row.data() + t * 16, 16);
+    for (int g = 0; g < G; ++g) {
+      sc[((size_t)g * N + n) * 2] = sr[(size_t)2 * g];
+      sc[((size_t)g * N + n) * 2 + 1] = sr[(size_t)2 * g + 1];
+    }
   }
   return true;
 }
@@ -215,8 +236,8 @@ moe_status moe_pack(const moe_config* cfg, int32_t inter, const float* w_gate, c
                             reinterpret_cast<uint16_t*>(rec + lay.gate_sc)) &&
                 pack_matrix(w_up + (size_t)e * gu_elems, I, H, bits, rec + lay.up_codes,
                             reinterpret_cast<uint16_t*>(rec + lay.up_sc)) &&
-                pack_matrix(w_down + (size_t)e * d_elems, H, I, bits, rec + lay.down_codes,
-                            reinterpret_cast<uint16_t*>(rec + lay.down_sc));
+                pack_matrix_tiled(w_down + (size_t)e * d_elems, H, I, bits, rec + lay.down_codes,
+                                  reinterpret_cast<uint16_t*>(rec + lay.down_sc));
       if (!ok) {
         int64_t expect = -1;
         bad.compare_exchange_strong(expect, e);
@@ -245,16 +266,33 @@ moe_status moe_unpack(const moe_config* cfg, int32_t inter, const void* record, 
   if (!record || !q_out || !sc_out) return fail(MOE_EINVAL, "moe_unpack: NULL pointer");
   const RecordLayout lay = record_layout(*cfg, inter);
   const uint8_t* rec = static_cast<const uint8_t*>(record);
-  const size_t elems = 3 * (size_t)cfg->hidden * inter;
+  const size_t H = cfg->hidden, I = inter;
+  const size_t elems = 3 * H * I;
+  // codes in record order with the down tiles put back into rows
+  std::vector<uint8_t> bytes(elems * cfg->bits / 8);
+  std::memcpy(bytes.data(), rec, lay.down_codes);
+  const size_t drow = I * cfg->bits / 8, tiles = drow / 16;
+  for (size_t n = 0; n < H; ++n)
+    for (size_t t = 0; t < tiles; ++t)
+      std::memcpy(bytes.data() + lay.down_codes + n * drow + t * 16, rec + lay.down_codes + (t * H + n) * 16, 16);
   if (cfg->bits == 8) {
-    std::memcpy(q_out, rec, elems);
+    std::memcpy(q_out, bytes.data(), elems);
   } else {
     for (size_t i = 0; i < elems / 2; ++i) {
-      q_out[2 * i] = rec[i] & 0x0F;
-      q_out[2 * i + 1] = rec[i] >> 4;
+      q_out[2 * i] = bytes[i] & 0x0F;
+      q_out[2 * i + 1] = bytes[i] >> 4;
     }
   }
-  std::memcpy(sc_out, rec + lay.gate_sc, lay.end - lay.gate_sc);
+  // (s, c) pairs: gate and up as stored, down back to [H][I/64][2]
+  std::memcpy(sc_out, rec + lay.gate_sc, lay.down_sc - lay.gate_sc);
+  uint16_t* dsc = sc_out + (lay.down_sc - lay.gate_sc) / 2;
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(rec + lay.down_sc);
+  const size_t G = I / 64;
+  for (size_t n = 0; n < H; ++n)
+    for (size_t g = 0; g < G; ++g) {
+      dsc[(n * G + g) * 2] = src[(g * H + n) * 2];
+      dsc[(n * G + g) * 2 + 1] = src[(g * H + n) * 2 + 1];
+    }
   return MOE_OK;
 }
 

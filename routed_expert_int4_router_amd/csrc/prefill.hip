@@ -609,8 +609,9 @@ struct DownSources {
   const uint16_t* hi[2];  // A (instruction t): row 8 (2w + t) + lane / 8, chunk (lane % 8) ^ (row % 8)
   const uint16_t* lo[2];
   bool live[2];
-  const uint8_t* b[2];    // code rows: instruction t covers rows 64w + 32t + lane / 2, half lane % 2
+  const uint8_t* b[2];    // code rows: instruction t covers rows 64w + 32t + lane / 2, tile half lane % 2
   const uint8_t* s;       // scale word of row 64w + lane
+  size_t bq, sq;          // bytes from one I group to the next: codes (2 tiles of H rows), scales (H words)
 };
 
 // DMAs of group gn into the free stages; the restrict qualifiers keep the
@@ -619,9 +620,9 @@ struct DownSources {
 __device__ __forceinline__ void down_issue(uint8_t* __restrict__ wrH, uint8_t* __restrict__ wrL,
                                            uint8_t* __restrict__ wrB, uint8_t* __restrict__ wrS,
                                            const DownSources& src, int gn, int wv) {
-  dma16(src.b[0] + 32 * gn, wrB + (2 * wv) * 1024);
-  dma16(src.b[1] + 32 * gn, wrB + (2 * wv + 1) * 1024);
-  dma4(src.s + 4 * gn, wrS + wv * 256);
+  dma16(src.b[0] + (size_t)gn * src.bq, wrB + (2 * wv) * 1024);
+  dma16(src.b[1] + (size_t)gn * src.bq, wrB + (2 * wv + 1) * 1024);
+  dma4(src.s + (size_t)gn * src.sq, wrS + wv * 256);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     if (src.live[t]) dma16(src.hi[t] + 64 * gn, wrH + (2 * wv + t) * 1024);
@@ -704,17 +705,21 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   float* sHs = reinterpret_cast<float*>(sS + DN_NS * DS_STAGE);     // [GI][64 rows]
 
   DownSources src;
+  // down codes are stored in 16-byte tiles [I/32][H][16 B] (group g = tiles
+  // 2g, 2g + 1) and the (s, c) words group-major [I/64][H]
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int q = (2 * wv + t) * 64 + lane, row = q >> 1;
-    src.b[t] = rec + a.down_codes + (size_t)(n0 + row) * (a.I / 2) + 16 * (q & 1);
+    src.b[t] = rec + a.down_codes + ((size_t)(q & 1) * a.H + n0 + row) * 16;
   }
-  src.s = rec + a.down_sc + (size_t)(n0 + 64 * wv + lane) * GI * 4;
+  src.s = rec + a.down_sc + (size_t)(n0 + 64 * wv + lane) * 4;
+  src.bq = (size_t)2 * a.H * 16;
+  src.sq = (size_t)a.H * 4;
   for (int g = 0; g < DN_PF; ++g) {
     const int gc = min(g, GI - 1);
-    dma16(src.b[0] + 32 * gc, sB + g * DB_STAGE + (2 * wv) * 1024);
-    dma16(src.b[1] + 32 * gc, sB + g * DB_STAGE + (2 * wv + 1) * 1024);
-    dma4(src.s + 4 * gc, sS + g * DS_STAGE + wv * 256);
+    dma16(src.b[0] + (size_t)gc * src.bq, sB + g * DB_STAGE + (2 * wv) * 1024);
+    dma16(src.b[1] + (size_t)gc * src.bq, sB + g * DB_STAGE + (2 * wv + 1) * 1024);
+    dma4(src.s + (size_t)gc * src.sq, sS + g * DS_STAGE + wv * 256);
   }
   const int rows = a.e_off[e + 1] - a.e_off[e];
   const int base = a.e_off[e] + r0;

@@ -46,8 +46,9 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 
 // One wave routes one token. logits: E values (global memory). lds: kRouteLds
 // uint32 of this wave's LDS; on return lds[kRouteOrdered + 2q + 1] holds pick q
-// (selection order) for q < k. When out_idx is non-NULL, lane q < k writes
-// out_idx[q] and out_w[q] (and host_idx[q] when that is non-NULL too).
+// (selection order) and lds[kRouteOrdered + 2q] the bits of its weight, for
+// q < k. When out_idx is non-NULL, lane q < k also writes out_idx[q] and
+// out_w[q] (and host_idx[q] when that is non-NULL too).
 template <int NPL>
 __device__ __forceinline__ void wave_route(const float* __restrict__ logits, int E, int k, int norm_topk, uint32_t* lds,
                                            int32_t* out_idx, float* out_w, int32_t* host_idx) {
@@ -78,9 +79,6 @@ __device__ __forceinline__ void wave_route(const float* __restrict__ logits, int
       pick_e = (lane == j) ? (uint32_t)e : pick_e;
     }
   }
-  if (lane < k) lds[kRouteOrdered + 2 * lane + 1] = pick_e;
-  if (!out_idx) return;
-
   // weights: exp(l - l_max) over the picks (norm_topk) or over all E logits
   const float l = key_logit(pick_k);
   const float lmax = key_logit(__builtin_amdgcn_readfirstlane(pick_k));
@@ -96,9 +94,14 @@ __device__ __forceinline__ void wave_route(const float* __restrict__ logits, int
     s = dpp::wave_sum(part);
   }
   if (lane < k) {
-    out_idx[lane] = (int32_t)pick_e;
-    out_w[lane] = z / s;
-    if (host_idx) host_idx[lane] = (int32_t)pick_e;
+    const float wq = z / s;
+    lds[kRouteOrdered + 2 * lane] = __float_as_uint(wq);
+    lds[kRouteOrdered + 2 * lane + 1] = pick_e;
+    if (out_idx) {
+      out_idx[lane] = (int32_t)pick_e;
+      out_w[lane] = wq;
+      if (host_idx) host_idx[lane] = (int32_t)pick_e;
+    }
   }
 }
 
