@@ -63,7 +63,7 @@ def decode_kernel_bytes(cfg, stack: bool) -> dict:
     codes = I * H * b // 8          # one matrix
     sc = I * H // 64 * 4
     router = (E + 1) * H * 4 + E * 4 + H * 2 + (E + 1) * 4
-    parts = (k + 1) * (I * b // 128) * H * 4
+    parts = (k + 1) * (I // 32) * H * 4
     expert = (k + 1) * 3 * (codes + sc) + H * 2 + (E + 1) * 4 + parts
     reduce = parts + H * 4
     gateup = (k + 1) * 2 * (codes + sc) + H * 2 + (E + 1) * 4 + (k + 1) * I * 4

@@ -405,7 +405,7 @@ moe_status moe_model_create(const moe_config* cfg, int32_t storage, moe_model** 
     // decode scratch: h of the two-kernel path, or the fused path's partial rows
     const size_t slots = (size_t)cfg->top_k + 1;
     const size_t n_h = slots * cfg->inter;
-    const size_t n_part = slots * ((size_t)cfg->inter * cfg->bits / 128) * cfg->hidden;
+    const size_t n_part = slots * ((size_t)cfg->inter / 32) * cfg->hidden;  // 32-row I slices
     ok = ok && hipMalloc(&m->h, std::max(n_h, n_part) * sizeof(float)) == hipSuccess;
   }
   ok = ok && hipMalloc(&m->rbuf, H * sizeof(float)) == hipSuccess;

@@ -424,18 +424,21 @@ __global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src,
 //   4. writes w_j * (down[:, slice] . h[slice]) for all H outputs as one
 //      partial row (w_k = gamma for the shared expert).
 // The reduce kernel sums the (k + 1) * (I / SL) partial rows in a fixed
-// order, so results do not depend on scheduling. SL = 128 / BITS, so the down
-// slice of a row is one 16-byte chunk inside one quantisation group.
+// order, so results do not depend on scheduling. SL = 32: the down slice of a
+// row is DCH = SL * BITS / 128 16-byte tiles (1 int4, 2 int8) inside one
+// quantisation group.
 constexpr int kExpertWaves = 16;
+constexpr int kSlice = 32;
 
 template <int BITS, int LPR, int IT, int NPL, int DQ>
 __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, ExpertSource src,
                                                                   const uint8_t* __restrict__ shared_rec,
                                                                   StepBuffers b) {
   constexpr int EPC = 128 / BITS;  // codes per 16-byte chunk
-  constexpr int SL = EPC;          // I rows per block
+  constexpr int SL = kSlice;       // I rows per block
+  constexpr int DCH = SL / EPC;    // 16-byte down tiles per row slice
   constexpr int NT = 64 * kExpertWaves;
-  constexpr int RPWV = SL / kExpertWaves;  // gate/up rows per wave (2 for int4, 1 for int8)
+  constexpr int RPWV = SL / kExpertWaves;  // gate/up rows per wave
   constexpr int RPW = kWave / LPR; // rows per wave pass
   constexpr int RW = (RPWV + RPW - 1) / RPW;
   __shared__ __align__(16) uint32_t lds_route[kRouteLds];
@@ -493,16 +496,17 @@ __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, E
       su[rr][it] = *reinterpret_cast<const uint32_t*>(rec + g.up_sc + ((size_t)i * groups + grp) * 4);
     }
   }
-  // down tile sl of every row: contiguous in the record (tiles [I/SL][H][16 B],
-  // (s, c) group-major [I/64][H])
-  const uint8_t* dtile = rec + g.down_codes + (size_t)sl * g.H * 16;
+  // down tiles sl * DCH .. of every row: contiguous in the record (tiles
+  // [I * BITS / 128][H][16 B], (s, c) group-major [I/64][H])
+  const uint8_t* dtile = rec + g.down_codes + (size_t)sl * DCH * g.H * 16;
   const uint32_t* dsc = reinterpret_cast<const uint32_t*>(rec + g.down_sc) + (size_t)(sl * SL / 64) * g.H;
-  uint4 cd[DQ];
+  uint4 cd[DQ][DCH];
   uint32_t sd[DQ];
 #pragma unroll
   for (int q = 0; q < DQ; ++q) {
     const int n = min((int)threadIdx.x + NT * q, g.H - 1);
-    cd[q] = ld_stream(dtile + (size_t)n * 16);
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) cd[q][c] = ld_stream(dtile + ((size_t)c * g.H + n) * 16);
     sd[q] = dsc[n];
   }
   // the slot's weight (and the published shared gate) only after every weight
@@ -571,7 +575,9 @@ __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, E
 #pragma unroll
   for (int q = 0; q < DQ; ++q) {
     const int n = (int)threadIdx.x + NT * q;
-    const float d = chunk_dot<BITS>(cd[q], hv);
+    float d = 0.f;
+#pragma unroll
+    for (int c = 0; c < DCH; ++c) d += chunk_dot<BITS>(cd[q][c], hv + c * EPC);
     const float v = f16f(sd[q] & 0xFFFFu) * d + f16f(sd[q] >> 16) * hs;
     if (n < g.H) part[n] = wj * v;
   }
@@ -713,7 +719,7 @@ hipError_t down_bits(const Geometry& g, const ExpertSource& src, const uint8_t* 
 template <int BITS, int LPR, int IT, int NPL>
 hipError_t expert_dq(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
                      hipStream_t s) {
-  const dim3 grid((g.k + 1) * (g.I * BITS / 128)), block(64 * kExpertWaves);
+  const dim3 grid((g.k + 1) * (g.I / kSlice)), block(64 * kExpertWaves);
   switch (g.H <= 64 * kExpertWaves ? 1 : g.H / (64 * kExpertWaves)) {
     case 1: launch((expert_kernel<BITS, LPR, IT, NPL, 1>), grid, block, 0, s, g, src, shared_rec, b); break;
     case 2: launch((expert_kernel<BITS, LPR, IT, NPL, 2>), grid, block, 0, s, g, src, shared_rec, b); break;
@@ -798,10 +804,9 @@ hipError_t launch_route(const Geometry& g, const float* logits, int ld_logits, i
 }
 
 bool fused_expert_supported(const Geometry& g) {
-  // registers: the int4 gate/up rows of H = 4096 (two chunks per lane, 8 rows
-  // per wave) and the down rows of H > 2048 do not fit; those shapes keep the
-  // two-kernel path
-  return g.H <= 2048 && (g.bits == 8 || g.H * 4 / 128 <= 64) && g.I * g.bits / 128 >= 1;
+  // H <= 2048: the down rows of a larger H do not fit in registers; those
+  // shapes keep the two-kernel path
+  return g.H <= 2048 && g.I % kSlice == 0;
 }
 
 hipError_t launch_expert(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
@@ -810,7 +815,7 @@ hipError_t launch_expert(const Geometry& g, const ExpertSource& src, const uint8
 }
 
 hipError_t launch_reduce(const Geometry& g, const StepBuffers& b, const ResidualArgs& r, hipStream_t s) {
-  const int nparts = (g.k + 1) * (g.I * g.bits / 128);
+  const int nparts = (g.k + 1) * (g.I / kSlice);
   launch(reduce_kernel, dim3(g.H / 64), dim3(64 * kReduceWaves), 0, s, g.H, nparts, (const float*)b.partial, r);
   return hipGetLastError();
 }

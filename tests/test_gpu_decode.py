@@ -32,6 +32,7 @@ def _run_layer(model, cfg, xb, mode="decode"):
     dict(hidden=512, inter=256, shared_inter=256, n_experts=100, top_k=7),
     dict(hidden=1024, inter=64, shared_inter=64, n_experts=33, top_k=5, bits=8, norm_topk=0),
     dict(hidden=64, inter=64, shared_inter=64, n_experts=3, top_k=3),
+    dict(hidden=4096, inter=64, shared_inter=64, n_experts=5, top_k=2),   # gate/up + down kernels
 ])
 def test_small_layer_parity(variant):
     cfg = synth.get_config("tiny", **variant)
