@@ -516,7 +516,10 @@ moe_status moe_layer_decode(moe_model* m, int32_t layer, const uint16_t* x, int3
   clear_error();
   moe_status st = check_forward_args(m, layer, x, n_tok, out, "moe_layer_decode");
   if (st) return st;
-  if (n_tok == 0) return MOE_OK;
+  if (n_tok == 0) {
+    m->route_steps = 0;
+    return MOE_OK;
+  }
   st = ensure_route_cap(m, (size_t)n_tok);
   if (st) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -542,7 +545,10 @@ moe_status moe_layer_forward(moe_model* m, int32_t layer, const uint16_t* x, int
   clear_error();
   moe_status st = check_forward_args(m, layer, x, n_tok, out, "moe_layer_forward");
   if (st) return st;
-  if (n_tok == 0) return MOE_OK;
+  if (n_tok == 0) {
+    m->route_steps = 0;
+    return MOE_OK;
+  }
   if ((int64_t)n_tok * m->cfg.top_k >= 4 * (int64_t)m->cfg.n_experts && prefill_supported(m->cfg)) {
     st = ensure_route_cap(m, (size_t)n_tok);
     if (st) return st;
@@ -591,7 +597,10 @@ moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, in
   }
   for (int l = 0; l < m->cfg.n_layers; ++l)
     if (!m->layer_set[(size_t)l]) return fail(MOE_ESTATE, "moe_stack_decode: a layer was not set");
-  if (n_tok == 0) return MOE_OK;
+  if (n_tok == 0) {
+    m->route_steps = 0;
+    return MOE_OK;
+  }
   const int L = m->cfg.n_layers, k = m->cfg.top_k, E = m->cfg.n_experts;
   const size_t H = m->cfg.hidden;
   st = ensure_route_cap(m, (size_t)n_tok * L);
