@@ -415,8 +415,8 @@ __global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src,
 // of expert slot j (slot k = the shared expert), 16 waves (enough waves per
 // SIMD to overlap one wave's dequantisation arithmetic with another's
 // loads). The block
-//   1. routes the token (wave 0: top-k of the logits, weights in LDS; a pool
-//      step reads the route and the record table instead),
+//   1. routes the token (top-k of the logits by the whole block, weights in
+//      LDS; a pool step reads the route and the record table instead),
 //   2. issues the gate/up code rows of its SL rows and the down codes of the
 //      slice (16 bytes of every down row) together, so the weight latency is
 //      paid once,
@@ -460,12 +460,9 @@ __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, E
   }
   // 1. route
   if (j < g.k && !src.use_table) {
-    if (threadIdx.x < 64) {
-      const bool pub = blockIdx.x == 0;
-      wave_route<NPL>(b.logits, g.E, g.k, g.norm_topk, lds_route, pub ? b.route_idx : nullptr,
-                      pub ? b.route_w : nullptr, nullptr);
-    }
-    __syncthreads();
+    const bool pub = blockIdx.x == 0;
+    block_route<NPL, kExpertWaves>(b.logits, g.E, g.k, g.norm_topk, lds_route, pub ? b.route_idx : nullptr,
+                                   pub ? b.route_w : nullptr, nullptr);
   }
   const uint8_t* rec;
   if (j == g.k) {

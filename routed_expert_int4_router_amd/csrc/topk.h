@@ -8,10 +8,21 @@
 // section on the 35B correctness fix).
 //
 // Method. Each logit maps to a 32-bit key whose unsigned order is the logit
-// order. k rounds of: per-lane max of its keys, wave max with DPP (one v_max
-// per step), the lowest expert index holding that key by a DPP wave min over
-// per-lane candidates, and the owning lane clears it. The picks come out in selection order; everything is
-// wave-local (registers, DPP, ballots), with no LDS round trips on the path.
+// order; packing the key above the complemented expert index gives one
+// unsigned 64-bit value per expert whose order is the selection order, so
+// every comparison below is a single unsigned compare with no ties.
+//   1. Each lane holds NPL experts (e = lane + 64 i) and takes their maximum.
+//   2. The lane maxima are written to LDS and each lane counts how many beat
+//      its own (reads of one address by all lanes are LDS broadcasts). The
+//      k-th best lane maximum T is a lower bound of the whole top-k: the k
+//      lane maxima at or above T are k distinct experts.
+//   3. Experts at or above T are compacted into LDS with ballots (at most
+//      k * NPL of them, usually little more than k), each is ranked against
+//      the others the same way, and rank r < k is pick r.
+//   4. When more than kRouteCand experts reach T (many of the best logits in
+//      a few lanes; only possible when k * NPL > kRouteCand), k rounds of
+//      wave max / lowest-index selection with DPP take over.
+// The picks come out in selection order; the whole routine is one wave.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -23,7 +34,11 @@
 namespace moe {
 
 constexpr int kTopkMax = 16;
-constexpr int kRouteLds = 2 * kTopkMax;   // uint32 of LDS per routing wave
+constexpr int kRouteCand = 128;           // candidates ranked by the threshold pass
+constexpr int kRouteOut = 2 * kTopkMax;   // uint32: (weight bits, pick) per selection slot
+// uint32 of LDS per routing wave: the output, then u64 scratch for the 64 lane
+// maxima, the candidates and the ranked picks, then 64 rank counters
+constexpr int kRouteLds = kRouteOut + 2 * (64 + kRouteCand + kTopkMax) + 64;
 constexpr int kRouteOrdered = 0;          // pick q at lds[kRouteOrdered + 2q + 1]
 
 // Straight-line arithmetic (no data-dependent branches): NaN -> -inf, -0 -> +0,
@@ -44,39 +59,118 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// One wave routes one token. logits: E values (global memory). lds: kRouteLds
-// uint32 of this wave's LDS; on return lds[kRouteOrdered + 2q + 1] holds pick q
-// (selection order) and lds[kRouteOrdered + 2q] the bits of its weight, for
-// q < k. When out_idx is non-NULL, lane q < k also writes out_idx[q] and
-// out_w[q] (and host_idx[q] when that is non-NULL too).
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), lane);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// LDS written by this wave becomes readable by all its lanes (LDS operations
+// of one wave complete in order; the fence keeps the compiler from moving
+// accesses across this point).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Per-lane state of one routing wave: the logits and packed values of the
+// lane's NPL experts and their maximum.
 template <int NPL>
-__device__ __forceinline__ void wave_route(const float* __restrict__ logits, int E, int k, int norm_topk, uint32_t* lds,
-                                           int32_t* out_idx, float* out_w, int32_t* host_idx) {
-  const int lane = threadIdx.x & 63;
+struct RouteLane {
   float lv[NPL];
+  uint64_t p[NPL];
+  uint64_t pm;
+};
+
+template <int NPL>
+__device__ __forceinline__ void route_load(const float* __restrict__ logits, int E, RouteLane<NPL>& r) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) lv[i] = logits[min(lane + 64 * i, E - 1)];
-  uint32_t key[NPL];
+  for (int i = 0; i < NPL; ++i) r.lv[i] = logits[min(lane + 64 * i, E - 1)];
+  // packed (key, ~e): padding (e >= E) gets key 0, below every real logit
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) key[i] = logit_key(lv[i]) & ((lane + 64 * i < E) ? 0xFFFFFFFFu : 0u);
+  for (int i = 0; i < NPL; ++i) {
+    const uint32_t e = (uint32_t)(lane + 64 * i);
+    const uint32_t key = logit_key(r.lv[i]) & (e < (uint32_t)E ? 0xFFFFFFFFu : 0u);
+    r.p[i] = ((uint64_t)key << 32) | (uint32_t)~e;
+  }
+  r.pm = r.p[0];
+#pragma unroll
+  for (int i = 1; i < NPL; ++i) r.pm = r.p[i] > r.pm ? r.p[i] : r.pm;
+}
+
+__device__ __forceinline__ uint64_t* route_lane_best(uint32_t* lds) { return reinterpret_cast<uint64_t*>(lds + kRouteOut); }
+__device__ __forceinline__ uint32_t* route_rank_count(uint32_t* lds) {
+  return lds + kRouteOut + 2 * (64 + kRouteCand + kTopkMax);
+}
+
+// Number of the values v[0..n) greater than c, reading v two at a time.
+__device__ __forceinline__ int count_greater(const uint64_t* v, int n, uint64_t c) {
+  int q = 0;
+  for (int j = 0; j < n; j += 2) {
+    const ulonglong2 w = *reinterpret_cast<const ulonglong2*>(v + j);
+    q += w.x > c ? 1 : 0;
+    q += (j + 1 < n && w.y > c) ? 1 : 0;
+  }
+  return q;
+}
+
+// Steps 3-4 and the weights, given the threshold T (one wave).
+template <int NPL>
+__device__ __forceinline__ void route_finish(const RouteLane<NPL>& r, uint64_t T, int E, int k, int norm_topk,
+                                             uint32_t* lds, int32_t* out_idx, float* out_w, int32_t* host_idx) {
+  const int lane = threadIdx.x & 63;
+  uint64_t* cand = route_lane_best(lds) + 64;
+  uint64_t* ranked = cand + kRouteCand;
+  // 3. compaction of the experts at or above T: all ballots first, then the
+  //    prefix offsets (scalar) and the stores
+  uint64_t m[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) m[i] = __ballot(r.p[i] >= T);
+  int n_cand = 0;  // uniform
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int pos = n_cand + (int)lanes_below(m[i]);
+    if (((m[i] >> lane) & 1ull) && pos < kRouteCand) cand[pos] = r.p[i];
+    n_cand += __popcll(m[i]);
+  }
 
   uint32_t pick_k = 0u, pick_e = 0u;  // lane q keeps pick q
+  if (n_cand <= kRouteCand) {
+    wave_lds_sync();
+    const uint64_t c0 = lane < n_cand ? cand[lane] : 0ull;
+    const uint64_t c1 = lane + 64 < n_cand ? cand[lane + 64] : 0ull;
+    const int q0 = count_greater(cand, n_cand, c0);
+    const int q1 = n_cand > 64 ? count_greater(cand, n_cand, c1) : k;
+    if (lane < n_cand && q0 < k) ranked[q0] = c0;
+    if (lane + 64 < n_cand && q1 < k) ranked[q1] = c1;
+    wave_lds_sync();
+    const uint64_t pq = ranked[min(lane, k - 1)];
+    if (lane < k) {
+      pick_k = (uint32_t)(pq >> 32);
+      pick_e = ~(uint32_t)pq;
+    }
+  } else {
+    // 4. k rounds of wave max, lowest index holding it, owner clears it
+    uint32_t key[NPL];
 #pragma unroll
-  for (int j = 0; j < kTopkMax; ++j) {
-    if (j < k) {
-      uint32_t lm = key[0];
+    for (int i = 0; i < NPL; ++i) key[i] = (uint32_t)(r.p[i] >> 32);
 #pragma unroll
-      for (int i = 1; i < NPL; ++i) lm = key[i] > lm ? key[i] : lm;
-      const uint32_t wm = dpp::wave_max_u32(lm);
-      // lowest expert index holding wm: per-lane candidate, then a wave min
-      uint32_t li = 0xFFFFFFFFu;
+    for (int j = 0; j < kTopkMax; ++j) {
+      if (j < k) {
+        uint32_t lm = key[0];
 #pragma unroll
-      for (int i = NPL - 1; i >= 0; --i) li = (key[i] == wm) ? (uint32_t)(lane + 64 * i) : li;
-      const int e = (int)dpp::wave_min_u32(li);
+        for (int i = 1; i < NPL; ++i) lm = key[i] > lm ? key[i] : lm;
+        const uint32_t wm = dpp::wave_max_u32(lm);
+        uint32_t li = 0xFFFFFFFFu;
 #pragma unroll
-      for (int i = 0; i < NPL; ++i) key[i] = (lane + 64 * i == e) ? 0u : key[i];
-      pick_k = (lane == j) ? wm : pick_k;
-      pick_e = (lane == j) ? (uint32_t)e : pick_e;
+        for (int i = NPL - 1; i >= 0; --i) li = (key[i] == wm) ? (uint32_t)(lane + 64 * i) : li;
+        const int e = (int)dpp::wave_min_u32(li);
+#pragma unroll
+        for (int i = 0; i < NPL; ++i) key[i] = (lane + 64 * i == e) ? 0u : key[i];
+        pick_k = (lane == j) ? wm : pick_k;
+        pick_e = (lane == j) ? (uint32_t)e : pick_e;
+      }
     }
   }
   // weights: exp(l - l_max) over the picks (norm_topk) or over all E logits
@@ -90,7 +184,7 @@ __device__ __forceinline__ void wave_route(const float* __restrict__ logits, int
     float part = 0.f;
 #pragma unroll
     for (int i = 0; i < NPL; ++i)
-      if (lane + 64 * i < E) part += expf(lv[i] - lmax);
+      if (lane + 64 * i < E) part += expf(r.lv[i] - lmax);
     s = dpp::wave_sum(part);
   }
   if (lane < k) {
@@ -103,6 +197,66 @@ __device__ __forceinline__ void wave_route(const float* __restrict__ logits, int
       if (host_idx) host_idx[lane] = (int32_t)pick_e;
     }
   }
+}
+
+// T: the lane maximum of rank k - 1 (one lane has it: the 64 values are distinct).
+__device__ __forceinline__ uint64_t route_threshold(uint64_t pm, int rank, int k) {
+  const uint64_t tmask = __ballot(rank == k - 1);
+  return readlane_u64(pm, __builtin_ctzll(tmask));
+}
+
+// One wave routes one token. logits: E values (global memory). lds: kRouteLds
+// uint32 of this wave's LDS; on return lds[kRouteOrdered + 2q + 1] holds pick q
+// (selection order) and lds[kRouteOrdered + 2q] the bits of its weight, for
+// q < k. When out_idx is non-NULL, lane q < k also writes out_idx[q] and
+// out_w[q] (and host_idx[q] when that is non-NULL too).
+template <int NPL>
+__device__ __forceinline__ void wave_route(const float* __restrict__ logits, int E, int k, int norm_topk, uint32_t* lds,
+                                           int32_t* out_idx, float* out_w, int32_t* host_idx) {
+  const int lane = threadIdx.x & 63;
+  RouteLane<NPL> r;
+  route_load<NPL>(logits, E, r);
+  uint64_t* lane_best = route_lane_best(lds);
+  lane_best[lane] = r.pm;
+  wave_lds_sync();
+  const int rank = count_greater(lane_best, 64, r.pm);
+  route_finish<NPL>(r, route_threshold(r.pm, rank, k), E, k, norm_topk, lds, out_idx, out_w, host_idx);
+}
+
+// The same selection by a whole block of NW waves (every thread calls it;
+// it synchronises the block): wave 0 loads the logits and does steps 1, 3
+// and 4; the ranks of the 64 lane maxima are counted by all NW waves, each
+// against 64 / NW of them, and summed with LDS atomics. On return the picks
+// and weights are in lds as for wave_route, visible to the whole block.
+template <int NPL, int NW>
+__device__ __forceinline__ void block_route(const float* __restrict__ logits, int E, int k, int norm_topk, uint32_t* lds,
+                                            int32_t* out_idx, float* out_w, int32_t* host_idx) {
+  static_assert(64 % NW == 0, "the lane maxima are split evenly over the waves");
+  constexpr int PER = 64 / NW;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  uint64_t* lane_best = route_lane_best(lds);
+  uint32_t* rank_count = route_rank_count(lds);
+  RouteLane<NPL> r;
+  if (wv == 0) {
+    route_load<NPL>(logits, E, r);
+    lane_best[lane] = r.pm;
+    rank_count[lane] = 0u;
+  }
+  __syncthreads();
+  {
+    const uint64_t mine = lane_best[lane];
+    int c = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) c += lane_best[wv * PER + j] > mine ? 1 : 0;
+    if (c) atomicAdd(&rank_count[lane], (uint32_t)c);
+  }
+  __syncthreads();
+  if (wv == 0) {
+    const int rank = (int)rank_count[lane];
+    route_finish<NPL>(r, route_threshold(r.pm, rank, k), E, k, norm_topk, lds, out_idx, out_w, host_idx);
+  }
+  __syncthreads();
 }
 
 inline int topk_npl(int E) {

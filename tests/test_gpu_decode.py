@@ -105,6 +105,51 @@ def test_topk_exact_on_crafted_logits():
         model.close()
 
 
+def test_topk_exact_wide_routing_and_fallback():
+    """1024 experts, top-16. The selection ranks the experts at or above the
+    16th-best lane maximum; when the best logits crowd into a few lanes (here
+    every expert on lanes 0..15 of the 64-lane layout e = lane + 64 i) more than
+    128 experts reach that bound and the round-by-round selection runs instead."""
+    cfg = synth.get_config("tiny", n_experts=1024, top_k=16, hidden=256, inter=64, shared_inter=64)
+    from oracle import moe as omoe
+    from routed_expert_int4_router_amd import loader
+    torch = gh.torch_cuda()
+    rng = np.random.default_rng(9)
+    e = np.arange(1024)
+    crowded = rng.standard_normal(1024).astype(np.float32)
+    crowded[e % 64 < 16] += 8.0
+    rows = [
+        rng.standard_normal(1024).astype(np.float32),
+        crowded,
+        np.zeros(1024, np.float32),
+        (rng.integers(-1, 2, 1024) * 0.5).astype(np.float32),
+    ]
+    w = synth.SynthWeights(cfg)
+    for row in rows:
+        class Crafted:
+            def __getattr__(self, n):
+                return getattr(w, n)
+
+            def router(self, layer):
+                r = w.router(layer).copy()
+                r[0, :] = row
+                return r
+
+        model = loader.load_model(cfg, Crafted())
+        xb = np.zeros((1, cfg.hidden), np.uint16)
+        xb[0, 0] = 0x3F80  # bf16 1.0: logit e is exactly W_r[0, e]
+        x = gh.dev_bf16(xb)
+        out = gh.dev_f32((1, cfg.hidden))
+        model.layer_decode(0, x, out)
+        torch.cuda.synchronize()
+        idx, wts = model.debug_routing()
+        want = omoe.topk_order(row, cfg.top_k)
+        assert list(idx[0]) == list(want), (idx[0], want)
+        ref = omoe.route_weights(row.astype(np.float64), want, cfg.norm_topk)
+        assert np.allclose(wts[0], ref, rtol=1e-5, atol=1e-7)
+        model.close()
+
+
 def test_decode80b_full_size_sampled():
     """All 1024 tokens of the 80B-shaped layer in the benchmark's launch configuration;
     routing checked for every token, outputs on a sample the oracle recomputes."""
