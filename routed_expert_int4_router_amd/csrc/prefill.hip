@@ -12,9 +12,11 @@
 //   gateup      grouped GEMM per (expert, 64-row tile, 64-column tile):
 //               int4 codes -> exact bf16 values 16 + q, bf16 MFMA, fp32
 //               per-group scaling acc += s * P + (c - 16 s) * xsum, SwiGLU in
-//               the epilogue, h stored as a bf16 hi/lo pair (+ per-group sums)
-//   down        grouped GEMM on h (hi and lo MFMA passes), router weight in
-//               the epilogue, one fp32 row per (token, slot) and per token
+//               the epilogue, h stored in fp16 with one power-of-two scale
+//               per (tile, 64-group) that keeps it in range (+ per-group sums)
+//   down        grouped GEMM on h (fp16 MFMA, codes as fp16 16 + q), router
+//               weight in the epilogue, one fp32 row per (token, slot) and
+//               per token
 //   combine     out[t] = sum_j y[t,j] + y_shared[t] in fixed order
 // Pages for the method itself: top-k routing, resident router and shared
 // expert, int4/int8 group quantisation (cheshm.ai news article, paragraphs on
@@ -38,6 +40,7 @@ hipError_t launch_route(const Geometry& g, const float* logits, int ld_logits, i
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int BM = 64;        // tile rows (tokens or pairs)
@@ -53,8 +56,8 @@ struct Workspace {
   int32_t* e_off = nullptr;     // [E+2]: start of each expert's rows; [E] = T*k (shared rows), [E+1] = T*k + T
   int32_t* perm = nullptr;      // [T*k] sorted position -> pair id
   int32_t* tiles = nullptr;     // [1 + max_tiles * 2]: count, then (expert, row0) per tile
-  uint16_t* h_hi = nullptr;     // [T*k + T][I]
-  uint16_t* h_lo = nullptr;
+  uint16_t* h16 = nullptr;      // [T*k + T][I] fp16 bits, h / hscale
+  float* hscale = nullptr;      // [max_tiles][I/64] power-of-two scale of each (tile, group)
   float* hsum = nullptr;        // [T*k + T][I/64]
   float* y = nullptr;           // [T*k + T][H]
   int max_tiles = 0;
@@ -90,6 +93,17 @@ __device__ __forceinline__ bf16x8 nib_to_bf16(uint32_t w) {
   d[2] = ((w >> 5) & m) | mag;
   d[3] = ((w >> 9) & m) | mag;
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<uint4*>(d));
+}
+
+// 8 int4 codes of a dword -> fp16 values 16 + q in the same order.
+__device__ __forceinline__ f16x8 nib_to_f16(uint32_t w) {
+  const uint32_t m = 0x03C003C0u, mag = 0x4C004C00u;
+  uint32_t d[4];
+  d[0] = ((w << 6) & m) | mag;
+  d[1] = ((w << 2) & m) | mag;
+  d[2] = ((w >> 2) & m) | mag;
+  d[3] = ((w >> 6) & m) | mag;
+  return __builtin_bit_cast(f16x8, *reinterpret_cast<uint4*>(d));
 }
 
 // ------------------------------------------------------------------- xsum ---
@@ -312,8 +326,8 @@ struct GemmArgs {
   const int32_t* tiles;
   const float* route_w;       // [T*k]
   const float* route_gamma;   // [T]
-  uint16_t* h_hi;
-  uint16_t* h_lo;
+  uint16_t* h16;
+  float* hscale;
   float* hsum;
   float* y;
   int T, H, I, E, k;
@@ -550,10 +564,47 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   }
   __syncthreads();
   const int base = a.e_off[e] + r0;
-  // h is stored with each 8-chunk in nib_to_bf16 order, ready for the down GEMM's DMA
+  // h = silu(gate) * up of the tile's 64 x 64 (rows x group nt) block; the
+  // first pass only finds max |h| (the values are recomputed, identically,
+  // after the block-wide maximum is known)
+  auto h_at = [&](int r, int half) -> float {
+    const int m = (r >> 2) * 8 + hh * 4 + (r & 3) + 32 * half;
+    const float gt = sg[m * SGS + nl];
+    const float u = half ? acc1[r] : acc0[r];
+    return gt / (1.0f + expf(-gt)) * u;
+  };
+  const bool h_lane = mat == 1 && n0 + nl < a.I;
+  float amax = 0.f;
+  if (h_lane) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m0 = (r >> 2) * 8 + hh * 4 + (r & 3);
+#pragma unroll
+      for (int half = 0; half < 2; ++half)
+        if (r0 + m0 + 32 * half < rows) amax = fmaxf(amax, fabsf(h_at(r, half)));
+    }
+  }
+  // The block's scale: 2^e with e >= 0 the least that brings max |h| below
+  // 2^15, so every scaled value is a finite fp16 (e = 0 unless |h| >= 65504).
+  __shared__ uint32_t s_amax[4];
+  {
+    const uint32_t wm = dpp::wave_max_u32(__float_as_uint(amax));  // non-negative floats order as integers
+    if (lane == 0) s_amax[wv] = wm;
+  }
+  __syncthreads();
+  const float tmax = __uint_as_float(max(max(s_amax[0], s_amax[1]), max(s_amax[2], s_amax[3])));
+  int ex = 0;
+  if (tmax >= 65504.f) {
+    int x2;
+    (void)frexpf(tmax, &x2);  // tmax < 2^x2
+    ex = x2 - 15;
+  }
+  if (tid == 0 && n0 < a.I) a.hscale[(size_t)tile * (a.I / 64) + nt] = ldexpf(1.f, ex);
+  // h / 2^e in fp16, each 8-chunk in nib_to_f16 order for the down GEMM's DMA;
+  // sg keeps 2^e * fp16 value, what the down GEMM multiplies
   const int p = nl & 7;
   const int col = n0 + (nl & ~7) + (p < 4 ? 2 * p : 2 * (p - 4) + 1);
-  if (mat == 1 && n0 + nl < a.I) {
+  if (h_lane) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m0 = (r >> 2) * 8 + hh * 4 + (r & 3);
@@ -561,15 +612,9 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
       for (int half = 0; half < 2; ++half) {
         const int m = m0 + 32 * half;
         if (r0 + m < rows) {
-          const float gt = sg[m * SGS + nl];
-          const float u = half ? acc1[r] : acc0[r];
-          const float hv = gt / (1.0f + expf(-gt)) * u;
-          const uint16_t hi = to_bf16_rne(hv);
-          const uint16_t lo = to_bf16_rne(hv - bf16f(hi));
-          const size_t o = (size_t)(base + m) * a.I + col;
-          a.h_hi[o] = hi;
-          a.h_lo[o] = lo;
-          sg[m * SGS + nl] = bf16f(hi) + bf16f(lo);  // what the down GEMM multiplies
+          const _Float16 hq = (_Float16)ldexpf(h_at(r, half), -ex);
+          a.h16[(size_t)(base + m) * a.I + col] = __builtin_bit_cast(uint16_t, hq);
+          sg[m * SGS + nl] = ldexpf((float)hq, ex);
         }
       }
     }
@@ -589,25 +634,25 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
 // ------------------------------------------------------- grouped GEMM 2 ---
 // Block = (tile, 256 output columns of H), 4 waves, two blocks per CU: 64
 // rows of one expert x 256 columns; wave w computes columns [64w, 64w + 64)
-// as 2 x 2 tiles of 32x32x16 MFMA. A = h as a bf16 (hi, lo) pair (two MFMAs
-// per step, together exact to about 16 significant bits), K over the
-// 64-groups of I. Operands move by global->LDS DMA into DN_NS-stage rings,
-// DN_PF groups ahead, 7 DMAs per wave per group (hi 2, lo 2, codes 2, scales
-// 1); the affine term uses the per-group sums of h written by the gate/up
-// kernel. Output: y[pair][n] = weight * acc (one fp32 row per (token, slot),
-// the shared expert's rows after them).
+// as 2 x 2 tiles of 32x32x16 fp16 MFMA. A = h / 2^e in fp16 (2^e the
+// (tile, group) scale from the gate/up kernel, folded into the group's
+// weight scale), B = the codes as fp16 16 + q, K over the 64-groups of I.
+// Operands move by global->LDS DMA into DN_NS-stage rings, DN_PF groups
+// ahead, 5 DMAs per wave per group (h 2, codes 2, scales 1); the affine term
+// uses the per-group sums of h written by the gate/up kernel. Output:
+// y[pair][n] = weight * acc (one fp32 row per (token, slot), the shared
+// expert's rows after them).
 constexpr int DN_BN = 256;                 // H columns per block
 constexpr int DN_NS = 3;                   // ring stages
 constexpr int DN_PF = DN_NS - 1;           // prefetch distance in groups
-constexpr int DA_STAGE = BM * 64 * 2;      // 64 rows x 64 bf16, for each of hi and lo
+constexpr int DA_STAGE = BM * 64 * 2;      // 64 rows x 64 fp16
 constexpr int DB_STAGE = DN_BN * 32;       // 256 code rows x 64 int4
 constexpr int DS_STAGE = DN_BN * 4;        // 256 (s, c) words
 
-size_t down_lds_bytes(int GI) { return (size_t)DN_NS * (2 * DA_STAGE + DB_STAGE + DS_STAGE) + (size_t)256 * GI; }
+size_t down_lds_bytes(int GI) { return (size_t)DN_NS * (DA_STAGE + DB_STAGE + DS_STAGE) + (size_t)256 * GI; }
 
 struct DownSources {
-  const uint16_t* hi[2];  // A (instruction t): row 8 (2w + t) + lane / 8, chunk (lane % 8) ^ (row % 8)
-  const uint16_t* lo[2];
+  const uint16_t* h[2];   // A (instruction t): row 8 (2w + t) + lane / 8, chunk (lane % 8) ^ (row % 8)
   bool live[2];
   const uint8_t* b[2];    // code rows: instruction t covers rows 64w + 32t + lane / 2, tile half lane % 2
   const uint8_t* s;       // scale word of row 64w + lane
@@ -617,57 +662,49 @@ struct DownSources {
 // DMAs of group gn into the free stages; the restrict qualifiers keep the
 // compiler from ordering them against this group's LDS reads (the caller's
 // wait + barrier does).
-__device__ __forceinline__ void down_issue(uint8_t* __restrict__ wrH, uint8_t* __restrict__ wrL,
-                                           uint8_t* __restrict__ wrB, uint8_t* __restrict__ wrS,
-                                           const DownSources& src, int gn, int wv) {
+__device__ __forceinline__ void down_issue(uint8_t* __restrict__ wrH, uint8_t* __restrict__ wrB,
+                                           uint8_t* __restrict__ wrS, const DownSources& src, int gn, int wv) {
   dma16(src.b[0] + (size_t)gn * src.bq, wrB + (2 * wv) * 1024);
   dma16(src.b[1] + (size_t)gn * src.bq, wrB + (2 * wv + 1) * 1024);
   dma4(src.s + (size_t)gn * src.sq, wrS + wv * 256);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    if (src.live[t]) dma16(src.hi[t] + 64 * gn, wrH + (2 * wv + t) * 1024);
-    if (src.live[t]) dma16(src.lo[t] + 64 * gn, wrL + (2 * wv + t) * 1024);
-  }
+  for (int t = 0; t < 2; ++t)
+    if (src.live[t]) dma16(src.h[t] + 64 * gn, wrH + (2 * wv + t) * 1024);
 }
 
-// One group: acc += s * (A_hi + A_lo) . (16 + q); for an odd group also the
-// affine term of the pair (g - 1, g) (lanes of k-half hh take group g-1+hh).
-__device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, const uint8_t* __restrict__ rdL,
-                                           const uint8_t* __restrict__ rdB, const uint8_t* __restrict__ rdS,
-                                           const float* __restrict__ sHs, uint8_t* __restrict__ wrH,
-                                           uint8_t* __restrict__ wrL, uint8_t* __restrict__ wrB,
+// One group: acc += s * 2^e * A . (16 + q); for an odd group also the affine
+// term of the pair (g - 1, g) (lanes of k-half hh take group g-1+hh).
+__device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, const uint8_t* __restrict__ rdB,
+                                           const uint8_t* __restrict__ rdS, const float* __restrict__ sHs,
+                                           float hscale, uint8_t* __restrict__ wrH, uint8_t* __restrict__ wrB,
                                            uint8_t* __restrict__ wrS, const DownSources& src, int gn, int g,
                                            int wv, int brow, int hh, int mrow, float (&cprev)[2], f32x16 (&acc)[4]) {
-  down_issue(wrH, wrL, wrB, wrS, src, gn, wv);
-  bf16x8 ah[2][4], al[2][4];
+  down_issue(wrH, wrB, wrS, src, gn, wv);
+  f16x8 ah[2][4];
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     const int off = ((4 * hh + st) ^ (mrow & 7)) * 16;
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      ah[mm][st] = *reinterpret_cast<const bf16x8*>(rdH + (32 * mm + mrow) * 128 + off);
-      al[mm][st] = *reinterpret_cast<const bf16x8*>(rdL + (32 * mm + mrow) * 128 + off);
-    }
+    for (int mm = 0; mm < 2; ++mm) ah[mm][st] = *reinterpret_cast<const f16x8*>(rdH + (32 * mm + mrow) * 128 + off);
   }
   float cval[2];
 #pragma unroll
   for (int nn = 0; nn < 2; ++nn) {
     const uint4 cw = *reinterpret_cast<const uint4*>(rdB + (brow + 32 * nn) * 32 + hh * 16);
     const uint32_t sw = *reinterpret_cast<const uint32_t*>(rdS + (brow + 32 * nn) * 4);
-    const bf16x8 b[4] = {nib_to_bf16(cw.x), nib_to_bf16(cw.y), nib_to_bf16(cw.z), nib_to_bf16(cw.w)};
+    const f16x8 b[4] = {nib_to_f16(cw.x), nib_to_f16(cw.y), nib_to_f16(cw.z), nib_to_f16(cw.w)};
     f32x16 p0 = {}, p1 = {};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[0][st], b[st], p0, 0, 0, 0);
-      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[1][st], b[st], p1, 0, 0, 0);
-      p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[0][st], b[st], p0, 0, 0, 0);
-      p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[1][st], b[st], p1, 0, 0, 0);
+      p0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][st], b[st], p0, 0, 0, 0);
+      p1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][st], b[st], p1, 0, 0, 0);
     }
     const float sv = f16f(sw & 0xFFFFu);
+    const float svh = sv * hscale;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      acc[2 * nn][r] += sv * p0[r];
-      acc[2 * nn + 1][r] += sv * p1[r];
+      acc[2 * nn][r] += svh * p0[r];
+      acc[2 * nn + 1][r] += svh * p1[r];
     }
     cval[nn] = f16f(sw >> 16) - 16.0f * sv;
   }
@@ -698,9 +735,9 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   const int n0 = nt * DN_BN;
   const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
   const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  __shared__ float s_hscale[64];
   uint8_t* sH = smem;                                               // [NS][64][8 slots of 16 B]
-  uint8_t* sL = sH + DN_NS * DA_STAGE;
-  uint8_t* sB = sL + DN_NS * DA_STAGE;                              // [NS][256 rows][32 B]
+  uint8_t* sB = sH + DN_NS * DA_STAGE;                              // [NS][256 rows][32 B]
   uint8_t* sS = sB + DN_NS * DB_STAGE;                              // [NS][256 rows] words
   float* sHs = reinterpret_cast<float*>(sS + DN_NS * DS_STAGE);     // [GI][64 rows]
 
@@ -739,6 +776,7 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
     }
     s_dst[tid] = dst;
     s_w[tid] = w;
+    if (tid < GI) s_hscale[tid] = a.hscale[(size_t)tile * GI + tid];
   }
   const int nrow = min(rows - r0, BM);  // rows of this tile (>= 1)
   // h group sums: instruction g loads group g of the 64 rows
@@ -750,17 +788,14 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   for (int t = 0; t < 2; ++t) {
     const int row = 8 * (2 * wv + t) + (lane >> 3), chunk = (lane & 7) ^ (row & 7);
     const size_t hrow = (size_t)base + min(row, nrow - 1);
-    src.hi[t] = a.h_hi + hrow * a.I + 8 * chunk;
-    src.lo[t] = a.h_lo + hrow * a.I + 8 * chunk;
+    src.h[t] = a.h16 + hrow * a.I + 8 * chunk;
     src.live[t] = row < nrow || lane == 0;
   }
   for (int g = 0; g < DN_PF; ++g) {
     const int gc = min(g, GI - 1);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (src.live[t]) dma16(src.hi[t] + 64 * gc, sH + g * DA_STAGE + (2 * wv + t) * 1024);
-      if (src.live[t]) dma16(src.lo[t] + 64 * gc, sL + g * DA_STAGE + (2 * wv + t) * 1024);
-    }
+    for (int t = 0; t < 2; ++t)
+      if (src.live[t]) dma16(src.h[t] + 64 * gc, sH + g * DA_STAGE + (2 * wv + t) * 1024);
   }
   const int nl = 64 * wv + (lane & 31);  // first column of this lane (second: + 32)
   const int brow = nl;
@@ -768,19 +803,21 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   const int mrow = lane & 31;
   f32x16 acc[4] = {};
   float cprev[2] = {0.f, 0.f};
-  // Waits (PF = 2): step 0 needs A(0), after which only A(1) (4 DMAs) was
-  // issued; step g >= 1 needs group g, issued one step (7 DMAs) earlier.
+  // Waits (PF = 2): step 0 needs A(0), after which only A(1) (2 DMAs) was
+  // issued; step g >= 1 needs group g, issued one step (5 DMAs) earlier. The
+  // barrier of step 0 also publishes s_hscale.
   static_assert(DN_PF == 2, "wait counts below are written for PF = 2");
   for (int g = 0; g < GI; ++g) {
     if (g == 0)
-      __builtin_amdgcn_s_waitcnt(0x0070 | 4);
+      __builtin_amdgcn_s_waitcnt(0x0070 | 2);
     else
-      __builtin_amdgcn_s_waitcnt(0x0070 | 7);
+      __builtin_amdgcn_s_waitcnt(0x0070 | 5);
     __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no LDS read moves above the barrier
     const int rd = g % DN_NS, wr = (g + DN_PF) % DN_NS;
-    down_group(sH + rd * DA_STAGE, sL + rd * DA_STAGE, sB + rd * DB_STAGE, sS + rd * DS_STAGE, sHs,
-               sH + wr * DA_STAGE, sL + wr * DA_STAGE, sB + wr * DB_STAGE, sS + wr * DS_STAGE, src,
-               min(g + DN_PF, GI - 1), g, wv, brow, hh, mrow, cprev, acc);
+    down_group(sH + rd * DA_STAGE, sB + rd * DB_STAGE, sS + rd * DS_STAGE, sHs, s_hscale[g], sH + wr * DA_STAGE,
+               sB + wr * DB_STAGE, sS + wr * DS_STAGE, src, min(g + DN_PF, GI - 1), g, wv, brow, hh, mrow, cprev,
+               acc);
   }
   if (GI & 1) {  // odd group count: the last group's affine term, paired with zeros
     const float x0 = hh ? 0.f : sHs[(GI - 1) * 64 + mrow], x1 = hh ? 0.f : sHs[(GI - 1) * 64 + 32 + mrow];
@@ -859,8 +896,8 @@ GemmArgs gemm_args(const Workspace* w, const PrefillArgs& pa) {
   ga.tiles = w->tiles;
   ga.route_w = pa.route_w;
   ga.route_gamma = pa.route_gamma;
-  ga.h_hi = w->h_hi;
-  ga.h_lo = w->h_lo;
+  ga.h16 = w->h16;
+  ga.hscale = w->hscale;
   ga.hsum = w->hsum;
   ga.y = w->y;
   ga.T = pa.n_tok;
@@ -892,8 +929,8 @@ void prefill_free(void* ws) {
   hipFree(w->e_off);
   hipFree(w->perm);
   hipFree(w->tiles);
-  hipFree(w->h_hi);
-  hipFree(w->h_lo);
+  hipFree(w->h16);
+  hipFree(w->hscale);
   hipFree(w->hsum);
   hipFree(w->y);
   delete w;
@@ -915,7 +952,8 @@ moe_status prefill_reserve(void** wsp, const moe_config& c, int T) {
   const bool ok = grow(w->logits, (size_t)T * (E + 1)) && grow(w->xsum, (size_t)T * (H / 64)) && grow(w->xp, (size_t)T * H) &&
                   grow(w->cnt, (size_t)nchunk * E) && grow(w->chunk_off, (size_t)nchunk * E) &&
                   grow(w->e_off, (size_t)E + 2) && grow(w->perm, P) && grow(w->tiles, (size_t)1 + 2 * max_tiles) &&
-                  grow(w->h_hi, rows * I) && grow(w->h_lo, rows * I) && grow(w->hsum, rows * (I / 64)) &&
+                  grow(w->h16, rows * I) && grow(w->hscale, (size_t)max_tiles * (I / 64)) &&
+                  grow(w->hsum, rows * (I / 64)) &&
                   grow(w->y, rows * H);
   if (!ok) return MOE_ENOMEM;
   w->T = T;
