@@ -548,41 +548,38 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
     gateup_affine(af, acc0, acc1);
   }
 #undef GU_STEP
-  // SwiGLU: gate waves publish through LDS (the A ring, once no DMA is in flight)
+  // Epilogue. Gate and up tiles go through LDS (the rings are idle once no
+  // DMA is in flight) so that all four waves share the SwiGLU arithmetic.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
-  constexpr int SGS = GU_BN + 1;
-  static_assert(BM * SGS * 4 <= GU_NA * A_STAGE, "SwiGLU exchange must fit the A ring");
-  float* sg = reinterpret_cast<float*>(sA);  // [64][GU_BN + 1]
-  if (mat == 0) {
+  constexpr int SGS = GU_BN + 1;  // padded row stride (floats)
+  static_assert(BM * SGS * 4 <= GU_NA * A_STAGE, "gate tile must fit the A ring");
+  static_assert(BM * SGS * 4 <= 2 * BQ_STAGE, "up tile must fit the code ring");
+  float* sg = reinterpret_cast<float*>(sA);  // [64][SGS]: gate, then h, then the dequantised h
+  float* su = reinterpret_cast<float*>(sB);  // [64][SGS]: up, then the fp16 rows [64][64] for the stores
+  {
+    float* dst = mat == 0 ? sg : su;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
-      sg[m * SGS + nl] = acc0[r];
-      sg[(32 + m) * SGS + nl] = acc1[r];
+      dst[m * SGS + nl] = acc0[r];
+      dst[(32 + m) * SGS + nl] = acc1[r];
     }
   }
   __syncthreads();
   const int base = a.e_off[e] + r0;
-  // h = silu(gate) * up of the tile's 64 x 64 (rows x group nt) block; the
-  // first pass only finds max |h| (the values are recomputed, identically,
-  // after the block-wide maximum is known)
-  auto h_at = [&](int r, int half) -> float {
-    const int m = (r >> 2) * 8 + hh * 4 + (r & 3) + 32 * half;
-    const float gt = sg[m * SGS + nl];
-    const float u = half ? acc1[r] : acc0[r];
-    return gt / (1.0f + expf(-gt)) * u;
-  };
-  const bool h_lane = mat == 1 && n0 + nl < a.I;
+  const int nrow = min(rows - r0, BM);
+  const int c = tid & 63;           // column of the group handled by this thread
+  const bool c_live = n0 + c < a.I;
+  // h = silu(gate) * up for rows tid / 64 + 4 j; hardware exp2 and reciprocal
   float amax = 0.f;
-  if (h_lane) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m0 = (r >> 2) * 8 + hh * 4 + (r & 3);
-#pragma unroll
-      for (int half = 0; half < 2; ++half)
-        if (r0 + m0 + 32 * half < rows) amax = fmaxf(amax, fabsf(h_at(r, half)));
-    }
+  for (int j = 0; j < 16; ++j) {
+    const int m = (tid >> 6) + 4 * j;
+    const float gt = sg[m * SGS + c];
+    const float hv = gt * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt)) * su[m * SGS + c];
+    sg[m * SGS + c] = hv;
+    if (m < nrow && c_live) amax = fmaxf(amax, fabsf(hv));
   }
   // The block's scale: 2^e with e >= 0 the least that brings max |h| below
   // 2^15, so every scaled value is a finite fp16 (e = 0 unless |h| >= 65504).
@@ -600,34 +597,40 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
     ex = x2 - 15;
   }
   if (tid == 0 && n0 < a.I) a.hscale[(size_t)tile * (a.I / 64) + nt] = ldexpf(1.f, ex);
-  // h / 2^e in fp16, each 8-chunk in nib_to_f16 order for the down GEMM's DMA;
-  // sg keeps 2^e * fp16 value, what the down GEMM multiplies
-  const int p = nl & 7;
-  const int col = n0 + (nl & ~7) + (p < 4 ? 2 * p : 2 * (p - 4) + 1);
-  if (h_lane) {
+  // h / 2^e in fp16, each 8-chunk in nib_to_f16 order (position of column c
+  // within its chunk: 0,2,4,6,1,3,5,7), staged for 16-byte row stores; sg
+  // keeps 2^e * fp16 value, what the down GEMM multiplies
+  uint16_t* sh16 = reinterpret_cast<uint16_t*>(su);
+  {
+    const int p = c & 7;
+    const int pos = (c & ~7) + (p < 4 ? 2 * p : 2 * (p - 4) + 1);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int m0 = (r >> 2) * 8 + hh * 4 + (r & 3);
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int m = m0 + 32 * half;
-        if (r0 + m < rows) {
-          const _Float16 hq = (_Float16)ldexpf(h_at(r, half), -ex);
-          a.h16[(size_t)(base + m) * a.I + col] = __builtin_bit_cast(uint16_t, hq);
-          sg[m * SGS + nl] = ldexpf((float)hq, ex);
-        }
-      }
+    for (int j = 0; j < 16; ++j) {
+      const int m = (tid >> 6) + 4 * j;
+      const _Float16 hq = (_Float16)ldexpf(sg[m * SGS + c], -ex);
+      sg[m * SGS + c] = ldexpf((float)hq, ex);
+      sh16[m * 64 + pos] = __builtin_bit_cast(uint16_t, hq);
     }
   }
   __syncthreads();
-  // per-row sum of this 64-column group of h (a quant group of the down matrix)
-  if (tid < BM) {
-    const int m = tid;
-    if (r0 + m < rows && n0 < a.I) {
-      float sum = 0.f;
-      for (int c = 0; c < 64; ++c) sum += sg[m * SGS + c];
-      a.hsum[(size_t)(base + m) * (a.I / 64) + nt] = sum;
+  // rows of h (128 bytes each) and per-row group sums: 4 threads per row,
+  // 16 columns each, combined ((q0 + q1) + (q2 + q3))
+  if (n0 < a.I) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int ch = tid + 256 * q;  // 16-byte chunk: row ch / 8, chunk ch % 8
+      const int m = ch >> 3;
+      if (m < nrow)
+        *reinterpret_cast<uint4*>(a.h16 + (size_t)(base + m) * a.I + n0 + 8 * (ch & 7)) =
+            *reinterpret_cast<const uint4*>(sh16 + m * 64 + 8 * (ch & 7));
     }
+    const int m = tid >> 2, qq = tid & 3;
+    float sum = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 16; ++cc) sum += sg[m * SGS + 16 * qq + cc];
+    sum += __uint_as_float(dpp::mov<dpp::kQuadXor1, 0xF>(0u, __float_as_uint(sum)));
+    sum += __uint_as_float(dpp::mov<dpp::kQuadXor2, 0xF>(0u, __float_as_uint(sum)));
+    if (qq == 0 && m < nrow) a.hsum[(size_t)(base + m) * (a.I / 64) + nt] = sum;
   }
 }
 
