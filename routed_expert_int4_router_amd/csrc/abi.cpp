@@ -70,12 +70,12 @@ namespace {
 
 enum KernelKind {
   K_ROUTER, K_ROUTE, K_GATEUP, K_DOWN, K_EXPERT, K_REDUCE,
-  K_PF_XSUM, K_PF_ROUTER, K_PF_ROUTE, K_PF_COUNT, K_PF_SCAN, K_PF_SCATTER, K_PF_GATEUP, K_PF_DOWN, K_PF_COMBINE,
+  K_PF_XPREP, K_PF_ROUTER, K_PF_ROUTE, K_PF_COUNT, K_PF_SCAN, K_PF_SCATTER, K_PF_GATEUP, K_PF_DOWN, K_PF_COMBINE,
   K_COUNT
 };
 const char* const kKindName[K_COUNT] = {"router",         "route",          "gateup",         "down",
                                         "expert",         "reduce",
-                                        "prefill_xsum",   "prefill_router", "prefill_route",  "prefill_count",
+                                        "prefill_xprep",  "prefill_router", "prefill_route",  "prefill_count",
                                         "prefill_scan",   "prefill_scatter", "prefill_gateup", "prefill_down",
                                         "prefill_combine"};
 
@@ -571,10 +571,10 @@ moe_status moe_layer_forward(moe_model* m, int32_t layer, const uint16_t* x, int
     hipStream_t s = static_cast<hipStream_t>(stream);
     void* ws = m->prefill;
     using Stage = hipError_t (*)(void*, const PrefillArgs&, hipStream_t);
-    static const Stage kStages[] = {prefill_xsum,  prefill_router,  prefill_route,  prefill_count,  prefill_scan,
+    static const Stage kStages[] = {prefill_xprep, prefill_router,  prefill_route,  prefill_count,  prefill_scan,
                                     prefill_scatter, prefill_gateup, prefill_down, prefill_combine};
     for (int i = 0; i < 9; ++i)
-      HIP_TRY(m->prof.run(K_PF_XSUM + i, s, [&] { return kStages[i](ws, a, s); }), "moe_layer_forward: prefill stage");
+      HIP_TRY(m->prof.run(K_PF_XPREP + i, s, [&] { return kStages[i](ws, a, s); }), "moe_layer_forward: prefill stage");
     m->route_steps = (size_t)n_tok;
     return MOE_OK;
   }

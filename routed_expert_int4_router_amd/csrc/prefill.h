@@ -35,7 +35,7 @@ moe_status prefill_reserve(void** workspace, const moe_config& cfg, int n_tok);
 void prefill_free(void* workspace);
 
 // The stages, one kernel each, in this order on one stream.
-hipError_t prefill_xsum(void* workspace, const PrefillArgs& a, hipStream_t s);     // per-token 64-group sums of x
+hipError_t prefill_xprep(void* workspace, const PrefillArgs& a, hipStream_t s);    // per-token scale, fp16 copy of x
 hipError_t prefill_router(void* workspace, const PrefillArgs& a, hipStream_t s);   // logits [T][E+1] (MFMA)
 hipError_t prefill_route(void* workspace, const PrefillArgs& a, hipStream_t s);    // top-k, weights, shared gate
 hipError_t prefill_count(void* workspace, const PrefillArgs& a, hipStream_t s);    // pairs per (chunk, expert)

@@ -3,17 +3,18 @@
 // The pages' runtime has no batched prefill: long prompts run token by token
 // (alphalab.site field test, FAQ item 4, and the method section on prompt
 // length). Here a batch of T tokens takes the layer in nine launches:
-//   xsum        per-token sums of x over each 64-group (bias term of the grid)
+//   xprep       per token: a power-of-two scale 2^e that keeps x / 2^e in
+//               fp16 range and that fp16 copy, k-permuted for the GEMM
 //   router      logits [T][E+1] = x . W_r^T with bf16 MFMA on an exact
 //               three-way bf16 split of the fp32 router rows, fp32 accumulate
 //   route       top-k + weights + shared gate per token (one wave each)
 //   bucket x3   stable counting sort of the T*k (token, slot) pairs by expert
 //               (per-chunk counts, scan + tile list, scatter), deterministic
 //   gateup      grouped GEMM per (expert, 64-row tile, 64-column tile):
-//               int4 codes -> exact bf16 values 16 + q, bf16 MFMA, fp32
-//               per-group scaling acc += s * P + (c - 16 s) * xsum, SwiGLU in
-//               the epilogue, h stored in fp16 with one power-of-two scale
-//               per (tile, 64-group) that keeps it in range (+ per-group sums)
+//               int4 codes -> fp16 weights s * q + c (one rounding), fp16
+//               MFMA with fp32 accumulate, the token scale and SwiGLU in the
+//               epilogue, h stored in fp16 with one power-of-two scale per
+//               (tile, 64-group) that keeps it in range (+ per-group sums)
 //   down        grouped GEMM on h (fp16 MFMA, codes as fp16 16 + q), router
 //               weight in the epilogue, one fp32 row per (token, slot) and
 //               per token
@@ -41,6 +42,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int BM = 64;        // tile rows (tokens or pairs)
@@ -49,8 +51,8 @@ constexpr int CHUNK = 512;    // pairs per bucketing chunk
 struct Workspace {
   int T = 0, E = 0, k = 0, H = 0, I = 0;
   float* logits = nullptr;      // [T][E+1]
-  float* xsum = nullptr;        // [T][H/64]
-  uint16_t* xp = nullptr;       // [T][H] k-permuted copy of x
+  float* xscale = nullptr;      // [T] power-of-two scale of each token
+  uint16_t* xp = nullptr;       // [T][H] fp16 bits of x / xscale, k-permuted
   int32_t* cnt = nullptr;       // [nchunk][E]
   int32_t* chunk_off = nullptr; // [nchunk][E]
   int32_t* e_off = nullptr;     // [E+2]: start of each expert's rows; [E] = T*k (shared rows), [E+1] = T*k + T
@@ -106,29 +108,70 @@ __device__ __forceinline__ f16x8 nib_to_f16(uint32_t w) {
   return __builtin_bit_cast(f16x8, *reinterpret_cast<uint4*>(d));
 }
 
-// ------------------------------------------------------------------- xsum ---
-// Per (token, 64-group): the group sum of x (the bias term of the grid) and a
-// copy of the 64 values with every 8-chunk in the order (0,4,1,5,2,6,3,7), the
-// order in which nib_to_bf16 emits the codes of a dword. The grouped GEMM
-// streams that copy into LDS unchanged.
-__global__ void __launch_bounds__(256) xsum_kernel(const uint16_t* __restrict__ x, int T, int H, float* xsum,
-                                                   uint16_t* xp) {
-  const int G = H / 64;
-  const int idx = blockIdx.x * 256 + threadIdx.x;  // one (token, group)
-  if (idx >= T * G) return;
-  const int t = idx / G, g = idx % G;
-  const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * H + 64 * g);
-  uint4* q = reinterpret_cast<uint4*>(xp + (size_t)t * H + 64 * g);
-  float s = 0.f;
+// 8 int4 codes of a dword -> fp16 weights s * q + c (q exact, one fused
+// rounding) in the order (0,4,1,5,2,6,3,7); s2 = (s, s), c2 = (c, c).
+__device__ __forceinline__ f16x8 nib_dequant_f16(uint32_t w, f16x2 s2, f16x2 c2) {
+  const f16x8 v = nib_to_f16(w);  // 16 + q, exact
+  const f16x2 k16 = {(_Float16)16.0f, (_Float16)16.0f};
+  f16x8 o;
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const uint4 v = p[c];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) s += bf16f(w[i] & 0xFFFFu) + bf16f(w[i] >> 16);
-    q[c] = perm8(v);
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 q = f16x2{v[2 * i], v[2 * i + 1]} - k16;
+    const f16x2 r = __builtin_elementwise_fma(q, s2, c2);
+    o[2 * i] = r[0];
+    o[2 * i + 1] = r[1];
   }
-  xsum[idx] = s;
+  return o;
+}
+
+// ------------------------------------------------------------------ xprep ---
+// One wave per token: the scale 2^e (e >= 0 the least with max |x| / 2^e <
+// 2^15, so e = 0 unless |x| >= 65504) and x / 2^e in fp16 (exact for bf16
+// values in fp16's normal range) with every 8-chunk in the order
+// (0,4,1,5,2,6,3,7), the order in which nib_to_f16 emits the codes of a
+// dword. The grouped GEMM streams that copy into LDS unchanged. NC = 16-byte
+// chunks per lane (H / 512, at least 1).
+template <int NC>
+__global__ void __launch_bounds__(256) xprep_kernel(const uint16_t* __restrict__ x, int T, int H, float* xscale,
+                                                    uint16_t* xp) {
+  const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (t >= T) return;  // whole waves
+  const int nch = H / 8;
+  const uint4* p = reinterpret_cast<const uint4*>(x + (size_t)t * H);
+  uint4 v[NC];
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = lane + 64 * c;
+    v[c] = p[min(ch, nch - 1)];
+    const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fmaxf(fabsf(bf16f(w[i] & 0xFFFFu)), fabsf(bf16f(w[i] >> 16))));
+  }
+  amax = __uint_as_float(dpp::wave_max_u32(__float_as_uint(amax)));  // non-negative floats order as integers
+  int ex = 0;
+  if (amax >= 65504.f) {
+    int x2;
+    (void)frexpf(amax, &x2);  // amax < 2^x2
+    ex = x2 - 15;
+  }
+  if (lane == 0) xscale[t] = ldexpf(1.f, ex);
+  uint4* q = reinterpret_cast<uint4*>(xp + (size_t)t * H);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int ch = lane + 64 * c;
+    if (ch < nch) {
+      const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(bf16f(w[i] & 0xFFFFu), -ex));
+        const uint32_t hi = __builtin_bit_cast(uint16_t, (_Float16)ldexpf(bf16f(w[i] >> 16), -ex));
+        o[i] = lo | (hi << 16);
+      }
+      q[ch] = perm8(make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  }
 }
 
 // ------------------------------------------------------- router (MFMA) ---
@@ -310,13 +353,15 @@ __global__ void __launch_bounds__(CHUNK) bucket_scatter_kernel(const int32_t* __
 // DMAs in the same order, so fixed "all but the newest n" waits plus one
 // barrier per group make a group's stages visible to every wave.
 //
-// Per group: P = A . (16 + q) on the matrix cores (exact integer operands,
-// fp32 accumulate) and acc += s * P. The affine term sum_g (c - 16 s) * sum_k x
-// runs as fp32 MFMAs (K = 2 per step) once per quad.
+// Per group: the lane's 32 codes become fp16 weights s * q + c (packed fp16
+// FMA, one rounding) and acc += A . w on the matrix cores, A = x / 2^e_t in
+// fp16; the token scale 2^e_t multiplies the rows in the epilogue. The
+// conversion of a group does not depend on any MFMA result, so it overlaps
+// the previous group's MFMAs.
 struct GemmArgs {
   const uint16_t* x;          // [T][H]
-  const uint16_t* xp;         // [T][H], 8-chunks in nib_to_bf16 order
-  const float* xsum;          // [T][H/64]
+  const uint16_t* xp;         // [T][H] fp16 x / xscale, 8-chunks in nib_to_f16 order
+  const float* xscale;        // [T]
   const uint8_t* experts;     // routed records of the layer
   const uint8_t* shared;      // shared record
   uint64_t stride;
@@ -342,6 +387,13 @@ __device__ __forceinline__ void dma4(const void* g, uint8_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds_wave_base, 4, 0, 0);
 }
 
+// LDS rows of 128 bytes hold their eight 16-byte chunks permuted: chunk c of
+// row r sits in slot c ^ swz(r). A 16-byte read by 16 lanes of 16
+// consecutive rows then touches 16 different 16-byte bank groups (the
+// group of slot s of row r is 8 (r & 1) + s modulo 16), so it runs
+// without bank conflicts.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
 // Logical block index. The 8 XCDs take blocks round-robin, so XCD x gets the
 // contiguous logical range [x * per, (x + 1) * per) of the n_real blocks that
 // have work (the grid is sized for the worst case; n_real is known only on the
@@ -361,9 +413,7 @@ constexpr int A_STAGE = BM * 64 * 2;          // 64 rows x 64 bf16 (8 KB)
 constexpr int BQ_STAGE = 2 * GU_BN * 128;     // 128 code rows x 4 groups (16 KB)
 constexpr int SQ_STAGE = 2 * GU_BN * 16;      // 128 rows x 4 (s, c) words (2 KB)
 
-size_t gateup_lds_bytes(int G) {
-  return (size_t)GU_NA * A_STAGE + 2 * (size_t)BQ_STAGE + 2 * (size_t)SQ_STAGE + (size_t)256 * G;
-}
+size_t gateup_lds_bytes() { return (size_t)GU_NA * A_STAGE + 2 * (size_t)BQ_STAGE + 2 * (size_t)SQ_STAGE; }
 
 // Per-lane DMA sources (group / quad 0).
 struct GateUpSources {
@@ -375,13 +425,10 @@ struct GateUpSources {
 
 // Operands of one K group for one lane, read one group ahead of their use.
 struct GroupFrag {
-  bf16x8 a0[4], a1[4];  // A rows mrow and 32 + mrow for the 4 MFMA steps
+  f16x8 a0[4], a1[4];   // A rows mrow and 32 + mrow for the 4 MFMA steps
   uint4 codes;          // 32 codes of column brow (k half hh)
-  uint32_t sc;          // (s, c) of column brow
-};
-// Affine-term operands of one quad, read with its last group.
-struct AffineFrag {
-  float cp[2], x0[2], x1[2];
+  uint32_t sc;          // (s, c) of column brow: fp16 bits, s low
+  f16x8 b[4];           // the codes as fp16 weights, for the 4 MFMA steps
 };
 
 // Step for group g = 4Q + J: issue (for J == 0) the next quad's code rows and
@@ -393,9 +440,8 @@ template <int J>
 __device__ __forceinline__ void gateup_fetch(const uint8_t* __restrict__ rdA, const uint8_t* __restrict__ rdB,
                                              const uint8_t* __restrict__ rdS, uint8_t* __restrict__ wrA,
                                              uint8_t* __restrict__ wrB, uint8_t* __restrict__ wrS,
-                                             const float* __restrict__ sX, const GateUpSources& src, int qn, int gn,
-                                             int Q, int wv, int lane, int brow, int hh, int mrow, GroupFrag& f,
-                                             AffineFrag& af) {
+                                             const GateUpSources& src, int qn, int gn, int wv, int lane, int brow,
+                                             int hh, int mrow, GroupFrag& f) {
   if constexpr (J == 0) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) dma16(src.b[t] + 128 * qn, wrB + (4 * wv + t) * 1024);
@@ -403,57 +449,40 @@ __device__ __forceinline__ void gateup_fetch(const uint8_t* __restrict__ rdA, co
   }
   if (src.a_live[0]) dma16(src.a[0] + 64 * gn, wrA + (2 * wv) * 1024);
   if (src.a_live[1]) dma16(src.a[1] + 64 * gn, wrA + (2 * wv + 1) * 1024);
-  const int slot = (2 * J + hh) ^ (brow & 7);
+  const int slot = (2 * J + hh) ^ swz(brow);
   f.codes = *reinterpret_cast<const uint4*>(rdB + brow * 128 + slot * 16);
   f.sc = *reinterpret_cast<const uint32_t*>(rdS + brow * 16 + J * 4);
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
-    const int off = ((4 * hh + st) ^ (mrow & 7)) * 16;
-    f.a0[st] = *reinterpret_cast<const bf16x8*>(rdA + mrow * 128 + off);
-    f.a1[st] = *reinterpret_cast<const bf16x8*>(rdA + (32 + mrow) * 128 + off);
-  }
-  if constexpr (J == 3) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int j = 2 * u + hh, g = 4 * Q + j;
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(rdS + brow * 16 + j * 4);
-      af.cp[u] = f16f(w >> 16) - 16.0f * f16f(w & 0xFFFFu);
-      af.x0[u] = sX[g * 64 + mrow];
-      af.x1[u] = sX[g * 64 + 32 + mrow];
-    }
+    const int off = ((4 * hh + st) ^ swz(mrow)) * 16;  // swz(32 + mrow) == swz(mrow)
+    f.a0[st] = *reinterpret_cast<const f16x8*>(rdA + mrow * 128 + off);
+    f.a1[st] = *reinterpret_cast<const f16x8*>(rdA + (32 + mrow) * 128 + off);
   }
 }
 
-// P = A . (16 + q) for one group (exact operands, fp32 accumulate), acc += s * P.
-__device__ __forceinline__ void gateup_compute(const GroupFrag& f, f32x16& acc0, f32x16& acc1) {
-  const bf16x8 b[4] = {nib_to_bf16(f.codes.x), nib_to_bf16(f.codes.y), nib_to_bf16(f.codes.z),
-                       nib_to_bf16(f.codes.w)};
-  f32x16 p0 = {}, p1 = {};
+// The group's weights w = s * q + c in fp16.
+__device__ __forceinline__ void gateup_dequant(GroupFrag& f) {
+  const f16x2 s2 = __builtin_bit_cast(f16x2, (f.sc & 0xFFFFu) * 0x00010001u);
+  const f16x2 c2 = __builtin_bit_cast(f16x2, (f.sc >> 16) * 0x00010001u);
+  f.b[0] = nib_dequant_f16(f.codes.x, s2, c2);
+  f.b[1] = nib_dequant_f16(f.codes.y, s2, c2);
+  f.b[2] = nib_dequant_f16(f.codes.z, s2, c2);
+  f.b[3] = nib_dequant_f16(f.codes.w, s2, c2);
+}
+
+// acc += A . w for one group (weights converted beforehand).
+__device__ __forceinline__ void gateup_mfma(const GroupFrag& f, f32x16& acc0, f32x16& acc1) {
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
-    p0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a0[st], b[st], p0, 0, 0, 0);
-    p1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a1[st], b[st], p1, 0, 0, 0);
-  }
-  const float sv = f16f(f.sc & 0xFFFFu);
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    acc0[r] += sv * p0[r];
-    acc1[r] += sv * p1[r];
-  }
-}
-
-// Affine term of one quad: acc[m][n] += sum_{g in quad} xs[m][g] * (c - 16 s)[n][g].
-__device__ __forceinline__ void gateup_affine(const AffineFrag& af, f32x16& acc0, f32x16& acc1) {
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x2f32(af.x0[u], af.cp[u], acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_32x32x2f32(af.x1[u], af.cp[u], acc1, 0, 0, 0);
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a0[st], f.b[st], acc0, 0, 0, 0);
+    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a1[st], f.b[st], acc1, 0, 0, 0);
   }
 }
 
 __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int32_t s_tok[BM];
+  __shared__ float s_xs[BM];  // token scale of each row
   const int G = a.H / 64, NQ = G / 4, NT = (a.I + GU_BN - 1) / GU_BN;
   const int L = xcd_block(a.tiles[0] * NT);
   if (L < 0) return;
@@ -465,12 +494,11 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   uint8_t* sA = smem;                                       // [NA][64 rows][8 slots of 16 B]
   uint8_t* sB = sA + GU_NA * A_STAGE;                       // [2][128 rows][8 slots of 16 B] (4 groups)
   uint8_t* sS = sB + 2 * BQ_STAGE;                          // [2][128 rows][4 words]
-  float* sX = reinterpret_cast<float*>(sS + 2 * SQ_STAGE);  // [G][64 rows]
 
   GateUpSources src;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int row = 32 * wv + 8 * t + (lane >> 3), chunk = (lane & 7) ^ (row & 7);
+    const int row = 32 * wv + 8 * t + (lane >> 3), chunk = (lane & 7) ^ swz(row);
     const int n = min(n0 + (row & (GU_BN - 1)), a.I - 1);
     src.b[t] = rec + (row < GU_BN ? a.gate_codes : a.up_codes) + (size_t)n * (a.H / 2) + 16 * chunk;
   }
@@ -490,16 +518,12 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
     int tok = -1;
     if (r < rows) tok = e < a.E ? a.perm[a.e_off[e] + r] / a.k : r;
     s_tok[tid] = tok;
+    s_xs[tid] = tok >= 0 ? a.xscale[tok] : 1.f;
   }
   __syncthreads();
-  // x sums: instruction g loads group g of the 64 rows
-  {
-    const int tok = max(s_tok[lane], 0);
-    for (int g = wv; g < G; g += 4) dma4(a.xsum + (size_t)tok * G + g, reinterpret_cast<uint8_t*>(sX) + g * 256);
-  }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int row = 8 * (2 * wv + t) + (lane >> 3), chunk = (lane & 7) ^ (row & 7);
+    const int row = 8 * (2 * wv + t) + (lane >> 3), chunk = (lane & 7) ^ swz(row);
     src.a[t] = a.xp + (size_t)max(s_tok[row], 0) * a.H + 8 * chunk;
     src.a_live[t] = s_tok[row] >= 0 || lane == 0;
   }
@@ -516,7 +540,6 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   const int mrow = lane & 31;
   f32x16 acc0 = {}, acc1 = {};
   GroupFrag fa, fb;
-  AffineFrag af;
   // Step g (wait, barrier, DMAs, LDS -> registers) runs one group ahead of
   // compute g. Per step a wave issues A(g + 3) (2 DMAs), preceded at a quad's
   // first group by the next quad's codes and scales (5 DMAs). Waiting for
@@ -532,20 +555,26 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
     __builtin_amdgcn_s_barrier();                                                                                 \
     gateup_fetch<J>(sA + (g % GU_NA) * A_STAGE, sB + ((Q) & 1) * BQ_STAGE, sS + ((Q) & 1) * SQ_STAGE,            \
                     sA + ((g + GU_PF) % GU_NA) * A_STAGE, sB + (((Q) + 1) & 1) * BQ_STAGE,                        \
-                    sS + (((Q) + 1) & 1) * SQ_STAGE, sX, src, min((Q) + 1, NQ - 1), min(g + GU_PF, G - 1), (Q), \
-                    wv, lane, brow, hh, mrow, F, af);                                                             \
+                    sS + (((Q) + 1) & 1) * SQ_STAGE, src, min((Q) + 1, NQ - 1), min(g + GU_PF, G - 1), wv, lane,  \
+                    brow, hh, mrow, F);                                                                           \
   }
+  // The weights of group g + 1 are converted right after the MFMAs of group
+  // g are issued, so the conversion runs while those MFMAs execute.
   GU_STEP(0, 0, 4, fa)
+  gateup_dequant(fa);
   for (int Q = 0; Q < NQ; ++Q) {
     GU_STEP(Q, 1, 9, fb)
-    gateup_compute(fa, acc0, acc1);
+    gateup_mfma(fa, acc0, acc1);
+    gateup_dequant(fb);
     GU_STEP(Q, 2, 9, fa)
-    gateup_compute(fb, acc0, acc1);
+    gateup_mfma(fb, acc0, acc1);
+    gateup_dequant(fa);
     GU_STEP(Q, 3, 4, fb)
-    gateup_compute(fa, acc0, acc1);
+    gateup_mfma(fa, acc0, acc1);
+    gateup_dequant(fb);
     if (Q + 1 < NQ) GU_STEP(Q + 1, 0, 4, fa)
-    gateup_compute(fb, acc0, acc1);
-    gateup_affine(af, acc0, acc1);
+    gateup_mfma(fb, acc0, acc1);
+    if (Q + 1 < NQ) gateup_dequant(fa);
   }
 #undef GU_STEP
   // Epilogue. Gate and up tiles go through LDS (the rings are idle once no
@@ -562,8 +591,8 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
-      dst[m * SGS + nl] = acc0[r];
-      dst[(32 + m) * SGS + nl] = acc1[r];
+      dst[m * SGS + nl] = acc0[r] * s_xs[m];  // powers of two: exact
+      dst[(32 + m) * SGS + nl] = acc1[r] * s_xs[32 + m];
     }
   }
   __syncthreads();
@@ -686,14 +715,15 @@ __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, cons
   f16x8 ah[2][4];
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
-    const int off = ((4 * hh + st) ^ (mrow & 7)) * 16;
+    const int off = ((4 * hh + st) ^ swz(mrow)) * 16;  // swz(32 + mrow) == swz(mrow)
 #pragma unroll
     for (int mm = 0; mm < 2; ++mm) ah[mm][st] = *reinterpret_cast<const f16x8*>(rdH + (32 * mm + mrow) * 128 + off);
   }
   float cval[2];
 #pragma unroll
   for (int nn = 0; nn < 2; ++nn) {
-    const uint4 cw = *reinterpret_cast<const uint4*>(rdB + (brow + 32 * nn) * 32 + hh * 16);
+    const int crow = brow + 32 * nn;  // 32-byte rows: tile half t sits in half t ^ ((row >> 3) & 1)
+    const uint4 cw = *reinterpret_cast<const uint4*>(rdB + crow * 32 + (hh ^ ((crow >> 3) & 1)) * 16);
     const uint32_t sw = *reinterpret_cast<const uint32_t*>(rdS + (brow + 32 * nn) * 4);
     const f16x8 b[4] = {nib_to_f16(cw.x), nib_to_f16(cw.y), nib_to_f16(cw.z), nib_to_f16(cw.w)};
     f32x16 p0 = {}, p1 = {};
@@ -750,7 +780,7 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int q = (2 * wv + t) * 64 + lane, row = q >> 1;
-    src.b[t] = rec + a.down_codes + ((size_t)(q & 1) * a.H + n0 + row) * 16;
+    src.b[t] = rec + a.down_codes + ((size_t)((q & 1) ^ ((row >> 3) & 1)) * a.H + n0 + row) * 16;
   }
   src.s = rec + a.down_sc + (size_t)(n0 + 64 * wv + lane) * 4;
   src.bq = (size_t)2 * a.H * 16;
@@ -789,7 +819,7 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int row = 8 * (2 * wv + t) + (lane >> 3), chunk = (lane & 7) ^ (row & 7);
+    const int row = 8 * (2 * wv + t) + (lane >> 3), chunk = (lane & 7) ^ swz(row);
     const size_t hrow = (size_t)base + min(row, nrow - 1);
     src.h[t] = a.h16 + hrow * a.I + 8 * chunk;
     src.live[t] = row < nrow || lane == 0;
@@ -883,7 +913,7 @@ Workspace* ws_of(void* p) { return static_cast<Workspace*>(p); }
 GemmArgs gemm_args(const Workspace* w, const PrefillArgs& pa) {
   GemmArgs ga{};
   ga.x = pa.x;
-  ga.xsum = w->xsum;
+  ga.xscale = w->xscale;
   ga.xp = w->xp;
   ga.experts = pa.experts;
   ga.shared = pa.shared;
@@ -925,7 +955,7 @@ void prefill_free(void* ws) {
   if (!ws) return;
   Workspace* w = ws_of(ws);
   hipFree(w->logits);
-  hipFree(w->xsum);
+  hipFree(w->xscale);
   hipFree(w->xp);
   hipFree(w->cnt);
   hipFree(w->chunk_off);
@@ -952,7 +982,7 @@ moe_status prefill_reserve(void** wsp, const moe_config& c, int T) {
   const int nchunk = (int)((P + CHUNK - 1) / CHUNK);
   const int max_tiles = (int)((P + BM - 1) / BM) + E + (T + BM - 1) / BM;
   w->T = 0;  // invalid until every buffer is in place
-  const bool ok = grow(w->logits, (size_t)T * (E + 1)) && grow(w->xsum, (size_t)T * (H / 64)) && grow(w->xp, (size_t)T * H) &&
+  const bool ok = grow(w->logits, (size_t)T * (E + 1)) && grow(w->xscale, (size_t)T) && grow(w->xp, (size_t)T * H) &&
                   grow(w->cnt, (size_t)nchunk * E) && grow(w->chunk_off, (size_t)nchunk * E) &&
                   grow(w->e_off, (size_t)E + 2) && grow(w->perm, P) && grow(w->tiles, (size_t)1 + 2 * max_tiles) &&
                   grow(w->h16, rows * I) && grow(w->hscale, (size_t)max_tiles * (I / 64)) &&
@@ -968,10 +998,17 @@ moe_status prefill_reserve(void** wsp, const moe_config& c, int T) {
   return MOE_OK;
 }
 
-hipError_t prefill_xsum(void* ws, const PrefillArgs& pa, hipStream_t s) {
+hipError_t prefill_xprep(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
   const int T = pa.n_tok, H = pa.cfg.hidden;
-  launch(xsum_kernel, dim3((T * (H / 64) + 255) / 256), dim3(256), 0, s, pa.x, T, H, w->xsum, w->xp);
+  const dim3 grid((T + 3) / 4), block(256);
+  switch (H <= 512 ? 1 : H / 512) {
+    case 1: launch(xprep_kernel<1>, grid, block, 0, s, pa.x, T, H, w->xscale, w->xp); break;
+    case 2: launch(xprep_kernel<2>, grid, block, 0, s, pa.x, T, H, w->xscale, w->xp); break;
+    case 4: launch(xprep_kernel<4>, grid, block, 0, s, pa.x, T, H, w->xscale, w->xp); break;
+    case 8: launch(xprep_kernel<8>, grid, block, 0, s, pa.x, T, H, w->xscale, w->xp); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -1013,8 +1050,7 @@ hipError_t prefill_scatter(void* ws, const PrefillArgs& pa, hipStream_t s) {
 
 hipError_t prefill_gateup(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
-  const int G = pa.cfg.hidden / 64;
-  const size_t lds = gateup_lds_bytes(G);
+  const size_t lds = gateup_lds_bytes();
   // dynamic LDS above 64 KB has to be allowed per kernel (LDS is 160 KB per CU)
   static size_t attr_bytes = 0;
   if (attr_bytes < lds) {
