@@ -137,11 +137,14 @@ def measured_traffic(kernel: str, workload: str):
         if ":" in line and not line.startswith("#"):
             a, b = line.split(":", 1)
             kv[a.strip()] = b.strip()
-    src = os.path.join(ROOT, "routed_expert_int4_router_amd", "csrc", kv.get("source", "decode.hip"))
-    if not os.path.exists(src):
-        return None
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    if kv.get("source_sha256_16") != h:
+    # the hash covers every source the kernel is built from, in the listed order
+    h = hashlib.sha256()
+    for name in kv.get("source", "").split():
+        src = os.path.join(ROOT, "routed_expert_int4_router_amd", "csrc", name)
+        if not os.path.exists(src):
+            return None
+        h.update(open(src, "rb").read())
+    if not kv.get("source") or kv.get("source_sha256_16") != h.hexdigest()[:16]:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
