@@ -19,7 +19,7 @@ from . import moe, quant
 def expert_record(cfg: synth.Config, layer: int, e: int) -> np.ndarray:
     """Oracle-packed record bytes (padded to the stride) of routed expert e, or of the shared expert (e == E)."""
     inter = cfg.shared_inter if e == cfg.n_experts else cfg.inter
-    wg, wu, wd = synth.expert_weights(cfg.seed, layer, e, cfg.hidden, inter)
+    wg, wu, wd = synth.expert_weights(cfg.seed, layer, e, cfg.hidden, inter, cfg.expert_std)
     return quant.pack_record(quant.quantize_expert(wg, wu, wd, cfg.bits), cfg.bits)
 
 

@@ -26,7 +26,14 @@ _TOKENS = 7
 _LAYER_SLOT = 1 << 20   # "expert" field used for per-layer, non-expert tensors
 _TOKEN_SLOT = 1 << 21   # "layer" field used for token streams
 
-WEIGHT_STD = 0.02       # routed/shared expert, router and shared-gate weights
+WEIGHT_STD = 0.02       # router and shared-gate weights; expert weights by default
+# Expert weight std of the layer stacks. With no normalisation between layers
+# the residual r_{l+1} = r_l + out_l grows, and an expert's output is
+# quadratic in its input (SwiGLU), so at 0.02 the 48-layer 80B-shaped stack
+# runs away after ~32 layers (rms 2 -> inf by layer 44) and the 40-layer
+# 35B-shaped one nearly so. An expert's output scales as std^3, and 0.014
+# keeps every stack's residual within a few per cent of unit rms.
+STACK_EXPERT_STD = 0.014
 ZIPF_S = 1.1            # popularity exponent of the pooled-stack workload
 
 
@@ -47,6 +54,7 @@ class Config:
     zipf_lambda: float = 0.0
     pool_budget: Optional[int] = None   # bytes of HBM expert pool, None = all resident
     norm_topk: int = 1
+    expert_std: float = WEIGHT_STD       # std of the routed and shared expert weights
     description: str = ""
 
     def replace(self, **kw) -> "Config":
@@ -66,11 +74,11 @@ CONFIGS: Dict[str, Config] = {
         description="80B-shaped single MoE layer, batch-1 decode, 1024 sequential tokens, all experts in HBM"),
     "stack35b_int8": Config(
         "stack35b_int8", hidden=2048, n_experts=256, top_k=8, inter=512, shared_inter=512, bits=8, group=64,
-        n_layers=40, n_tokens=512, seed=0,
+        n_layers=40, n_tokens=512, seed=0, expert_std=STACK_EXPERT_STD,
         description="35B-shaped 40-layer MoE stack, int8, batch-1 decode, 512 tokens, all experts in HBM"),
     "stack35b_int4": Config(
         "stack35b_int4", hidden=2048, n_experts=256, top_k=8, inter=512, shared_inter=512, bits=4, group=64,
-        n_layers=40, n_tokens=512, seed=0,
+        n_layers=40, n_tokens=512, seed=0, expert_std=STACK_EXPERT_STD,
         description="35B-shaped 40-layer MoE stack, int4, batch-1 decode, 512 tokens, all experts in HBM"),
     "prefill80b": Config(
         "prefill80b", hidden=2048, n_experts=512, top_k=10, inter=512, shared_inter=512, bits=4, group=64,
@@ -79,10 +87,12 @@ CONFIGS: Dict[str, Config] = {
     "pool80b": Config(
         "pool80b", hidden=2048, n_experts=512, top_k=10, inter=512, shared_inter=512, bits=4, group=64,
         n_layers=48, n_tokens=1024, seed=0, bias="zipf", zipf_lambda=0.6, pool_budget=2 * GiB,
+        expert_std=STACK_EXPERT_STD,
         description="80B-shaped 48-layer stack decode, experts in pinned host memory, 2 GiB HBM pool"),
     "resident80b": Config(
         "resident80b", hidden=2048, n_experts=512, top_k=10, inter=512, shared_inter=512, bits=4, group=64,
         n_layers=48, n_tokens=1024, seed=0, bias="zipf", zipf_lambda=0.6, pool_budget=None,
+        expert_std=STACK_EXPERT_STD,
         description="80B-shaped 48-layer stack decode with every expert resident in HBM"),
 }
 
@@ -104,18 +114,19 @@ def _normal(shape, *key: int, std: float = WEIGHT_STD) -> np.ndarray:
     return a.reshape(shape)
 
 
-def expert_weights(seed: int, layer: int, expert: int, hidden: int, inter: int
+def expert_weights(seed: int, layer: int, expert: int, hidden: int, inter: int, std: float = WEIGHT_STD
                    ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
-    """fp32 gate [inter][hidden], up [inter][hidden], down [hidden][inter], each ~N(0, 0.02)."""
-    wg = _normal((inter, hidden), seed, layer, expert, _GATE)
-    wu = _normal((inter, hidden), seed, layer, expert, _UP)
-    wd = _normal((hidden, inter), seed, layer, expert, _DOWN)
+    """fp32 gate [inter][hidden], up [inter][hidden], down [hidden][inter], each ~N(0, std)."""
+    wg = _normal((inter, hidden), seed, layer, expert, _GATE, std=std)
+    wu = _normal((inter, hidden), seed, layer, expert, _UP, std=std)
+    wd = _normal((hidden, inter), seed, layer, expert, _DOWN, std=std)
     return wg, wu, wd
 
 
-def shared_expert_weights(seed: int, layer: int, n_experts: int, hidden: int, shared_inter: int):
+def shared_expert_weights(seed: int, layer: int, n_experts: int, hidden: int, shared_inter: int,
+                          std: float = WEIGHT_STD):
     """The shared expert is drawn as expert index ``n_experts`` of its layer."""
-    return expert_weights(seed, layer, n_experts, hidden, shared_inter)
+    return expert_weights(seed, layer, n_experts, hidden, shared_inter, std)
 
 
 def router_weight(seed: int, layer: int, hidden: int, n_experts: int) -> np.ndarray:
@@ -178,11 +189,11 @@ class SynthWeights:
 
     def expert(self, layer: int, e: int):
         c = self.cfg
-        return expert_weights(c.seed, layer, e, c.hidden, c.inter)
+        return expert_weights(c.seed, layer, e, c.hidden, c.inter, c.expert_std)
 
     def shared(self, layer: int):
         c = self.cfg
-        return shared_expert_weights(c.seed, layer, c.n_experts, c.hidden, c.shared_inter)
+        return shared_expert_weights(c.seed, layer, c.n_experts, c.hidden, c.shared_inter, c.expert_std)
 
     def router(self, layer: int) -> np.ndarray:
         c = self.cfg
