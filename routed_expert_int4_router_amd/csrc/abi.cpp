@@ -192,8 +192,11 @@ struct moe_pool {
   int64_t n_slots = 0;
   uint8_t* arena = nullptr;         // device [n_slots][stride]
   PoolTable table{1};
-  hipStream_t copy_stream = nullptr;
-  hipEvent_t copies_done = nullptr;
+  // Misses are spread round-robin over several copy streams (default
+  // priority) so that their host->device transfers run side by side.
+  static constexpr int kCopyStreams = 4;
+  hipStream_t copy_stream[kCopyStreams] = {};
+  hipEvent_t copies_done[kCopyStreams] = {};
   hipEvent_t route_ready = nullptr;
   int32_t* host_route = nullptr;    // pinned, mapped [k]
   int32_t* host_route_dev = nullptr;
@@ -636,24 +639,26 @@ moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, in
       HIP_TRY(hipEventSynchronize(pool->route_ready), "route sync");
       for (int j = 0; j < k; ++j) gids[(size_t)j] = (int64_t)l * E + pool->host_route[j];
       pool->table.step(gids.data(), k, slots.data(), miss.data());
-      bool any_miss = false;
       ExpertSource src{};
       src.base = pool->arena;
       src.stride = m->stride;
       src.use_table = 1;
+      // Victim slots are free to overwrite: the host waited for this layer's
+      // route, recorded after every earlier kernel on the stream.
+      int n_miss = 0;
       for (int j = 0; j < k; ++j) {
         src.table[j] = slots[(size_t)j];
         if (miss[(size_t)j]) {
-          any_miss = true;
+          const int c = n_miss++ % moe_pool::kCopyStreams;
           HIP_TRY(hipMemcpyAsync(pool->arena + (size_t)slots[(size_t)j] * m->stride,
                                  m->experts + (size_t)gids[(size_t)j] * m->stride, m->rec_bytes,
-                                 hipMemcpyHostToDevice, pool->copy_stream),
+                                 hipMemcpyHostToDevice, pool->copy_stream[c]),
                   "miss copy");
         }
       }
-      if (any_miss) {
-        HIP_TRY(hipEventRecord(pool->copies_done, pool->copy_stream), "event record");
-        HIP_TRY(hipStreamWaitEvent(s, pool->copies_done, 0), "stream wait");
+      for (int c = 0; c < moe_pool::kCopyStreams && c < n_miss; ++c) {
+        HIP_TRY(hipEventRecord(pool->copies_done[c], pool->copy_stream[c]), "event record");
+        HIP_TRY(hipStreamWaitEvent(s, pool->copies_done[c], 0), "stream wait");
       }
       st = expert_steps(m, l, b, src, r, s);
       if (st) return st;
@@ -722,8 +727,10 @@ moe_status moe_pool_create(moe_model* m, size_t budget_bytes, moe_pool** out) {
   p->n_slots = slots;
   p->table = PoolTable(slots);
   bool ok = hipMalloc(&p->arena, (size_t)slots * m->stride) == hipSuccess;
-  ok = ok && hipStreamCreateWithFlags(&p->copy_stream, hipStreamNonBlocking) == hipSuccess;
-  ok = ok && hipEventCreateWithFlags(&p->copies_done, hipEventDisableTiming) == hipSuccess;
+  for (int c = 0; c < moe_pool::kCopyStreams; ++c) {
+    ok = ok && hipStreamCreateWithFlags(&p->copy_stream[c], hipStreamNonBlocking) == hipSuccess;
+    ok = ok && hipEventCreateWithFlags(&p->copies_done[c], hipEventDisableTiming) == hipSuccess;
+  }
   ok = ok && hipEventCreateWithFlags(&p->route_ready, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipHostMalloc(&p->host_route, kMaxTopK * sizeof(int32_t), hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
   ok = ok && hipHostGetDevicePointer((void**)&p->host_route_dev, p->host_route, 0) == hipSuccess;
@@ -774,8 +781,10 @@ void moe_pool_destroy(moe_pool* p) {
   if (!p || !live_has(p) || p->magic != kPoolMagic) return;
   hipDeviceSynchronize();
   hipFree(p->arena);
-  if (p->copy_stream) hipStreamDestroy(p->copy_stream);
-  if (p->copies_done) hipEventDestroy(p->copies_done);
+  for (int c = 0; c < moe_pool::kCopyStreams; ++c) {
+    if (p->copy_stream[c]) hipStreamDestroy(p->copy_stream[c]);
+    if (p->copies_done[c]) hipEventDestroy(p->copies_done[c]);
+  }
   if (p->route_ready) hipEventDestroy(p->route_ready);
   if (p->host_route) hipHostFree(p->host_route);
   p->magic = 0;
