@@ -141,3 +141,27 @@ def test_prefill80b_full_size_sampled():
     print(f"prefill80b: routing near-ties {ties}, sampled max rel L2 {err:.3e}")
     assert err <= gh.REL_L2_TOL
     model.close()
+
+
+@pytest.mark.parametrize("shift,which", [(17, "all"), (12, "half"), (12, "one")])
+def test_prefill_large_activations_use_the_range_scales(shift, which):
+    """x scaled by 2^shift (exact in bf16): with 2^17 every token needs its
+    fp16 range scale (max |x| >= 65504) and h, quadratic in x, needs the
+    tile scales; with 2^12 on half the tokens, or on one token, the tiles mix
+    magnitudes 2^24 apart and share one scale per 64-row group."""
+    cfg = synth.get_config("tiny", n_experts=8, top_k=2, hidden=256, inter=128, shared_inter=128)
+    n_tok = 48
+    assert _takes_prefill(cfg, n_tok)
+    model = gh.build(cfg)
+    xb = synth.tokens(cfg.seed + 21, n_tok, cfg.hidden)
+    rows = {"all": slice(None), "half": slice(0, n_tok, 2), "one": slice(5, 6)}[which]
+    x = synth.bf16_bits_to_f32(xb)
+    x[rows] *= np.float32(2.0 ** shift)
+    xb = synth.f32_to_bf16_bits(x)
+    out, idx, w = _forward(model, cfg, xb)
+    assert np.all(np.isfinite(out))
+    err, ties = gh.check_layer(cfg, OracleModel(cfg), 0, xb, out, idx, list(range(n_tok)),
+                               eps_rel=gh.prefill_eps_rel(cfg.hidden))
+    print(f"shift {shift} on {which}: max rel L2 {err:.3e}, near-ties {ties}")
+    assert err <= gh.REL_L2_TOL
+    model.close()
