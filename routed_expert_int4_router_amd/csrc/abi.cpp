@@ -159,6 +159,7 @@ struct moe_model {
   size_t experts_bytes = 0;
   uint8_t* shared = nullptr;        // device [L] records
   float* wr_rows = nullptr;         // device [L][E+1][H]
+  uint16_t* wr_split = nullptr;     // device [L][3][E+1][H] bf16: wr_rows = hi + mid + lo exactly
   float* bias = nullptr;            // device [L][E]
   float* logits = nullptr;          // device [E+1]
   float* h = nullptr;               // device [(k+1)][I]
@@ -265,6 +266,23 @@ ExpertSource resident_source(moe_model* m, int layer) {
 
 const float* layer_wr(moe_model* m, int layer) {
   return m->wr_rows + (size_t)layer * (m->cfg.n_experts + 1) * m->cfg.hidden;
+}
+const uint16_t* layer_wr_split(moe_model* m, int layer) {
+  return m->wr_split + (size_t)layer * 3 * (m->cfg.n_experts + 1) * m->cfg.hidden;
+}
+
+// bf16 bits of v rounded to nearest, ties to even (finite v).
+uint16_t bf16_rne_bits(float v) {
+  uint32_t u;
+  std::memcpy(&u, &v, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+float bf16_value(uint16_t b) {
+  const uint32_t u = (uint32_t)b << 16;
+  float v;
+  std::memcpy(&v, &u, 4);
+  return v;
 }
 const float* layer_bias(moe_model* m, int layer) { return m->bias + (size_t)layer * m->cfg.n_experts; }
 const uint8_t* layer_shared(moe_model* m, int layer) { return m->shared + (size_t)layer * m->shared_stride; }
@@ -402,6 +420,7 @@ moe_status moe_model_create(const moe_config* cfg, int32_t storage, moe_model** 
   }
   ok = ok && hipMalloc(&m->shared, L * m->shared_stride) == hipSuccess;
   ok = ok && hipMalloc(&m->wr_rows, L * (E + 1) * H * sizeof(float)) == hipSuccess;
+  ok = ok && hipMalloc(&m->wr_split, L * 3 * (E + 1) * H * sizeof(uint16_t)) == hipSuccess;
   ok = ok && hipMalloc(&m->bias, L * E * sizeof(float)) == hipSuccess;
   ok = ok && hipMalloc(&m->logits, (E + 1) * sizeof(float)) == hipSuccess;
   {
@@ -416,6 +435,7 @@ moe_status moe_model_create(const moe_config* cfg, int32_t storage, moe_model** 
   if (ok) ok = hipMemset(m->bias, 0, L * E * sizeof(float)) == hipSuccess;
   if (ok) ok = hipMemset(m->shared, 0, L * m->shared_stride) == hipSuccess;
   if (ok) ok = hipMemset(m->wr_rows, 0, L * (E + 1) * H * sizeof(float)) == hipSuccess;
+  if (ok) ok = hipMemset(m->wr_split, 0, L * 3 * (E + 1) * H * sizeof(uint16_t)) == hipSuccess;
   if (ok) ok = hipDeviceSynchronize() == hipSuccess;
   if (!ok) {
     live_add(m);
@@ -446,6 +466,22 @@ moe_status moe_model_set_layer(moe_model* m, int32_t layer, const float* router_
   std::memcpy(rows.data() + E * H, shared_gate, H * sizeof(float));
   HIP_TRY(hipMemcpy((void*)layer_wr(m, layer), rows.data(), rows.size() * sizeof(float), hipMemcpyHostToDevice),
           "moe_model_set_layer: router upload");
+  // The batched router's operand: each fp32 weight as three bf16 whose sum is
+  // the weight exactly (leading 8 significand bits, then those of the two
+  // rounding residuals; both subtractions are exact in fp32).
+  std::vector<uint16_t> split(3 * rows.size());
+  for (size_t i = 0; i < rows.size(); ++i) {
+    const uint16_t hi = bf16_rne_bits(rows[i]);
+    const float r1 = rows[i] - bf16_value(hi);
+    const uint16_t mid = bf16_rne_bits(r1);
+    const uint16_t lo = bf16_rne_bits(r1 - bf16_value(mid));
+    split[i] = hi;
+    split[rows.size() + i] = mid;
+    split[2 * rows.size() + i] = lo;
+  }
+  HIP_TRY(hipMemcpy((void*)layer_wr_split(m, layer), split.data(), split.size() * sizeof(uint16_t),
+                    hipMemcpyHostToDevice),
+          "moe_model_set_layer: router split upload");
   if (router_bias) {
     HIP_TRY(hipMemcpy((void*)layer_bias(m, layer), router_bias, E * sizeof(float), hipMemcpyHostToDevice),
             "moe_model_set_layer: bias upload");
@@ -497,6 +533,7 @@ void moe_model_destroy(moe_model* m) {
   else hipFree(m->experts);
   hipFree(m->shared);
   hipFree(m->wr_rows);
+  hipFree(m->wr_split);
   hipFree(m->bias);
   hipFree(m->logits);
   hipFree(m->h);
@@ -561,7 +598,7 @@ moe_status moe_layer_forward(moe_model* m, int32_t layer, const uint16_t* x, int
     a.experts = m->experts + (size_t)layer * m->cfg.n_experts * m->stride;
     a.stride = m->stride;
     a.shared = layer_shared(m, layer);
-    a.wr_rows = layer_wr(m, layer);
+    a.wr_split = layer_wr_split(m, layer);
     a.bias = layer_bias(m, layer);
     a.x = x;
     a.n_tok = n_tok;

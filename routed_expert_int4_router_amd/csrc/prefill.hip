@@ -43,6 +43,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int BM = 64;        // tile rows (tokens or pairs)
@@ -66,12 +67,6 @@ struct Workspace {
 };
 
 __device__ __forceinline__ float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
-
-__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
 
 __device__ __forceinline__ float f16f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
 
@@ -175,20 +170,24 @@ __global__ void __launch_bounds__(256) xprep_kernel(const uint16_t* __restrict__
 }
 
 // ------------------------------------------------------- router (MFMA) ---
-// fp32 value -> three bf16 whose exact sum is the value: the leading 8
-// significand bits, then those of the two rounding residuals (3 x 8 >= 24).
-__device__ __forceinline__ void split3(float v, uint16_t& a, uint16_t& b, uint16_t& c) {
-  a = to_bf16_rne(v);
-  const float r1 = v - bf16f(a);
-  b = to_bf16_rne(r1);
-  c = to_bf16_rne(r1 - bf16f(b));
+// Block barrier that waits for this wave's LDS accesses only (lgkmcnt(0);
+// vmcnt and expcnt at their maximum), so global loads stay in flight across
+// it; the compiler may not move memory accesses across it either.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // logits[t][e] = sum_h x[t][h] * w[e][h] (+ bias[e] for e < E), rows e <= E of
-// the fp32 router matrix (row E = shared gate). Each bf16 x fp32 product is
-// taken exactly as three bf16 x bf16 MFMA products; accumulation is fp32.
-// Block: 64 tokens x 64 rows, 4 waves of 32 x 32 (32x32x16 MFMA).
-__global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* __restrict__ x, const float* __restrict__ w,
+// the fp32 router matrix (row E = shared gate). Each fp32 weight enters as
+// the three bf16 of its exact split (hi + mid + lo, prepared once per layer
+// when the layer is set), so every bf16 x fp32 product is taken exactly as
+// three bf16 x bf16 MFMA products; accumulation is fp32. Block: 64 tokens x
+// 64 rows, 4 waves of 32 x 32 (32x32x16 MFMA); the operands of K step k + 1
+// are loaded into registers while step k runs on the matrix cores.
+__global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* __restrict__ x,
+                                                          const uint16_t* __restrict__ ws,
                                                           const float* __restrict__ bias, int T, int H, int E,
                                                           float* logits) {
   __shared__ __align__(16) uint16_t sa[64][72];
@@ -200,30 +199,33 @@ __global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* __rest
   f32x16 acc = {};
   const int lr = threadIdx.x >> 2, lq = threadIdx.x & 3;  // staging: row, 16-element quarter
   const int ta = min(t0 + lr, T - 1), eb = min(e0 + lr, R - 1);
-  const uint4* ga = reinterpret_cast<const uint4*>(x + (size_t)ta * H + 16 * lq);
-  const float4* gb = reinterpret_cast<const float4*>(w + (size_t)eb * H + 16 * lq);
+  const u32x4* ga = reinterpret_cast<const u32x4*>(x + (size_t)ta * H + 16 * lq);
+  const u32x4* gb0 = reinterpret_cast<const u32x4*>(ws + ((size_t)0 * R + eb) * H + 16 * lq);
+  const u32x4* gb1 = reinterpret_cast<const u32x4*>(ws + ((size_t)1 * R + eb) * H + 16 * lq);
+  const u32x4* gb2 = reinterpret_cast<const u32x4*>(ws + ((size_t)2 * R + eb) * H + 16 * lq);
+  u32x4 a0 = ga[0], a1 = ga[1];
+  u32x4 b00 = gb0[0], b01 = gb0[1], b10 = gb1[0], b11 = gb1[1], b20 = gb2[0], b21 = gb2[1];
   for (int k0 = 0; k0 < H; k0 += 64) {
-    const uint4 a0 = ga[k0 / 8], a1 = ga[k0 / 8 + 1];
-    float4 b[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) b[q] = gb[k0 / 4 + q];
-    __syncthreads();
-    *reinterpret_cast<uint4*>(&sa[lr][16 * lq]) = a0;
-    *reinterpret_cast<uint4*>(&sa[lr][16 * lq + 8]) = a1;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float v[4] = {b[q].x, b[q].y, b[q].z, b[q].w};
-      uint16_t hi[4], mid[4], lo[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) split3(v[i], hi[i], mid[i], lo[i]);
-      *reinterpret_cast<uint2*>(&sb[0][lr][16 * lq + 4 * q]) =
-          make_uint2(hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16));
-      *reinterpret_cast<uint2*>(&sb[1][lr][16 * lq + 4 * q]) =
-          make_uint2(mid[0] | ((uint32_t)mid[1] << 16), mid[2] | ((uint32_t)mid[3] << 16));
-      *reinterpret_cast<uint2*>(&sb[2][lr][16 * lq + 4 * q]) =
-          make_uint2(lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16));
-    }
-    __syncthreads();
+    lds_barrier();  // every wave is done reading the previous step from LDS
+    *reinterpret_cast<u32x4*>(&sa[lr][16 * lq]) = a0;
+    *reinterpret_cast<u32x4*>(&sa[lr][16 * lq + 8]) = a1;
+    *reinterpret_cast<u32x4*>(&sb[0][lr][16 * lq]) = b00;
+    *reinterpret_cast<u32x4*>(&sb[0][lr][16 * lq + 8]) = b01;
+    *reinterpret_cast<u32x4*>(&sb[1][lr][16 * lq]) = b10;
+    *reinterpret_cast<u32x4*>(&sb[1][lr][16 * lq + 8]) = b11;
+    *reinterpret_cast<u32x4*>(&sb[2][lr][16 * lq]) = b20;
+    *reinterpret_cast<u32x4*>(&sb[2][lr][16 * lq + 8]) = b21;
+    // next step's operands (the last step reloads itself: every load issues)
+    const int kn = min(k0 + 64, H - 64) / 8;
+    a0 = ga[kn];
+    a1 = ga[kn + 1];
+    b00 = gb0[kn];
+    b01 = gb0[kn + 1];
+    b10 = gb1[kn];
+    b11 = gb1[kn + 1];
+    b20 = gb2[kn];
+    b21 = gb2[kn + 1];
+    lds_barrier();  // the step is in LDS; the next step's loads are in flight
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int kk = 16 * s + 8 * (lane >> 5);
@@ -1015,7 +1017,7 @@ hipError_t prefill_xprep(void* ws, const PrefillArgs& pa, hipStream_t s) {
 hipError_t prefill_router(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
   const int T = pa.n_tok, H = pa.cfg.hidden, E = pa.cfg.n_experts;
-  launch(router_gemm_kernel, dim3((T + 63) / 64, (E + 1 + 63) / 64), dim3(256), 0, s, pa.x, pa.wr_rows, pa.bias, T, H,
+  launch(router_gemm_kernel, dim3((T + 63) / 64, (E + 1 + 63) / 64), dim3(256), 0, s, pa.x, pa.wr_split, pa.bias, T, H,
          E, w->logits);
   return hipGetLastError();
 }
