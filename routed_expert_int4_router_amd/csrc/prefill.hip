@@ -81,37 +81,44 @@ __device__ __forceinline__ uint4 perm8(uint4 v) {
   return o;
 }
 
-// 8 int4 codes of a dword -> bf16 values 16 + q in the order (0,4,1,5,2,6,3,7).
-__device__ __forceinline__ bf16x8 nib_to_bf16(uint32_t w) {
-  const uint32_t m = 0x00780078u, mag = 0x41804180u;
-  uint32_t d[4];
-  d[0] = ((w << 3) & m) | mag;
-  d[1] = ((w >> 1) & m) | mag;
-  d[2] = ((w >> 5) & m) | mag;
-  d[3] = ((w >> 9) & m) | mag;
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<uint4*>(d));
+// Nibble-to-fp16 constants, kept opaque to the compiler (an empty asm
+// "changes" them) so that (x & mask) | (magic & ~mask) stays one v_bfi_b32
+// instead of being folded into an and plus an or. Set once per kernel.
+struct NibConst {
+  uint32_t mask16, magic16;      // 16 + q: nibble at bits 6..9 of each half, fp16 16.0 = 0x4C00
+  uint32_t mask1024, magic1024;  // 1024 + q: nibble at bits 0..3 of each half, fp16 1024.0 = 0x6400
+};
+__device__ __forceinline__ NibConst nib_const() {
+  NibConst k{0x03C003C0u, 0x4C004C00u, 0x000F000Fu, 0x64006400u};
+  asm volatile("" : "+s"(k.mask16), "+v"(k.magic16), "+s"(k.mask1024), "+v"(k.magic1024));
+  return k;
 }
+__device__ __forceinline__ uint32_t bfi(uint32_t mask, uint32_t x, uint32_t y) { return (x & mask) | (y & ~mask); }
 
-// 8 int4 codes of a dword -> fp16 values 16 + q in the same order.
-__device__ __forceinline__ f16x8 nib_to_f16(uint32_t w) {
-  const uint32_t m = 0x03C003C0u, mag = 0x4C004C00u;
+// 8 int4 codes of a dword -> fp16 values 16 + q in the order (0,4,1,5,2,6,3,7).
+__device__ __forceinline__ f16x8 nib_to_f16(uint32_t w, const NibConst& k) {
   uint32_t d[4];
-  d[0] = ((w << 6) & m) | mag;
-  d[1] = ((w << 2) & m) | mag;
-  d[2] = ((w >> 2) & m) | mag;
-  d[3] = ((w >> 6) & m) | mag;
+  d[0] = bfi(k.mask16, w << 6, k.magic16);
+  d[1] = bfi(k.mask16, w << 2, k.magic16);
+  d[2] = bfi(k.mask16, w >> 2, k.magic16);
+  d[3] = bfi(k.mask16, w >> 6, k.magic16);
   return __builtin_bit_cast(f16x8, *reinterpret_cast<uint4*>(d));
 }
 
 // 8 int4 codes of a dword -> fp16 weights s * q + c (q exact, one fused
-// rounding) in the order (0,4,1,5,2,6,3,7); s2 = (s, s), c2 = (c, c).
-__device__ __forceinline__ f16x8 nib_dequant_f16(uint32_t w, f16x2 s2, f16x2 c2) {
-  const f16x8 v = nib_to_f16(w);  // 16 + q, exact
-  const f16x2 k16 = {(_Float16)16.0f, (_Float16)16.0f};
+// rounding) in the same order; s2 = (s, s), c2 = (c, c). The codes enter as
+// 1024 + q (no shift for the first pair), then q = v - 1024 exactly.
+__device__ __forceinline__ f16x8 nib_dequant_f16(uint32_t w, f16x2 s2, f16x2 c2, const NibConst& k) {
+  uint32_t d[4];
+  d[0] = bfi(k.mask1024, w, k.magic1024);
+  d[1] = bfi(k.mask1024, w >> 4, k.magic1024);
+  d[2] = bfi(k.mask1024, w >> 8, k.magic1024);
+  d[3] = bfi(k.mask1024, w >> 12, k.magic1024);
+  const f16x2 k1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
   f16x8 o;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const f16x2 q = f16x2{v[2 * i], v[2 * i + 1]} - k16;
+    const f16x2 q = __builtin_bit_cast(f16x2, d[i]) - k1024;
     const f16x2 r = __builtin_elementwise_fma(q, s2, c2);
     o[2 * i] = r[0];
     o[2 * i + 1] = r[1];
@@ -463,13 +470,13 @@ __device__ __forceinline__ void gateup_fetch(const uint8_t* __restrict__ rdA, co
 }
 
 // The group's weights w = s * q + c in fp16.
-__device__ __forceinline__ void gateup_dequant(GroupFrag& f) {
+__device__ __forceinline__ void gateup_dequant(GroupFrag& f, const NibConst& k) {
   const f16x2 s2 = __builtin_bit_cast(f16x2, (f.sc & 0xFFFFu) * 0x00010001u);
   const f16x2 c2 = __builtin_bit_cast(f16x2, (f.sc >> 16) * 0x00010001u);
-  f.b[0] = nib_dequant_f16(f.codes.x, s2, c2);
-  f.b[1] = nib_dequant_f16(f.codes.y, s2, c2);
-  f.b[2] = nib_dequant_f16(f.codes.z, s2, c2);
-  f.b[3] = nib_dequant_f16(f.codes.w, s2, c2);
+  f.b[0] = nib_dequant_f16(f.codes.x, s2, c2, k);
+  f.b[1] = nib_dequant_f16(f.codes.y, s2, c2, k);
+  f.b[2] = nib_dequant_f16(f.codes.z, s2, c2, k);
+  f.b[3] = nib_dequant_f16(f.codes.w, s2, c2, k);
 }
 
 // acc += A . w for one group (weights converted beforehand).
@@ -562,21 +569,22 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   }
   // The weights of group g + 1 are converted right after the MFMAs of group
   // g are issued, so the conversion runs while those MFMAs execute.
+  const NibConst nk = nib_const();
   GU_STEP(0, 0, 4, fa)
-  gateup_dequant(fa);
+  gateup_dequant(fa, nk);
   for (int Q = 0; Q < NQ; ++Q) {
     GU_STEP(Q, 1, 9, fb)
     gateup_mfma(fa, acc0, acc1);
-    gateup_dequant(fb);
+    gateup_dequant(fb, nk);
     GU_STEP(Q, 2, 9, fa)
     gateup_mfma(fb, acc0, acc1);
-    gateup_dequant(fa);
+    gateup_dequant(fa, nk);
     GU_STEP(Q, 3, 4, fb)
     gateup_mfma(fa, acc0, acc1);
-    gateup_dequant(fb);
+    gateup_dequant(fb, nk);
     if (Q + 1 < NQ) GU_STEP(Q + 1, 0, 4, fa)
     gateup_mfma(fb, acc0, acc1);
-    if (Q + 1 < NQ) gateup_dequant(fa);
+    if (Q + 1 < NQ) gateup_dequant(fa, nk);
   }
 #undef GU_STEP
   // Epilogue. Gate and up tiles go through LDS (the rings are idle once no
@@ -712,7 +720,8 @@ __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, cons
                                            const uint8_t* __restrict__ rdS, const float* __restrict__ sHs,
                                            float hscale, uint8_t* __restrict__ wrH, uint8_t* __restrict__ wrB,
                                            uint8_t* __restrict__ wrS, const DownSources& src, int gn, int g,
-                                           int wv, int brow, int hh, int mrow, float (&cprev)[2], f32x16 (&acc)[4]) {
+                                           int wv, int brow, int hh, int mrow, float (&cprev)[2], f32x16 (&acc)[4],
+                                           const NibConst& nk) {
   down_issue(wrH, wrB, wrS, src, gn, wv);
   f16x8 ah[2][4];
 #pragma unroll
@@ -727,7 +736,7 @@ __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, cons
     const int crow = brow + 32 * nn;  // 32-byte rows: tile half t sits in half t ^ ((row >> 3) & 1)
     const uint4 cw = *reinterpret_cast<const uint4*>(rdB + crow * 32 + (hh ^ ((crow >> 3) & 1)) * 16);
     const uint32_t sw = *reinterpret_cast<const uint32_t*>(rdS + (brow + 32 * nn) * 4);
-    const f16x8 b[4] = {nib_to_f16(cw.x), nib_to_f16(cw.y), nib_to_f16(cw.z), nib_to_f16(cw.w)};
+    const f16x8 b[4] = {nib_to_f16(cw.x, nk), nib_to_f16(cw.y, nk), nib_to_f16(cw.z, nk), nib_to_f16(cw.w, nk)};
     f32x16 p0 = {}, p1 = {};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
@@ -842,6 +851,7 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   // issued; step g >= 1 needs group g, issued one step (5 DMAs) earlier. The
   // barrier of step 0 also publishes s_hscale.
   static_assert(DN_PF == 2, "wait counts below are written for PF = 2");
+  const NibConst nk = nib_const();
   for (int g = 0; g < GI; ++g) {
     if (g == 0)
       __builtin_amdgcn_s_waitcnt(0x0070 | 2);
@@ -852,7 +862,7 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
     const int rd = g % DN_NS, wr = (g + DN_PF) % DN_NS;
     down_group(sH + rd * DA_STAGE, sB + rd * DB_STAGE, sS + rd * DS_STAGE, sHs, s_hscale[g], sH + wr * DA_STAGE,
                sB + wr * DB_STAGE, sS + wr * DS_STAGE, src, min(g + DN_PF, GI - 1), g, wv, brow, hh, mrow, cprev,
-               acc);
+               acc, nk);
   }
   if (GI & 1) {  // odd group count: the last group's affine term, paired with zeros
     const float x0 = hh ? 0.f : sHs[(GI - 1) * 64 + mrow], x1 = hh ? 0.f : sHs[(GI - 1) * 64 + 32 + mrow];
