@@ -187,6 +187,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-pass", action="store_true")
+    ap.add_argument("--pool-gb", type=float, default=None,
+                    help="HBM pool budget in GiB for the pooled workload (default: the workload's 2 GiB)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed steps, copy BYTES of device memory once with a plain copy "
                          "kernel (a known-size reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -205,6 +207,11 @@ def main() -> int:
         print("no GPU visible", file=sys.stderr)
         return 1
     cfg = synth.get_config(args.workload)
+    if args.pool_gb is not None:
+        if not cfg.pool_budget:
+            print(f"--pool-gb applies to a pooled workload; {cfg.name} keeps every expert resident", file=sys.stderr)
+            return 2
+        cfg = cfg.replace(pool_budget=int(args.pool_gb * (1 << 30)))
     T = cfg.n_tokens
     if args.steps is None:
         args.steps = 20 if cfg.n_layers == 1 else (2 if cfg.pool_budget else 3)
