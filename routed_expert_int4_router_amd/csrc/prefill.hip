@@ -450,7 +450,7 @@ __device__ __forceinline__ void gateup_fetch(const uint8_t* __restrict__ rdA, co
                                              const uint8_t* __restrict__ rdS, uint8_t* __restrict__ wrA,
                                              uint8_t* __restrict__ wrB, uint8_t* __restrict__ wrS,
                                              const GateUpSources& src, int qn, int gn, int wv, int lane, int brow,
-                                             int hh, int mrow, GroupFrag& f) {
+                                             int hh, int mrow, bool full, GroupFrag& f) {
   if constexpr (J == 0) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) dma16(src.b[t] + 128 * qn, wrB + (4 * wv + t) * 1024);
@@ -465,7 +465,7 @@ __device__ __forceinline__ void gateup_fetch(const uint8_t* __restrict__ rdA, co
   for (int st = 0; st < 4; ++st) {
     const int off = ((4 * hh + st) ^ swz(mrow)) * 16;  // swz(32 + mrow) == swz(mrow)
     f.a0[st] = *reinterpret_cast<const f16x8*>(rdA + mrow * 128 + off);
-    f.a1[st] = *reinterpret_cast<const f16x8*>(rdA + (32 + mrow) * 128 + off);
+    if (full) f.a1[st] = *reinterpret_cast<const f16x8*>(rdA + (32 + mrow) * 128 + off);
   }
 }
 
@@ -479,12 +479,14 @@ __device__ __forceinline__ void gateup_dequant(GroupFrag& f, const NibConst& k) 
   f.b[3] = nib_dequant_f16(f.codes.w, s2, c2, k);
 }
 
-// acc += A . w for one group (weights converted beforehand).
-__device__ __forceinline__ void gateup_mfma(const GroupFrag& f, f32x16& acc0, f32x16& acc1) {
+// acc += A . w for one group (weights converted beforehand); rows 32..63
+// only when the tile has them (full, uniform over the block).
+__device__ __forceinline__ void gateup_mfma(const GroupFrag& f, f32x16& acc0, f32x16& acc1, bool full) {
 #pragma unroll
-  for (int st = 0; st < 4; ++st) {
-    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a0[st], f.b[st], acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a1[st], f.b[st], acc1, 0, 0, 0);
+  for (int st = 0; st < 4; ++st) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a0[st], f.b[st], acc0, 0, 0, 0);
+  if (full) {
+#pragma unroll
+    for (int st = 0; st < 4; ++st) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a1[st], f.b[st], acc1, 0, 0, 0);
   }
 }
 
@@ -522,6 +524,10 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   if (lane < 32) dma16(src.s, sS + wv * 512);
 
   const int rows = a.e_off[e + 1] - a.e_off[e];
+  const int nrow = min(rows - r0, BM);  // rows of this tile (>= 1)
+  // A tile of at most 32 rows leaves the second 32-row MFMA tile of every
+  // wave out (its accumulator stays zero and is never stored).
+  const bool full = __builtin_amdgcn_readfirstlane(nrow) > 32;
   if (tid < BM) {
     const int r = r0 + tid;
     int tok = -1;
@@ -565,7 +571,7 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
     gateup_fetch<J>(sA + (g % GU_NA) * A_STAGE, sB + ((Q) & 1) * BQ_STAGE, sS + ((Q) & 1) * SQ_STAGE,            \
                     sA + ((g + GU_PF) % GU_NA) * A_STAGE, sB + (((Q) + 1) & 1) * BQ_STAGE,                        \
                     sS + (((Q) + 1) & 1) * SQ_STAGE, src, min((Q) + 1, NQ - 1), min(g + GU_PF, G - 1), wv, lane,  \
-                    brow, hh, mrow, F);                                                                           \
+                    brow, hh, mrow, full, F);                                                                     \
   }
   // The weights of group g + 1 are converted right after the MFMAs of group
   // g are issued, so the conversion runs while those MFMAs execute.
@@ -574,16 +580,16 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   gateup_dequant(fa, nk);
   for (int Q = 0; Q < NQ; ++Q) {
     GU_STEP(Q, 1, 9, fb)
-    gateup_mfma(fa, acc0, acc1);
+    gateup_mfma(fa, acc0, acc1, full);
     gateup_dequant(fb, nk);
     GU_STEP(Q, 2, 9, fa)
-    gateup_mfma(fb, acc0, acc1);
+    gateup_mfma(fb, acc0, acc1, full);
     gateup_dequant(fa, nk);
     GU_STEP(Q, 3, 4, fb)
-    gateup_mfma(fa, acc0, acc1);
+    gateup_mfma(fa, acc0, acc1, full);
     gateup_dequant(fb, nk);
     if (Q + 1 < NQ) GU_STEP(Q + 1, 0, 4, fa)
-    gateup_mfma(fb, acc0, acc1);
+    gateup_mfma(fb, acc0, acc1, full);
     if (Q + 1 < NQ) gateup_dequant(fa, nk);
   }
 #undef GU_STEP
@@ -607,7 +613,6 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   }
   __syncthreads();
   const int base = a.e_off[e] + r0;
-  const int nrow = min(rows - r0, BM);
   const int c = tid & 63;           // column of the group handled by this thread
   const bool c_live = n0 + c < a.I;
   // h = silu(gate) * up for rows tid / 64 + 4 j; hardware exp2 and reciprocal
@@ -720,15 +725,15 @@ __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, cons
                                            const uint8_t* __restrict__ rdS, const float* __restrict__ sHs,
                                            float hscale, uint8_t* __restrict__ wrH, uint8_t* __restrict__ wrB,
                                            uint8_t* __restrict__ wrS, const DownSources& src, int gn, int g,
-                                           int wv, int brow, int hh, int mrow, float (&cprev)[2], f32x16 (&acc)[4],
-                                           const NibConst& nk) {
+                                           int wv, int brow, int hh, int mrow, bool full, float (&cprev)[2],
+                                           f32x16 (&acc)[4], const NibConst& nk) {
   down_issue(wrH, wrB, wrS, src, gn, wv);
   f16x8 ah[2][4];
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     const int off = ((4 * hh + st) ^ swz(mrow)) * 16;  // swz(32 + mrow) == swz(mrow)
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm) ah[mm][st] = *reinterpret_cast<const f16x8*>(rdH + (32 * mm + mrow) * 128 + off);
+    ah[0][st] = *reinterpret_cast<const f16x8*>(rdH + mrow * 128 + off);
+    if (full) ah[1][st] = *reinterpret_cast<const f16x8*>(rdH + (32 + mrow) * 128 + off);
   }
   float cval[2];
 #pragma unroll
@@ -739,16 +744,18 @@ __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, cons
     const f16x8 b[4] = {nib_to_f16(cw.x, nk), nib_to_f16(cw.y, nk), nib_to_f16(cw.z, nk), nib_to_f16(cw.w, nk)};
     f32x16 p0 = {}, p1 = {};
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-      p0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][st], b[st], p0, 0, 0, 0);
-      p1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][st], b[st], p1, 0, 0, 0);
+    for (int st = 0; st < 4; ++st) p0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][st], b[st], p0, 0, 0, 0);
+    if (full) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) p1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][st], b[st], p1, 0, 0, 0);
     }
     const float sv = f16f(sw & 0xFFFFu);
     const float svh = sv * hscale;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      acc[2 * nn][r] += svh * p0[r];
-      acc[2 * nn + 1][r] += svh * p1[r];
+    for (int r = 0; r < 16; ++r) acc[2 * nn][r] += svh * p0[r];
+    if (full) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[2 * nn + 1][r] += svh * p1[r];
     }
     cval[nn] = f16f(sw >> 16) - 16.0f * sv;
   }
@@ -759,7 +766,7 @@ __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, cons
     for (int nn = 0; nn < 2; ++nn) {
       const float cp = hh ? cval[nn] : cprev[nn];
       acc[2 * nn] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, cp, acc[2 * nn], 0, 0, 0);
-      acc[2 * nn + 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, cp, acc[2 * nn + 1], 0, 0, 0);
+      if (full) acc[2 * nn + 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, cp, acc[2 * nn + 1], 0, 0, 0);
     }
   } else {
     cprev[0] = cval[0];
@@ -823,6 +830,9 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
     if (tid < GI) s_hscale[tid] = a.hscale[(size_t)tile * GI + tid];
   }
   const int nrow = min(rows - r0, BM);  // rows of this tile (>= 1)
+  // A tile of at most 32 rows leaves the second 32-row MFMA tile of every
+  // wave out (its accumulators stay zero and are never stored).
+  const bool full = __builtin_amdgcn_readfirstlane(nrow) > 32;
   // h group sums: instruction g loads group g of the 64 rows
   {
     const size_t hrow = (size_t)base + min(lane, nrow - 1);
@@ -861,8 +871,8 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
     __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no LDS read moves above the barrier
     const int rd = g % DN_NS, wr = (g + DN_PF) % DN_NS;
     down_group(sH + rd * DA_STAGE, sB + rd * DB_STAGE, sS + rd * DS_STAGE, sHs, s_hscale[g], sH + wr * DA_STAGE,
-               sB + wr * DB_STAGE, sS + wr * DS_STAGE, src, min(g + DN_PF, GI - 1), g, wv, brow, hh, mrow, cprev,
-               acc, nk);
+               sB + wr * DB_STAGE, sS + wr * DS_STAGE, src, min(g + DN_PF, GI - 1), g, wv, brow, hh, mrow, full,
+               cprev, acc, nk);
   }
   if (GI & 1) {  // odd group count: the last group's affine term, paired with zeros
     const float x0 = hh ? 0.f : sHs[(GI - 1) * 64 + mrow], x1 = hh ? 0.f : sHs[(GI - 1) * 64 + 32 + mrow];
