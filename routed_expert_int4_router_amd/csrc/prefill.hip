@@ -445,12 +445,12 @@ struct GroupFrag {
 // restrict qualifiers tell the compiler that the stages read are not the
 // ones written, so it adds no wait of its own between DMAs and LDS reads;
 // the caller's vmcnt wait + barrier orders them.
-template <int J>
+template <int J, bool FULL>
 __device__ __forceinline__ void gateup_fetch(const uint8_t* __restrict__ rdA, const uint8_t* __restrict__ rdB,
                                              const uint8_t* __restrict__ rdS, uint8_t* __restrict__ wrA,
                                              uint8_t* __restrict__ wrB, uint8_t* __restrict__ wrS,
                                              const GateUpSources& src, int qn, int gn, int wv, int lane, int brow,
-                                             int hh, int mrow, bool full, GroupFrag& f) {
+                                             int hh, int mrow, GroupFrag& f) {
   if constexpr (J == 0) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) dma16(src.b[t] + 128 * qn, wrB + (4 * wv + t) * 1024);
@@ -465,7 +465,7 @@ __device__ __forceinline__ void gateup_fetch(const uint8_t* __restrict__ rdA, co
   for (int st = 0; st < 4; ++st) {
     const int off = ((4 * hh + st) ^ swz(mrow)) * 16;  // swz(32 + mrow) == swz(mrow)
     f.a0[st] = *reinterpret_cast<const f16x8*>(rdA + mrow * 128 + off);
-    if (full) f.a1[st] = *reinterpret_cast<const f16x8*>(rdA + (32 + mrow) * 128 + off);
+    if constexpr (FULL) f.a1[st] = *reinterpret_cast<const f16x8*>(rdA + (32 + mrow) * 128 + off);
   }
 }
 
@@ -480,14 +480,61 @@ __device__ __forceinline__ void gateup_dequant(GroupFrag& f, const NibConst& k) 
 }
 
 // acc += A . w for one group (weights converted beforehand); rows 32..63
-// only when the tile has them (full, uniform over the block).
-__device__ __forceinline__ void gateup_mfma(const GroupFrag& f, f32x16& acc0, f32x16& acc1, bool full) {
+// only when the tile has them (FULL).
+template <bool FULL>
+__device__ __forceinline__ void gateup_mfma(const GroupFrag& f, f32x16& acc0, f32x16& acc1) {
 #pragma unroll
-  for (int st = 0; st < 4; ++st) acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a0[st], f.b[st], acc0, 0, 0, 0);
-  if (full) {
-#pragma unroll
-    for (int st = 0; st < 4; ++st) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a1[st], f.b[st], acc1, 0, 0, 0);
+  for (int st = 0; st < 4; ++st) {
+    acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a0[st], f.b[st], acc0, 0, 0, 0);
+    if constexpr (FULL) acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a1[st], f.b[st], acc1, 0, 0, 0);
   }
+}
+
+// The K loop of a gate/up block, instantiated for tiles of more than 32 rows
+// (FULL) and for the rest, so neither copy branches inside the loop.
+template <bool FULL>
+__device__ __forceinline__ void gateup_loop(uint8_t* sA, uint8_t* sB, uint8_t* sS, const GateUpSources& src, int G,
+                                            int NQ, int wv, int lane, int brow, int hh, int mrow, f32x16& acc0,
+                                            f32x16& acc1) {
+  GroupFrag fa, fb;
+  // Step g (wait, barrier, DMAs, LDS -> registers) runs one group ahead of
+  // compute g. Per step a wave issues A(g + 3) (2 DMAs), preceded at a quad's
+  // first group by the next quad's codes and scales (5 DMAs). Waiting for
+  // A(g) leaves the DMAs of steps g-2 and g-1 in flight: 4 when neither
+  // starts a quad (J = 0, 3), 9 otherwise; the codes and scales of quad Q
+  // were issued before A(4Q) and so are covered at J = 0. lgkmcnt(0) makes
+  // this wave's reads of the stages about to be overwritten complete.
+  static_assert(GU_PF == 3, "wait counts below are written for PF = 3");
+#define GU_STEP(Q, J, WAIT, F)                                                                                   \
+  {                                                                                                              \
+    const int g = 4 * (Q) + (J);                                                                                 \
+    __builtin_amdgcn_s_waitcnt(0x0070 | (WAIT));                                                                 \
+    __builtin_amdgcn_s_barrier();                                                                                \
+    gateup_fetch<J, FULL>(sA + (g % GU_NA) * A_STAGE, sB + ((Q) & 1) * BQ_STAGE, sS + ((Q) & 1) * SQ_STAGE,      \
+                          sA + ((g + GU_PF) % GU_NA) * A_STAGE, sB + (((Q) + 1) & 1) * BQ_STAGE,                 \
+                          sS + (((Q) + 1) & 1) * SQ_STAGE, src, min((Q) + 1, NQ - 1), min(g + GU_PF, G - 1), wv, \
+                          lane, brow, hh, mrow, F);                                                              \
+  }
+  // The weights of group g + 1 are converted right after the MFMAs of group
+  // g are issued, so the conversion runs while those MFMAs execute.
+  const NibConst nk = nib_const();
+  GU_STEP(0, 0, 4, fa)
+  gateup_dequant(fa, nk);
+  for (int Q = 0; Q < NQ; ++Q) {
+    GU_STEP(Q, 1, 9, fb)
+    gateup_mfma<FULL>(fa, acc0, acc1);
+    gateup_dequant(fb, nk);
+    GU_STEP(Q, 2, 9, fa)
+    gateup_mfma<FULL>(fb, acc0, acc1);
+    gateup_dequant(fa, nk);
+    GU_STEP(Q, 3, 4, fb)
+    gateup_mfma<FULL>(fa, acc0, acc1);
+    gateup_dequant(fb, nk);
+    if (Q + 1 < NQ) GU_STEP(Q + 1, 0, 4, fa)
+    gateup_mfma<FULL>(fb, acc0, acc1);
+    if (Q + 1 < NQ) gateup_dequant(fa, nk);
+  }
+#undef GU_STEP
 }
 
 __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
@@ -501,7 +548,7 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   const int e = a.tiles[1 + 2 * tile], r0 = a.tiles[2 + 2 * tile];
   const int n0 = nt * GU_BN;
   const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   uint8_t* sA = smem;                                       // [NA][64 rows][8 slots of 16 B]
   uint8_t* sB = sA + GU_NA * A_STAGE;                       // [2][128 rows][8 slots of 16 B] (4 groups)
   uint8_t* sS = sB + 2 * BQ_STAGE;                          // [2][128 rows][4 words]
@@ -554,45 +601,10 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   const int hh = lane >> 5;
   const int mrow = lane & 31;
   f32x16 acc0 = {}, acc1 = {};
-  GroupFrag fa, fb;
-  // Step g (wait, barrier, DMAs, LDS -> registers) runs one group ahead of
-  // compute g. Per step a wave issues A(g + 3) (2 DMAs), preceded at a quad's
-  // first group by the next quad's codes and scales (5 DMAs). Waiting for
-  // A(g) leaves the DMAs of steps g-2 and g-1 in flight: 4 when neither
-  // starts a quad (J = 0, 3), 9 otherwise; the codes and scales of quad Q
-  // were issued before A(4Q) and so are covered at J = 0. lgkmcnt(0) makes
-  // this wave's reads of the stages about to be overwritten complete.
-  static_assert(GU_PF == 3, "wait counts below are written for PF = 3");
-#define GU_STEP(Q, J, WAIT, F)                                                                                    \
-  {                                                                                                               \
-    const int g = 4 * (Q) + (J);                                                                                  \
-    __builtin_amdgcn_s_waitcnt(0x0070 | (WAIT));                                                                  \
-    __builtin_amdgcn_s_barrier();                                                                                 \
-    gateup_fetch<J>(sA + (g % GU_NA) * A_STAGE, sB + ((Q) & 1) * BQ_STAGE, sS + ((Q) & 1) * SQ_STAGE,            \
-                    sA + ((g + GU_PF) % GU_NA) * A_STAGE, sB + (((Q) + 1) & 1) * BQ_STAGE,                        \
-                    sS + (((Q) + 1) & 1) * SQ_STAGE, src, min((Q) + 1, NQ - 1), min(g + GU_PF, G - 1), wv, lane,  \
-                    brow, hh, mrow, full, F);                                                                     \
-  }
-  // The weights of group g + 1 are converted right after the MFMAs of group
-  // g are issued, so the conversion runs while those MFMAs execute.
-  const NibConst nk = nib_const();
-  GU_STEP(0, 0, 4, fa)
-  gateup_dequant(fa, nk);
-  for (int Q = 0; Q < NQ; ++Q) {
-    GU_STEP(Q, 1, 9, fb)
-    gateup_mfma(fa, acc0, acc1, full);
-    gateup_dequant(fb, nk);
-    GU_STEP(Q, 2, 9, fa)
-    gateup_mfma(fb, acc0, acc1, full);
-    gateup_dequant(fa, nk);
-    GU_STEP(Q, 3, 4, fb)
-    gateup_mfma(fa, acc0, acc1, full);
-    gateup_dequant(fb, nk);
-    if (Q + 1 < NQ) GU_STEP(Q + 1, 0, 4, fa)
-    gateup_mfma(fb, acc0, acc1, full);
-    if (Q + 1 < NQ) gateup_dequant(fa, nk);
-  }
-#undef GU_STEP
+  if (full)
+    gateup_loop<true>(sA, sB, sS, src, G, NQ, wv, lane, brow, hh, mrow, acc0, acc1);
+  else
+    gateup_loop<false>(sA, sB, sS, src, G, NQ, wv, lane, brow, hh, mrow, acc0, acc1);
   // Epilogue. Gate and up tiles go through LDS (the rings are idle once no
   // DMA is in flight) so that all four waves share the SwiGLU arithmetic.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -785,7 +797,7 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   const int e = a.tiles[1 + 2 * tile], r0 = a.tiles[2 + 2 * tile];
   const int n0 = nt * DN_BN;
   const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
-  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   __shared__ float s_hscale[64];
   uint8_t* sH = smem;                                               // [NS][64][8 slots of 16 B]
   uint8_t* sB = sH + DN_NS * DA_STAGE;                              // [NS][256 rows][32 B]
