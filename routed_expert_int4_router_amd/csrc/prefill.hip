@@ -732,12 +732,14 @@ __device__ __forceinline__ void down_issue(uint8_t* __restrict__ wrH, uint8_t* _
 }
 
 // One group: acc += s * 2^e * A . (16 + q); for an odd group also the affine
-// term of the pair (g - 1, g) (lanes of k-half hh take group g-1+hh).
+// term of the pair (g - 1, g) (lanes of k-half hh take group g-1+hh). Rows
+// 32..63 only for a tile that has them (FULL).
+template <bool FULL>
 __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, const uint8_t* __restrict__ rdB,
                                            const uint8_t* __restrict__ rdS, const float* __restrict__ sHs,
                                            float hscale, uint8_t* __restrict__ wrH, uint8_t* __restrict__ wrB,
                                            uint8_t* __restrict__ wrS, const DownSources& src, int gn, int g,
-                                           int wv, int brow, int hh, int mrow, bool full, float (&cprev)[2],
+                                           int wv, int brow, int hh, int mrow, float (&cprev)[2],
                                            f32x16 (&acc)[4], const NibConst& nk) {
   down_issue(wrH, wrB, wrS, src, gn, wv);
   f16x8 ah[2][4];
@@ -745,7 +747,7 @@ __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, cons
   for (int st = 0; st < 4; ++st) {
     const int off = ((4 * hh + st) ^ swz(mrow)) * 16;  // swz(32 + mrow) == swz(mrow)
     ah[0][st] = *reinterpret_cast<const f16x8*>(rdH + mrow * 128 + off);
-    if (full) ah[1][st] = *reinterpret_cast<const f16x8*>(rdH + (32 + mrow) * 128 + off);
+    if constexpr (FULL) ah[1][st] = *reinterpret_cast<const f16x8*>(rdH + (32 + mrow) * 128 + off);
   }
   float cval[2];
 #pragma unroll
@@ -756,16 +758,15 @@ __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, cons
     const f16x8 b[4] = {nib_to_f16(cw.x, nk), nib_to_f16(cw.y, nk), nib_to_f16(cw.z, nk), nib_to_f16(cw.w, nk)};
     f32x16 p0 = {}, p1 = {};
 #pragma unroll
-    for (int st = 0; st < 4; ++st) p0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][st], b[st], p0, 0, 0, 0);
-    if (full) {
-#pragma unroll
-      for (int st = 0; st < 4; ++st) p1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][st], b[st], p1, 0, 0, 0);
+    for (int st = 0; st < 4; ++st) {
+      p0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][st], b[st], p0, 0, 0, 0);
+      if constexpr (FULL) p1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][st], b[st], p1, 0, 0, 0);
     }
     const float sv = f16f(sw & 0xFFFFu);
     const float svh = sv * hscale;
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[2 * nn][r] += svh * p0[r];
-    if (full) {
+    if constexpr (FULL) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[2 * nn + 1][r] += svh * p1[r];
     }
@@ -778,11 +779,35 @@ __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, cons
     for (int nn = 0; nn < 2; ++nn) {
       const float cp = hh ? cval[nn] : cprev[nn];
       acc[2 * nn] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, cp, acc[2 * nn], 0, 0, 0);
-      if (full) acc[2 * nn + 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, cp, acc[2 * nn + 1], 0, 0, 0);
+      if constexpr (FULL) acc[2 * nn + 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, cp, acc[2 * nn + 1], 0, 0, 0);
     }
   } else {
     cprev[0] = cval[0];
     cprev[1] = cval[1];
+  }
+}
+
+// The K loop of a down block, instantiated for tiles of more than 32 rows
+// (FULL) and for the rest, so neither copy branches inside the loop.
+template <bool FULL>
+__device__ __forceinline__ void down_loop(uint8_t* sH, uint8_t* sB, uint8_t* sS, const float* sHs,
+                                          const float* s_hscale, const DownSources& src, int GI, int wv, int brow, int hh, int mrow,
+                                          float (&cprev)[2], f32x16 (&acc)[4], const NibConst& nk) {
+  // Waits (PF = 2): step 0 needs A(0), after which only A(1) (2 DMAs) was
+  // issued; step g >= 1 needs group g, issued one step (5 DMAs) earlier. The
+  // barrier of step 0 also publishes s_hscale.
+  static_assert(DN_PF == 2, "wait counts below are written for PF = 2");
+  for (int g = 0; g < GI; ++g) {
+    if (g == 0)
+      __builtin_amdgcn_s_waitcnt(0x0070 | 2);
+    else
+      __builtin_amdgcn_s_waitcnt(0x0070 | 5);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no LDS read moves above the barrier
+    const int rd = g % DN_NS, wr = (g + DN_PF) % DN_NS;
+    down_group<FULL>(sH + rd * DA_STAGE, sB + rd * DB_STAGE, sS + rd * DS_STAGE, sHs, s_hscale[g],
+                     sH + wr * DA_STAGE, sB + wr * DB_STAGE, sS + wr * DS_STAGE, src, min(g + DN_PF, GI - 1), g, wv,
+                     brow, hh, mrow, cprev, acc, nk);
   }
 }
 
@@ -869,23 +894,11 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   const int mrow = lane & 31;
   f32x16 acc[4] = {};
   float cprev[2] = {0.f, 0.f};
-  // Waits (PF = 2): step 0 needs A(0), after which only A(1) (2 DMAs) was
-  // issued; step g >= 1 needs group g, issued one step (5 DMAs) earlier. The
-  // barrier of step 0 also publishes s_hscale.
-  static_assert(DN_PF == 2, "wait counts below are written for PF = 2");
   const NibConst nk = nib_const();
-  for (int g = 0; g < GI; ++g) {
-    if (g == 0)
-      __builtin_amdgcn_s_waitcnt(0x0070 | 2);
-    else
-      __builtin_amdgcn_s_waitcnt(0x0070 | 5);
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no LDS read moves above the barrier
-    const int rd = g % DN_NS, wr = (g + DN_PF) % DN_NS;
-    down_group(sH + rd * DA_STAGE, sB + rd * DB_STAGE, sS + rd * DS_STAGE, sHs, s_hscale[g], sH + wr * DA_STAGE,
-               sB + wr * DB_STAGE, sS + wr * DS_STAGE, src, min(g + DN_PF, GI - 1), g, wv, brow, hh, mrow, full,
-               cprev, acc, nk);
-  }
+  if (full)
+    down_loop<true>(sH, sB, sS, sHs, s_hscale, src, GI, wv, brow, hh, mrow, cprev, acc, nk);
+  else
+    down_loop<false>(sH, sB, sS, sHs, s_hscale, src, GI, wv, brow, hh, mrow, cprev, acc, nk);
   if (GI & 1) {  // odd group count: the last group's affine term, paired with zeros
     const float x0 = hh ? 0.f : sHs[(GI - 1) * 64 + mrow], x1 = hh ? 0.f : sHs[(GI - 1) * 64 + 32 + mrow];
 #pragma unroll
