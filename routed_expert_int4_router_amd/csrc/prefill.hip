@@ -56,9 +56,9 @@ struct Workspace {
   uint16_t* xp = nullptr;       // [T][H] fp16 bits of x / xscale, k-permuted
   int32_t* cnt = nullptr;       // [nchunk][E]
   int32_t* chunk_off = nullptr; // [nchunk][E]
-  int32_t* e_off = nullptr;     // [E+2]: start of each expert's rows; [E] = T*k (shared rows), [E+1] = T*k + T
   int32_t* perm = nullptr;      // [T*k] sorted position -> pair id
-  int32_t* tiles = nullptr;     // [1 + max_tiles * 2]: count, then (expert, row0) per tile
+  float* wperm = nullptr;       // [T*k] sorted position -> router weight of the pair
+  int32_t* tiles = nullptr;     // [4 + 4 max_tiles]: count (3 unused), then per tile (expert, row0, base, rows)
   uint16_t* h16 = nullptr;      // [T*k + T][I] fp16 bits, h / hscale
   float* hscale = nullptr;      // [max_tiles][I/64] power-of-two scale of each (tile, group)
   float* hsum = nullptr;        // [T*k + T][I/64]
@@ -263,12 +263,13 @@ __global__ void __launch_bounds__(CHUNK) bucket_count_kernel(const int32_t* __re
   for (int e = threadIdx.x; e < E; e += CHUNK) cnt[(size_t)blockIdx.x * E + e] = hist[e];
 }
 
-// One block: per-expert totals, expert offsets, per-chunk offsets and the tile
-// list (routed experts, then the shared expert over all T tokens).
+// One block: per-expert totals, per-chunk offsets and the tile list (routed
+// experts, then the shared expert over all T tokens; each tile carries its
+// expert, first row within the expert, first row in the bucketed order and
+// row count).
 __global__ void __launch_bounds__(1024) bucket_scan_kernel(const int32_t* __restrict__ cnt, int nchunk, int E, int T,
-                                                           int k, int32_t* __restrict__ chunk_off,
-                                                           int32_t* __restrict__ e_off, int32_t* __restrict__ tiles,
-                                                           int max_tiles) {
+                                                           int32_t* __restrict__ chunk_off,
+                                                           int32_t* __restrict__ tiles, int max_tiles) {
   __shared__ int32_t s_tot[1024], s_tiles[1024];
   __shared__ int32_t s_base, s_tbase;
   const int e = threadIdx.x;
@@ -303,35 +304,32 @@ __global__ void __launch_bounds__(1024) bucket_scan_kernel(const int32_t* __rest
   const int off = s_tot[wv] + (int)inc_t - tot;
   const int toff = s_tiles[wv] + (int)inc_n - ntile;
   if (e < E) {
-    e_off[e] = off;
     int run = off;
 #pragma unroll 8
     for (int c = 0; c < nchunk; ++c) {
       chunk_off[(size_t)c * E + e] = run;
       run += cnt[(size_t)c * E + e];
     }
-    for (int i = 0; i < ntile; ++i) {
-      tiles[1 + 2 * (toff + i)] = e;
-      tiles[2 + 2 * (toff + i)] = i * BM;
-    }
+    for (int i = 0; i < ntile; ++i)
+      *reinterpret_cast<int4*>(tiles + 4 + 4 * (toff + i)) =
+          make_int4(e, i * BM, off + i * BM, min(tot - i * BM, BM));
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    e_off[E] = s_base;         // == T * k
-    e_off[E + 1] = s_base + T;
     const int nsh = (T + BM - 1) / BM;
-    for (int i = 0; i < nsh; ++i) {
-      tiles[1 + 2 * (s_tbase + i)] = E;
-      tiles[2 + 2 * (s_tbase + i)] = i * BM;
-    }
+    for (int i = 0; i < nsh; ++i)
+      *reinterpret_cast<int4*>(tiles + 4 + 4 * (s_tbase + i)) =
+          make_int4(E, i * BM, s_base + i * BM, min(T - i * BM, BM));
     tiles[0] = min(s_tbase + nsh, max_tiles);
   }
 }
 
 // Stable scatter: a pair's position is its chunk's offset for its expert plus
 // the number of earlier pairs of the same expert in the chunk.
-__global__ void __launch_bounds__(CHUNK) bucket_scatter_kernel(const int32_t* __restrict__ idx, int P, int E,
-                                                               const int32_t* __restrict__ chunk_off, int32_t* perm) {
+__global__ void __launch_bounds__(CHUNK) bucket_scatter_kernel(const int32_t* __restrict__ idx,
+                                                               const float* __restrict__ route_w, int P, int E,
+                                                               const int32_t* __restrict__ chunk_off, int32_t* perm,
+                                                               float* wperm) {
   __shared__ int32_t s_e[CHUNK];
   const int p = blockIdx.x * CHUNK + threadIdx.x;
   const int e = p < P ? idx[p] : -1;
@@ -340,7 +338,9 @@ __global__ void __launch_bounds__(CHUNK) bucket_scatter_kernel(const int32_t* __
   if (p >= P) return;
   int rank = 0;
   for (int q = 0; q < (int)threadIdx.x; ++q) rank += (s_e[q] == e) ? 1 : 0;
-  perm[chunk_off[(size_t)blockIdx.x * E + e] + rank] = p;
+  const int pos = chunk_off[(size_t)blockIdx.x * E + e] + rank;
+  perm[pos] = p;
+  wperm[pos] = route_w[p];
 }
 
 // ------------------------------------------------------- grouped GEMM 1 ---
@@ -375,9 +375,9 @@ struct GemmArgs {
   const uint8_t* shared;      // shared record
   uint64_t stride;
   uint64_t gate_codes, up_codes, down_codes, gate_sc, up_sc, down_sc;
-  const int32_t* e_off;       // [E+2]
   const int32_t* perm;        // [T*k]
-  const int32_t* tiles;
+  const float* wperm;         // [T*k] router weight at each sorted position
+  const int32_t* tiles;       // count at [0], then (expert, row0, base, rows) per tile from [4]
   const float* route_w;       // [T*k]
   const float* route_gamma;   // [T]
   uint16_t* h16;
@@ -545,7 +545,9 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   const int L = xcd_block(a.tiles[0] * NT);
   if (L < 0) return;
   const int tile = L / NT, nt = L % NT;
-  const int e = a.tiles[1 + 2 * tile], r0 = a.tiles[2 + 2 * tile];
+  const int4 td = *reinterpret_cast<const int4*>(a.tiles + 4 + 4 * tile);
+  const int e = td.x, r0 = td.y, base = td.z;
+  const int nrow = td.w;  // rows of this tile (>= 1)
   const int n0 = nt * GU_BN;
   const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -570,19 +572,18 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   for (int t = 0; t < 4; ++t) dma16(src.b[t], sB + (4 * wv + t) * 1024);
   if (lane < 32) dma16(src.s, sS + wv * 512);
 
-  const int rows = a.e_off[e + 1] - a.e_off[e];
-  const int nrow = min(rows - r0, BM);  // rows of this tile (>= 1)
   // A tile of at most 32 rows leaves the second 32-row MFMA tile of every
   // wave out (its accumulator stays zero and is never stored).
   const bool full = __builtin_amdgcn_readfirstlane(nrow) > 32;
+  int tok = -1;
   if (tid < BM) {
-    const int r = r0 + tid;
-    int tok = -1;
-    if (r < rows) tok = e < a.E ? a.perm[a.e_off[e] + r] / a.k : r;
+    if (tid < nrow) tok = e < a.E ? a.perm[base + tid] / a.k : r0 + tid;
     s_tok[tid] = tok;
-    s_xs[tid] = tok >= 0 ? a.xscale[tok] : 1.f;
   }
   __syncthreads();
+  // the token scales are needed only in the epilogue: loaded beside the
+  // first A DMAs
+  const float xs = tok >= 0 ? a.xscale[tok] : 1.f;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int row = 8 * (2 * wv + t) + (lane >> 3), chunk = (lane & 7) ^ swz(row);
@@ -608,6 +609,7 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   // Epilogue. Gate and up tiles go through LDS (the rings are idle once no
   // DMA is in flight) so that all four waves share the SwiGLU arithmetic.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  if (tid < BM) s_xs[tid] = xs;
   __syncthreads();
   constexpr int SGS = GU_BN + 1;  // padded row stride (floats)
   static_assert(BM * SGS * 4 <= GU_NA * A_STAGE, "gate tile must fit the A ring");
@@ -624,7 +626,6 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
     }
   }
   __syncthreads();
-  const int base = a.e_off[e] + r0;
   const int c = tid & 63;           // column of the group handled by this thread
   const bool c_live = n0 + c < a.I;
   // h = silu(gate) * up for rows tid / 64 + 4 j; hardware exp2 and reciprocal
@@ -819,7 +820,9 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   const int L = xcd_block(a.tiles[0] * NT);
   if (L < 0) return;
   const int tile = L / NT, nt = L % NT;
-  const int e = a.tiles[1 + 2 * tile], r0 = a.tiles[2 + 2 * tile];
+  const int4 td = *reinterpret_cast<const int4*>(a.tiles + 4 + 4 * tile);
+  const int e = td.x, r0 = td.y, base = td.z;
+  const int nrow = td.w;  // rows of this tile (>= 1)
   const int n0 = nt * DN_BN;
   const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -846,27 +849,20 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
     dma16(src.b[1] + (size_t)gc * src.bq, sB + g * DB_STAGE + (2 * wv + 1) * 1024);
     dma4(src.s + (size_t)gc * src.sq, sS + g * DS_STAGE + wv * 256);
   }
-  const int rows = a.e_off[e + 1] - a.e_off[e];
-  const int base = a.e_off[e] + r0;
-  if (tid < BM) {
-    const int r = r0 + tid;
-    int dst = -1;
-    float w = 0.f;
-    if (r < rows) {
-      if (e < a.E) {
-        const int p = a.perm[a.e_off[e] + r];
-        dst = p;
-        w = a.route_w[p];
-      } else {
-        dst = a.T * a.k + r;
-        w = a.route_gamma[r];
-      }
+  // destination rows, router weights and the h scales: independent loads,
+  // in flight together with the h DMAs below
+  int dst = -1;
+  float w = 0.f, hs = 1.f;
+  if (tid < nrow) {
+    if (e < a.E) {
+      dst = a.perm[base + tid];
+      w = a.wperm[base + tid];
+    } else {
+      dst = a.T * a.k + r0 + tid;
+      w = a.route_gamma[r0 + tid];
     }
-    s_dst[tid] = dst;
-    s_w[tid] = w;
-    if (tid < GI) s_hscale[tid] = a.hscale[(size_t)tile * GI + tid];
   }
-  const int nrow = min(rows - r0, BM);  // rows of this tile (>= 1)
+  if (tid < GI) hs = a.hscale[(size_t)tile * GI + tid];
   // A tile of at most 32 rows leaves the second 32-row MFMA tile of every
   // wave out (its accumulators stay zero and are never stored).
   const bool full = __builtin_amdgcn_readfirstlane(nrow) > 32;
@@ -888,6 +884,11 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
     for (int t = 0; t < 2; ++t)
       if (src.live[t]) dma16(src.h[t] + 64 * gc, sH + g * DA_STAGE + (2 * wv + t) * 1024);
   }
+  if (tid < BM) {
+    s_dst[tid] = dst;
+    s_w[tid] = w;
+  }
+  if (tid < GI) s_hscale[tid] = hs;
   const int nl = 64 * wv + (lane & 31);  // first column of this lane (second: + 32)
   const int brow = nl;
   const int hh = lane >> 5;
@@ -971,8 +972,8 @@ GemmArgs gemm_args(const Workspace* w, const PrefillArgs& pa) {
   ga.gate_sc = pa.geo.gate_sc;
   ga.up_sc = pa.geo.up_sc;
   ga.down_sc = pa.geo.down_sc;
-  ga.e_off = w->e_off;
   ga.perm = w->perm;
+  ga.wperm = w->wperm;
   ga.tiles = w->tiles;
   ga.route_w = pa.route_w;
   ga.route_gamma = pa.route_gamma;
@@ -1006,8 +1007,8 @@ void prefill_free(void* ws) {
   hipFree(w->xp);
   hipFree(w->cnt);
   hipFree(w->chunk_off);
-  hipFree(w->e_off);
   hipFree(w->perm);
+  hipFree(w->wperm);
   hipFree(w->tiles);
   hipFree(w->h16);
   hipFree(w->hscale);
@@ -1031,7 +1032,8 @@ moe_status prefill_reserve(void** wsp, const moe_config& c, int T) {
   w->T = 0;  // invalid until every buffer is in place
   const bool ok = grow(w->logits, (size_t)T * (E + 1)) && grow(w->xscale, (size_t)T) && grow(w->xp, (size_t)T * H) &&
                   grow(w->cnt, (size_t)nchunk * E) && grow(w->chunk_off, (size_t)nchunk * E) &&
-                  grow(w->e_off, (size_t)E + 2) && grow(w->perm, P) && grow(w->tiles, (size_t)1 + 2 * max_tiles) &&
+                  grow(w->perm, P) && grow(w->wperm, P) &&
+                  grow(w->tiles, (size_t)4 + 4 * max_tiles) &&
                   grow(w->h16, rows * I) && grow(w->hscale, (size_t)max_tiles * (I / 64)) &&
                   grow(w->hsum, rows * (I / 64)) &&
                   grow(w->y, rows * H);
@@ -1084,14 +1086,15 @@ hipError_t prefill_count(void* ws, const PrefillArgs& pa, hipStream_t s) {
 hipError_t prefill_scan(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
   launch(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, w->cnt, n_chunks(pa), pa.cfg.n_experts, pa.n_tok,
-         pa.cfg.top_k, w->chunk_off, w->e_off, w->tiles, w->max_tiles);
+         w->chunk_off, w->tiles, w->max_tiles);
   return hipGetLastError();
 }
 
 hipError_t prefill_scatter(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
   const int E = pa.cfg.n_experts, P = pa.n_tok * pa.cfg.top_k;
-  launch(bucket_scatter_kernel, dim3(n_chunks(pa)), dim3(CHUNK), 0, s, pa.route_idx, P, E, w->chunk_off, w->perm);
+  launch(bucket_scatter_kernel, dim3(n_chunks(pa)), dim3(CHUNK), 0, s, pa.route_idx, pa.route_w, P, E, w->chunk_off,
+         w->perm, w->wperm);
   return hipGetLastError();
 }
 
