@@ -403,17 +403,32 @@ __device__ __forceinline__ void dma4(const void* g, uint8_t* lds_wave_base) {
 // without bank conflicts.
 __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
-// Logical block index. The 8 XCDs take blocks round-robin, so XCD x gets the
-// contiguous logical range [x * per, (x + 1) * per) of the n_real blocks that
-// have work (the grid is sized for the worst case; n_real is known only on the
-// device): the column tiles of one row tile, and neighbouring row tiles of one
-// expert, share that XCD's L2. Returns -1 for a block with nothing to do.
-__device__ __forceinline__ int xcd_block(int n_real) {
-  const int per = (n_real + 7) / 8;
+// Tile of a block. The 8 XCDs take blocks round-robin (block b runs on XCD
+// b % 8). XCD x gets an equal share of the shared expert's tiles (all full,
+// the tile list's last nsh entries) first, then a contiguous range of the
+// routed tiles, each tile as NT consecutive blocks: the column tiles of one
+// row tile, and neighbouring row tiles of one expert, share that XCD's L2,
+// and no XCD gets more than its share of the long tiles. The grid is sized
+// for the worst case (the tile count is known only on the device); a block
+// with nothing to do gets -1.
+__device__ __forceinline__ int xcd_tile(int ntile, int nsh, int NT, int& nt) {
+  const int nr = ntile - nsh;
+  const int psh = (nsh + 7) / 8, pr = (nr + 7) / 8;
   const int x = (int)(blockIdx.x % 8), i = (int)(blockIdx.x / 8);
-  const int l = x * per + i;
-  return (i < per && l < n_real) ? l : -1;
+  const int nsx = min(max(nsh - x * psh, 0), psh), nrx = min(max(nr - x * pr, 0), pr);
+  if (i < nsx * NT) {
+    nt = i % NT;
+    return nr + x * psh + i / NT;
+  }
+  const int j = i - nsx * NT;
+  if (j >= nrx * NT) return -1;
+  nt = j % NT;
+  return x * pr + j / NT;
 }
+
+// Blocks per XCD that xcd_tile may ask for: shared tiles ceil(nsh / 8), routed
+// at most ceil((max_tiles - nsh) / 8).
+int xcd_grid(int max_tiles, int nsh, int NT) { return 8 * ((nsh + 7) / 8 + (max_tiles - nsh + 7) / 8) * NT; }
 
 constexpr int GU_BN = 64;                     // I columns per block
 constexpr int GU_NA = 4;                      // A ring stages (one group each)
@@ -542,9 +557,9 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   __shared__ int32_t s_tok[BM];
   __shared__ float s_xs[BM];  // token scale of each row
   const int G = a.H / 64, NQ = G / 4, NT = (a.I + GU_BN - 1) / GU_BN;
-  const int L = xcd_block(a.tiles[0] * NT);
-  if (L < 0) return;
-  const int tile = L / NT, nt = L % NT;
+  int nt = 0;
+  const int tile = xcd_tile(a.tiles[0], (a.T + BM - 1) / BM, NT, nt);
+  if (tile < 0) return;
   const int4 td = *reinterpret_cast<const int4*>(a.tiles + 4 + 4 * tile);
   const int e = td.x, r0 = td.y, base = td.z;
   const int nrow = td.w;  // rows of this tile (>= 1)
@@ -817,9 +832,9 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   __shared__ int32_t s_dst[BM];
   __shared__ float s_w[BM];
   const int GI = a.I / 64, NT = a.H / DN_BN;
-  const int L = xcd_block(a.tiles[0] * NT);
-  if (L < 0) return;
-  const int tile = L / NT, nt = L % NT;
+  int nt = 0;
+  const int tile = xcd_tile(a.tiles[0], (a.T + BM - 1) / BM, NT, nt);
+  if (tile < 0) return;
   const int4 td = *reinterpret_cast<const int4*>(a.tiles + 4 + 4 * tile);
   const int e = td.x, r0 = td.y, base = td.z;
   const int nrow = td.w;  // rows of this tile (>= 1)
@@ -1109,8 +1124,8 @@ hipError_t prefill_gateup(void* ws, const PrefillArgs& pa, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_bytes = lds;
   }
-  const int nblk = w->max_tiles * ((pa.cfg.inter + GU_BN - 1) / GU_BN);
-  launch(gemm_gateup_kernel, dim3((unsigned)(8 * ((nblk + 7) / 8))), dim3(256), (uint32_t)lds, s, gemm_args(w, pa));
+  const int nblk = xcd_grid(w->max_tiles, (pa.n_tok + BM - 1) / BM, (pa.cfg.inter + GU_BN - 1) / GU_BN);
+  launch(gemm_gateup_kernel, dim3((unsigned)nblk), dim3(256), (uint32_t)lds, s, gemm_args(w, pa));
   return hipGetLastError();
 }
 
@@ -1124,8 +1139,8 @@ hipError_t prefill_down(void* ws, const PrefillArgs& pa, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_bytes = lds;
   }
-  const int nblk = w->max_tiles * (pa.cfg.hidden / DN_BN);
-  launch(gemm_down_kernel, dim3((unsigned)(8 * ((nblk + 7) / 8))), dim3(256), (uint32_t)lds, s, gemm_args(w, pa));
+  const int nblk = xcd_grid(w->max_tiles, (pa.n_tok + BM - 1) / BM, pa.cfg.hidden / DN_BN);
+  launch(gemm_down_kernel, dim3((unsigned)nblk), dim3(256), (uint32_t)lds, s, gemm_args(w, pa));
   return hipGetLastError();
 }
 
