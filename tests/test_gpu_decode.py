@@ -223,3 +223,64 @@ def test_pool_bit_identical_to_resident_and_trace_matches_oracle(slots):
     assert st["h2d_bytes"] == sim.misses * moe.expert_bytes(cfg)
     err, ties = gh.check_stack(cfg, OracleModel(cfg), xb, a, ip, [0, 5, 11])
     assert err <= gh.REL_L2_TOL
+
+
+def test_stack35b_int4_full_depth_sampled():
+    """The 40-layer 35B-shaped int4 stack at full depth, all 10,240 experts
+    resident, 64 tokens (a captured sequence, as in the benchmark): every
+    layer's routing of two tokens is checked against the oracle's top-k and
+    their delta r_40 - r_0 is recomputed by the oracle through all 40 layers."""
+    cfg = synth.get_config("stack35b_int4")
+    torch = gh.torch_cuda()
+    model = gh.build(cfg)
+    n = 64
+    xb = synth.tokens(cfg.seed, n, cfg.hidden)
+    x = gh.dev_bf16(xb)
+    out = gh.dev_f32((n, cfg.hidden))
+    model.stack_decode(x, out)
+    torch.cuda.synchronize()
+    idx, _ = model.debug_routing()
+    assert idx.shape == (n * cfg.n_layers, cfg.top_k)
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err, ties = gh.check_stack(cfg, OracleModel(cfg), xb, got, idx, [0, n - 1])
+    print(f"stack35b_int4 x40: max rel L2 of delta {err:.3e}, near-ties {ties}")
+    assert err <= gh.REL_L2_TOL
+    model.close()
+
+
+def test_pool80b_full_depth_trace_and_sampled_parity():
+    """The 48-layer 80B-shaped stack with its 2 GiB pool (24,576 experts in
+    pinned host memory, 1213 slots) as the benchmark runs it, for 64 tokens:
+    the pool's hit/miss/victim trace over all 30,720 lookups equals the
+    oracle simulator replayed on the GPU's routing, the counters agree, and
+    token 0's delta is recomputed by the oracle through all 48 layers."""
+    cfg = synth.get_config("pool80b")
+    torch = gh.torch_cuda()
+    model = gh.build(cfg, storage=moe.STORE_HOST)
+    pool = moe.Pool(model, cfg.pool_budget)
+    n = 64
+    xb = synth.tokens(cfg.seed, n, cfg.hidden)
+    x = gh.dev_bf16(xb)
+    out = gh.dev_f32((n, cfg.hidden))
+    model.stack_decode(x, out, pool=pool)
+    torch.cuda.synchronize()
+    idx, _ = model.debug_routing()
+    assert idx.shape == (n * cfg.n_layers, cfg.top_k)
+    slots = cfg.pool_budget // moe.expert_stride(cfg)
+    assert slots == 1213
+    sim = opool.replay(slots, moe.expert_bytes(cfg), idx, cfg.n_experts, cfg.n_layers)
+    hit, victim = pool.trace()
+    assert list(hit) == sim.trace_hit
+    assert list(victim) == sim.trace_victim
+    st = pool.stats()
+    assert st["accesses"] == n * cfg.n_layers * cfg.top_k
+    assert st["misses"] == sim.misses and st["hits"] == sim.hits
+    assert st["h2d_bytes"] == sim.misses * moe.expert_bytes(cfg)
+    got = out.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err, ties = gh.check_stack(cfg, OracleModel(cfg), xb, got, idx, [0])
+    print(f"pool80b x48: hits {sim.hits} of {st['accesses']}, max rel L2 of delta {err:.3e}, near-ties {ties}")
+    assert err <= gh.REL_L2_TOL
+    pool.close()
+    model.close()
