@@ -357,8 +357,10 @@ __global__ void __launch_bounds__(CHUNK) bucket_scatter_kernel(const int32_t* __
 // fetched) one group (8 KB) at a time, GU_PF groups ahead, into a GU_NA-stage
 // ring; the code rows and (s, c) words a quad of 4 groups at a time (one
 // 128-byte line per code row, 16 bytes of scales per row), one quad ahead,
-// into 2-stage rings. Few, full-line requests matter here: the L2 request
-// rate, not its bandwidth, limits this kernel. Every wave issues the same
+// into 2-stage rings. Few, full-line requests matter: with partial-line code
+// requests the L2 request rate, not its bandwidth, limited the kernel. A tile
+// of at most 32 rows runs a copy of the K loop without each wave's lower
+// 32-row MFMA tile. Every wave issues the same
 // DMAs in the same order, so fixed "all but the newest n" waits plus one
 // barrier per group make a group's stages visible to every wave.
 //
