@@ -325,19 +325,26 @@ __global__ void __launch_bounds__(1024) bucket_scan_kernel(const int32_t* __rest
 }
 
 // Stable scatter: a pair's position is its chunk's offset for its expert plus
-// the number of earlier pairs of the same expert in the chunk.
+// the number of earlier pairs of the same expert in the chunk, counted as
+// the same-expert lanes below it in its wave (64 uniform readlane compares)
+// plus the same-expert pairs of the earlier waves (per-wave histograms in
+// LDS, [CHUNK / 64][E]).
 __global__ void __launch_bounds__(CHUNK) bucket_scatter_kernel(const int32_t* __restrict__ idx,
                                                                const float* __restrict__ route_w, int P, int E,
                                                                const int32_t* __restrict__ chunk_off, int32_t* perm,
                                                                float* wperm) {
-  __shared__ int32_t s_e[CHUNK];
+  extern __shared__ int32_t s_hist[];
   const int p = blockIdx.x * CHUNK + threadIdx.x;
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = p < P ? idx[p] : -1;
-  s_e[threadIdx.x] = e;
+  for (int i = threadIdx.x; i < (CHUNK / 64) * E; i += CHUNK) s_hist[i] = 0;
+  int rank = 0;
+  for (int j = 0; j < 64; ++j) rank += (j < lane && __builtin_amdgcn_readlane(e, j) == e) ? 1 : 0;
+  __syncthreads();
+  if (e >= 0) atomicAdd(&s_hist[wv * E + e], 1);
   __syncthreads();
   if (p >= P) return;
-  int rank = 0;
-  for (int q = 0; q < (int)threadIdx.x; ++q) rank += (s_e[q] == e) ? 1 : 0;
+  for (int w = 0; w < wv; ++w) rank += s_hist[w * E + e];
   const int pos = chunk_off[(size_t)blockIdx.x * E + e] + rank;
   perm[pos] = p;
   wperm[pos] = route_w[p];
@@ -1110,8 +1117,8 @@ hipError_t prefill_scan(void* ws, const PrefillArgs& pa, hipStream_t s) {
 hipError_t prefill_scatter(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
   const int E = pa.cfg.n_experts, P = pa.n_tok * pa.cfg.top_k;
-  launch(bucket_scatter_kernel, dim3(n_chunks(pa)), dim3(CHUNK), 0, s, pa.route_idx, pa.route_w, P, E, w->chunk_off,
-         w->perm, w->wperm);
+  launch(bucket_scatter_kernel, dim3(n_chunks(pa)), dim3(CHUNK), (uint32_t)((CHUNK / 64) * E * sizeof(int32_t)), s,
+         pa.route_idx, pa.route_w, P, E, w->chunk_off, w->perm, w->wperm);
   return hipGetLastError();
 }
 
