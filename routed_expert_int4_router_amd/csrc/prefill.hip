@@ -190,22 +190,26 @@ __device__ __forceinline__ void lds_barrier() {
 // the fp32 router matrix (row E = shared gate). Each fp32 weight enters as
 // the three bf16 of its exact split (hi + mid + lo, prepared once per layer
 // when the layer is set), so every bf16 x fp32 product is taken exactly as
-// three bf16 x bf16 MFMA products; accumulation is fp32. Block: 64 tokens x
-// 64 rows, 4 waves of 32 x 32 (32x32x16 MFMA); the operands of K step k + 1
-// are loaded into registers while step k runs on the matrix cores.
-__global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* __restrict__ x,
+// three bf16 x bf16 MFMA products; accumulation is fp32. Block: 128 tokens x
+// 64 rows, 8 waves of 32 x 32 (32x32x16 MFMA), waves 0-3 on tokens 0-63 and
+// 4-7 on 64-127 of the same rows; all waves stage x, waves 0-3 also the
+// three planes' rows (read from L2 once per 128 tokens). The operands of K
+// step k + 1 are loaded into registers while step k runs on the matrix
+// cores. 144 blocks for T = 2048, E = 512: one per CU at most.
+__global__ void __launch_bounds__(512) router_gemm_kernel(const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ ws,
                                                           const float* __restrict__ bias, int T, int H, int E,
                                                           float* logits) {
-  __shared__ __align__(16) uint16_t sa[64][72];
+  __shared__ __align__(16) uint16_t sa[128][72];
   __shared__ __align__(16) uint16_t sb[3][64][72];
-  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int wm = (wv >> 1) * 32, wn = (wv & 1) * 32;
+  const int t0 = blockIdx.x * 128, e0 = blockIdx.y * 64;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)), lane = threadIdx.x & 63;
+  const int wm = (wv >> 2) * 64 + ((wv & 3) >> 1) * 32, wn = (wv & 1) * 32;
+  const bool wload = wv < 4;  // waves 0-3 also stage the 64 router rows
   const int R = E + 1;
   f32x16 acc = {};
   const int lr = threadIdx.x >> 2, lq = threadIdx.x & 3;  // staging: row, 16-element quarter
-  const int ta = min(t0 + lr, T - 1), eb = min(e0 + lr, R - 1);
+  const int ta = min(t0 + lr, T - 1), eb = min(e0 + (lr & 63), R - 1);
   const u32x4* ga = reinterpret_cast<const u32x4*>(x + (size_t)ta * H + 16 * lq);
   const u32x4* gb0 = reinterpret_cast<const u32x4*>(ws + ((size_t)0 * R + eb) * H + 16 * lq);
   const u32x4* gb1 = reinterpret_cast<const u32x4*>(ws + ((size_t)1 * R + eb) * H + 16 * lq);
@@ -216,22 +220,26 @@ __global__ void __launch_bounds__(256) router_gemm_kernel(const uint16_t* __rest
     lds_barrier();  // every wave is done reading the previous step from LDS
     *reinterpret_cast<u32x4*>(&sa[lr][16 * lq]) = a0;
     *reinterpret_cast<u32x4*>(&sa[lr][16 * lq + 8]) = a1;
-    *reinterpret_cast<u32x4*>(&sb[0][lr][16 * lq]) = b00;
-    *reinterpret_cast<u32x4*>(&sb[0][lr][16 * lq + 8]) = b01;
-    *reinterpret_cast<u32x4*>(&sb[1][lr][16 * lq]) = b10;
-    *reinterpret_cast<u32x4*>(&sb[1][lr][16 * lq + 8]) = b11;
-    *reinterpret_cast<u32x4*>(&sb[2][lr][16 * lq]) = b20;
-    *reinterpret_cast<u32x4*>(&sb[2][lr][16 * lq + 8]) = b21;
+    if (wload) {
+      *reinterpret_cast<u32x4*>(&sb[0][lr][16 * lq]) = b00;
+      *reinterpret_cast<u32x4*>(&sb[0][lr][16 * lq + 8]) = b01;
+      *reinterpret_cast<u32x4*>(&sb[1][lr][16 * lq]) = b10;
+      *reinterpret_cast<u32x4*>(&sb[1][lr][16 * lq + 8]) = b11;
+      *reinterpret_cast<u32x4*>(&sb[2][lr][16 * lq]) = b20;
+      *reinterpret_cast<u32x4*>(&sb[2][lr][16 * lq + 8]) = b21;
+    }
     // next step's operands (the last step reloads itself: every load issues)
     const int kn = min(k0 + 64, H - 64) / 8;
     a0 = ga[kn];
     a1 = ga[kn + 1];
-    b00 = gb0[kn];
-    b01 = gb0[kn + 1];
-    b10 = gb1[kn];
-    b11 = gb1[kn + 1];
-    b20 = gb2[kn];
-    b21 = gb2[kn + 1];
+    if (wload) {
+      b00 = gb0[kn];
+      b01 = gb0[kn + 1];
+      b10 = gb1[kn];
+      b11 = gb1[kn + 1];
+      b20 = gb2[kn];
+      b21 = gb2[kn + 1];
+    }
     lds_barrier();  // the step is in LDS; the next step's loads are in flight
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -1088,8 +1096,8 @@ hipError_t prefill_xprep(void* ws, const PrefillArgs& pa, hipStream_t s) {
 hipError_t prefill_router(void* ws, const PrefillArgs& pa, hipStream_t s) {
   Workspace* w = ws_of(ws);
   const int T = pa.n_tok, H = pa.cfg.hidden, E = pa.cfg.n_experts;
-  launch(router_gemm_kernel, dim3((T + 63) / 64, (E + 1 + 63) / 64), dim3(256), 0, s, pa.x, pa.wr_split, pa.bias, T, H,
-         E, w->logits);
+  launch(router_gemm_kernel, dim3((T + 127) / 128, (E + 1 + 63) / 64), dim3(512), 0, s, pa.x, pa.wr_split, pa.bias, T,
+         H, E, w->logits);
   return hipGetLastError();
 }
 
