@@ -172,10 +172,10 @@ void moe_model_destroy(moe_model* m); /* NULL is a no-op; waits for the device *
 /* One MoE layer on n_tok tokens: out[t] = sum_j w[t,j] * expert_{idx[t,j]}(x_t)
  * + sigmoid(x_t . g_s) * shared(x_t), every token independent.
  * x: dev bf16 bit patterns [n_tok][H]; out: dev fp32 [n_tok][H]; stream: the
- * stream to run on. Small batches use the decode GEMV kernels token by token;
- * large batches (n_tok * k >= 4 * E) of int4 layers with H % 256 == 0 bucket
- * the (token, expert) pairs and run the MFMA grouped GEMM (other layers keep
- * the GEMV path). The
+ * stream to run on. Batches of fewer than 8 tokens use the decode GEMV
+ * kernels token by token; larger batches of int4 layers with H % 256 == 0
+ * (and H, I <= 4096, E <= 1024) bucket the (token, expert) pairs and run the
+ * MFMA grouped GEMM (other layers keep the GEMV path). The
  * batched path keeps a workspace sized for the largest batch seen so far; a
  * call that has to grow it synchronises the device and allocates (about
  * n_tok * (k + 1) * (4 H + 4 I + I / 16) bytes). Needs MOE_STORE_DEVICE.

@@ -1,7 +1,7 @@
 """GPU parity of the batched (prefill) path: router GEMM, top-k, bucketing of
 (token, slot) pairs by expert, grouped MFMA GEMMs and combine, against the
 fp64 oracle through the C ABI. moe_layer_forward takes this path when
-n_tok * top_k >= 4 * n_experts and the layer is int4."""
+n_tok >= 8 and the layer is int4 with H % 256 == 0."""
 import numpy as np
 import pytest
 
@@ -25,7 +25,7 @@ def _forward(model, cfg, xb):
 
 
 def _takes_prefill(cfg, n):
-    return n * cfg.top_k >= 4 * cfg.n_experts and cfg.hidden % 256 == 0 and cfg.bits == 4
+    return n >= 8 and cfg.hidden % 256 == 0 and cfg.bits == 4
 
 
 # Shapes chosen to hit the tile edges: several 64-row tiles per expert with a
@@ -49,6 +49,31 @@ def test_prefill_small_parity(variant, n_tok):
     xb = synth.tokens(cfg.seed + 11, n_tok, cfg.hidden)
     out, idx, w = _forward(model, cfg, xb)
     assert idx.shape == (n_tok, cfg.top_k)
+    assert np.all(np.isfinite(out))
+    err, ties = gh.check_layer(cfg, OracleModel(cfg), 0, xb, out, idx, list(range(n_tok)),
+                               eps_rel=gh.prefill_eps_rel(cfg.hidden))
+    print(f"{variant} T={n_tok}: max rel L2 {err:.3e}, near-ties {ties}")
+    assert err <= gh.REL_L2_TOL
+    model.close()
+
+
+# Batches just above the batched path's threshold (8 tokens): nearly every
+# touched expert holds one or two rows of a 64-row tile; up to the full 80B
+# layer shape.
+SMALL_BATCH_CASES = [
+    (dict(), 8),
+    (dict(n_experts=64, top_k=8, hidden=2048, inter=512, shared_inter=512, bias="normal"), 9),
+    (dict(n_experts=512, top_k=10, hidden=2048, inter=512, shared_inter=512), 13),
+]
+
+
+@pytest.mark.parametrize("variant,n_tok", SMALL_BATCH_CASES)
+def test_prefill_small_batches_at_the_threshold(variant, n_tok):
+    cfg = synth.get_config("tiny", **variant)
+    assert _takes_prefill(cfg, n_tok)
+    model = gh.build(cfg)
+    xb = synth.tokens(cfg.seed + 21, n_tok, cfg.hidden)
+    out, idx, w = _forward(model, cfg, xb)
     assert np.all(np.isfinite(out))
     err, ties = gh.check_layer(cfg, OracleModel(cfg), 0, xb, out, idx, list(range(n_tok)),
                                eps_rel=gh.prefill_eps_rel(cfg.hidden))
