@@ -605,6 +605,7 @@ moe_status moe_layer_forward(moe_model* m, int32_t layer, const uint16_t* x, int
     a.experts = m->experts + (size_t)layer * m->cfg.n_experts * m->stride;
     a.stride = m->stride;
     a.shared = layer_shared(m, layer);
+    a.wr_rows = layer_wr(m, layer);
     a.wr_split = layer_wr_split(m, layer);
     a.bias = layer_bias(m, layer);
     a.x = x;

@@ -17,6 +17,7 @@ struct PrefillArgs {
   const uint8_t* experts;   // device, routed records of this layer (E records at stride)
   uint64_t stride;
   const uint8_t* shared;    // device, shared-expert record of this layer
+  const float* wr_rows;     // device fp32 [E+1][H]: the router rows (row E = shared gate)
   const uint16_t* wr_split; // device bf16 [3][E+1][H]: the router rows as hi + mid + lo (exact)
   const float* bias;        // device [E]
   const uint16_t* x;        // device bf16 [n_tok][H]
