@@ -7,6 +7,8 @@
 //               fp16 range and that fp16 copy, k-permuted for the GEMM
 //   router      logits [T][E+1] = x . W_r^T with bf16 MFMA on an exact
 //               three-way bf16 split of the fp32 router rows, fp32 accumulate
+//               (batches of at most 64 tokens: one wave per fp32 router row,
+//               fp64 accumulation)
 //   route       top-k + weights + shared gate per token (one wave each)
 //   bucket x3   stable counting sort of the T*k (token, slot) pairs by expert
 //               (per-chunk counts, scan + tile list, scatter), deterministic
