@@ -3,8 +3,8 @@
 // The pages' runtime has no batched prefill: long prompts run token by token
 // (alphalab.site field test, FAQ item 4, and the method section on prompt
 // length). Here a batch of T tokens takes the layer in nine launches:
-//   xprep       per token: a power-of-two scale 2^e that keeps x / 2^e in
-//               fp16 range and that fp16 copy, k-permuted for the GEMM
+//   xprep       per token: a power-of-two scale 2^e that brings max |x| / 2^e
+//               into [2^14, 2^15) and that fp16 copy, k-permuted for the GEMM
 //   router      logits [T][E+1] = x . W_r^T with bf16 MFMA on an exact
 //               three-way bf16 split of the fp32 router rows, fp32 accumulate
 //               (batches of at most 64 tokens: one wave per fp32 router row,
@@ -15,11 +15,12 @@
 //   gateup      grouped GEMM per (expert, 64-row tile, 64-column tile):
 //               int4 codes -> fp16 weights s * q + c (one rounding), fp16
 //               MFMA with fp32 accumulate, the token scale and SwiGLU in the
-//               epilogue, h stored in fp16 with one power-of-two scale per
-//               (tile, 64-group) that keeps it in range (+ per-group sums)
-//   down        grouped GEMM on h (fp16 MFMA, codes as fp16 16 + q), router
-//               weight in the epilogue, one fp32 row per (token, slot) and
-//               per token
+//               epilogue, h stored in fp16 under power-of-two range scales
+//               (one per (tile, 64-group), plus a factor of its own for a row
+//               far below the tile's largest) and per-group sums
+//   down        grouped GEMM on h (fp16 MFMA, codes as fp16 16 + q), the range
+//               scales and router weight applied to the fp32 partial sums,
+//               one fp32 row per (token, slot) and per token
 //   combine     out[t] = sum_j y[t,j] + y_shared[t] in fixed order
 // Pages for the method itself: top-k routing, resident router and shared
 // expert, int4/int8 group quantisation (cheshm.ai news article, paragraphs on
@@ -62,7 +63,8 @@ struct Workspace {
   float* wperm = nullptr;       // [T*k] sorted position -> router weight of the pair
   int32_t* tiles = nullptr;     // [4 + 4 max_tiles]: count (3 unused), then per tile (expert, row0, base, rows)
   uint16_t* h16 = nullptr;      // [T*k + T][I] fp16 bits, h / hscale
-  float* hscale = nullptr;      // [max_tiles][I/64] power-of-two scale of each (tile, group)
+  float* hscale = nullptr;      // [max_tiles][I/64] power-of-two scale of each (tile, group), sign = mixed
+  float* hrowf = nullptr;       // [T*k + T][I/64] power-of-two factor of each row relative to its tile-group
   float* hsum = nullptr;        // [T*k + T][I/64]
   float* y = nullptr;           // [T*k + T][H]
   int max_tiles = 0;
@@ -129,12 +131,14 @@ __device__ __forceinline__ f16x8 nib_dequant_f16(uint32_t w, f16x2 s2, f16x2 c2,
 }
 
 // ------------------------------------------------------------------ xprep ---
-// One wave per token: the scale 2^e (e >= 0 the least with max |x| / 2^e <
-// 2^15, so e = 0 unless |x| >= 65504) and x / 2^e in fp16 (exact for bf16
-// values in fp16's normal range) with every 8-chunk in the order
-// (0,4,1,5,2,6,3,7), the order in which nib_to_f16 emits the codes of a
-// dword. The grouped GEMM streams that copy into LDS unchanged. NC = 16-byte
-// chunks per lane (H / 512, at least 1).
+// One wave per token: the scale 2^e, e of either sign, that brings max |x| /
+// 2^e into [2^14, 2^15) (e = 0 for an all-zero token), and x / 2^e in fp16
+// with every 8-chunk in the order (0,4,1,5,2,6,3,7), the order in which
+// nib_to_f16 emits the codes of a dword. Both small and large activations
+// then use fp16's full precision: a bf16 value x / 2^e is exact in fp16 down
+// to 2^-14, i.e. for every element above max |x| * 2^-29. The grouped GEMM
+// streams that copy into LDS unchanged. NC = 16-byte chunks per lane (H /
+// 512, at least 1).
 template <int NC>
 __global__ void __launch_bounds__(256) xprep_kernel(const uint16_t* __restrict__ x, int T, int H, float* xscale,
                                                     uint16_t* xp) {
@@ -154,9 +158,9 @@ __global__ void __launch_bounds__(256) xprep_kernel(const uint16_t* __restrict__
   }
   amax = __uint_as_float(dpp::wave_max_u32(__float_as_uint(amax)));  // non-negative floats order as integers
   int ex = 0;
-  if (amax >= 65504.f) {
+  if (amax > 0.f) {
     int x2;
-    (void)frexpf(amax, &x2);  // amax < 2^x2
+    (void)frexpf(amax, &x2);  // 2^(x2-1) <= amax < 2^x2
     ex = x2 - 15;
   }
   if (lane == 0) xscale[t] = ldexpf(1.f, ex);
@@ -439,7 +443,10 @@ __global__ void __launch_bounds__(CHUNK) bucket_scatter_kernel(const int32_t* __
 // FMA, one rounding) and acc += A . w on the matrix cores, A = x / 2^e_t in
 // fp16; the token scale 2^e_t multiplies the rows in the epilogue. The
 // conversion of a group does not depend on any MFMA result, so it overlaps
-// the previous group's MFMAs.
+// the previous group's MFMAs. The epilogue computes h = silu(gate) * up in
+// fp32 and stores it in fp16 under power-of-two range scales chosen from the
+// tile's values, in either direction, so small and large activations keep
+// fp16's 11 significant bits.
 struct GemmArgs {
   const uint16_t* x;          // [T][H]
   const uint16_t* xp;         // [T][H] fp16 x / xscale, 8-chunks in nib_to_f16 order
@@ -454,7 +461,8 @@ struct GemmArgs {
   const float* route_w;       // [T*k]
   const float* route_gamma;   // [T]
   uint16_t* h16;
-  float* hscale;
+  float* hscale;              // [tiles][I/64] 2^T per (tile, group), negative when rows carry own factors
+  float* hrowf;               // [T*k + T][I/64] per-row factor 2^(e_row - T) (1 for most rows)
   float* hsum;
   float* y;
   int T, H, I, E, k;
@@ -702,8 +710,8 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   constexpr int SGS = GU_BN + 1;  // padded row stride (floats)
   static_assert(BM * SGS * 4 <= GU_NA * A_STAGE, "gate tile must fit the A ring");
   static_assert(BM * SGS * 4 <= 2 * BQ_STAGE, "up tile must fit the code ring");
-  float* sg = reinterpret_cast<float*>(sA);  // [64][SGS]: gate, then h, then the dequantised h
-  float* su = reinterpret_cast<float*>(sB);  // [64][SGS]: up, then the fp16 rows [64][64] for the stores
+  float* sg = reinterpret_cast<float*>(sA);  // [64][SGS]: gate, then h
+  float* su = reinterpret_cast<float*>(sB);  // [64][SGS]: up
   {
     float* dst = mat == 0 ? sg : su;
 #pragma unroll
@@ -714,68 +722,89 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
     }
   }
   __syncthreads();
-  const int c = tid & 63;           // column of the group handled by this thread
-  const bool c_live = n0 + c < a.I;
-  // h = silu(gate) * up for rows tid / 64 + 4 j; hardware exp2 and reciprocal
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int m = (tid >> 6) + 4 * j;
-    const float gt = sg[m * SGS + c];
-    const float hv = gt * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt)) * su[m * SGS + c];
-    sg[m * SGS + c] = hv;
-    if (m < nrow && c_live) amax = fmaxf(amax, fabsf(hv));
-  }
-  // The block's scale: 2^e with e >= 0 the least that brings max |h| below
-  // 2^15, so every scaled value is a finite fp16 (e = 0 unless |h| >= 65504).
-  __shared__ uint32_t s_amax[4];
   {
-    const uint32_t wm = dpp::wave_max_u32(__float_as_uint(amax));  // non-negative floats order as integers
-    if (lane == 0) s_amax[wv] = wm;
-  }
-  __syncthreads();
-  const float tmax = __uint_as_float(max(max(s_amax[0], s_amax[1]), max(s_amax[2], s_amax[3])));
-  int ex = 0;
-  if (tmax >= 65504.f) {
-    int x2;
-    (void)frexpf(tmax, &x2);  // tmax < 2^x2
-    ex = x2 - 15;
-  }
-  if (tid == 0 && n0 < a.I) a.hscale[(size_t)tile * (a.I / 64) + nt] = ldexpf(1.f, ex);
-  // h / 2^e in fp16, each 8-chunk in nib_to_f16 order (position of column c
-  // within its chunk: 0,2,4,6,1,3,5,7), staged for 16-byte row stores; sg
-  // keeps 2^e * fp16 value, what the down GEMM multiplies
-  uint16_t* sh16 = reinterpret_cast<uint16_t*>(su);
-  {
-    const int p = c & 7;
-    const int pos = (c & ~7) + (p < 4 ? 2 * p : 2 * (p - 4) + 1);
+    // h = silu(gate) * up, thread (tid / 64 + 4 j, tid % 64); hardware exp2
+    // and reciprocal
+    const int c = tid & 63;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int m = (tid >> 6) + 4 * j;
-      const _Float16 hq = (_Float16)ldexpf(sg[m * SGS + c], -ex);
-      sg[m * SGS + c] = ldexpf((float)hq, ex);
-      sh16[m * 64 + pos] = __builtin_bit_cast(uint16_t, hq);
+      const float gt = sg[m * SGS + c];
+      sg[m * SGS + c] =
+          gt * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt)) * su[m * SGS + c];
     }
   }
   __syncthreads();
-  // rows of h (128 bytes each) and per-row group sums: 4 threads per row,
-  // 16 columns each, combined ((q0 + q1) + (q2 + q3))
-  if (n0 < a.I) {
+  // fp16 range scales. Row m (4 threads, 16 columns each) has the natural
+  // exponent n_m: max |h_m| / 2^n_m in [2^14, 2^15). The tile-group scale is
+  // 2^T with T = the largest n_m over the tile's rows. A row within 2^12 of
+  // the tile's largest stores h / 2^T (its maximum stays >= 4, so only values
+  // below 2^-16 of it leave fp16's normal range); a smaller row stores
+  // h / 2^n_m and the factor 2^(n_m - T) that the down GEMM applies to its
+  // partial sums. hscale = 2^T, negated when any row of the tile-group has
+  // its own factor.
+  const int m = tid >> 2, qq = tid & 3;
+  float hv[16];
+  float rmax = 0.f;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int ch = tid + 256 * q;  // 16-byte chunk: row ch / 8, chunk ch % 8
-      const int m = ch >> 3;
-      if (m < nrow)
-        *reinterpret_cast<uint4*>(a.h16 + (size_t)(base + m) * a.I + n0 + 8 * (ch & 7)) =
-            *reinterpret_cast<const uint4*>(sh16 + m * 64 + 8 * (ch & 7));
+  for (int cc = 0; cc < 16; ++cc) {
+    hv[cc] = sg[m * SGS + 16 * qq + cc];
+    rmax = fmaxf(rmax, fabsf(hv[cc]));
+  }
+  rmax = fmaxf(rmax, __uint_as_float(dpp::mov<dpp::kQuadXor1, 0xF>(0u, __float_as_uint(rmax))));
+  rmax = fmaxf(rmax, __uint_as_float(dpp::mov<dpp::kQuadXor2, 0xF>(0u, __float_as_uint(rmax))));
+  // exponents biased by 256 so that they order as unsigned integers; 0 = no
+  // value (a padding row, or a row of zeros)
+  uint32_t nb = 0;
+  if (m < nrow && rmax > 0.f) {
+    int x2;
+    (void)frexpf(rmax, &x2);  // 2^(x2-1) <= rmax < 2^x2
+    nb = (uint32_t)(x2 - 15 + 256);
+  }
+  __shared__ uint32_t s_tmax[4];
+  {
+    const uint32_t wm = dpp::wave_max_u32(nb);
+    if (lane == 0) s_tmax[wv] = wm;
+  }
+  __syncthreads();
+  const uint32_t tb = max(max(s_tmax[0], s_tmax[1]), max(s_tmax[2], s_tmax[3]));
+  const int T = tb ? (int)tb - 256 : 0;
+  int er = T;  // this row's exponent
+  if (nb && (int)nb - 256 < T - 12) er = max((int)nb - 256, T - 126);
+  const bool own = m < nrow && er != T;
+  // h / 2^er in fp16, each 8-chunk in nib_to_f16 order (0,4,1,5,2,6,3,7);
+  // the group sum of the values the down GEMM multiplies, 2^er * fp16
+  uint32_t pk[8];
+  float sum = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) {
+    const _Float16 hq = (_Float16)ldexpf(hv[cc], -er);
+    sum += ldexpf((float)hq, er);
+    const uint32_t b = __builtin_bit_cast(uint16_t, hq);
+    const int ch = cc >> 3, p = cc & 7;
+    const int w = 4 * ch + (p & 3);  // dword of the pair (p, p + 4)
+    if (p < 4) pk[w] = b;
+    else pk[w] |= b << 16;
+  }
+  sum += __uint_as_float(dpp::mov<dpp::kQuadXor1, 0xF>(0u, __float_as_uint(sum)));
+  sum += __uint_as_float(dpp::mov<dpp::kQuadXor2, 0xF>(0u, __float_as_uint(sum)));
+  const int GI = a.I / 64;
+  if (m < nrow) {
+    uint16_t* dst = a.h16 + (size_t)(base + m) * a.I + n0 + 16 * qq;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    *reinterpret_cast<uint4*>(dst + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    if (qq == 0) {
+      a.hsum[(size_t)(base + m) * GI + nt] = sum;
+      a.hrowf[(size_t)(base + m) * GI + nt] = ldexpf(1.f, er - T);
     }
-    const int m = tid >> 2, qq = tid & 3;
-    float sum = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < 16; ++cc) sum += sg[m * SGS + 16 * qq + cc];
-    sum += __uint_as_float(dpp::mov<dpp::kQuadXor1, 0xF>(0u, __float_as_uint(sum)));
-    sum += __uint_as_float(dpp::mov<dpp::kQuadXor2, 0xF>(0u, __float_as_uint(sum)));
-    if (qq == 0 && m < nrow) a.hsum[(size_t)(base + m) * (a.I / 64) + nt] = sum;
+  }
+  const uint64_t any_own = __ballot(own);
+  __shared__ uint32_t s_own[4];
+  if (lane == 0) s_own[wv] = any_own != 0;
+  __syncthreads();
+  if (tid == 0) {
+    const float sc = ldexpf(1.f, T);
+    a.hscale[(size_t)tile * GI + nt] = (s_own[0] | s_own[1] | s_own[2] | s_own[3]) ? -sc : sc;
   }
 }
 
@@ -784,7 +813,10 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
 // rows of one expert x 256 columns; wave w computes columns [64w, 64w + 64)
 // as 2 x 2 tiles of 32x32x16 fp16 MFMA. A = h / 2^e in fp16 (2^e the
 // (tile, group) scale from the gate/up kernel, folded into the group's
-// weight scale), B = the codes as fp16 16 + q, K over the 64-groups of I.
+// weight scale), B = the codes as fp16 16 + q, K over the 64-groups of I. A
+// tile where some rows carry their own range factor (rows far below the
+// tile's largest) runs a copy of the K loop that multiplies those rows'
+// partial sums by their factors before the group scale.
 // Operands move by global->LDS DMA into DN_NS-stage rings, DN_PF groups
 // ahead, 5 DMAs per wave per group (h 2, codes 2, scales 1); the affine term
 // uses the per-group sums of h written by the gate/up kernel. Output:
@@ -797,7 +829,7 @@ constexpr int DA_STAGE = BM * 64 * 2;      // 64 rows x 64 fp16
 constexpr int DB_STAGE = DN_BN * 32;       // 256 code rows x 64 int4
 constexpr int DS_STAGE = DN_BN * 4;        // 256 (s, c) words
 
-size_t down_lds_bytes(int GI) { return (size_t)DN_NS * (DA_STAGE + DB_STAGE + DS_STAGE) + (size_t)256 * GI; }
+size_t down_lds_bytes(int GI) { return (size_t)DN_NS * (DA_STAGE + DB_STAGE + DS_STAGE) + (size_t)2 * 256 * GI; }
 
 struct DownSources {
   const uint16_t* h[2];   // A (instruction t): row 8 (2w + t) + lane / 8, chunk (lane % 8) ^ (row % 8)
@@ -823,10 +855,11 @@ __device__ __forceinline__ void down_issue(uint8_t* __restrict__ wrH, uint8_t* _
 // One group: acc += s * 2^e * A . (16 + q); for an odd group also the affine
 // term of the pair (g - 1, g) (lanes of k-half hh take group g-1+hh). Rows
 // 32..63 only for a tile that has them (FULL).
-template <bool FULL>
+template <bool FULL, bool MIXED>
 __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, const uint8_t* __restrict__ rdB,
                                            const uint8_t* __restrict__ rdS, const float* __restrict__ sHs,
-                                           float hscale, uint8_t* __restrict__ wrH, uint8_t* __restrict__ wrB,
+                                           const float* __restrict__ sRf, float hscale, uint8_t* __restrict__ wrH,
+                                           uint8_t* __restrict__ wrB,
                                            uint8_t* __restrict__ wrS, const DownSources& src, int gn, int g,
                                            int wv, int brow, int hh, int mrow, float (&cprev)[2],
                                            f32x16 (&acc)[4], const NibConst& nk) {
@@ -850,6 +883,25 @@ __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, cons
     for (int st = 0; st < 4; ++st) {
       p0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][st], b[st], p0, 0, 0, 0);
       if constexpr (FULL) p1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][st], b[st], p1, 0, 0, 0);
+    }
+    if constexpr (MIXED) {
+      // rows with their own range scale: 2^(e_row - T) on their partial sums
+      // (exact); lane rows (r / 4) * 8 + 4 hh + r % 4 are four runs of four
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float4 f0 = *reinterpret_cast<const float4*>(sRf + g * 64 + 8 * i + 4 * hh);
+        p0[4 * i] *= f0.x;
+        p0[4 * i + 1] *= f0.y;
+        p0[4 * i + 2] *= f0.z;
+        p0[4 * i + 3] *= f0.w;
+        if constexpr (FULL) {
+          const float4 f1 = *reinterpret_cast<const float4*>(sRf + g * 64 + 32 + 8 * i + 4 * hh);
+          p1[4 * i] *= f1.x;
+          p1[4 * i + 1] *= f1.y;
+          p1[4 * i + 2] *= f1.z;
+          p1[4 * i + 3] *= f1.w;
+        }
+      }
     }
     const float sv = f16f(sw & 0xFFFFu);
     const float svh = sv * hscale;
@@ -878,13 +930,12 @@ __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, cons
 
 // The K loop of a down block, instantiated for tiles of more than 32 rows
 // (FULL) and for the rest, so neither copy branches inside the loop.
-template <bool FULL>
-__device__ __forceinline__ void down_loop(uint8_t* sH, uint8_t* sB, uint8_t* sS, const float* sHs,
-                                          const float* s_hscale, const DownSources& src, int GI, int wv, int brow, int hh, int mrow,
-                                          float (&cprev)[2], f32x16 (&acc)[4], const NibConst& nk) {
+template <bool FULL, bool MIXED>
+__device__ __forceinline__ void down_loop(uint8_t* sH, uint8_t* sB, uint8_t* sS, const float* sHs, const float* sRf,
+                                          const float* s_hscale, const DownSources& src, int GI, int wv, int brow,
+                                          int hh, int mrow, float (&cprev)[2], f32x16 (&acc)[4], const NibConst& nk) {
   // Waits (PF = 2): step 0 needs A(0), after which only A(1) (2 DMAs) was
-  // issued; step g >= 1 needs group g, issued one step (5 DMAs) earlier. The
-  // barrier of step 0 also publishes s_hscale.
+  // issued; step g >= 1 needs group g, issued one step (5 DMAs) earlier.
   static_assert(DN_PF == 2, "wait counts below are written for PF = 2");
   for (int g = 0; g < GI; ++g) {
     if (g == 0)
@@ -894,7 +945,7 @@ __device__ __forceinline__ void down_loop(uint8_t* sH, uint8_t* sB, uint8_t* sS,
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);  // no LDS read moves above the barrier
     const int rd = g % DN_NS, wr = (g + DN_PF) % DN_NS;
-    down_group<FULL>(sH + rd * DA_STAGE, sB + rd * DB_STAGE, sS + rd * DS_STAGE, sHs, s_hscale[g],
+    down_group<FULL, MIXED>(sH + rd * DA_STAGE, sB + rd * DB_STAGE, sS + rd * DS_STAGE, sHs, sRf, s_hscale[g],
                      sH + wr * DA_STAGE, sB + wr * DB_STAGE, sS + wr * DS_STAGE, src, min(g + DN_PF, GI - 1), g, wv,
                      brow, hh, mrow, cprev, acc, nk);
   }
@@ -918,7 +969,8 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   uint8_t* sH = smem;                                               // [NS][64][8 slots of 16 B]
   uint8_t* sB = sH + DN_NS * DA_STAGE;                              // [NS][256 rows][32 B]
   uint8_t* sS = sB + DN_NS * DB_STAGE;                              // [NS][256 rows] words
-  float* sHs = reinterpret_cast<float*>(sS + DN_NS * DS_STAGE);     // [GI][64 rows]
+  float* sHs = reinterpret_cast<float*>(sS + DN_NS * DS_STAGE);     // [GI][64 rows] group sums of h
+  float* sRf = sHs + 64 * GI;                                       // [GI][64 rows] row factors
 
   DownSources src;
   // down codes are stored in 16-byte tiles [I/32][H][16 B] (group g = tiles
@@ -954,10 +1006,13 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   // A tile of at most 32 rows leaves the second 32-row MFMA tile of every
   // wave out (its accumulators stay zero and are never stored).
   const bool full = __builtin_amdgcn_readfirstlane(nrow) > 32;
-  // h group sums: instruction g loads group g of the 64 rows
+  // h group sums and row factors: instruction g loads group g of the 64 rows
   {
     const size_t hrow = (size_t)base + min(lane, nrow - 1);
-    for (int g = wv; g < GI; g += 4) dma4(a.hsum + hrow * GI + g, reinterpret_cast<uint8_t*>(sHs) + g * 256);
+    for (int g = wv; g < GI; g += 4) {
+      dma4(a.hsum + hrow * GI + g, reinterpret_cast<uint8_t*>(sHs) + g * 256);
+      dma4(a.hrowf + hrow * GI + g, reinterpret_cast<uint8_t*>(sRf) + g * 256);
+    }
   }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -976,7 +1031,16 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
     s_dst[tid] = dst;
     s_w[tid] = w;
   }
-  if (tid < GI) s_hscale[tid] = hs;
+  // tile-group scales 2^T; a negative entry marks a group where some rows
+  // carry their own factor, and the block then runs the loop that applies them
+  __shared__ uint32_t s_mixed;
+  if (tid < GI) s_hscale[tid] = fabsf(hs);
+  if (wv == 0) {
+    const uint64_t b = __ballot(tid < GI && hs < 0.f);
+    if (lane == 0) s_mixed = b != 0;
+  }
+  __syncthreads();
+  const bool mixed = __builtin_amdgcn_readfirstlane(s_mixed) != 0;
   const int nl = 64 * wv + (lane & 31);  // first column of this lane (second: + 32)
   const int brow = nl;
   const int hh = lane >> 5;
@@ -984,10 +1048,17 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
   f32x16 acc[4] = {};
   float cprev[2] = {0.f, 0.f};
   const NibConst nk = nib_const();
-  if (full)
-    down_loop<true>(sH, sB, sS, sHs, s_hscale, src, GI, wv, brow, hh, mrow, cprev, acc, nk);
-  else
-    down_loop<false>(sH, sB, sS, sHs, s_hscale, src, GI, wv, brow, hh, mrow, cprev, acc, nk);
+  if (mixed) {
+    if (full)
+      down_loop<true, true>(sH, sB, sS, sHs, sRf, s_hscale, src, GI, wv, brow, hh, mrow, cprev, acc, nk);
+    else
+      down_loop<false, true>(sH, sB, sS, sHs, sRf, s_hscale, src, GI, wv, brow, hh, mrow, cprev, acc, nk);
+  } else {
+    if (full)
+      down_loop<true, false>(sH, sB, sS, sHs, sRf, s_hscale, src, GI, wv, brow, hh, mrow, cprev, acc, nk);
+    else
+      down_loop<false, false>(sH, sB, sS, sHs, sRf, s_hscale, src, GI, wv, brow, hh, mrow, cprev, acc, nk);
+  }
   if (GI & 1) {  // odd group count: the last group's affine term, paired with zeros
     const float x0 = hh ? 0.f : sHs[(GI - 1) * 64 + mrow], x1 = hh ? 0.f : sHs[(GI - 1) * 64 + 32 + mrow];
 #pragma unroll
@@ -1067,6 +1138,7 @@ GemmArgs gemm_args(const Workspace* w, const PrefillArgs& pa) {
   ga.route_gamma = pa.route_gamma;
   ga.h16 = w->h16;
   ga.hscale = w->hscale;
+  ga.hrowf = w->hrowf;
   ga.hsum = w->hsum;
   ga.y = w->y;
   ga.T = pa.n_tok;
@@ -1100,6 +1172,7 @@ void prefill_free(void* ws) {
   hipFree(w->tiles);
   hipFree(w->h16);
   hipFree(w->hscale);
+  hipFree(w->hrowf);
   hipFree(w->hsum);
   hipFree(w->y);
   delete w;
@@ -1123,7 +1196,7 @@ moe_status prefill_reserve(void** wsp, const moe_config& c, int T) {
                   grow(w->perm, P) && grow(w->wperm, P) &&
                   grow(w->tiles, (size_t)4 + 4 * max_tiles) &&
                   grow(w->h16, rows * I) && grow(w->hscale, (size_t)max_tiles * (I / 64)) &&
-                  grow(w->hsum, rows * (I / 64)) &&
+                  grow(w->hrowf, rows * (I / 64)) && grow(w->hsum, rows * (I / 64)) &&
                   grow(w->y, rows * H);
   if (!ok) return MOE_ENOMEM;
   w->T = T;

@@ -148,32 +148,38 @@ def test_prefill_workspace_regrows_and_shrinks():
     model.close()
 
 
-def test_prefill80b_full_size_sampled():
+def test_prefill80b_full_size_every_token():
     """2048-token batch of the 80B-shaped layer in the benchmark's launch
-    configuration: routing checked for every token, outputs on a sample the
-    oracle recomputes (first, last, and tokens in between)."""
+    configuration: every token's routing and output against the oracle (which
+    groups the 20,480 pairs by expert and dequantises each touched expert once)."""
     cfg = synth.get_config("prefill80b")
     model = gh.build(cfg)
     xb = synth.tokens(cfg.seed, cfg.n_tokens, cfg.hidden)
     out, idx, w = _forward(model, cfg, xb)
+    model.close()
     assert idx.shape == (cfg.n_tokens, cfg.top_k)
     assert np.all(np.isfinite(out))
-    eps = gh.prefill_eps_rel(cfg.hidden)
-    ties = gh.check_routing_only(cfg, 0, xb, idx, eps_rel=eps)
     assert np.allclose(w.sum(axis=1), 1.0, atol=1e-5)
-    sample = [0, 1, 63, 64, 1000, 2046, 2047]
-    err, _ = gh.check_layer(cfg, OracleModel(cfg), 0, xb, out, idx, sample, eps_rel=eps)
-    print(f"prefill80b: routing near-ties {ties}, sampled max rel L2 {err:.3e}")
+    gh.log("prefill80b: oracle on all tokens")
+    err, ties = gh.check_layer(cfg, OracleModel(cfg), 0, xb, out, idx, list(range(cfg.n_tokens)),
+                               eps_rel=gh.prefill_eps_rel(cfg.hidden))
+    print(f"prefill80b: all {cfg.n_tokens} tokens, max rel L2 {err:.3e}, near-ties {ties}")
     assert err <= gh.REL_L2_TOL
-    model.close()
 
 
-@pytest.mark.parametrize("shift,which", [(17, "all"), (12, "half"), (12, "one")])
-def test_prefill_large_activations_use_the_range_scales(shift, which):
-    """x scaled by 2^shift (exact in bf16): with 2^17 every token needs its
-    fp16 range scale (max |x| >= 65504) and h, quadratic in x, needs the
-    tile scales; with 2^12 on half the tokens, or on one token, the tiles mix
-    magnitudes 2^24 apart and share one scale per 64-row group."""
+RANGE_CASES = [(17, "all"), (17, "half"), (17, "one"), (12, "half"), (12, "one"),
+               (-8, "all"), (-8, "half"), (-8, "one"), (-16, "all"), (-16, "half"), (-16, "one")]
+
+
+@pytest.mark.parametrize("shift,which", RANGE_CASES)
+def test_prefill_scaled_activations_use_the_range_scales(shift, which):
+    """x scaled by 2^shift (exact in bf16) on every token, on every second
+    token, or on one token. The fp16 copies of x and h take power-of-two
+    scales in either direction: large activations (2^17: max |x| >= 65504)
+    are scaled down, small ones (2^-8, 2^-16: h near or below fp16's
+    subnormal range) scaled up. Where the scaled tokens share 64-row tiles
+    with unscaled ones, h of the two kinds differs by 2^16 to 2^34 in one
+    tile, and the small rows keep a range factor of their own."""
     cfg = synth.get_config("tiny", n_experts=8, top_k=2, hidden=256, inter=128, shared_inter=128)
     n_tok = 48
     assert _takes_prefill(cfg, n_tok)
@@ -188,5 +194,27 @@ def test_prefill_large_activations_use_the_range_scales(shift, which):
     err, ties = gh.check_layer(cfg, OracleModel(cfg), 0, xb, out, idx, list(range(n_tok)),
                                eps_rel=gh.prefill_eps_rel(cfg.hidden))
     print(f"shift {shift} on {which}: max rel L2 {err:.3e}, near-ties {ties}")
+    assert err <= gh.REL_L2_TOL
+    model.close()
+
+
+@pytest.mark.parametrize("shift", [-16, 17])
+def test_decode_scaled_activations(shift):
+    """The decode kernels (fp32 arithmetic on exact codes) on the same scaled
+    tokens: one token at a time, each within the bound."""
+    cfg = synth.get_config("tiny", n_experts=8, top_k=2, hidden=256, inter=128, shared_inter=128)
+    n_tok = 6
+    model = gh.build(cfg)
+    xb = synth.tokens(cfg.seed + 21, n_tok, cfg.hidden)
+    x = synth.bf16_bits_to_f32(xb) * np.float32(2.0 ** shift)
+    xb = synth.f32_to_bf16_bits(x)
+    torch = gh.torch_cuda()
+    xd = gh.dev_bf16(xb)
+    out = gh.dev_f32((n_tok, cfg.hidden))
+    model.layer_decode(0, xd, out)
+    torch.cuda.synchronize()
+    idx, _ = model.debug_routing()
+    err, ties = gh.check_layer(cfg, OracleModel(cfg), 0, xb, out.cpu().numpy(), idx, list(range(n_tok)))
+    print(f"decode shift {shift}: max rel L2 {err:.3e}, near-ties {ties}")
     assert err <= gh.REL_L2_TOL
     model.close()
