@@ -20,7 +20,6 @@ Pages:
 """
 from __future__ import annotations
 
-import math
 from fractions import Fraction
 from typing import Callable, Dict, List, NamedTuple, Optional, Tuple
 
@@ -105,15 +104,6 @@ def route(x: np.ndarray, w_r: np.ndarray, rho: Optional[np.ndarray], k: int, nor
         idx[t] = topk_order(logits[t], k)
         w[t] = route_weights(logits[t], idx[t], norm_topk)
     return Route(idx, w, logits)
-
-
-def topk_gap(logits_row: np.ndarray, k: int) -> float:
-    """Smallest gap l_(j) - l_(j+1) over j <= k in the sorted order (inf when k == E)."""
-    s = np.sort(np.asarray(logits_row, dtype=np.float64))[::-1]
-    n = min(k + 1, s.shape[0])
-    if n < 2:
-        return math.inf
-    return float(np.min(s[: n - 1] - s[1:n]))
 
 
 # ----------------------------------------------------------------- experts ---

@@ -60,11 +60,6 @@ def bf16_rne_from_f64(a) -> np.ndarray:
     return np.where(big, np.copysign(np.inf, a), r)
 
 
-def bf16_bits_from_f64(a) -> np.ndarray:
-    v = bf16_rne_from_f64(a).astype(np.float32)   # exact: a bf16 value fits fp32
-    return (v.view(np.uint32) >> 16).astype(np.uint16)
-
-
 def f64_from_bf16_bits(b) -> np.ndarray:
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 

@@ -158,11 +158,14 @@ def _hand_groups():
     b = np.full(64, 0.5, dtype=np.float32)
     c = np.zeros(64, dtype=np.float32)
     c[:5] = [0, 1.875, 0.0625, 0.1875, 0.3125]
-    return [a, b, c]
+    d = (0.125 * (np.arange(64) % 16)).astype(np.float32)
+    d[np.arange(64) % 16 == 0] = -0.0
+    return [a, b, c, d]
 
 
 def test_quant_hand_examples():
     ex = _golden("quant_hand_examples.json")["examples"]
+    assert len(ex) == len(_hand_groups())
     for w, e in zip(_hand_groups(), ex):
         m = quant.quantize(w[None, :], 4)
         assert int(m.s.view(np.uint16)[0, 0]) == int(e["scale_fp16_bits"], 16), e["name"]
