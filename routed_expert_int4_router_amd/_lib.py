@@ -143,6 +143,28 @@ def _ptr(a) -> int:
     return int(a)
 
 
+def _check_io(x, out, n: int, hidden: int) -> None:
+    """Refuse buffers the kernels would read or write out of bounds: x and out
+    must be device tensors of the right type holding at least n rows of
+    ``hidden`` elements (no check for an empty call)."""
+    if n < 0:
+        raise ValueError("n_tok must be >= 0")
+    if n == 0:
+        return
+    import torch
+    for name, t, dtypes in (("x", x, (torch.int16, torch.bfloat16)), ("out", out, (torch.float32,))):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor on the GPU")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be on the GPU")
+        if t.dtype not in dtypes:
+            raise TypeError(f"{name} must be of dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+        if t.dim() < 1 or t.shape[-1] != hidden:
+            raise ValueError(f"{name} must have rows of hidden = {hidden} elements, got shape {tuple(t.shape)}")
+        if t.numel() < n * hidden:
+            raise ValueError(f"{name} holds {t.numel() // hidden} rows, fewer than n_tok = {n}")
+
+
 def _stream(stream) -> Optional[int]:
     if stream is None:
         import torch
@@ -248,14 +270,17 @@ class Model:
 
     def layer_forward(self, layer: int, x, out, n_tok: Optional[int] = None, stream=None):
         n = x.shape[0] if n_tok is None else n_tok
+        _check_io(x, out, n, self.cfg.hidden)
         _check(lib().moe_layer_forward(self._h, layer, _ptr(x), n, _ptr(out), _stream(stream)))
 
     def layer_decode(self, layer: int, x, out, n_tok: Optional[int] = None, stream=None):
         n = x.shape[0] if n_tok is None else n_tok
+        _check_io(x, out, n, self.cfg.hidden)
         _check(lib().moe_layer_decode(self._h, layer, _ptr(x), n, _ptr(out), _stream(stream)))
 
     def stack_decode(self, x0, out, pool: Optional["Pool"] = None, n_tok: Optional[int] = None, stream=None):
         n = x0.shape[0] if n_tok is None else n_tok
+        _check_io(x0, out, n, self.cfg.hidden)
         _check(lib().moe_stack_decode(self._h, None if pool is None else pool.handle, _ptr(x0), n, _ptr(out),
                                       _stream(stream)))
 

@@ -180,6 +180,7 @@ struct moe_model {
     const void* x;
     void* out;
     hipGraphExec_t exec;
+    hipEvent_t done;  // recorded after the entry's latest launch
     uint64_t stamp;
   };
   std::vector<GraphEntry> graphs;
@@ -217,8 +218,12 @@ moe_status check_pool(const moe_pool* p, const char* fn) {
   return MOE_OK;
 }
 
+// Every graph may still be executing: callers synchronise the device first.
 void drop_graphs(moe_model* m) {
-  for (auto& g : m->graphs) hipGraphExecDestroy(g.exec);
+  for (auto& g : m->graphs) {
+    hipGraphExecDestroy(g.exec);
+    hipEventDestroy(g.done);
+  }
   m->graphs.clear();
 }
 
@@ -352,19 +357,34 @@ moe_status run_graph(moe_model* m, int kind, int layer, const void* x, void* out
     e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
     hipGraphDestroy(graph);
     if (e != hipSuccess) return hip_fail(e, "graph instantiate");
+    hipEvent_t done = nullptr;
+    e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+    if (e != hipSuccess) {
+      hipGraphExecDestroy(exec);
+      return hip_fail(e, "graph event");
+    }
     if (m->graphs.size() >= kGraphCacheSize) {
       auto lru = std::min_element(m->graphs.begin(), m->graphs.end(),
                                   [](const moe_model::GraphEntry& a, const moe_model::GraphEntry& b) {
                                     return a.stamp < b.stamp;
                                   });
+      // the evicted graph's last launch may still be running on some stream
+      e = hipEventSynchronize(lru->done);
       hipGraphExecDestroy(lru->exec);
+      hipEventDestroy(lru->done);
       m->graphs.erase(lru);
+      if (e != hipSuccess) {
+        hipGraphExecDestroy(exec);
+        hipEventDestroy(done);
+        return hip_fail(e, "graph eviction wait");
+      }
     }
-    m->graphs.push_back({kind, layer, n, x, out, exec, 0});
+    m->graphs.push_back({kind, layer, n, x, out, exec, done, 0});
     hit = &m->graphs.back();
   }
   hit->stamp = ++m->graph_clock;
   HIP_TRY(hipGraphLaunch(hit->exec, user), "graph launch");
+  HIP_TRY(hipEventRecord(hit->done, user), "graph event record");
   return MOE_OK;
 }
 

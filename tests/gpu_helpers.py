@@ -13,6 +13,8 @@ Matching rules:
 """
 from __future__ import annotations
 
+from typing import NamedTuple
+
 import numpy as np
 
 import routed_expert_int4_router_amd as moe
@@ -22,6 +24,18 @@ from oracle import moe as omoe
 from oracle import quant
 
 REL_L2_TOL = 2e-3
+
+_T0 = None
+
+
+def log(msg: str) -> None:
+    """Progress line of a long GPU test (flushed, so a slow step is visibly alive)."""
+    import sys
+    import time
+    global _T0
+    if _T0 is None:
+        _T0 = time.time()
+    print(f"[{time.time() - _T0:8.1f}s] {msg}", file=sys.stderr, flush=True)
 
 
 def torch_cuda():
@@ -42,7 +56,13 @@ def dev_f32(shape):
 
 
 def build(cfg: synth.Config, storage=moe.STORE_DEVICE):
-    return loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage)
+    big = cfg.n_layers * cfg.n_experts >= 4096
+    if big:
+        log(f"loading {cfg.name}: {cfg.n_layers} layers x {cfg.n_experts} experts")
+    m = loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage)
+    if big:
+        log(f"loaded {cfg.name}")
+    return m
 
 
 DECODE_EPS_REL = 2.0 ** -16
@@ -70,26 +90,6 @@ def selection_ok(gpu_sel, oracle_logits, x_row, w_r, k, eps_rel=DECODE_EPS_REL, 
         if a != b and abs(l[a] - l[b]) > eps[a] + eps[b]:
             return False, 1
     return True, 1
-
-
-def recast_slack(r, w_r, layer):
-    """Logit slack from the bf16 recast x_l = bf16(r_l) between stack layers.
-    The GPU's fp32 residual is taken to agree with the oracle's fp64 one to
-    within layer * 2^-20 * rms(r) + 2^-24 |r_h| per element (a few fp32 roundings
-    per layer; the measured deltas agree to ~1e-6). An element whose oracle
-    value lies that close to a bf16 rounding boundary may round to the other
-    neighbour on the GPU, moving logit e by up to ulp_h * |w_r[h, e]|; the slack
-    of e sums that over such elements. w_r is [H][E + 1] or [H][E]."""
-    r = np.asarray(r, dtype=np.float64)
-    xv = quant.bf16_rne_from_f64(r)
-    ax = np.abs(xv)
-    expo = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
-    ulp = np.where(ax > 0, 2.0 ** (expo - 7), 2.0 ** -133)
-    delta = layer * 2.0 ** -20 * np.sqrt(np.mean(r * r)) + 2.0 ** -24 * np.abs(r)
-    to_boundary = np.abs(ulp / 2 - np.abs(r - xv))
-    near = to_boundary <= delta
-    w = np.abs(np.asarray(w_r, dtype=np.float64))
-    return (ulp * near) @ w
 
 
 def check_layer(cfg, om, layer, x_bits, gpu_out, gpu_idx, tokens, eps_rel=DECODE_EPS_REL, lw=None):
@@ -126,27 +126,87 @@ def check_routing_only(cfg, layer, x_bits, gpu_idx, eps_rel=DECODE_EPS_REL):
     return ties
 
 
+class Replay(NamedTuple):
+    x: np.ndarray        # uint16 [L][T][H]: bf16 input of every layer
+    idx: np.ndarray      # int32 [L][T][k]: the selection of every (layer, token)
+    out: np.ndarray      # float32 [L][len(keep)][H]: layer outputs of the kept tokens
+    r_final: np.ndarray  # float32 [T][H]: r_L
+
+
+def replay_layers(model, cfg, x0_bits, keep=()):
+    """Run a resident stack one layer at a time through moe_layer_decode, with
+    the fp32 residual r_{l+1} = r_l + out_l and the recast x_{l+1} = bf16(r_{l+1})
+    done by torch (IEEE fp32 add, round to nearest even): the same operations
+    the stack's own epilogue performs, so r_L must equal moe_stack_decode's
+    output bit for bit. Gives each layer's actual input, selection and output."""
+    torch = torch_cuda()
+    L, T, H = cfg.n_layers, x0_bits.shape[0], cfg.hidden
+    x = dev_bf16(x0_bits)
+    r = x.view(torch.bfloat16).float()
+    xs = np.empty((L, T, H), np.uint16)
+    idxs = np.empty((L, T, cfg.top_k), np.int32)
+    outs = np.empty((L, len(keep), H), np.float32)
+    keep_t = torch.as_tensor(list(keep), dtype=torch.long, device="cuda")
+    out = dev_f32((T, H))
+    for l in range(L):
+        if l % 8 == 0:
+            log(f"replay: layer {l} of {L}")
+        model.layer_decode(l, x, out)
+        idx, _ = model.debug_routing()   # synchronises the device
+        xs[l] = x.cpu().numpy().view(np.uint16)
+        idxs[l] = idx
+        if len(keep):
+            outs[l] = out[keep_t].cpu().numpy()
+        r = r + out
+        x = r.to(torch.bfloat16).view(torch.int16).contiguous()
+    return Replay(xs, idxs, outs, r.cpu().numpy())
+
+
+def check_layers_local(cfg, om, rep, keep=(), eps_rel=DECODE_EPS_REL):
+    """Layer-local parity of a stack at its actual layer inputs: every
+    (layer, token) selection against the oracle's exactly rounded logits of
+    that layer's GPU input x_l (no slack beyond the fp32 router's), and the
+    outputs of the kept tokens against the oracle's layer at the same x_l.
+    Returns (max rel L2 over kept tokens and layers, near-ties)."""
+    ties = 0
+    worst = 0.0
+    for l in range(cfg.n_layers):
+        if l % 8 == 0:
+            log(f"layer-local oracle checks: layer {l} of {cfg.n_layers}")
+        w_r = synth.router_weight(cfg.seed, l, cfg.hidden, cfg.n_experts)
+        rho = synth.router_bias(cfg, l)
+        x = quant.f64_from_bf16_bits(rep.x[l])
+        logits = omoe.router_logits(x, w_r, rho)
+        for t in range(x.shape[0]):
+            ok, tie = selection_ok(rep.idx[l, t], logits[t], x[t], w_r, cfg.top_k, eps_rel)
+            assert ok, (f"layer {l} token {t}: selection {list(rep.idx[l, t])} vs "
+                        f"{list(omoe.topk_order(logits[t], cfg.top_k))}")
+            ties += tie
+        if len(keep):
+            err, _ = check_layer(cfg, om, l, rep.x[l], _scatter(rep.out[l], keep, rep.x.shape[1]),
+                                 rep.idx[l], list(keep), eps_rel)
+            worst = max(worst, err)
+    return worst, ties
+
+
+def _scatter(rows, keep, T):
+    full = np.zeros((T, rows.shape[1]), np.float32)
+    full[list(keep)] = rows
+    return full
+
+
 def check_stack(cfg, om, x0_bits, gpu_out, gpu_idx, tokens):
-    """Stack parity on sampled tokens: the oracle follows the GPU's selections
-    (each checked to be the oracle top-k up to near-ties); compares
-    delta = r_L - r_0 per token."""
+    """End-to-end stack parity on sampled tokens: the oracle runs the whole
+    stack in fp64 from x0 (r0 = x0, x_l = bf16(r_l)), taking at each layer the
+    GPU's selection (each one is checked against the oracle at the GPU's own
+    layer input by check_layers_local), and delta = r_L - r_0 is compared per
+    token. The oracle's x_l can differ from the GPU's in an element whose
+    residual lies within rounding of a bf16 boundary; its effect on delta is
+    part of the measured error."""
     L, k = cfg.n_layers, cfg.top_k
     x0 = quant.f64_from_bf16_bits(x0_bits[tokens])
     sels = [np.stack([gpu_idx[t * L + l] for t in tokens]) for l in range(L)]
-    layers = om.layers()
-    st = omoe.stack_forward(x0, layers, k, cfg.norm_topk, sels=sels)
-    # validate every GPU selection against the oracle's logits at the oracle's own x_l
-    ties = 0
-    r = x0.copy()
-    for l, lw in enumerate(layers):
-        xl = quant.bf16_rne_from_f64(r)
-        logits = st.routes[l].logits
-        for i, t in enumerate(tokens):
-            extra = recast_slack(r[i], lw.w_r, l) if l > 0 else None
-            ok, tie = selection_ok(sels[l][i], logits[i], xl[i], lw.w_r, k, extra=extra)
-            assert ok, f"token {t} layer {l}: selection {list(sels[l][i])} vs {list(omoe.topk_order(logits[i], k))}"
-            ties += tie
-        r = r + omoe.layer_forward(xl, lw, k, cfg.norm_topk, sel=sels[l]).out
+    st = omoe.stack_forward(x0, om.layers(), k, cfg.norm_topk, sels=sels)
     delta_gpu = gpu_out[tokens].astype(np.float64) - x0
     err = omoe.rel_l2_per_token(delta_gpu, st.delta)
-    return float(err.max()), ties
+    return float(err.max())

@@ -152,21 +152,36 @@ def test_topk_exact_wide_routing_and_fallback():
         model.close()
 
 
-def test_decode80b_full_size_sampled():
-    """All 1024 tokens of the 80B-shaped layer in the benchmark's launch configuration;
-    routing checked for every token, outputs on a sample the oracle recomputes."""
+def test_decode80b_full_size_every_token():
+    """All 1024 tokens of the 80B-shaped layer in the benchmark's launch
+    configuration: every token's routing and output against the oracle (which
+    groups the tokens by expert, so each of the 512 experts is dequantised once)."""
     cfg = synth.get_config("decode80b")
     model = gh.build(cfg)
     xb = synth.tokens(cfg.seed, cfg.n_tokens, cfg.hidden)
     out, idx, w = _run_layer(model, cfg, xb)
+    model.close()
     assert idx.shape == (cfg.n_tokens, cfg.top_k)
     assert np.all(np.isfinite(out))
-    ties = gh.check_routing_only(cfg, 0, xb, idx)
     assert np.allclose(w.sum(axis=1), 1.0, atol=1e-5)
-    sample = [0, 1, 2, 511, 777, 1023]
-    err, t2 = gh.check_layer(cfg, OracleModel(cfg), 0, xb, out, idx, sample)
-    print(f"decode80b: routing near-ties {ties}, sampled max rel L2 {err:.3e}")
+    gh.log("decode80b: oracle on all tokens")
+    err, ties = gh.check_layer(cfg, OracleModel(cfg), 0, xb, out, idx, list(range(cfg.n_tokens)))
+    print(f"decode80b: all {cfg.n_tokens} tokens, max rel L2 {err:.3e}, near-ties {ties}")
     assert err <= gh.REL_L2_TOL
+
+
+def _stack_checks(cfg, model, xb, out, idx, keep, delta_tokens):
+    """A resident stack's output against its layer-by-layer replay (bit for
+    bit), every (layer, token) routing and the kept tokens' layer outputs at
+    the actual layer inputs, and the sampled tokens' end-to-end delta."""
+    L, n = cfg.n_layers, xb.shape[0]
+    rep = gh.replay_layers(model, cfg, xb, keep=keep)
+    assert np.array_equal(rep.r_final.view(np.uint32), out.view(np.uint32)), "stack != its layers one by one"
+    assert np.array_equal(rep.idx.transpose(1, 0, 2).reshape(n * L, cfg.top_k), idx)
+    om = OracleModel(cfg)
+    lerr, ties = gh.check_layers_local(cfg, om, rep, keep)
+    derr = gh.check_stack(cfg, om, xb, out, idx, delta_tokens)
+    return lerr, ties, derr
 
 
 @pytest.mark.parametrize("bits", [8, 4])
@@ -182,9 +197,10 @@ def test_stack35b_shape_parity(bits):
     torch.cuda.synchronize()
     idx, _ = model.debug_routing()
     assert idx.shape == (6 * cfg.n_layers, cfg.top_k)
-    err, ties = gh.check_stack(cfg, OracleModel(cfg), xb, out.cpu().numpy(), idx, list(range(6)))
-    print(f"stack bits={bits}: max rel L2 of delta {err:.3e}, near-ties {ties}")
-    assert err <= gh.REL_L2_TOL
+    lerr, ties, derr = _stack_checks(cfg, model, xb, out.cpu().numpy(), idx, list(range(6)), list(range(6)))
+    print(f"stack bits={bits}: layer-local max rel L2 {lerr:.3e}, delta {derr:.3e}, near-ties {ties}")
+    assert lerr <= gh.REL_L2_TOL and derr <= gh.REL_L2_TOL
+    model.close()
 
 
 def _pool_case(cfg, budget_slots, n_tok):
@@ -206,6 +222,19 @@ def _pool_case(cfg, budget_slots, n_tok):
     return host_model, dev_model, pool, xb, a, b, idx_pool, idx_res
 
 
+def _check_pool_trace(cfg, pool, slots, idx, n_tok):
+    sim = opool.replay(slots, moe.expert_bytes(cfg), idx, cfg.n_experts, cfg.n_layers)
+    hit, victim = pool.trace()
+    assert len(hit) == n_tok * cfg.n_layers * cfg.top_k
+    assert np.array_equal(hit, np.asarray(sim.trace_hit, np.uint8))
+    assert np.array_equal(victim, np.asarray(sim.trace_victim, np.int64))
+    st = pool.stats()
+    assert st["accesses"] == n_tok * cfg.n_layers * cfg.top_k
+    assert st["misses"] == sim.misses and st["hits"] == sim.hits
+    assert st["h2d_bytes"] == sim.misses * moe.expert_bytes(cfg)
+    return sim
+
+
 @pytest.mark.parametrize("slots", [10, 37])
 def test_pool_bit_identical_to_resident_and_trace_matches_oracle(slots):
     """Pool on == pool off bit for bit; the pool's hit/miss/victim trace equals the
@@ -215,24 +244,21 @@ def test_pool_bit_identical_to_resident_and_trace_matches_oracle(slots):
     host_model, dev_model, pool, xb, a, b, ip, ir = _pool_case(cfg, slots, 12)
     assert np.array_equal(ip, ir)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
-    hit, victim = pool.trace()
-    sim = opool.replay(slots, moe.expert_bytes(cfg), ip, cfg.n_experts, cfg.n_layers)
-    assert list(hit) == sim.trace_hit
-    assert list(victim) == sim.trace_victim
-    st = pool.stats()
-    assert st["accesses"] == 12 * cfg.n_layers * cfg.top_k
-    assert st["misses"] == sim.misses and st["hits"] == sim.hits
-    assert st["h2d_bytes"] == sim.misses * moe.expert_bytes(cfg)
-    err, ties = gh.check_stack(cfg, OracleModel(cfg), xb, a, ip, [0, 5, 11])
-    assert err <= gh.REL_L2_TOL
+    _check_pool_trace(cfg, pool, slots, ip, 12)
+    lerr, ties, derr = _stack_checks(cfg, dev_model, xb, b, ir, [0, 5, 11], [0, 5, 11])
+    assert lerr <= gh.REL_L2_TOL and derr <= gh.REL_L2_TOL
 
 
-def test_stack35b_int4_full_depth_sampled():
-    """The 40-layer 35B-shaped int4 stack at full depth, all 10,240 experts
-    resident, 64 tokens (a captured sequence, as in the benchmark): every
-    layer's routing of two tokens is checked against the oracle's top-k and
-    their delta r_40 - r_0 is recomputed by the oracle through all 40 layers."""
-    cfg = synth.get_config("stack35b_int4")
+@pytest.mark.parametrize("workload", ["stack35b_int8", "stack35b_int4"])
+def test_stack35b_full_depth(workload):
+    """The 40-layer 35B-shaped stack at full depth (int8: 34.2 GB, int4:
+    18.1 GB, all 10,240 experts resident), 64 tokens as a captured sequence
+    (as in the benchmark): the stack equals its 40 layers run one by one bit
+    for bit; every layer's routing of all 64 tokens is checked against the
+    oracle at the layer's actual input, two tokens' outputs at every layer, and
+    those two tokens' delta r_40 - r_0 is recomputed by the oracle through all
+    40 layers."""
+    cfg = synth.get_config(workload)
     torch = gh.torch_cuda()
     model = gh.build(cfg)
     n = 64
@@ -245,25 +271,29 @@ def test_stack35b_int4_full_depth_sampled():
     assert idx.shape == (n * cfg.n_layers, cfg.top_k)
     got = out.cpu().numpy()
     assert np.all(np.isfinite(got))
-    err, ties = gh.check_stack(cfg, OracleModel(cfg), xb, got, idx, [0, n - 1])
-    print(f"stack35b_int4 x40: max rel L2 of delta {err:.3e}, near-ties {ties}")
-    assert err <= gh.REL_L2_TOL
+    lerr, ties, derr = _stack_checks(cfg, model, xb, got, idx, [0, n - 1], [0, n - 1])
+    print(f"{workload} x{cfg.n_layers}: layer-local max rel L2 {lerr:.3e}, delta {derr:.3e}, near-ties {ties}")
+    assert lerr <= gh.REL_L2_TOL and derr <= gh.REL_L2_TOL
     model.close()
 
 
-def test_pool80b_full_depth_trace_and_sampled_parity():
+def test_pool80b_full_depth_every_token():
     """The 48-layer 80B-shaped stack with its 2 GiB pool (24,576 experts in
-    pinned host memory, 1213 slots) as the benchmark runs it, for 64 tokens:
-    the pool's hit/miss/victim trace over all 30,720 lookups equals the
-    oracle simulator replayed on the GPU's routing, the counters agree, and
-    token 0's delta is recomputed by the oracle through all 48 layers."""
+    pinned host memory, 1213 slots) for all 1024 tokens, as the benchmark runs
+    it: the pool's hit/miss/victim trace over all 491,520 lookups equals the
+    oracle simulator replayed on the GPU's routing and the counters agree; the
+    output equals the all-resident stack's bit for bit, which equals its 48
+    layers run one by one; every (layer, token) routing is checked against the
+    oracle at that layer's actual input, tokens 0 and 1023 at every layer's
+    output, and their deltas through all 48 layers."""
     cfg = synth.get_config("pool80b")
     torch = gh.torch_cuda()
-    model = gh.build(cfg, storage=moe.STORE_HOST)
-    pool = moe.Pool(model, cfg.pool_budget)
-    n = 64
+    n = cfg.n_tokens
+    assert n == 1024
     xb = synth.tokens(cfg.seed, n, cfg.hidden)
     x = gh.dev_bf16(xb)
+    model = gh.build(cfg, storage=moe.STORE_HOST)
+    pool = moe.Pool(model, cfg.pool_budget)
     out = gh.dev_f32((n, cfg.hidden))
     model.stack_decode(x, out, pool=pool)
     torch.cuda.synchronize()
@@ -271,18 +301,22 @@ def test_pool80b_full_depth_trace_and_sampled_parity():
     assert idx.shape == (n * cfg.n_layers, cfg.top_k)
     slots = cfg.pool_budget // moe.expert_stride(cfg)
     assert slots == 1213
-    sim = opool.replay(slots, moe.expert_bytes(cfg), idx, cfg.n_experts, cfg.n_layers)
-    hit, victim = pool.trace()
-    assert list(hit) == sim.trace_hit
-    assert list(victim) == sim.trace_victim
-    st = pool.stats()
-    assert st["accesses"] == n * cfg.n_layers * cfg.top_k
-    assert st["misses"] == sim.misses and st["hits"] == sim.hits
-    assert st["h2d_bytes"] == sim.misses * moe.expert_bytes(cfg)
+    gh.log("pool80b: 1024 tokens decoded through the pool; replaying the trace")
+    sim = _check_pool_trace(cfg, pool, slots, idx, n)
+    gh.log("pool80b: trace equals the simulator")
     got = out.cpu().numpy()
-    assert np.all(np.isfinite(got))
-    err, ties = gh.check_stack(cfg, OracleModel(cfg), xb, got, idx, [0])
-    print(f"pool80b x48: hits {sim.hits} of {st['accesses']}, max rel L2 of delta {err:.3e}, near-ties {ties}")
-    assert err <= gh.REL_L2_TOL
     pool.close()
     model.close()
+    assert np.all(np.isfinite(got))
+    res = gh.build(cfg)
+    out_res = gh.dev_f32((n, cfg.hidden))
+    res.stack_decode(x, out_res)
+    torch.cuda.synchronize()
+    idx_res, _ = res.debug_routing()
+    assert np.array_equal(idx_res, idx)
+    assert np.array_equal(out_res.cpu().numpy().view(np.uint32), got.view(np.uint32)), "pool != resident"
+    lerr, ties, derr = _stack_checks(cfg, res, xb, got, idx, [0, n - 1], [0, n - 1])
+    res.close()
+    print(f"pool80b x48, {n} tokens: hits {sim.hits} of {sim.accesses}, layer-local max rel L2 {lerr:.3e}, "
+          f"delta {derr:.3e}, near-ties {ties}")
+    assert lerr <= gh.REL_L2_TOL and derr <= gh.REL_L2_TOL
