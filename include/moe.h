@@ -205,6 +205,26 @@ moe_status moe_layer_decode(moe_model* m, int32_t layer, const uint16_t* x, int3
 moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, int32_t n_tok, float* out,
                             void* stream);
 
+/* moe_layer_forward's batched path (router GEMM, top-k, bucketing, grouped
+ * GEMMs, combine) for callers that cannot allocate: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. It calls no
+ * hipMalloc, hipFree or other allocating routine: its workspace lives in one
+ * static 64 MiB device array, of which each GPU holds its own copy from the
+ * library's first use of this call on that GPU until the process ends. Same
+ * arguments and arithmetic as moe_layer_forward on a batch of 8 or more
+ * tokens (bit-identical results), for any 1 <= n_tok up to what the array
+ * holds: about 108 KB per token for the 80B-shaped layer (H 2048, E 512,
+ * k 10, I 512), so at most ~600 tokens per call; a larger n_tok returns
+ * MOE_EINVAL with the limit in the message. Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (two streams, two threads)
+ * race and must be serialised by the caller. Each call rewrites everything it
+ * reads, so nothing carries over from the previous call. The routing stays in
+ * the array: moe_debug_routing reports no steps after this call. Needs an
+ * int4 layer with H % 256 == 0 (MOE_EINVAL otherwise), MOE_STORE_DEVICE, and
+ * the model's device current (MOE_ESTATE otherwise). */
+moe_status moe_layer_forward_noalloc(moe_model* m, int32_t layer, const uint16_t* x, int32_t n_tok, float* out,
+                                     void* stream);
+
 /* Routing of the most recent forward/decode call: for each step (token-major,
  * then layer) the k selected experts in selection order (logit descending,
  * lower index first on ties) and their weights. Copies min(cap, steps) steps

@@ -24,7 +24,8 @@ _STATUS_NAMES = {MOE_EINVAL: "MOE_EINVAL", MOE_ENOMEM: "MOE_ENOMEM", MOE_EHIP: "
 EXPORTS = [
     "moe_expert_bytes", "moe_expert_stride", "moe_blob_offset", "moe_pack", "moe_unpack",
     "moe_model_create", "moe_model_set_layer", "moe_model_set_experts", "moe_model_host_blob",
-    "moe_model_destroy", "moe_layer_forward", "moe_layer_decode", "moe_stack_decode", "moe_debug_routing",
+    "moe_model_destroy", "moe_layer_forward", "moe_layer_decode", "moe_stack_decode",
+    "moe_layer_forward_noalloc", "moe_debug_routing",
     "moe_pool_create", "moe_pool_reset", "moe_pool_stats", "moe_pool_trace", "moe_pool_destroy",
     "moe_pool_simulate", "moe_profile_enable", "moe_profile_read", "moe_last_error",
 ]
@@ -86,6 +87,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer_forward": (I32, [P, I32, P, I32, P, P]),
             "moe_layer_decode": (I32, [P, I32, P, I32, P, P]),
             "moe_stack_decode": (I32, [P, P, P, I32, P, P]),
+            "moe_layer_forward_noalloc": (I32, [P, I32, P, I32, P, P]),
             "moe_debug_routing": (I32, [P, P, P, SZ, ctypes.POINTER(SZ)]),
             "moe_pool_create": (I32, [P, SZ, ctypes.POINTER(P)]),
             "moe_pool_reset": (I32, [P]),
@@ -277,6 +279,11 @@ class Model:
         n = x.shape[0] if n_tok is None else n_tok
         _check_io(x, out, n, self.cfg.hidden)
         _check(lib().moe_layer_decode(self._h, layer, _ptr(x), n, _ptr(out), _stream(stream)))
+
+    def layer_forward_noalloc(self, layer: int, x, out, n_tok: Optional[int] = None, stream=None):
+        n = x.shape[0] if n_tok is None else n_tok
+        _check_io(x, out, n, self.cfg.hidden)
+        _check(lib().moe_layer_forward_noalloc(self._h, layer, _ptr(x), n, _ptr(out), _stream(stream)))
 
     def stack_decode(self, x0, out, pool: Optional["Pool"] = None, n_tok: Optional[int] = None, stream=None):
         n = x0.shape[0] if n_tok is None else n_tok

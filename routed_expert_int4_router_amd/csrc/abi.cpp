@@ -388,6 +388,40 @@ moe_status run_graph(moe_model* m, int kind, int layer, const void* x, void* out
   return MOE_OK;
 }
 
+// ------------------------------------------------------------ no-alloc path ---
+// Scratch of moe_layer_forward_noalloc: one file-scope device array, of which
+// every GPU the library runs on holds its own copy until the process ends.
+// Host code never uses the array's name as an address: the device address
+// of each GPU's copy comes from hipGetSymbolAddress with that GPU current.
+constexpr size_t kNoAllocScratchBytes = 64ull << 20;
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+// The calling thread's current device's copy of the scratch array (looked up
+// once per device), or NULL with the error set.
+moe_status scratch_on_current_device(uint8_t** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev), "moe_layer_forward_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_EINVAL, "moe_layer_forward_noalloc: device index out of range");
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "moe_layer_forward_noalloc: hipGetSymbolAddress");
+    if (!p) return fail(MOE_EHIP, "moe_layer_forward_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -647,6 +681,53 @@ moe_status moe_layer_forward(moe_model* m, int32_t layer, const uint16_t* x, int
     return MOE_OK;
   }
   return moe_layer_decode(m, layer, x, n_tok, out, stream);
+}
+
+moe_status moe_layer_forward_noalloc(moe_model* m, int32_t layer, const uint16_t* x, int32_t n_tok, float* out,
+                                     void* stream) {
+  clear_error();
+  moe_status st = check_forward_args(m, layer, x, n_tok, out, "moe_layer_forward_noalloc");
+  if (st) return st;
+  if (!prefill_supported(m->cfg))
+    return fail(MOE_EINVAL, "moe_layer_forward_noalloc: the layer shape has no batched path (int4, H % 256 == 0)");
+  m->route_steps = 0;  // this call's routing stays in the scratch array
+  if (n_tok == 0) return MOE_OK;
+  const size_t need = prefill_placed_bytes(m->cfg, n_tok);
+  if (need > kNoAllocScratchBytes) {
+    int most = n_tok;
+    while (most > 0 && prefill_placed_bytes(m->cfg, most) > kNoAllocScratchBytes) most = most * 15 / 16;
+    while (prefill_placed_bytes(m->cfg, most + 1) <= kNoAllocScratchBytes) ++most;
+    return fail(MOE_EINVAL, "moe_layer_forward_noalloc: " + std::to_string(n_tok) + " tokens need " +
+                                std::to_string(need) + " bytes of scratch, more than its " +
+                                std::to_string(kNoAllocScratchBytes) + "; this layer shape takes at most " +
+                                std::to_string(most) + " tokens per call");
+  }
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev), "moe_layer_forward_noalloc: hipGetDevice");
+  if (dev != m->device) return fail(MOE_ESTATE, "moe_layer_forward_noalloc: the model lives on another device");
+  uint8_t* base = nullptr;
+  st = scratch_on_current_device(&base);
+  if (st) return st;
+  PrefillWorkspace ws{};
+  PrefillArgs a{};
+  prefill_place(&ws, m->cfg, n_tok, base, &a.route_idx, &a.route_w, &a.route_gamma);
+  a.cfg = m->cfg;
+  a.geo = m->geo;
+  a.experts = m->experts + (size_t)layer * m->cfg.n_experts * m->stride;
+  a.stride = m->stride;
+  a.shared = layer_shared(m, layer);
+  a.wr_rows = layer_wr(m, layer);
+  a.wr_split = layer_wr_split(m, layer);
+  a.bias = layer_bias(m, layer);
+  a.x = x;
+  a.n_tok = n_tok;
+  a.out = out;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  using Stage = hipError_t (*)(void*, const PrefillArgs&, hipStream_t);
+  static const Stage kStages[] = {prefill_xprep, prefill_router,  prefill_route,  prefill_count,  prefill_scan,
+                                  prefill_scatter, prefill_gateup, prefill_down, prefill_combine};
+  for (const Stage stage : kStages) HIP_TRY(stage(&ws, a, s), "moe_layer_forward_noalloc: prefill stage");
+  return MOE_OK;
 }
 
 moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, int32_t n_tok, float* out,

@@ -28,7 +28,34 @@ struct PrefillArgs {
   float* route_gamma;       // device [n_tok]
 };
 
+// Device arrays of the batched path for batches of up to T tokens.
+struct PrefillWorkspace {
+  int T = 0, E = 0, k = 0, H = 0, I = 0;
+  float* logits = nullptr;      // [T][E+1]
+  float* xscale = nullptr;      // [T] power-of-two scale of each token
+  uint16_t* xp = nullptr;       // [T][H] fp16 bits of x / xscale, k-permuted
+  int32_t* cnt = nullptr;       // [nchunk][E]
+  int32_t* chunk_off = nullptr; // [nchunk][E]
+  int32_t* perm = nullptr;      // [T*k] sorted position -> pair id
+  float* wperm = nullptr;       // [T*k] sorted position -> router weight of the pair
+  int32_t* tiles = nullptr;     // [4 + 4 max_tiles]: count (3 unused), then per tile (expert, row0, base, rows)
+  uint16_t* h16 = nullptr;      // [T*k + T][I] fp16 bits, h / range scale
+  float* hscale = nullptr;      // [max_tiles][I/64] power-of-two scale of each (tile, group), sign = mixed
+  float* hrowf = nullptr;       // [T*k + T][I/64] power-of-two factor of each row relative to its tile-group
+  float* hsum = nullptr;        // [T*k + T][I/64]
+  float* y = nullptr;           // [T*k + T][H]
+  int max_tiles = 0;
+};
+
 bool prefill_supported(const moe_config& cfg);
+
+// Bytes of a workspace for batches of up to n_tok tokens laid out in one
+// block of device memory, route arrays ([n_tok][k] idx and w, [n_tok] gamma)
+// included; prefill_place points w and the route arrays into such a block.
+// Nothing needs clearing: every kernel writes what a later one reads.
+size_t prefill_placed_bytes(const moe_config& cfg, int n_tok);
+void prefill_place(PrefillWorkspace* w, const moe_config& cfg, int n_tok, uint8_t* base, int32_t** route_idx,
+                   float** route_w, float** route_gamma);
 
 // Workspace for batches of up to n_tok tokens (grown on demand; synchronises
 // the device when it has to reallocate).

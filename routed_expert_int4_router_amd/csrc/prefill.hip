@@ -52,23 +52,7 @@ typedef __attribute__((ext_vector_type(16))) float f32x16;
 constexpr int BM = 64;        // tile rows (tokens or pairs)
 constexpr int CHUNK = 512;    // pairs per bucketing chunk
 
-struct Workspace {
-  int T = 0, E = 0, k = 0, H = 0, I = 0;
-  float* logits = nullptr;      // [T][E+1]
-  float* xscale = nullptr;      // [T] power-of-two scale of each token
-  uint16_t* xp = nullptr;       // [T][H] fp16 bits of x / xscale, k-permuted
-  int32_t* cnt = nullptr;       // [nchunk][E]
-  int32_t* chunk_off = nullptr; // [nchunk][E]
-  int32_t* perm = nullptr;      // [T*k] sorted position -> pair id
-  float* wperm = nullptr;       // [T*k] sorted position -> router weight of the pair
-  int32_t* tiles = nullptr;     // [4 + 4 max_tiles]: count (3 unused), then per tile (expert, row0, base, rows)
-  uint16_t* h16 = nullptr;      // [T*k + T][I] fp16 bits, h / hscale
-  float* hscale = nullptr;      // [max_tiles][I/64] power-of-two scale of each (tile, group), sign = mixed
-  float* hrowf = nullptr;       // [T*k + T][I/64] power-of-two factor of each row relative to its tile-group
-  float* hsum = nullptr;        // [T*k + T][I/64]
-  float* y = nullptr;           // [T*k + T][H]
-  int max_tiles = 0;
-};
+using Workspace = PrefillWorkspace;
 
 __device__ __forceinline__ float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -1117,6 +1101,50 @@ bool grow(T*& p, size_t n) {
 
 Workspace* ws_of(void* p) { return static_cast<Workspace*>(p); }
 
+int max_tiles_for(const moe_config& c, int T) {
+  const size_t P = (size_t)T * c.top_k;
+  return (int)((P + BM - 1) / BM) + c.n_experts + (T + BM - 1) / BM;
+}
+
+// The workspace arrays of a batch of up to T tokens, in one block: element
+// counts and sizes, each array starting on a 256-byte boundary.
+struct Placement {
+  size_t off[16];
+  size_t total;
+};
+Placement placement(const moe_config& c, int T) {
+  const size_t E = c.n_experts, k = c.top_k, H = c.hidden, I = c.inter;
+  const size_t P = (size_t)T * k, rows = P + T;
+  const size_t nchunk = (P + CHUNK - 1) / CHUNK;
+  const size_t mt = (size_t)max_tiles_for(c, T);
+  const size_t bytes[16] = {
+      (size_t)T * (E + 1) * 4,  // logits
+      (size_t)T * 4,            // xscale
+      (size_t)T * H * 2,        // xp
+      nchunk * E * 4,           // cnt
+      nchunk * E * 4,           // chunk_off
+      P * 4,                    // perm
+      P * 4,                    // wperm
+      (4 + 4 * mt) * 4,         // tiles
+      rows * I * 2,             // h16
+      mt * (I / 64) * 4,        // hscale
+      rows * (I / 64) * 4,      // hrowf
+      rows * (I / 64) * 4,      // hsum
+      rows * H * 4,             // y
+      P * 4,                    // route_idx
+      P * 4,                    // route_w
+      (size_t)T * 4,            // route_gamma
+  };
+  Placement p{};
+  size_t o = 0;
+  for (int i = 0; i < 16; ++i) {
+    p.off[i] = o;
+    o += (bytes[i] + 255) / 256 * 256;
+  }
+  p.total = o;
+  return p;
+}
+
 GemmArgs gemm_args(const Workspace* w, const PrefillArgs& pa) {
   GemmArgs ga{};
   ga.x = pa.x;
@@ -1178,6 +1206,35 @@ void prefill_free(void* ws) {
   delete w;
 }
 
+size_t prefill_placed_bytes(const moe_config& cfg, int n_tok) { return placement(cfg, n_tok).total; }
+
+void prefill_place(PrefillWorkspace* w, const moe_config& c, int T, uint8_t* base, int32_t** route_idx,
+                   float** route_w, float** route_gamma) {
+  const Placement p = placement(c, T);
+  w->logits = reinterpret_cast<float*>(base + p.off[0]);
+  w->xscale = reinterpret_cast<float*>(base + p.off[1]);
+  w->xp = reinterpret_cast<uint16_t*>(base + p.off[2]);
+  w->cnt = reinterpret_cast<int32_t*>(base + p.off[3]);
+  w->chunk_off = reinterpret_cast<int32_t*>(base + p.off[4]);
+  w->perm = reinterpret_cast<int32_t*>(base + p.off[5]);
+  w->wperm = reinterpret_cast<float*>(base + p.off[6]);
+  w->tiles = reinterpret_cast<int32_t*>(base + p.off[7]);
+  w->h16 = reinterpret_cast<uint16_t*>(base + p.off[8]);
+  w->hscale = reinterpret_cast<float*>(base + p.off[9]);
+  w->hrowf = reinterpret_cast<float*>(base + p.off[10]);
+  w->hsum = reinterpret_cast<float*>(base + p.off[11]);
+  w->y = reinterpret_cast<float*>(base + p.off[12]);
+  *route_idx = reinterpret_cast<int32_t*>(base + p.off[13]);
+  *route_w = reinterpret_cast<float*>(base + p.off[14]);
+  *route_gamma = reinterpret_cast<float*>(base + p.off[15]);
+  w->T = T;
+  w->E = c.n_experts;
+  w->k = c.top_k;
+  w->H = c.hidden;
+  w->I = c.inter;
+  w->max_tiles = max_tiles_for(c, T);
+}
+
 moe_status prefill_reserve(void** wsp, const moe_config& c, int T) {
   Workspace* w = ws_of(*wsp);
   if (!w) {
@@ -1189,7 +1246,7 @@ moe_status prefill_reserve(void** wsp, const moe_config& c, int T) {
   if (hipDeviceSynchronize() != hipSuccess) return MOE_EHIP;
   const size_t P = (size_t)T * k, rows = P + T;
   const int nchunk = (int)((P + CHUNK - 1) / CHUNK);
-  const int max_tiles = (int)((P + BM - 1) / BM) + E + (T + BM - 1) / BM;
+  const int max_tiles = max_tiles_for(c, T);
   w->T = 0;  // invalid until every buffer is in place
   const bool ok = grow(w->logits, (size_t)T * (E + 1)) && grow(w->xscale, (size_t)T) && grow(w->xp, (size_t)T * H) &&
                   grow(w->cnt, (size_t)nchunk * E) && grow(w->chunk_off, (size_t)nchunk * E) &&
