@@ -22,6 +22,11 @@ hipEvent pair that the launch fills with the kernel's own begin/end
 timestamps; the dominant kernel's average duration and its algorithmic bytes
 (or flops) give the roofline entry. The CPU oracle is timed
 on a bounded sample of the same workload, single-threaded.
+
+The default run (decode80b) also measures the batched path on prefill80b (a
+2048-token batch of the same layer shape) and reports its grouped GEMMs
+against the fp16 matrix-core peak under extra.prefill, so one run carries
+both halves of the headline metric.
 """
 from __future__ import annotations
 
@@ -41,7 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+FP16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 (and bf16) MFMA, TFLOP/s
 
 
 def log(msg: str) -> None:
@@ -51,28 +56,30 @@ def log(msg: str) -> None:
 # ------------------------------------------------------- algorithmic bytes ---
 
 def decode_kernel_bytes(cfg, stack: bool) -> dict:
-    """Bytes each decode kernel must move per launch (one token, one layer).
+    """Bytes of the method each decode kernel moves per launch (one token, one
+    layer), and the scratch it moves on top: {kernel: (algorithmic, scratch)}.
 
-    Fused path (expert + reduce): the expert kernel reads the k + 1 records
-    (gate, up, down codes and scales), x and the logits, and writes one fp32
-    partial row of H per (slot, I slice); reduce reads those rows and writes
-    out (a stack also reads the residual and writes the bf16 recast).
-    Two-kernel path (gateup + down, for shapes the fused kernel does not take).
+    Algorithmic bytes are what the step itself must read or write: the router
+    rows, the k + 1 expert records, x, the logits, out (and for a stack the
+    residual and the bf16 recast). Scratch is the fused path's partial rows,
+    fp32 [(k + 1) * I / 32][H], written by the expert kernel and read back by
+    reduce: an artefact of splitting the down projection over blocks, so it is
+    reported beside the roofline, never in it.
     """
     H, I, E, k, b = cfg.hidden, cfg.inter, cfg.n_experts, cfg.top_k, cfg.bits
     codes = I * H * b // 8          # one matrix
     sc = I * H // 64 * 4
-    router = (E + 1) * H * 4 + E * 4 + H * 2 + (E + 1) * 4
+    rec = 3 * (codes + sc)
+    logits = (E + 1) * 4
     parts = (k + 1) * (I // 32) * H * 4
-    expert = (k + 1) * 3 * (codes + sc) + H * 2 + (E + 1) * 4 + parts
-    reduce = parts + H * 4
-    gateup = (k + 1) * 2 * (codes + sc) + H * 2 + (E + 1) * 4 + (k + 1) * I * 4
-    down = (k + 1) * (codes + sc) + (k + 1) * I * 4 + (k + 1) * 4 + H * 4
-    if stack:
-        reduce += H * 4 + H * 2     # residual read + bf16 recast write
-        down += H * 4 + H * 2
-    return {"router": router, "expert": expert, "reduce": reduce, "gateup": gateup, "down": down,
-            "topk": (E + 1) * 4 + 2 * k * 4}
+    glue = (H * 4 + H * 2) if stack else 0     # residual read + bf16 recast write
+    return {
+        "router": ((E + 1) * H * 4 + E * 4 + H * 2 + logits, 0),
+        "expert": ((k + 1) * rec + H * 2 + logits, parts),
+        "reduce": (H * 4 + glue, parts),
+        "gateup": ((k + 1) * 2 * (codes + sc) + H * 2 + logits, (k + 1) * I * 4),
+        "down": ((k + 1) * (codes + sc) + (k + 1) * 4 + H * 4 + glue, (k + 1) * I * 4),
+    }
 
 
 def step_bytes_per_token(cfg) -> int:
@@ -120,7 +127,18 @@ def cpu_baseline(cfg, xb, budget_s: float) -> dict:
         sample = f"first {done} of {xb.shape[0]} tokens through all {cfg.n_layers} layers"
     dt = time.perf_counter() - t0
     return {"value": unit_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle", "sample": sample,
-            "seconds": round(dt, 2)}
+            "seconds": round(dt, 2), "cpu_model": cpu_model(), "host_cores": os.cpu_count()}
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (lscpu's, from /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 # ------------------------------------------------------------------ traffic ---
@@ -177,6 +195,131 @@ def link_probe(torch, chunk: int, n: int = 512) -> float:
 
 # -------------------------------------------------------------------- main ---
 
+def kernel_pass(model, step, n_prof, torch) -> dict:
+    """Per-kernel launch count and total ms over n_prof instrumented steps."""
+    model.profile_enable(True)
+    for _ in range(n_prof):
+        step()
+    torch.cuda.synchronize()
+    prof = model.profile_read()
+    model.profile_enable(False)
+    return {k: v for k, v in prof.items() if v[0] > 0}
+
+
+def kernel_table(prof: dict) -> dict:
+    total = max(1e-9, sum(p[1] for p in prof.values()))
+    return {k: {"launches": v[0], "avg_us": round(1000.0 * v[1] / v[0], 3), "share": round(v[1] / total, 3)}
+            for k, v in prof.items()}
+
+
+def gemm_roofline(cfg, T, prof) -> tuple:
+    """Roofline of the grouped GEMMs (fp16 matrix cores) from the kernel pass:
+    the dominant one, and both, each as algorithmic flops / average duration."""
+    fl = prefill_flops(cfg, T)
+    gemms = {k: v for k, v in prof.items() if k in fl}
+    if not gemms:
+        return None, {}
+    per = {}
+    for k, v in gemms.items():
+        avg_s = v[1] / v[0] / 1000.0
+        ach = fl[k] / avg_s / 1e12
+        per[k] = {"flops_per_launch": fl[k], "avg_us": round(avg_s * 1e6, 3), "achieved_TFLOPs": round(ach, 1),
+                  "frac": round(ach / FP16_MFMA_PEAK_TFLOPS, 4)}
+    both_s = sum(gemms[k][1] / gemms[k][0] / 1000.0 for k in gemms)
+    both = sum(fl[k] for k in gemms) / both_s / 1e12
+    per["both"] = {"avg_us": round(both_s * 1e6, 3), "achieved_TFLOPs": round(both, 1),
+                   "frac": round(both / FP16_MFMA_PEAK_TFLOPS, 4)}
+    dom = max(gemms, key=lambda k: gemms[k][1])
+    ach = per[dom]["achieved_TFLOPs"]
+    roof = {"bound": "mfma", "kernel": dom, "achieved": ach, "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": per[dom]["frac"], "traffic": measured_traffic(dom, cfg.name),
+            "flops_per_launch": fl[dom], "avg_launch_us": per[dom]["avg_us"]}
+    return roof, per
+
+
+def measure(cfg, args, torch, moe, loader, synth, steps: int, warmup: int, kernels: bool) -> dict:
+    """Load the workload, run warmup + timed steps, then the instrumented pass."""
+    T = cfg.n_tokens
+    log(f"workload {cfg.name}: {cfg.description}")
+    t0 = time.perf_counter()
+    storage = moe.STORE_HOST if cfg.pool_budget else moe.STORE_DEVICE
+    model = loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage)
+    log(f"model loaded in {time.perf_counter() - t0:.1f}s")
+    pool = moe.Pool(model, cfg.pool_budget) if cfg.pool_budget else None
+    xb = synth.tokens(cfg.seed, T, cfg.hidden)
+    x = torch.from_numpy(xb.view(np.int16)).cuda()
+    out = torch.empty((T, cfg.hidden), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    prefill = cfg.name.startswith("prefill")
+
+    if prefill:
+        def step():
+            model.layer_forward(0, x, out, stream=stream)
+    elif cfg.n_layers == 1:
+        def step():
+            model.layer_decode(0, x, out, stream=stream)
+    else:
+        def step():
+            if pool is not None:
+                pool.reset()
+            model.stack_decode(x, out, pool=pool, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup done ({warmup} steps)")
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"timed {steps} steps in {elapsed:.3f}s")
+    res = {"tok_s": steps * T / elapsed, "ms_step": 1000.0 * elapsed / steps, "xb": xb, "extra": {},
+           "roofline": None}
+    extra = res["extra"]
+    if pool is not None:
+        st = pool.stats()  # counts of the last timed step (the pool is reset at every step)
+        extra["pool"] = {**st, "hit_rate": round(st["hits"] / max(1, st["accesses"]), 4),
+                         "h2d_GBps": round(st["h2d_bytes"] / (elapsed / steps) / 1e9, 2),
+                         "link_probe_GBps": link_probe(torch, moe.expert_bytes(cfg))}
+    if args.copy_calibration > 0:
+        n = args.copy_calibration // 4
+        src_t = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst_t = torch.empty_like(src_t)
+        torch.cuda.synchronize()
+        dst_t.copy_(src_t)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {4 * n} bytes")
+        del src_t, dst_t
+    if kernels:
+        n_prof = max(1, min(steps, 5 if cfg.n_layers == 1 else 1))
+        prof = kernel_pass(model, step, n_prof, torch)
+        extra["kernels"] = kernel_table(prof)
+        log(f"kernel pass: {extra['kernels']}")
+        if prefill:
+            res["roofline"], extra["gemms"] = gemm_roofline(cfg, T, prof)
+        else:
+            by = decode_kernel_bytes(cfg, stack=cfg.n_layers > 1)
+            cands = {k: v for k, v in prof.items() if k in by}
+            dom = max(cands, key=lambda k: cands[k][1])
+            avg_s = cands[dom][1] / cands[dom][0] / 1000.0
+            alg, scratch = by[dom]
+            ach = alg / avg_s / 1e9
+            res["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                               "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                               "traffic": measured_traffic(dom, cfg.name),
+                               "bytes_per_launch": alg, "scratch_bytes_per_launch": scratch,
+                               "avg_launch_us": round(avg_s * 1e6, 3)}
+            per_tok = step_bytes_per_token(cfg) * cfg.n_layers
+            extra["whole_step"] = {"bytes_per_token": per_tok,
+                                   "GBps": round(per_tok * res["tok_s"] / 1e9, 1),
+                                   "frac_of_hbm_peak": round(per_tok * res["tok_s"] / 1e9 / HBM_PEAK_GBS, 4)}
+    if pool is not None:
+        pool.close()
+    model.close()
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -187,6 +330,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-pass", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="skip the prefill80b measurement that the default decode80b run adds under extra.prefill")
     ap.add_argument("--pool-gb", type=float, default=None,
                     help="HBM pool budget in GiB for the pooled workload (default: the workload's 2 GiB)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -212,117 +357,41 @@ def main() -> int:
             print(f"--pool-gb applies to a pooled workload; {cfg.name} keeps every expert resident", file=sys.stderr)
             return 2
         cfg = cfg.replace(pool_budget=int(args.pool_gb * (1 << 30)))
-    T = cfg.n_tokens
     if args.steps is None:
         args.steps = 20 if cfg.n_layers == 1 else (2 if cfg.pool_budget else 3)
     if args.warmup is None:
         args.warmup = 3 if cfg.n_layers == 1 else 1
-    log(f"workload {cfg.name}: {cfg.description}")
-    t0 = time.perf_counter()
-    storage = moe.STORE_HOST if cfg.pool_budget else moe.STORE_DEVICE
-    model = loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage)
-    log(f"model loaded in {time.perf_counter() - t0:.1f}s")
-    pool = moe.Pool(model, cfg.pool_budget) if cfg.pool_budget else None
-    xb = synth.tokens(cfg.seed, T, cfg.hidden)
-    x = torch.from_numpy(xb.view(np.int16)).cuda()
-    out = torch.empty((T, cfg.hidden), dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
+    r = measure(cfg, args, torch, moe, loader, synth, args.steps, args.warmup, not args.no_kernel_pass)
+    extra = r["extra"]
+    prefill = cfg.name.startswith("prefill")
 
-    if cfg.name.startswith("prefill"):
-        def step():
-            model.layer_forward(0, x, out, stream=stream)
-    elif cfg.n_layers == 1:
-        def step():
-            model.layer_decode(0, x, out, stream=stream)
-    else:
-        def step():
-            if pool is not None:
-                pool.reset()
-            model.stack_decode(x, out, pool=pool, stream=stream)
-
-    for i in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    log(f"warmup done ({args.warmup} steps)")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    log(f"timed {args.steps} steps in {elapsed:.3f}s")
-    tok_s = args.steps * T / elapsed
-    ms_step = 1000.0 * elapsed / args.steps
-
-    extra = {}
-    if pool is not None:
-        st = pool.stats()  # counts of the last timed step (the pool is reset at every step)
-        extra["pool"] = {**st, "hit_rate": round(st["hits"] / max(1, st["accesses"]), 4),
-                         "h2d_GBps": round(st["h2d_bytes"] / (elapsed / args.steps) / 1e9, 2),
-                         "link_probe_GBps": link_probe(torch, moe.expert_bytes(cfg))}
-    if args.copy_calibration > 0:
-        n = args.copy_calibration // 4
-        src_t = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst_t = torch.empty_like(src_t)
-        torch.cuda.synchronize()
-        dst_t.copy_(src_t)
-        torch.cuda.synchronize()
-        log(f"copy calibration: {4 * n} bytes")
-        del src_t, dst_t
-    roofline = None
-    if not args.no_kernel_pass:
-        n_prof = max(1, min(args.steps, 5 if cfg.n_layers == 1 else 1))
-        model.profile_enable(True)
-        for i in range(n_prof):
-            step()
-        torch.cuda.synchronize()
-        prof = model.profile_read()
-        model.profile_enable(False)
-        prof = {k: v for k, v in prof.items() if v[0] > 0}
-        extra["kernels"] = {k: {"launches": v[0], "avg_us": round(1000.0 * v[1] / v[0], 3),
-                                "share": round(v[1] / max(1e-9, sum(p[1] for p in prof.values())), 3)}
-                            for k, v in prof.items()}
-        log(f"kernel pass: {extra['kernels']}")
-        if cfg.name.startswith("prefill"):
-            fl = prefill_flops(cfg, T)
-            gemms = {k: v for k, v in prof.items() if k in fl}
-            if gemms:
-                dom = max(gemms, key=lambda k: gemms[k][1])
-                avg_s = gemms[dom][1] / gemms[dom][0] / 1000.0
-                ach = fl[dom] / avg_s / 1e12
-                roofline = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 2),
-                            "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                            "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4),
-                            "traffic": measured_traffic(dom, cfg.name)}
-        else:
-            by = decode_kernel_bytes(cfg, stack=cfg.n_layers > 1)
-            cands = {k: v for k, v in prof.items() if k in by}
-            dom = max(cands, key=lambda k: cands[k][1])
-            avg_s = cands[dom][1] / cands[dom][0] / 1000.0
-            ach = by[dom] / avg_s / 1e9
-            roofline = {"bound": "hbm", "kernel": dom, "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
-                        "traffic": measured_traffic(dom, cfg.name),
-                        "bytes_per_launch": by[dom], "avg_launch_us": round(avg_s * 1e6, 3)}
-            per_tok = step_bytes_per_token(cfg) * cfg.n_layers
-            extra["whole_step"] = {"bytes_per_token": per_tok,
-                                   "GBps": round(per_tok * tok_s / 1e9, 1),
-                                   "frac_of_hbm_peak": round(per_tok * tok_s / 1e9 / HBM_PEAK_GBS, 4)}
+    if cfg.name == "decode80b" and not args.no_prefill:
+        pcfg = synth.get_config("prefill80b")
+        p = measure(pcfg, args, torch, moe, loader, synth, max(args.steps // 2, 1), args.warmup,
+                    not args.no_kernel_pass)
+        extra["prefill"] = {"workload": pcfg.name, "value": round(p["tok_s"], 1), "unit": "tokens/s",
+                            "ms_per_step": round(p["ms_step"], 4), "dtype": "fp16",
+                            "tokens_per_step": pcfg.n_tokens, "roofline": p["roofline"],
+                            "gemms": p["extra"].get("gemms"), "kernels": p["extra"].get("kernels")}
 
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(cfg, xb, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, r["xb"], args.cpu_seconds)
         log(f"oracle: {cpu}")
 
-    dtype = "bf16" if cfg.name.startswith("prefill") else "f32"
+    # the arithmetic the path computes in: the decode kernels work in fp32 on
+    # exact integer codes; the batched path's grouped GEMMs run fp16 MFMA
+    dtype = "fp16" if prefill else "f32"
+    T = cfg.n_tokens
     line = {
         "metric": "MoE decode tok/s & % HBM roofline (80B-shape, bs=1); prefill % MFMA peak",
-        "value": round(tok_s, 1),
+        "value": round(r["tok_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(r["ms_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -330,9 +399,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": cfg.name, "hidden": cfg.hidden, "experts": cfg.n_experts, "top_k": cfg.top_k,
                    "inter": cfg.inter, "bits": cfg.bits, "group": cfg.group, "layers": cfg.n_layers,
-                   "tokens_per_step": T, "batch": T if cfg.name.startswith("prefill") else 1,
+                   "tokens_per_step": T, "batch": T if prefill else 1,
                    "pool_budget": cfg.pool_budget},
-        "roofline": roofline,
+        "roofline": r["roofline"],
         "cpu_baseline": cpu,
         "extra": extra,
     }
