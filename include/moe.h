@@ -102,10 +102,15 @@ typedef struct moe_pool moe_pool;
 /* Bytes of one packed record with intermediate size `inter`
  * (3*H*inter*bits/8 + 3*(H*inter/64)*4), or 0 if the config is invalid.
  * Pass inter = cfg->inter for routed experts, cfg->shared_inter for the
- * shared expert. */
+ * shared expert. This is the pages' expertSize, the bytes one read fetches
+ * (paotong.dev commentary, paragraph on the fetch path; alphalab.site field
+ * test, section on SSD reads, where 480 such reads come to about 810 MiB). */
 size_t moe_expert_bytes(const moe_config* cfg, int32_t inter);
 
-/* round_up(moe_expert_bytes(cfg, inter), 4096), or 0 if invalid. */
+/* round_up(moe_expert_bytes(cfg, inter), 4096), or 0 if invalid: the pages'
+ * expertStride, the fixed distance between records in the repacked blob
+ * (paotong.dev commentary, paragraph on the fetch path; cheshm.ai article,
+ * paragraph on how it works). */
 size_t moe_expert_stride(const moe_config* cfg, int32_t inter);
 
 /* base + gid * stride in 64-bit arithmetic (the 48-layer 80B blob exceeds
@@ -170,7 +175,12 @@ void moe_model_destroy(moe_model* m); /* NULL is a no-op; waits for the device *
 /* --------------------------------------------------------------- forward ---*/
 
 /* One MoE layer on n_tok tokens: out[t] = sum_j w[t,j] * expert_{idx[t,j]}(x_t)
- * + sigmoid(x_t . g_s) * shared(x_t), every token independent.
+ * + sigmoid(x_t . g_s) * shared(x_t), every token independent. (Top-k routing
+ * per layer and the resident shared expert: cheshm.ai article, paragraph on
+ * how it works; paotong.dev commentary, paragraphs on the principle and the
+ * resident set. Renormalised top-k weights: alphalab.site field test, section
+ * on the 35B correctness fix. The pages' runtime has no batched prefill,
+ * alphalab.site FAQ on long prompts; the batched path is this library's.)
  * x: dev bf16 bit patterns [n_tok][H]; out: dev fp32 [n_tok][H]; stream: the
  * stream to run on. Batches of fewer than 8 tokens use the decode GEMV
  * kernels token by token; larger batches of int4 layers with H % 256 == 0
@@ -187,11 +197,17 @@ moe_status moe_layer_forward(moe_model* m, int32_t layer, const uint16_t* x, int
 /* Batch-1 decode of one layer over n_tok tokens processed strictly one after
  * another (each token's router -> top-k -> expert GEMV -> combine chain
  * completes before the next token starts). Same arguments and result as
- * moe_layer_forward; always the GEMV path. */
+ * moe_layer_forward; always the GEMV path. (The pages' decode loop handles one
+ * token at a time: alphalab.site field test, method section and FAQ on
+ * token-by-token processing; paotong.dev commentary, paragraph on the bounded
+ * pool, on the loop being dispatch-bound.) */
 moe_status moe_layer_decode(moe_model* m, int32_t layer, const uint16_t* x, int32_t n_tok, float* out,
                             void* stream);
 
-/* Batch-1 decode of the whole L-layer stack, tokens one at a time:
+/* Batch-1 decode of the whole L-layer stack, tokens one at a time (the 48
+ * layers and 480 expert fetches per token: alphalab.site field test, sections
+ * on MoE expert streaming and on SSD reads; the on-demand fetch into a bounded
+ * pool: paotong.dev commentary, paragraphs on the fetch path and the pool):
  * r_0 = x0; x_l = bf16_rne(r_l); r_{l+1} = r_l + layer_l(x_l); out = r_L.
  * pool == NULL: every expert must be resident (MOE_STORE_DEVICE).
  * pool != NULL: experts are served from the pool; on each (token, layer) the
@@ -225,9 +241,10 @@ moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, in
 moe_status moe_layer_forward_noalloc(moe_model* m, int32_t layer, const uint16_t* x, int32_t n_tok, float* out,
                                      void* stream);
 
-/* Routing of the most recent forward/decode call: for each step (token-major,
- * then layer) the k selected experts in selection order (logit descending,
- * lower index first on ties) and their weights. Copies min(cap, steps) steps
+/* Test support, not a step of the method. Routing of the most recent
+ * forward/decode call: for each step (token-major, then layer) the k selected
+ * experts in selection order (logit descending, lower index first on ties)
+ * and their weights. Copies min(cap, steps) steps
  * into idx (int32 [cap][k]) and w (fp32 [cap][k]) on the host; *n_steps
  * receives the number of steps recorded. Synchronises the device. */
 moe_status moe_debug_routing(moe_model* m, int32_t* idx, float* w, size_t cap, size_t* n_steps);
@@ -249,16 +266,22 @@ moe_status moe_pool_create(moe_model* m, size_t budget_bytes, moe_pool** out);
 /* Empty every slot and zero the statistics and trace. */
 moe_status moe_pool_reset(moe_pool* p);
 
+/* Counters since creation/reset: lookups, hits, misses, evictions, and the
+ * bytes copied vs requested (the pages report 43-70% hit rates and ~810 MiB
+ * of logical reads per token with no hit: paotong.dev commentary, paragraph
+ * on the bounded pool; alphalab.site field test, section on SSD reads). */
 moe_status moe_pool_stats(const moe_pool* p, moe_pool_stats_t* out);
 
 /* Per-access trace since creation/reset, in access order: hit[i] = 1/0 and
  * victim[i] = evicted gid or -1. Copies min(cap, n) entries; *n receives the
- * total count. Either output pointer may be NULL. */
+ * total count. Either output pointer may be NULL. (The LFU + recency policy it
+ * records: paotong.dev commentary, paragraph on the bounded pool; cheshm.ai
+ * article, paragraph on how it works.) */
 moe_status moe_pool_trace(const moe_pool* p, uint8_t* hit, int64_t* victim, size_t cap, size_t* n);
 
 void moe_pool_destroy(moe_pool* p); /* NULL is a no-op */
 
-/* Host-only replay of the pool policy: n_slots slots, n_steps steps of k
+/* Test support: host-only replay of the pool policy: n_slots slots, n_steps steps of k
  * gids each (gids [n_steps][k], visited in ascending order within a step).
  * Writes hit [n_steps*k] and victim [n_steps*k]. No GPU involved. */
 moe_status moe_pool_simulate(int64_t n_slots, int32_t k, int64_t n_steps, const int64_t* gids, uint8_t* hit,
@@ -269,11 +292,13 @@ moe_status moe_pool_simulate(int64_t n_slots, int32_t k, int64_t n_steps, const 
 typedef struct {
   char name[32];      /* kernel family: "router", "route", "gateup", "down", "prefill_*" */
   uint64_t launches;  /* launches recorded */
-  double total_ms;    /* sum of per-launch durations (hipEvent pairs around each launch) */
+  double total_ms;    /* sum of per-launch durations (each kernel's own begin/end timestamps) */
 } moe_kernel_time_t;
 
-/* enable = 1: from now on record a hipEvent pair on the launch stream around
- * every kernel this model launches (adds two event records per launch);
+/* Measurement support, not a step of the method. enable = 1: from now on
+ * every kernel this model launches takes a hipEvent pair that the launch
+ * fills with the kernel's own begin and end timestamps (hipExtLaunchKernel),
+ * and decode sequences run as ordinary launches instead of replayed graphs;
  * enable = 0: stop recording. Errors: MOE_EINVAL, MOE_ESTATE. */
 moe_status moe_profile_enable(moe_model* m, int32_t enable);
 
