@@ -243,7 +243,24 @@ def measure(cfg, args, torch, moe, loader, synth, steps: int, warmup: int, kerne
     log(f"workload {cfg.name}: {cfg.description}")
     t0 = time.perf_counter()
     storage = moe.STORE_HOST if cfg.pool_budget else moe.STORE_DEVICE
-    model = loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage)
+    blob_path = None
+    if cfg.pool_budget and args.storage == "file":
+        storage = moe.STORE_FILE
+        blob_path = os.path.join(args.blob_dir, f"{cfg.name}.qblob")
+        size = cfg.n_layers * cfg.n_experts * moe.expert_stride(cfg)
+        if args.keep_blob and os.path.exists(blob_path) and os.path.getsize(blob_path) == size:
+            log(f"reusing the blob file {blob_path}")
+            model = moe.Model(cfg, moe.STORE_FILE)
+            loader.fill_dense(model, synth.SynthWeights(cfg))
+            with open(blob_path, "rb") as f:   # cold start, as after writing it
+                os.posix_fadvise(f.fileno(), 0, 0, os.POSIX_FADV_DONTNEED)
+            model.open_blob(blob_path, 0, not args.buffered)
+        else:
+            log(f"writing the blob file {blob_path} ({size} bytes)")
+            model = loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage, blob_path=blob_path,
+                                      direct=not args.buffered)
+    else:
+        model = loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage)
     log(f"model loaded in {time.perf_counter() - t0:.1f}s")
     pool = moe.Pool(model, cfg.pool_budget) if cfg.pool_budget else None
     xb = synth.tokens(cfg.seed, T, cfg.hidden)
@@ -281,6 +298,7 @@ def measure(cfg, args, torch, moe, loader, synth, steps: int, warmup: int, kerne
         st = pool.stats()  # counts of the last timed step (the pool is reset at every step)
         extra["pool"] = {**st, "hit_rate": round(st["hits"] / max(1, st["accesses"]), 4),
                          "h2d_GBps": round(st["h2d_bytes"] / (elapsed / steps) / 1e9, 2),
+                         "storage_GBps": round(st["storage_bytes"] / (elapsed / steps) / 1e9, 2),
                          "link_probe_GBps": link_probe(torch, moe.expert_bytes(cfg))}
     if args.copy_calibration > 0:
         n = args.copy_calibration // 4
@@ -317,6 +335,8 @@ def measure(cfg, args, torch, moe, loader, synth, steps: int, warmup: int, kerne
     if pool is not None:
         pool.close()
     model.close()
+    if blob_path and not args.keep_blob:
+        os.remove(blob_path)
     return res
 
 
@@ -334,6 +354,18 @@ def main() -> int:
                     help="skip the prefill80b measurement that the default decode80b run adds under extra.prefill")
     ap.add_argument("--pool-gb", type=float, default=None,
                     help="HBM pool budget in GiB for the pooled workload (default: the workload's 2 GiB)")
+    ap.add_argument("--storage", choices=("host", "file"), default="host",
+                    help="pooled workload: misses come from the pinned host blob (default) or from a blob file "
+                         "read with pread (O_DIRECT unless --buffered)")
+    ap.add_argument("--blob-dir", default=os.environ.get("TMPDIR", "/tmp"),
+                    help="directory for the blob file of --storage file (deleted afterwards)")
+    ap.add_argument("--buffered", action="store_true", help="--storage file: read through the page cache")
+    ap.add_argument("--keep-blob", action="store_true",
+                    help="--storage file: keep the blob file afterwards, and reuse one of the right size "
+                         "(evicted from the page cache first) instead of writing it again")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="tokens per step instead of the workload's own count (for sweeps of the slow "
+                         "storage-backed path; the reported config says so)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="after the timed steps, copy BYTES of device memory once with a plain copy "
                          "kernel (a known-size reference for rocprofv3 FETCH_SIZE / WRITE_SIZE)")
@@ -357,6 +389,8 @@ def main() -> int:
             print(f"--pool-gb applies to a pooled workload; {cfg.name} keeps every expert resident", file=sys.stderr)
             return 2
         cfg = cfg.replace(pool_budget=int(args.pool_gb * (1 << 30)))
+    if args.tokens is not None:
+        cfg = cfg.replace(n_tokens=args.tokens)
     if args.steps is None:
         args.steps = 20 if cfg.n_layers == 1 else (2 if cfg.pool_budget else 3)
     if args.warmup is None:
@@ -400,7 +434,9 @@ def main() -> int:
         "config": {"workload": cfg.name, "hidden": cfg.hidden, "experts": cfg.n_experts, "top_k": cfg.top_k,
                    "inter": cfg.inter, "bits": cfg.bits, "group": cfg.group, "layers": cfg.n_layers,
                    "tokens_per_step": T, "batch": T if prefill else 1,
-                   "pool_budget": cfg.pool_budget},
+                   "pool_budget": cfg.pool_budget,
+                   "expert_storage": (args.storage + ("-buffered" if args.buffered else "")) if cfg.pool_budget
+                   else "hbm"},
         "roofline": r["roofline"],
         "cpu_baseline": cpu,
         "extra": extra,

@@ -79,6 +79,9 @@ typedef struct {
   uint64_t evictions;
   uint64_t h2d_bytes;       /* misses * record bytes copied host -> HBM */
   uint64_t requested_bytes; /* accesses * record bytes (logical reads) */
+  uint64_t storage_reads;   /* file-backed model: records read from the blob file */
+  uint64_t storage_bytes;   /* bytes those reads took from storage (whole strides for direct I/O) */
+  uint64_t direct_io;       /* 1 when the blob file bypasses the page cache (O_DIRECT) */
 } moe_pool_stats_t;
 
 typedef struct moe_model moe_model;
@@ -141,11 +144,14 @@ moe_status moe_unpack(const moe_config* cfg, int32_t inter, const void* record, 
 
 /* ----------------------------------------------------------------- model ---*/
 
-enum { MOE_STORE_DEVICE = 0, MOE_STORE_HOST = 1 };
+enum { MOE_STORE_DEVICE = 0, MOE_STORE_HOST = 1, MOE_STORE_FILE = 2 };
+enum { MOE_FILE_DIRECT = 1 };
 
 /* Create a model on the current HIP device. Allocates the routed-expert
  * store (L*E records at the routed stride): in HBM for MOE_STORE_DEVICE, in
- * pinned host memory for MOE_STORE_HOST (the backing blob of a pool), plus
+ * pinned host memory for MOE_STORE_HOST (the backing blob of a pool), or
+ * none for MOE_STORE_FILE (the records stay in a blob file on storage, opened
+ * with moe_model_open_blob and served through a pool), plus
  * HBM for the resident dense part (routers, router biases, shared experts,
  * shared gates) and per-call scratch. Contents start zeroed/unset; fill them
  * with moe_model_set_layer and moe_model_set_experts (or write records
@@ -169,6 +175,23 @@ moe_status moe_model_set_experts(moe_model* m, int64_t first_gid, int64_t n, con
 /* For MOE_STORE_HOST models: the pinned host blob (L*E*stride bytes) that
  * backs the pool; the caller may pack records straight into it. */
 moe_status moe_model_host_blob(moe_model* m, void** ptr, size_t* bytes);
+
+/* For MOE_STORE_FILE models: open the blob file at `path` read-only. Record
+ * gid is the moe_expert_bytes(cfg, inter) bytes at file offset base + gid *
+ * stride; the file must hold base + L*E*stride bytes. A pool of this model
+ * serves each miss with one pread of the record from the file into a pinned
+ * staging buffer (the misses of a step read in parallel on up to 8 worker
+ * threads) followed by the host->device copy into the slot (paotong.dev
+ * commentary, paragraph on the fetch path: one pread of expertSize at
+ * blobBase + expertIndex * expertStride; alphalab.site field test, section on
+ * SSD reads: plain open() reads are served by the page cache when they hit).
+ * flags = MOE_FILE_DIRECT asks for O_DIRECT, which bypasses the page cache
+ * when the filesystem supports it and base is a multiple of 4096 (each read
+ * then covers the whole stride); otherwise, or with flags = 0, reads are
+ * buffered. moe_pool_stats reports which. The file is closed by
+ * moe_model_destroy or by opening another. Errors: MOE_EINVAL (NULL path,
+ * unknown flags, missing or short file), MOE_ESTATE (not a file-backed model). */
+moe_status moe_model_open_blob(moe_model* m, const char* path, uint64_t base, int32_t flags);
 
 void moe_model_destroy(moe_model* m); /* NULL is a no-op; waits for the device */
 
@@ -251,7 +274,9 @@ moe_status moe_debug_routing(moe_model* m, int32_t* idx, float* w, size_t cap, s
 
 /* ------------------------------------------------------------------ pool ---*/
 
-/* Bounded HBM expert pool for a MOE_STORE_HOST model: slots =
+/* Bounded HBM expert pool for a MOE_STORE_HOST model, or a MOE_STORE_FILE
+ * model whose blob file is open (which adds k pinned staging buffers of one
+ * stride each and the read workers): slots =
  * floor(budget_bytes / stride), allocated in HBM, starting empty (filled
  * lazily). LFU + recency: a hit bumps the slot's use count and last-use tick;
  * a miss takes the lowest empty slot, else evicts the slot with the smallest
@@ -266,10 +291,11 @@ moe_status moe_pool_create(moe_model* m, size_t budget_bytes, moe_pool** out);
 /* Empty every slot and zero the statistics and trace. */
 moe_status moe_pool_reset(moe_pool* p);
 
-/* Counters since creation/reset: lookups, hits, misses, evictions, and the
+/* Counters since creation/reset: lookups, hits, misses, evictions, the
  * bytes copied vs requested (the pages report 43-70% hit rates and ~810 MiB
  * of logical reads per token with no hit: paotong.dev commentary, paragraph
- * on the bounded pool; alphalab.site field test, section on SSD reads). */
+ * on the bounded pool; alphalab.site field test, section on SSD reads), and
+ * for a file-backed model the reads taken from the blob file. */
 moe_status moe_pool_stats(const moe_pool* p, moe_pool_stats_t* out);
 
 /* Per-access trace since creation/reset, in access order: hit[i] = 1/0 and

@@ -11,7 +11,9 @@ from ._lib import (  # noqa: F401
     MOE_ENOMEM,
     MOE_ESTATE,
     MOE_OK,
+    FILE_DIRECT,
     STORE_DEVICE,
+    STORE_FILE,
     STORE_HOST,
     Config,
     Model,

@@ -17,13 +17,14 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ESTATE = 0, -1, -2, -3, -4
-STORE_DEVICE, STORE_HOST = 0, 1
+STORE_DEVICE, STORE_HOST, STORE_FILE = 0, 1, 2
+FILE_DIRECT = 1
 _STATUS_NAMES = {MOE_EINVAL: "MOE_EINVAL", MOE_ENOMEM: "MOE_ENOMEM", MOE_EHIP: "MOE_EHIP", MOE_ESTATE: "MOE_ESTATE"}
 
 # every symbol moe.h declares
 EXPORTS = [
     "moe_expert_bytes", "moe_expert_stride", "moe_blob_offset", "moe_pack", "moe_unpack",
-    "moe_model_create", "moe_model_set_layer", "moe_model_set_experts", "moe_model_host_blob",
+    "moe_model_create", "moe_model_set_layer", "moe_model_set_experts", "moe_model_host_blob", "moe_model_open_blob",
     "moe_model_destroy", "moe_layer_forward", "moe_layer_decode", "moe_stack_decode",
     "moe_layer_forward_noalloc", "moe_debug_routing",
     "moe_pool_create", "moe_pool_reset", "moe_pool_stats", "moe_pool_trace", "moe_pool_destroy",
@@ -48,7 +49,8 @@ class KernelTime(ctypes.Structure):
 
 class PoolStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in
-                ("accesses", "hits", "misses", "evictions", "h2d_bytes", "requested_bytes")]
+                ("accesses", "hits", "misses", "evictions", "h2d_bytes", "requested_bytes",
+                 "storage_reads", "storage_bytes", "direct_io")]
 
     def as_dict(self):
         return {n: int(getattr(self, n)) for n, _ in self._fields_}
@@ -83,6 +85,7 @@ def lib() -> ctypes.CDLL:
             "moe_model_set_layer": (I32, [P, I32, P, P, P, P]),
             "moe_model_set_experts": (I32, [P, I64, I64, P]),
             "moe_model_host_blob": (I32, [P, ctypes.POINTER(P), ctypes.POINTER(SZ)]),
+            "moe_model_open_blob": (I32, [P, ctypes.c_char_p, U64, I32]),
             "moe_model_destroy": (None, [P]),
             "moe_layer_forward": (I32, [P, I32, P, I32, P, P]),
             "moe_layer_decode": (I32, [P, I32, P, I32, P, P]),
@@ -269,6 +272,10 @@ class Model:
         n = ctypes.c_size_t()
         _check(lib().moe_model_host_blob(self._h, ctypes.byref(p), ctypes.byref(n)))
         return np.ctypeslib.as_array((ctypes.c_uint8 * n.value).from_address(p.value))
+
+    def open_blob(self, path: str, base: int = 0, direct: bool = True):
+        """File-backed model: read records from the blob file at `path` (O_DIRECT when allowed)."""
+        _check(lib().moe_model_open_blob(self._h, os.fsencode(path), base, FILE_DIRECT if direct else 0))
 
     def layer_forward(self, layer: int, x, out, n_tok: Optional[int] = None, stream=None):
         n = x.shape[0] if n_tok is None else n_tok

@@ -2,7 +2,7 @@
 
 Usage: python -m routed_expert_int4_router_amd.build   (or build() from Python)
 
-Host-only C++ (packer, pool policy) is compiled with g++ and strict IEEE
+Host-only C++ (packer, pool policy, blob-file reader) is compiled with g++ and strict IEEE
 float semantics (no FMA contraction); the HIP sources and the ABI layer with
 hipcc for gfx950. Objects go to _build/ at the repository root, the library
 next to this file.
@@ -26,7 +26,7 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
-HOST_SOURCES = ["pack.cpp", "pool_policy.cpp"]
+HOST_SOURCES = ["pack.cpp", "pool_policy.cpp", "blob_file.cpp"]
 HIP_SOURCES = ["abi.cpp", "decode.hip", "prefill.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}"]

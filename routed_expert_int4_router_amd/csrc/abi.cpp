@@ -13,12 +13,14 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <set>
 #include <string>
 #include <vector>
 
+#include "blob_file.h"
 #include "common.h"
 #include "kernels.h"
 #include "launch.h"
@@ -155,8 +157,9 @@ struct moe_model {
   int device = 0;
   Geometry geo{};
   size_t rec_bytes = 0, stride = 0, shared_stride = 0;
-  uint8_t* experts = nullptr;       // device (STORE_DEVICE) or pinned host (STORE_HOST)
-  size_t experts_bytes = 0;
+  uint8_t* experts = nullptr;       // device (STORE_DEVICE) or pinned host (STORE_HOST); NULL for STORE_FILE
+  size_t experts_bytes = 0;         // L * E * stride: the store, or the file's blob region
+  BlobFile file;                    // STORE_FILE: the blob file
   uint8_t* shared = nullptr;        // device [L] records
   float* wr_rows = nullptr;         // device [L][E+1][H]
   uint16_t* wr_split = nullptr;     // device [L][3][E+1][H] bf16: wr_rows = hi + mid + lo exactly
@@ -202,6 +205,13 @@ struct moe_pool {
   hipEvent_t route_ready = nullptr;
   int32_t* host_route = nullptr;    // pinned, mapped [k]
   int32_t* host_route_dev = nullptr;
+  // storage-backed misses (STORE_FILE): pinned staging buffers, one per miss
+  // of a step (k of them, stride bytes each), filled by pread on the read
+  // workers, then copied to the slot like a host-blob miss
+  uint8_t* staging = nullptr;
+  uint8_t* bounce = nullptr;        // direct I/O: k ordinary 4096-aligned buffers the reads land in first
+  ReadWorkers* readers = nullptr;
+  uint64_t storage_reads = 0, storage_bytes = 0;
 };
 
 namespace {
@@ -325,7 +335,7 @@ moe_status check_forward_args(moe_model* m, int32_t layer, const void* x, int32_
   if (n_tok < 0 || n_tok > 65536) return fail(MOE_EINVAL, std::string(fn) + ": n_tok must be in [0, 65536]");
   if (n_tok > 0 && (!x || !out)) return fail(MOE_EINVAL, std::string(fn) + ": NULL pointer");
   if (m->storage != MOE_STORE_DEVICE)
-    return fail(MOE_ESTATE, std::string(fn) + ": experts are in host storage; use moe_stack_decode with a pool");
+    return fail(MOE_ESTATE, std::string(fn) + ": experts are in host or file storage; use moe_stack_decode with a pool");
   if (n_tok > 0 && !m->layer_set[(size_t)layer])
     return fail(MOE_ESTATE, std::string(fn) + ": moe_model_set_layer was not called for this layer");
   return MOE_OK;
@@ -422,6 +432,53 @@ moe_status scratch_on_current_device(uint8_t** out) {
   return MOE_OK;
 }
 
+// Misses of one step from the blob file: one pread per missing record into
+// its pinned staging buffer (all of them in flight on the read workers), and
+// each record's host->device copy into its slot issued as soon as its read
+// has landed. A direct (O_DIRECT) file reads whole strides: record offsets
+// and strides are multiples of 4096.
+moe_status read_misses(moe_model* m, moe_pool* pool, const int64_t* gids, const int64_t* slots, const uint8_t* miss,
+                       ExpertSource& src, int* n_miss) {
+  const int k = m->cfg.top_k;
+  std::vector<uint64_t> off;
+  std::vector<void*> dst, bounce;
+  std::vector<size_t> bytes;
+  std::vector<int> which;
+  const size_t len = m->file.direct() ? m->stride : m->rec_bytes;
+  for (int j = 0; j < k; ++j) {
+    src.table[j] = slots[j];
+    if (!miss[j]) continue;
+    off.push_back((uint64_t)gids[j] * m->stride);
+    dst.push_back(pool->staging + which.size() * m->stride);
+    if (pool->bounce) bounce.push_back(pool->bounce + which.size() * m->stride);
+    bytes.push_back(len);
+    which.push_back(j);
+  }
+  *n_miss = (int)which.size();
+  if (which.empty()) return MOE_OK;
+  // the staging buffers were last read by the previous step's copies
+  for (int c = 0; c < moe_pool::kCopyStreams; ++c)
+    HIP_TRY(hipEventSynchronize(pool->copies_done[c]), "staging reuse wait");
+  pool->readers->start(&m->file, off, dst, bytes, bounce);
+  for (size_t i = 0; i < which.size(); ++i) {
+    std::string err;
+    if (!pool->readers->wait(i, &err)) {
+      pool->readers->drain();
+      return fail(MOE_EHIP, "moe_stack_decode: expert read from the blob file failed: " + err);
+    }
+    const int c = (int)(i % moe_pool::kCopyStreams);
+    const hipError_t e = hipMemcpyAsync(pool->arena + (size_t)slots[which[i]] * m->stride, dst[i], m->rec_bytes,
+                                        hipMemcpyHostToDevice, pool->copy_stream[c]);
+    if (e != hipSuccess) {
+      pool->readers->drain();
+      return hip_fail(e, "miss copy");
+    }
+  }
+  pool->storage_reads += which.size();
+  pool->storage_bytes += which.size() * len;
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -432,8 +489,8 @@ moe_status moe_model_create(const moe_config* cfg, int32_t storage, moe_model** 
   *out = nullptr;
   std::string why = check_config(cfg);
   if (!why.empty()) return fail(MOE_EINVAL, "moe_model_create: " + why);
-  if (storage != MOE_STORE_DEVICE && storage != MOE_STORE_HOST)
-    return fail(MOE_EINVAL, "moe_model_create: storage must be MOE_STORE_DEVICE or MOE_STORE_HOST");
+  if (storage != MOE_STORE_DEVICE && storage != MOE_STORE_HOST && storage != MOE_STORE_FILE)
+    return fail(MOE_EINVAL, "moe_model_create: storage must be MOE_STORE_DEVICE, MOE_STORE_HOST or MOE_STORE_FILE");
   Geometry g{};
   g.H = cfg->hidden;
   g.I = cfg->inter;
@@ -468,10 +525,10 @@ moe_status moe_model_create(const moe_config* cfg, int32_t storage, moe_model** 
     e = hipMalloc(&m->experts, m->experts_bytes);
     ok = ok && e == hipSuccess;
     if (ok) ok = hipMemset(m->experts, 0, m->experts_bytes) == hipSuccess;
-  } else {
+  } else if (storage == MOE_STORE_HOST) {
     e = hipHostMalloc(&m->experts, m->experts_bytes, hipHostMallocDefault);
     ok = ok && e == hipSuccess;
-  }
+  }  // MOE_STORE_FILE: the records stay in the blob file (moe_model_open_blob)
   ok = ok && hipMalloc(&m->shared, L * m->shared_stride) == hipSuccess;
   ok = ok && hipMalloc(&m->wr_rows, L * (E + 1) * H * sizeof(float)) == hipSuccess;
   ok = ok && hipMalloc(&m->wr_split, L * 3 * (E + 1) * H * sizeof(uint16_t)) == hipSuccess;
@@ -559,6 +616,8 @@ moe_status moe_model_set_experts(moe_model* m, int64_t first_gid, int64_t n, con
     return fail(MOE_EINVAL, "moe_model_set_experts: gid range outside [0, L*E)");
   if (n == 0) return MOE_OK;
   if (!records) return fail(MOE_EINVAL, "moe_model_set_experts: records is NULL");
+  if (m->storage == MOE_STORE_FILE)
+    return fail(MOE_ESTATE, "moe_model_set_experts: a file-backed model reads its records from the blob file");
   uint8_t* dst = m->experts + (size_t)first_gid * m->stride;
   const size_t bytes = (size_t)n * m->stride;
   if (m->storage == MOE_STORE_DEVICE) {
@@ -580,9 +639,24 @@ moe_status moe_model_host_blob(moe_model* m, void** ptr, size_t* bytes) {
   return MOE_OK;
 }
 
+moe_status moe_model_open_blob(moe_model* m, const char* path, uint64_t base, int32_t flags) {
+  clear_error();
+  moe_status st = check_model(m, "moe_model_open_blob");
+  if (st) return st;
+  if (!path) return fail(MOE_EINVAL, "moe_model_open_blob: path is NULL");
+  if (flags != 0 && flags != MOE_FILE_DIRECT) return fail(MOE_EINVAL, "moe_model_open_blob: unknown flags");
+  if (m->storage != MOE_STORE_FILE)
+    return fail(MOE_ESTATE, "moe_model_open_blob: the model was not created with MOE_STORE_FILE");
+  std::string err;
+  if (!m->file.open(path, base, m->experts_bytes, flags == MOE_FILE_DIRECT, &err))
+    return fail(MOE_EINVAL, "moe_model_open_blob: " + err);
+  return MOE_OK;
+}
+
 void moe_model_destroy(moe_model* m) {
   if (!m || !live_has(m) || m->magic != kModelMagic) return;
   hipDeviceSynchronize();
+  m->file.close();
   if (m->storage == MOE_STORE_HOST) hipHostFree(m->experts);
   else hipFree(m->experts);
   hipFree(m->shared);
@@ -742,7 +816,7 @@ moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, in
     if (st) return st;
     if (pool->model != m) return fail(MOE_ESTATE, "moe_stack_decode: pool belongs to another model");
   } else if (m->storage != MOE_STORE_DEVICE) {
-    return fail(MOE_ESTATE, "moe_stack_decode: experts are in host storage; a pool is required");
+    return fail(MOE_ESTATE, "moe_stack_decode: experts are in host or file storage; a pool is required");
   }
   for (int l = 0; l < m->cfg.n_layers; ++l)
     if (!m->layer_set[(size_t)l]) return fail(MOE_ESTATE, "moe_stack_decode: a layer was not set");
@@ -792,14 +866,19 @@ moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, in
       // Victim slots are free to overwrite: the host waited for this layer's
       // route, recorded after every earlier kernel on the stream.
       int n_miss = 0;
-      for (int j = 0; j < k; ++j) {
-        src.table[j] = slots[(size_t)j];
-        if (miss[(size_t)j]) {
-          const int c = n_miss++ % moe_pool::kCopyStreams;
-          HIP_TRY(hipMemcpyAsync(pool->arena + (size_t)slots[(size_t)j] * m->stride,
-                                 m->experts + (size_t)gids[(size_t)j] * m->stride, m->rec_bytes,
-                                 hipMemcpyHostToDevice, pool->copy_stream[c]),
-                  "miss copy");
+      if (m->storage == MOE_STORE_FILE) {
+        st = read_misses(m, pool, gids.data(), slots.data(), miss.data(), src, &n_miss);
+        if (st) return st;
+      } else {
+        for (int j = 0; j < k; ++j) {
+          src.table[j] = slots[(size_t)j];
+          if (miss[(size_t)j]) {
+            const int c = n_miss++ % moe_pool::kCopyStreams;
+            HIP_TRY(hipMemcpyAsync(pool->arena + (size_t)slots[(size_t)j] * m->stride,
+                                   m->experts + (size_t)gids[(size_t)j] * m->stride, m->rec_bytes,
+                                   hipMemcpyHostToDevice, pool->copy_stream[c]),
+                    "miss copy");
+          }
         }
       }
       for (int c = 0; c < moe_pool::kCopyStreams && c < n_miss; ++c) {
@@ -864,7 +943,9 @@ moe_status moe_pool_create(moe_model* m, size_t budget_bytes, moe_pool** out) {
   *out = nullptr;
   moe_status st = check_model(m, "moe_pool_create");
   if (st) return st;
-  if (m->storage != MOE_STORE_HOST) return fail(MOE_ESTATE, "moe_pool_create: the model keeps its experts in HBM");
+  if (m->storage == MOE_STORE_DEVICE) return fail(MOE_ESTATE, "moe_pool_create: the model keeps its experts in HBM");
+  if (m->storage == MOE_STORE_FILE && !m->file.is_open())
+    return fail(MOE_ESTATE, "moe_pool_create: open the blob file first (moe_model_open_blob)");
   const int64_t slots = (int64_t)(budget_bytes / m->stride);
   if (slots < m->cfg.top_k)
     return fail(MOE_EINVAL, "moe_pool_create: budget holds " + std::to_string(slots) + " slots, fewer than top_k");
@@ -880,6 +961,18 @@ moe_status moe_pool_create(moe_model* m, size_t budget_bytes, moe_pool** out) {
   ok = ok && hipEventCreateWithFlags(&p->route_ready, hipEventDisableTiming) == hipSuccess;
   ok = ok && hipHostMalloc(&p->host_route, kMaxTopK * sizeof(int32_t), hipHostMallocMapped | hipHostMallocCoherent) == hipSuccess;
   ok = ok && hipHostGetDevicePointer((void**)&p->host_route_dev, p->host_route, 0) == hipSuccess;
+  if (ok && m->storage == MOE_STORE_FILE) {
+    ok = hipHostMalloc(&p->staging, (size_t)m->cfg.top_k * m->stride, hipHostMallocDefault) == hipSuccess;
+    if (ok && m->file.direct()) {
+      void* b = nullptr;
+      ok = posix_memalign(&b, kDirectAlign, (size_t)m->cfg.top_k * m->stride) == 0;
+      p->bounce = static_cast<uint8_t*>(b);
+    }
+    // completed events, so the first step's staging wait returns at once
+    for (int c = 0; ok && c < moe_pool::kCopyStreams; ++c)
+      ok = hipEventRecord(p->copies_done[c], p->copy_stream[c]) == hipSuccess;
+    if (ok) p->readers = new ReadWorkers(std::min(m->cfg.top_k, 8));
+  }
   live_add(p);
   if (!ok) {
     moe_pool_destroy(p);
@@ -894,6 +987,7 @@ moe_status moe_pool_reset(moe_pool* p) {
   moe_status st = check_pool(p, "moe_pool_reset");
   if (st) return st;
   p->table.reset();
+  p->storage_reads = p->storage_bytes = 0;
   return MOE_OK;
 }
 
@@ -908,6 +1002,9 @@ moe_status moe_pool_stats(const moe_pool* p, moe_pool_stats_t* out) {
   out->evictions = p->table.evictions;
   out->h2d_bytes = p->table.misses * (uint64_t)p->model->rec_bytes;
   out->requested_bytes = p->table.accesses * (uint64_t)p->model->rec_bytes;
+  out->storage_reads = p->storage_reads;
+  out->storage_bytes = p->storage_bytes;
+  out->direct_io = p->model->storage == MOE_STORE_FILE && p->model->file.direct() ? 1 : 0;
   return MOE_OK;
 }
 
@@ -933,6 +1030,9 @@ void moe_pool_destroy(moe_pool* p) {
   }
   if (p->route_ready) hipEventDestroy(p->route_ready);
   if (p->host_route) hipHostFree(p->host_route);
+  delete p->readers;
+  if (p->staging) hipHostFree(p->staging);
+  free(p->bounce);
   p->magic = 0;
   live_del(p);
   delete p;

@@ -8,10 +8,13 @@
     shared_gate(layer) -> [H] fp32
 Experts are produced by a thread pool and packed in chunks, so host memory
 stays bounded (a chunk of fp32 weights, not the whole model). For a
-host-storage model the records are packed straight into the pinned blob.
+host-storage model the records are packed straight into the pinned blob; for
+a file-backed model they are written, in gid order at the stride, into a
+blob file that the model then reads its misses from.
 """
 from __future__ import annotations
 
+import os
 from concurrent.futures import ThreadPoolExecutor
 from typing import Optional
 
@@ -21,18 +24,49 @@ from . import _lib
 
 
 def load_model(cfg, weights, storage: int = _lib.STORE_DEVICE, threads: int = 16, chunk: int = 64,
-               layers: Optional[range] = None) -> _lib.Model:
+               layers: Optional[range] = None, blob_path: Optional[str] = None, direct: bool = True) -> _lib.Model:
+    """A model filled from ``weights``. A file-backed model (STORE_FILE) needs
+    ``blob_path``: the records are written there (replacing the file) and the
+    model opens it, with O_DIRECT when ``direct`` and the filesystem allow."""
     c = _lib.config_of(cfg)
+    if storage == _lib.STORE_FILE and not blob_path:
+        raise ValueError("a file-backed model needs blob_path")
     model = _lib.Model(c, storage)
     try:
-        fill_model(model, weights, threads=threads, chunk=chunk, layers=layers)
+        if storage == _lib.STORE_FILE:
+            with open(blob_path, "wb") as f:
+                fill_model(model, weights, threads=threads, chunk=chunk, layers=layers, blob_file=f)
+                # on storage and out of the page cache: the first read of every
+                # record comes from the device, buffered or not
+                f.flush()
+                os.fsync(f.fileno())
+                if hasattr(os, "posix_fadvise"):
+                    os.posix_fadvise(f.fileno(), 0, 0, os.POSIX_FADV_DONTNEED)
+            model.open_blob(blob_path, 0, direct)
+        else:
+            fill_model(model, weights, threads=threads, chunk=chunk, layers=layers)
     except Exception:
         model.close()
         raise
     return model
 
 
-def fill_model(model: _lib.Model, weights, threads: int = 16, chunk: int = 64, layers: Optional[range] = None):
+def fill_dense(model: _lib.Model, weights, layers: Optional[range] = None):
+    """Upload only the resident dense part of each layer: router, bias, shared
+    expert and shared gate (for a file-backed model whose blob file exists)."""
+    c = model.cfg
+    for layer in (range(c.n_layers) if layers is None else layers):
+        wg_s, wu_s, wd_s = weights.shared(layer)
+        shared_rec = _lib.pack(c, wg_s, wu_s, wd_s, inter=c.shared_inter)
+        model.set_layer(layer, weights.router(layer), weights.bias(layer), shared_rec, weights.shared_gate(layer))
+    return model
+
+
+def fill_model(model: _lib.Model, weights, threads: int = 16, chunk: int = 64, layers: Optional[range] = None,
+               blob_file=None):
+    """Upload the dense weights and pack the experts: into the pinned blob
+    (host storage), into a writable binary ``blob_file`` at gid * stride (file
+    storage), or into HBM (device storage)."""
     c = model.cfg
     H, I, E = c.hidden, c.inter, c.n_experts
     stride = _lib.expert_stride(c)
@@ -57,6 +91,9 @@ def fill_model(model: _lib.Model, weights, threads: int = 16, chunk: int = 64, l
                 gid = layer * E + e0
                 if blob is not None:
                     _lib.pack(c, wg, wu, wd, out=blob[gid * stride:(gid + n) * stride])
+                elif blob_file is not None:
+                    blob_file.seek(gid * stride)
+                    blob_file.write(_lib.pack(c, wg, wu, wd).tobytes())
                 else:
                     model.set_experts(gid, _lib.pack(c, wg, wu, wd))
     return model
