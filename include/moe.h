@@ -313,6 +313,26 @@ void moe_pool_destroy(moe_pool* p); /* NULL is a no-op */
 moe_status moe_pool_simulate(int64_t n_slots, int32_t k, int64_t n_steps, const int64_t* gids, uint8_t* hit,
                              int64_t* victim);
 
+/* ------------------------------------------------------ kernel variants ---*/
+
+enum { MOE_KERNELS_FAST = 0, MOE_KERNELS_SCALAR = 1 };
+
+/* Select the kernels the model's later forward and decode calls run.
+ * MOE_KERNELS_SCALAR swaps in plainly written variants of the decode expert
+ * kernel (route, gate/up + SwiGLU, weighted partial down rows: one thread per
+ * value) and of the two grouped GEMMs of the batched path (one wave per
+ * output tile, operands read from global memory right before each MFMA), which
+ * repeat the fast kernels' arithmetic operation for operation and so give
+ * bit-identical outputs, much more slowly: a reference on the GPU itself for
+ * debugging the fast kernels (the pages' runtime keeps fast and scalar
+ * kernels whose outputs must agree exactly: paotong.dev commentary,
+ * paragraph on the test fixtures). The router, bucketing, reduce and combine
+ * kernels are shared. A decode call on scalar kernels needs hidden <= 2048
+ * (else MOE_EINVAL from that call) and resident experts (a pooled
+ * moe_stack_decode returns MOE_EINVAL). Errors: MOE_EINVAL (unknown kernels),
+ * MOE_ESTATE. */
+moe_status moe_model_set_kernels(moe_model* m, int32_t kernels);
+
 /* ------------------------------------------------------------- profiling ---*/
 
 typedef struct {

@@ -12,6 +12,8 @@ from ._lib import (  # noqa: F401
     MOE_ESTATE,
     MOE_OK,
     FILE_DIRECT,
+    KERNELS_FAST,
+    KERNELS_SCALAR,
     STORE_DEVICE,
     STORE_FILE,
     STORE_HOST,

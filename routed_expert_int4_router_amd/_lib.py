@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libmoe.so")
 
 MOE_OK, MOE_EINVAL, MOE_ENOMEM, MOE_EHIP, MOE_ESTATE = 0, -1, -2, -3, -4
 STORE_DEVICE, STORE_HOST, STORE_FILE = 0, 1, 2
+KERNELS_FAST, KERNELS_SCALAR = 0, 1
 FILE_DIRECT = 1
 _STATUS_NAMES = {MOE_EINVAL: "MOE_EINVAL", MOE_ENOMEM: "MOE_ENOMEM", MOE_EHIP: "MOE_EHIP", MOE_ESTATE: "MOE_ESTATE"}
 
@@ -28,7 +29,7 @@ EXPORTS = [
     "moe_model_destroy", "moe_layer_forward", "moe_layer_decode", "moe_stack_decode",
     "moe_layer_forward_noalloc", "moe_debug_routing",
     "moe_pool_create", "moe_pool_reset", "moe_pool_stats", "moe_pool_trace", "moe_pool_destroy",
-    "moe_pool_simulate", "moe_profile_enable", "moe_profile_read", "moe_last_error",
+    "moe_pool_simulate", "moe_model_set_kernels", "moe_profile_enable", "moe_profile_read", "moe_last_error",
 ]
 
 
@@ -98,6 +99,7 @@ def lib() -> ctypes.CDLL:
             "moe_pool_trace": (I32, [P, P, P, SZ, ctypes.POINTER(SZ)]),
             "moe_pool_destroy": (None, [P]),
             "moe_pool_simulate": (I32, [I64, I32, I64, P, P, P]),
+            "moe_model_set_kernels": (I32, [P, I32]),
             "moe_profile_enable": (I32, [P, I32]),
             "moe_profile_read": (I32, [P, ctypes.POINTER(KernelTime), SZ, ctypes.POINTER(SZ)]),
             "moe_last_error": (ctypes.c_char_p, []),
@@ -297,6 +299,10 @@ class Model:
         _check_io(x0, out, n, self.cfg.hidden)
         _check(lib().moe_stack_decode(self._h, None if pool is None else pool.handle, _ptr(x0), n, _ptr(out),
                                       _stream(stream)))
+
+    def set_kernels(self, kernels: int):
+        """KERNELS_FAST, or KERNELS_SCALAR: the plainly written, bit-identical variants."""
+        _check(lib().moe_model_set_kernels(self._h, kernels))
 
     def profile_enable(self, enable: bool = True):
         _check(lib().moe_profile_enable(self._h, 1 if enable else 0))

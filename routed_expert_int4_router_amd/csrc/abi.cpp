@@ -26,6 +26,7 @@
 #include "launch.h"
 #include "pool_policy.h"
 #include "prefill.h"
+#include "scalar.h"
 
 using namespace moe;
 
@@ -166,6 +167,8 @@ struct moe_model {
   float* bias = nullptr;            // device [L][E]
   float* logits = nullptr;          // device [E+1]
   float* h = nullptr;               // device [(k+1)][I]
+  float* h_scalar = nullptr;        // device [(k+1)][I]: h of the scalar expert kernels
+  int32_t kernels = MOE_KERNELS_FAST;
   float* rbuf = nullptr;            // device [H]
   uint16_t* xbuf = nullptr;         // device [2][H]
   int32_t* route_idx = nullptr;     // device [route_cap][k]
@@ -303,9 +306,20 @@ const float* layer_bias(moe_model* m, int layer) { return m->bias + (size_t)laye
 const uint8_t* layer_shared(moe_model* m, int layer) { return m->shared + (size_t)layer * m->shared_stride; }
 
 // The expert kernels of one token-layer (after routing): fused expert +
-// reduce where the shape allows, else gate/up + down.
+// reduce where the shape allows, else gate/up + down; with the scalar kernels
+// selected, their plainly written equivalent + reduce.
 moe_status expert_steps(moe_model* m, int layer, const StepBuffers& b, const ExpertSource& src,
                         const ResidualArgs& r, hipStream_t s) {
+  if (m->kernels == MOE_KERNELS_SCALAR) {
+    // three launches, so outside the per-launch profiler
+    if (!fused_expert_supported(m->geo))
+      return fail(MOE_EINVAL, "scalar decode kernels need hidden <= 2048 (the fused path's shapes)");
+    HIP_TRY(launch_expert_scalar(m->geo, m->experts, m->stride, src.gid_base, layer_shared(m, layer), b, m->h_scalar,
+                                 s),
+            "scalar expert launch");
+    HIP_TRY(m->prof.run(K_REDUCE, s, [&] { return launch_reduce(m->geo, b, r, s); }), "reduce launch");
+    return MOE_OK;
+  }
   if (fused_expert_supported(m->geo)) {
     HIP_TRY(m->prof.run(K_EXPERT, s, [&] { return launch_expert(m->geo, src, layer_shared(m, layer), b, s); }),
             "expert launch");
@@ -540,6 +554,7 @@ moe_status moe_model_create(const moe_config* cfg, int32_t storage, moe_model** 
     const size_t n_h = slots * cfg->inter;
     const size_t n_part = slots * ((size_t)cfg->inter / 32) * cfg->hidden;  // 32-row I slices
     ok = ok && hipMalloc(&m->h, std::max(n_h, n_part) * sizeof(float)) == hipSuccess;
+    ok = ok && hipMalloc(&m->h_scalar, n_h * sizeof(float)) == hipSuccess;
   }
   ok = ok && hipMalloc(&m->rbuf, H * sizeof(float)) == hipSuccess;
   ok = ok && hipMalloc(&m->xbuf, 2 * H * sizeof(uint16_t)) == hipSuccess;
@@ -665,6 +680,7 @@ void moe_model_destroy(moe_model* m) {
   hipFree(m->bias);
   hipFree(m->logits);
   hipFree(m->h);
+  hipFree(m->h_scalar);
   hipFree(m->rbuf);
   hipFree(m->xbuf);
   hipFree(m->route_idx);
@@ -702,7 +718,8 @@ moe_status moe_layer_decode(moe_model* m, int32_t layer, const uint16_t* x, int3
     }
     return MOE_OK;
   };
-  st = (n_tok >= kGraphMinTokens && !m->prof.on) ? run_graph(m, 1, layer, x, out, n_tok, s, enqueue) : enqueue(s);
+  st = (n_tok >= kGraphMinTokens && !m->prof.on) ? run_graph(m, 1 + m->kernels, layer, x, out, n_tok, s, enqueue)
+                                                   : enqueue(s);
   if (st) return st;
   m->route_steps = (size_t)n_tok;
   return MOE_OK;
@@ -742,6 +759,7 @@ moe_status moe_layer_forward(moe_model* m, int32_t layer, const uint16_t* x, int
     a.route_idx = m->route_idx;
     a.route_w = m->route_w;
     a.route_gamma = m->route_gamma;
+    a.scalar = m->kernels == MOE_KERNELS_SCALAR;
     st = prefill_reserve(&m->prefill, m->cfg, n_tok);
     if (st) return fail(st, "moe_layer_forward: prefill workspace allocation failed");
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -796,6 +814,7 @@ moe_status moe_layer_forward_noalloc(moe_model* m, int32_t layer, const uint16_t
   a.x = x;
   a.n_tok = n_tok;
   a.out = out;
+  a.scalar = m->kernels == MOE_KERNELS_SCALAR;
   hipStream_t s = static_cast<hipStream_t>(stream);
   using Stage = hipError_t (*)(void*, const PrefillArgs&, hipStream_t);
   static const Stage kStages[] = {prefill_xprep, prefill_router,  prefill_route,  prefill_count,  prefill_scan,
@@ -815,6 +834,8 @@ moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, in
     st = check_pool(pool, "moe_stack_decode");
     if (st) return st;
     if (pool->model != m) return fail(MOE_ESTATE, "moe_stack_decode: pool belongs to another model");
+    if (m->kernels != MOE_KERNELS_FAST)
+      return fail(MOE_EINVAL, "moe_stack_decode: the scalar kernels read resident experts only; no pool");
   } else if (m->storage != MOE_STORE_DEVICE) {
     return fail(MOE_ESTATE, "moe_stack_decode: experts are in host or file storage; a pool is required");
   }
@@ -905,6 +926,16 @@ moe_status moe_debug_routing(moe_model* m, int32_t* idx, float* w, size_t cap, s
   const size_t k = (size_t)m->cfg.top_k;
   if (n && idx) HIP_TRY(hipMemcpy(idx, m->route_idx, n * k * sizeof(int32_t), hipMemcpyDeviceToHost), "copy idx");
   if (n && w) HIP_TRY(hipMemcpy(w, m->route_w, n * k * sizeof(float), hipMemcpyDeviceToHost), "copy w");
+  return MOE_OK;
+}
+
+moe_status moe_model_set_kernels(moe_model* m, int32_t kernels) {
+  clear_error();
+  moe_status st = check_model(m, "moe_model_set_kernels");
+  if (st) return st;
+  if (kernels != MOE_KERNELS_FAST && kernels != MOE_KERNELS_SCALAR)
+    return fail(MOE_EINVAL, "moe_model_set_kernels: kernels must be MOE_KERNELS_FAST or MOE_KERNELS_SCALAR");
+  m->kernels = kernels;
   return MOE_OK;
 }
 

@@ -24,6 +24,7 @@
 
 #include <cstdint>
 
+#include "decode_math.h"
 #include "dpp.h"
 #include "kernels.h"
 #include "launch.h"
@@ -38,54 +39,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_stream(const uint8_t* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
-
-__device__ __forceinline__ uint16_t to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float f16f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
-
-__device__ __forceinline__ float ub0(uint32_t v) { return (float)(v & 0xFFu); }
-__device__ __forceinline__ float ub1(uint32_t v) { return (float)((v >> 8) & 0xFFu); }
-__device__ __forceinline__ float ub2(uint32_t v) { return (float)((v >> 16) & 0xFFu); }
-__device__ __forceinline__ float ub3(uint32_t v) { return (float)(v >> 24); }
-
-// sum over the chunk of code * x; x holds EPC = 128 / BITS consecutive elements.
-template <int BITS>
-__device__ __forceinline__ float chunk_dot(const uint4 c, const float* x) {
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float a0 = 0.f, a1 = 0.f;
-  if constexpr (BITS == 4) {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const uint32_t lo = w[t] & 0x0F0F0F0Fu, hi = (w[t] >> 4) & 0x0F0F0F0Fu;
-      const float* xx = x + 8 * t;
-      a0 = fmaf(ub0(lo), xx[0], a0);
-      a1 = fmaf(ub0(hi), xx[1], a1);
-      a0 = fmaf(ub1(lo), xx[2], a0);
-      a1 = fmaf(ub1(hi), xx[3], a1);
-      a0 = fmaf(ub2(lo), xx[4], a0);
-      a1 = fmaf(ub2(hi), xx[5], a1);
-      a0 = fmaf(ub3(lo), xx[6], a0);
-      a1 = fmaf(ub3(hi), xx[7], a1);
-    }
-  } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const float* xx = x + 4 * t;
-      a0 = fmaf(ub0(w[t]), xx[0], a0);
-      a1 = fmaf(ub1(w[t]), xx[1], a1);
-      a0 = fmaf(ub2(w[t]), xx[2], a0);
-      a1 = fmaf(ub3(w[t]), xx[3], a1);
-    }
-  }
-  return a0 + a1;
 }
 
 template <int LPR>
@@ -263,15 +216,14 @@ __global__ void __launch_bounds__(256) gateup_kernel(Geometry g, ExpertSource sr
     for (int it = 0; it < IT; ++it) {
       const float dg = chunk_dot<BITS>(cg[rr][it], xv[it]);
       const float du = chunk_dot<BITS>(cu[rr][it], xv[it]);
-      ag += f16f(sg[rr][it] & 0xFFFFu) * dg + f16f(sg[rr][it] >> 16) * xs[it];
-      au += f16f(su[rr][it] & 0xFFFFu) * du + f16f(su[rr][it] >> 16) * xs[it];
+      ag += group_term(sg[rr][it], dg, xs[it]);
+      au += group_term(su[rr][it], du, xs[it]);
     }
     ag = group_sum<LPR>(ag);
     au = group_sum<LPR>(au);
     if (c0 == LPR - 1) {
       const int i = row0 + rsub + RPW * rr;
-      const float silu = ag / (1.0f + expf(-ag));
-      b.h[(size_t)j * g.I + i] = silu * au;
+      b.h[(size_t)j * g.I + i] = swiglu(ag, au);
     }
   }
 }
@@ -384,7 +336,7 @@ __global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src,
 #pragma unroll
         for (int rr = 0; rr < R; ++rr) {
           const float d = chunk_dot<BITS>(cd[m][rr][it], hv);
-          const float c = f16f(sd[m][rr][it] & 0xFFFFu) * d + f16f(sd[m][rr][it] >> 16) * hs;
+          const float c = group_term(sd[m][rr][it], d, hs);
           acc[rr] = fmaf(wj, c, acc[rr]);
         }
       }
@@ -545,13 +497,13 @@ __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, E
     for (int it = 0; it < IT; ++it) {
       const float dg = chunk_dot<BITS>(cg[rr][it], xv[it]);
       const float du = chunk_dot<BITS>(cu[rr][it], xv[it]);
-      ag += f16f(sg[rr][it] & 0xFFFFu) * dg + f16f(sg[rr][it] >> 16) * xs[it];
-      au += f16f(su[rr][it] & 0xFFFFu) * du + f16f(su[rr][it] >> 16) * xs[it];
+      ag += group_term(sg[rr][it], dg, xs[it]);
+      au += group_term(su[rr][it], du, xs[it]);
     }
     ag = group_sum<LPR>(ag);
     au = group_sum<LPR>(au);
     const int r = rsub + RPW * rr;
-    if (c0 == LPR - 1 && r < RPWV) sh_h[wv * RPWV + r] = ag / (1.0f + expf(-ag)) * au;
+    if (c0 == LPR - 1 && r < RPWV) sh_h[wv * RPWV + r] = swiglu(ag, au);
   }
   __syncthreads();
 
@@ -575,7 +527,7 @@ __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, E
     float d = 0.f;
 #pragma unroll
     for (int c = 0; c < DCH; ++c) d += chunk_dot<BITS>(cd[q][c], hv + c * EPC);
-    const float v = f16f(sd[q] & 0xFFFFu) * d + f16f(sd[q] >> 16) * hs;
+    const float v = group_term(sd[q], d, hs);
     if (n < g.H) part[n] = wj * v;
   }
 }

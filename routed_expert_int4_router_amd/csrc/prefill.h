@@ -26,6 +26,7 @@ struct PrefillArgs {
   int32_t* route_idx;       // device [n_tok][k]
   float* route_w;           // device [n_tok][k]
   float* route_gamma;       // device [n_tok]
+  int32_t scalar;           // 1: the plainly written grouped GEMMs (bit-identical, slow)
 };
 
 // Device arrays of the batched path for batches of up to T tokens.

@@ -402,6 +402,51 @@ __global__ void __launch_bounds__(CHUNK) bucket_scatter_kernel(const int32_t* __
   wperm[pos] = route_w[p];
 }
 
+// ------------------------------------------------- shared GEMM arithmetic ---
+// Element-wise steps of the grouped GEMMs' epilogues, used by the fast kernels
+// and by their plainly written variants alike.
+
+// h = silu(gate) * up with the hardware exp2 and reciprocal.
+__device__ __forceinline__ float silu_mul(float gt, float up) {
+  return gt * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt)) * up;
+}
+
+// Natural exponent n of a row whose largest |h| is rmax (max |h| / 2^n in
+// [2^14, 2^15)), biased by 256 so exponents order as unsigned integers; 0 for
+// no value (a padding row, or a row of zeros).
+__device__ __forceinline__ uint32_t row_exp_biased(float rmax, bool live) {
+  if (!live || !(rmax > 0.f)) return 0u;
+  int x2;
+  (void)frexpf(rmax, &x2);  // 2^(x2-1) <= rmax < 2^x2
+  return (uint32_t)(x2 - 15 + 256);
+}
+
+// A row's exponent given the tile-group's largest T: T for a row within 2^12
+// of it (its maximum stays >= 4 under 2^T, so only values below 2^-16 of it
+// leave fp16's normal range), else its own (at most 126 below T).
+__device__ __forceinline__ int row_exp(uint32_t nb, int T) {
+  if (nb && (int)nb - 256 < T - 12) return max((int)nb - 256, T - 126);
+  return T;
+}
+
+// 16 consecutive columns of a row as fp16 h / 2^er, each 8-chunk in
+// nib_to_f16 order (0,4,1,5,2,6,3,7) in pk, and the sum of the values the
+// down GEMM multiplies (2^er * fp16) in column order.
+__device__ __forceinline__ float pack16(const float* hv, int er, uint32_t (&pk)[8]) {
+  float sum = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) {
+    const _Float16 hq = (_Float16)ldexpf(hv[cc], -er);
+    sum += ldexpf((float)hq, er);
+    const uint32_t b = __builtin_bit_cast(uint16_t, hq);
+    const int ch = cc >> 3, p = cc & 7;
+    const int w = 4 * ch + (p & 3);  // dword of the pair (p, p + 4)
+    if (p < 4) pk[w] = b;
+    else pk[w] |= b << 16;
+  }
+  return sum;
+}
+
 // ------------------------------------------------------- grouped GEMM 1 ---
 // Block = (tile, 64 columns of I), 4 waves, two blocks per CU: 64 rows of one
 // expert (sorted pairs, or tokens for the shared expert) x 64 gate + 64 up
@@ -714,8 +759,7 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
     for (int j = 0; j < 16; ++j) {
       const int m = (tid >> 6) + 4 * j;
       const float gt = sg[m * SGS + c];
-      sg[m * SGS + c] =
-          gt * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-1.4426950408889634f * gt)) * su[m * SGS + c];
+      sg[m * SGS + c] = silu_mul(gt, su[m * SGS + c]);
     }
   }
   __syncthreads();
@@ -737,14 +781,7 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   }
   rmax = fmaxf(rmax, __uint_as_float(dpp::mov<dpp::kQuadXor1, 0xF>(0u, __float_as_uint(rmax))));
   rmax = fmaxf(rmax, __uint_as_float(dpp::mov<dpp::kQuadXor2, 0xF>(0u, __float_as_uint(rmax))));
-  // exponents biased by 256 so that they order as unsigned integers; 0 = no
-  // value (a padding row, or a row of zeros)
-  uint32_t nb = 0;
-  if (m < nrow && rmax > 0.f) {
-    int x2;
-    (void)frexpf(rmax, &x2);  // 2^(x2-1) <= rmax < 2^x2
-    nb = (uint32_t)(x2 - 15 + 256);
-  }
+  const uint32_t nb = row_exp_biased(rmax, m < nrow);
   __shared__ uint32_t s_tmax[4];
   {
     const uint32_t wm = dpp::wave_max_u32(nb);
@@ -753,23 +790,13 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   __syncthreads();
   const uint32_t tb = max(max(s_tmax[0], s_tmax[1]), max(s_tmax[2], s_tmax[3]));
   const int T = tb ? (int)tb - 256 : 0;
-  int er = T;  // this row's exponent
-  if (nb && (int)nb - 256 < T - 12) er = max((int)nb - 256, T - 126);
+  const int er = row_exp(nb, T);  // this row's exponent
   const bool own = m < nrow && er != T;
-  // h / 2^er in fp16, each 8-chunk in nib_to_f16 order (0,4,1,5,2,6,3,7);
-  // the group sum of the values the down GEMM multiplies, 2^er * fp16
+  // h / 2^er in fp16 and the group sum of the values the down GEMM
+  // multiplies: this thread's 16 columns, then the row's four quarters
+  // combined as (q0 + q1) + (q2 + q3)
   uint32_t pk[8];
-  float sum = 0.f;
-#pragma unroll
-  for (int cc = 0; cc < 16; ++cc) {
-    const _Float16 hq = (_Float16)ldexpf(hv[cc], -er);
-    sum += ldexpf((float)hq, er);
-    const uint32_t b = __builtin_bit_cast(uint16_t, hq);
-    const int ch = cc >> 3, p = cc & 7;
-    const int w = 4 * ch + (p & 3);  // dword of the pair (p, p + 4)
-    if (p < 4) pk[w] = b;
-    else pk[w] |= b << 16;
-  }
+  float sum = pack16(hv, er, pk);
   sum += __uint_as_float(dpp::mov<dpp::kQuadXor1, 0xF>(0u, __float_as_uint(sum)));
   sum += __uint_as_float(dpp::mov<dpp::kQuadXor2, 0xF>(0u, __float_as_uint(sum)));
   const int GI = a.I / 64;
@@ -890,12 +917,12 @@ __device__ __forceinline__ void down_group(const uint8_t* __restrict__ rdH, cons
     const float sv = f16f(sw & 0xFFFFu);
     const float svh = sv * hscale;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[2 * nn][r] += svh * p0[r];
+    for (int r = 0; r < 16; ++r) acc[2 * nn][r] = fmaf(svh, p0[r], acc[2 * nn][r]);
     if constexpr (FULL) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[2 * nn + 1][r] += svh * p1[r];
+      for (int r = 0; r < 16; ++r) acc[2 * nn + 1][r] = fmaf(svh, p1[r], acc[2 * nn + 1][r]);
     }
-    cval[nn] = f16f(sw >> 16) - 16.0f * sv;
+    cval[nn] = fmaf(-16.0f, sv, f16f(sw >> 16));
   }
   if (g & 1) {
     const int gx = g - 1 + hh;
@@ -1064,6 +1091,187 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
         const int m = m0 + 32 * half;
         const int dst = s_dst[m];
         if (dst >= 0) a.y[(size_t)dst * a.H + n] = s_w[m] * acc[2 * nn + half][r];
+      }
+    }
+  }
+}
+
+// ------------------------------------------- plain (scalar) GEMM variants ---
+// The two grouped GEMMs written plainly: one wave per block, no LDS rings, no
+// DMA, no prefetch, every operand read from global memory right before the
+// MFMA that uses it, the fast block's four waves done one after another. For
+// every output tile they issue the fast kernels' MFMAs with the same operands
+// in the same K order and repeat the epilogues' arithmetic (the shared
+// helpers above), so their results equal the fast kernels' bit for bit.
+// Rows past a tile's end hold zeros here and stale values in the fast
+// kernels; neither is ever stored or folded into a kept value. Block b takes
+// tile b / NT, column block b % NT.
+
+// 8 fp16 of a stored row (the k-permuted fp16 x of a token, or a bucketed row
+// of h): chunk c of 64-group g.
+__device__ __forceinline__ f16x8 ld_frag(const uint16_t* rowp, int g, int c) {
+  return *reinterpret_cast<const f16x8*>(rowp + 64 * g + 8 * c);
+}
+
+__global__ void __launch_bounds__(64) gemm_gateup_plain_kernel(GemmArgs a) {
+  __shared__ float sg[BM][GU_BN + 1], su[BM][GU_BN + 1];
+  __shared__ float s_xs[BM];
+  __shared__ int32_t s_tok[BM];
+  __shared__ uint32_t s_nb[BM];
+  const int G = a.H / 64, NT = (a.I + GU_BN - 1) / GU_BN;
+  const int tile = (int)blockIdx.x / NT, nt = (int)blockIdx.x % NT;
+  if (tile >= a.tiles[0]) return;
+  const int4 td = *reinterpret_cast<const int4*>(a.tiles + 4 + 4 * tile);
+  const int e = td.x, r0 = td.y, base = td.z, nrow = td.w;
+  const int n0 = nt * GU_BN;
+  const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
+  const int lane = threadIdx.x, hh = lane >> 5, mrow = lane & 31;
+  {
+    const int tok = lane < nrow ? (e < a.E ? a.perm[base + lane] / a.k : r0 + lane) : -1;
+    s_tok[lane] = tok;
+    s_xs[lane] = tok >= 0 ? a.xscale[tok] : 1.f;
+  }
+  __syncthreads();
+  const int tok0 = s_tok[mrow], tok1 = s_tok[32 + mrow];
+  const NibConst nk = nib_const();
+  for (int wv = 0; wv < 4; ++wv) {
+    const int mat = wv >> 1, nl = 32 * (wv & 1) + mrow;
+    const int n = min(n0 + nl, a.I - 1);
+    const uint8_t* crow = rec + (mat == 0 ? a.gate_codes : a.up_codes) + (size_t)n * (a.H / 2);
+    const uint8_t* srow = rec + (mat == 0 ? a.gate_sc : a.up_sc) + (size_t)n * G * 4;
+    f32x16 acc0 = {}, acc1 = {};
+    for (int g = 0; g < G; ++g) {
+      GroupFrag f;
+      f.codes = *reinterpret_cast<const uint4*>(crow + 32 * g + 16 * hh);
+      f.sc = *reinterpret_cast<const uint32_t*>(srow + 4 * g);
+      for (int st = 0; st < 4; ++st) {
+        f.a0[st] = tok0 >= 0 ? ld_frag(a.xp + (size_t)tok0 * a.H, g, 4 * hh + st) : f16x8{};
+        f.a1[st] = tok1 >= 0 ? ld_frag(a.xp + (size_t)tok1 * a.H, g, 4 * hh + st) : f16x8{};
+      }
+      gateup_dequant(f, nk);
+      gateup_mfma<true>(f, acc0, acc1);
+    }
+    float(*dst)[GU_BN + 1] = mat == 0 ? sg : su;
+    for (int r = 0; r < 16; ++r) {
+      const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
+      dst[m][nl] = acc0[r] * s_xs[m];
+      dst[32 + m][nl] = acc1[r] * s_xs[32 + m];
+    }
+  }
+  __syncthreads();
+  for (int m = 0; m < BM; ++m) sg[m][lane] = silu_mul(sg[m][lane], su[m][lane]);
+  __syncthreads();
+  // thread = row m
+  const int m = lane;
+  float rmax = 0.f;
+  for (int c = 0; c < GU_BN; ++c) rmax = fmaxf(rmax, fabsf(sg[m][c]));
+  s_nb[m] = row_exp_biased(rmax, m < nrow);
+  __syncthreads();
+  uint32_t tb = 0;
+  for (int q = 0; q < BM; ++q) tb = max(tb, s_nb[q]);
+  const int T = tb ? (int)tb - 256 : 0;
+  const int er = row_exp(s_nb[m], T);
+  const int GI = a.I / 64;
+  float part[4];
+  for (int qq = 0; qq < 4; ++qq) {
+    uint32_t pk[8];
+    part[qq] = pack16(&sg[m][16 * qq], er, pk);
+    if (m < nrow) {
+      uint16_t* hd = a.h16 + (size_t)(base + m) * a.I + n0 + 16 * qq;
+      *reinterpret_cast<uint4*>(hd) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      *reinterpret_cast<uint4*>(hd + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    }
+  }
+  if (m < nrow) {
+    a.hsum[(size_t)(base + m) * GI + nt] = (part[0] + part[1]) + (part[2] + part[3]);
+    a.hrowf[(size_t)(base + m) * GI + nt] = ldexpf(1.f, er - T);
+  }
+  const bool own = __ballot(m < nrow && er != T) != 0;
+  if (lane == 0) {
+    const float sc = ldexpf(1.f, T);
+    a.hscale[(size_t)tile * GI + nt] = own ? -sc : sc;
+  }
+}
+
+__global__ void __launch_bounds__(64) gemm_down_plain_kernel(GemmArgs a) {
+  const int GI = a.I / 64, NT = a.H / DN_BN;
+  const int tile = (int)blockIdx.x / NT, nt = (int)blockIdx.x % NT;
+  if (tile >= a.tiles[0]) return;
+  const int4 td = *reinterpret_cast<const int4*>(a.tiles + 4 + 4 * tile);
+  const int e = td.x, r0 = td.y, base = td.z, nrow = td.w;
+  const int n0 = nt * DN_BN;
+  const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
+  const int lane = threadIdx.x, hh = lane >> 5, mrow = lane & 31;
+  // the bucketed rows the fast kernel stages (rows past the end repeat the last)
+  const size_t ra = (size_t)base + min(mrow, nrow - 1), rb = (size_t)base + min(32 + mrow, nrow - 1);
+  const uint16_t* h0 = a.h16 + ra * a.I;
+  const uint16_t* h1 = a.h16 + rb * a.I;
+  const NibConst nk = nib_const();
+  for (int wv = 0; wv < 4; ++wv) {
+    const int brow = 64 * wv + mrow;
+    f32x16 acc[4] = {};
+    float cprev[2] = {0.f, 0.f};
+    for (int g = 0; g < GI; ++g) {
+      const float hscale = fabsf(a.hscale[(size_t)tile * GI + g]);
+      f16x8 ah[2][4];
+      for (int st = 0; st < 4; ++st) {
+        ah[0][st] = ld_frag(h0, g, 4 * hh + st);
+        ah[1][st] = ld_frag(h1, g, 4 * hh + st);
+      }
+      float cval[2];
+      for (int nn = 0; nn < 2; ++nn) {
+        const int n = n0 + brow + 32 * nn;
+        const uint4 cw = *reinterpret_cast<const uint4*>(rec + a.down_codes + ((size_t)(2 * g + hh) * a.H + n) * 16);
+        const uint32_t sw = *reinterpret_cast<const uint32_t*>(rec + a.down_sc + ((size_t)g * a.H + n) * 4);
+        const f16x8 b[4] = {nib_to_f16(cw.x, nk), nib_to_f16(cw.y, nk), nib_to_f16(cw.z, nk), nib_to_f16(cw.w, nk)};
+        f32x16 p0 = {}, p1 = {};
+        for (int st = 0; st < 4; ++st) {
+          p0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[0][st], b[st], p0, 0, 0, 0);
+          p1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[1][st], b[st], p1, 0, 0, 0);
+        }
+        // row factors (1 for every row of a tile-group without own factors)
+        for (int r = 0; r < 16; ++r) {
+          const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
+          p0[r] *= a.hrowf[((size_t)base + min(m, nrow - 1)) * GI + g];
+          p1[r] *= a.hrowf[((size_t)base + min(32 + m, nrow - 1)) * GI + g];
+        }
+        const float sv = f16f(sw & 0xFFFFu);
+        const float svh = sv * hscale;
+        for (int r = 0; r < 16; ++r) acc[2 * nn][r] = fmaf(svh, p0[r], acc[2 * nn][r]);
+        for (int r = 0; r < 16; ++r) acc[2 * nn + 1][r] = fmaf(svh, p1[r], acc[2 * nn + 1][r]);
+        cval[nn] = fmaf(-16.0f, sv, f16f(sw >> 16));
+      }
+      if (g & 1) {
+        const int gx = g - 1 + hh;
+        const float x0 = a.hsum[ra * GI + gx], x1 = a.hsum[rb * GI + gx];
+        for (int nn = 0; nn < 2; ++nn) {
+          const float cp = hh ? cval[nn] : cprev[nn];
+          acc[2 * nn] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, cp, acc[2 * nn], 0, 0, 0);
+          acc[2 * nn + 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, cp, acc[2 * nn + 1], 0, 0, 0);
+        }
+      } else {
+        cprev[0] = cval[0];
+        cprev[1] = cval[1];
+      }
+    }
+    if (GI & 1) {
+      const float x0 = hh ? 0.f : a.hsum[ra * GI + GI - 1], x1 = hh ? 0.f : a.hsum[rb * GI + GI - 1];
+      for (int nn = 0; nn < 2; ++nn) {
+        const float cp = hh ? 0.f : cprev[nn];
+        acc[2 * nn] = __builtin_amdgcn_mfma_f32_32x32x2f32(x0, cp, acc[2 * nn], 0, 0, 0);
+        acc[2 * nn + 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(x1, cp, acc[2 * nn + 1], 0, 0, 0);
+      }
+    }
+    for (int nn = 0; nn < 2; ++nn) {
+      const int n = n0 + brow + 32 * nn;
+      for (int r = 0; r < 16; ++r) {
+        for (int half = 0; half < 2; ++half) {
+          const int m = (r >> 2) * 8 + hh * 4 + (r & 3) + 32 * half;
+          if (m >= nrow) continue;
+          const size_t dst = e < a.E ? (size_t)a.perm[base + m] : (size_t)a.T * a.k + r0 + m;
+          const float w = e < a.E ? a.wperm[base + m] : a.route_gamma[r0 + m];
+          a.y[dst * a.H + n] = w * acc[2 * nn + half][r];
+        }
       }
     }
   }
@@ -1342,6 +1550,11 @@ hipError_t prefill_gateup(void* ws, const PrefillArgs& pa, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_bytes = lds;
   }
+  if (pa.scalar) {
+    const int nt = (pa.cfg.inter + GU_BN - 1) / GU_BN;
+    launch(gemm_gateup_plain_kernel, dim3((unsigned)(w->max_tiles * nt)), dim3(64), 0, s, gemm_args(w, pa));
+    return hipGetLastError();
+  }
   const int nblk = xcd_grid(w->max_tiles, (pa.n_tok + BM - 1) / BM, (pa.cfg.inter + GU_BN - 1) / GU_BN);
   launch(gemm_gateup_kernel, dim3((unsigned)nblk), dim3(256), (uint32_t)lds, s, gemm_args(w, pa));
   return hipGetLastError();
@@ -1356,6 +1569,11 @@ hipError_t prefill_down(void* ws, const PrefillArgs& pa, hipStream_t s) {
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr_bytes = lds;
+  }
+  if (pa.scalar) {
+    launch(gemm_down_plain_kernel, dim3((unsigned)(w->max_tiles * (pa.cfg.hidden / DN_BN))), dim3(64), 0, s,
+           gemm_args(w, pa));
+    return hipGetLastError();
   }
   const int nblk = xcd_grid(w->max_tiles, (pa.n_tok + BM - 1) / BM, pa.cfg.hidden / DN_BN);
   launch(gemm_down_kernel, dim3((unsigned)nblk), dim3(256), (uint32_t)lds, s, gemm_args(w, pa));
