@@ -205,3 +205,64 @@ class SynthWeights:
     def shared_gate(self, layer: int) -> np.ndarray:
         c = self.cfg
         return shared_gate(c.seed, layer, c.hidden)
+
+
+# ------------------------------------------------------------ DeltaNet step ---
+# Seeded inputs of the Gated DeltaNet decode step (the linear-attention layers
+# beside the MoE). Shapes follow the Qwen3-Next-80B linear-attention layer: 16
+# key heads and 32 value heads of dimension 128, a 4-tap causal convolution;
+# the distributions are this project's recipe.
+
+_GDN_CONV, _GDN_ALOG, _GDN_DT, _GDN_NORM, _GDN_QKV, _GDN_Z, _GDN_A, _GDN_B = 20, 21, 22, 23, 24, 25, 26, 27
+
+
+@dataclasses.dataclass(frozen=True)
+class GdnConfig:
+    name: str
+    n_k: int
+    n_v: int
+    d_k: int
+    d_v: int
+    n_layers: int
+    n_tokens: int
+    seed: int = 0
+    description: str = ""
+
+    @property
+    def channels(self) -> int:
+        return 2 * self.n_k * self.d_k + self.n_v * self.d_v
+
+    def replace(self, **kw) -> "GdnConfig":
+        return dataclasses.replace(self, **kw)
+
+
+GDN_CONFIGS: Dict[str, GdnConfig] = {
+    "gdn_tiny": GdnConfig("gdn_tiny", n_k=2, n_v=4, d_k=32, d_v=32, n_layers=2, n_tokens=16,
+                          description="tiny Gated DeltaNet: 2 key / 4 value heads of 32, 2 layers"),
+    "gdn80b": GdnConfig("gdn80b", n_k=16, n_v=32, d_k=128, d_v=128, n_layers=36, n_tokens=256,
+                        description="80B-shaped Gated DeltaNet decode: 36 layers, 16 key / 32 value heads of 128, "
+                                    "256 tokens one at a time"),
+}
+
+
+def get_gdn_config(name: str, **overrides) -> GdnConfig:
+    cfg = GDN_CONFIGS[name]
+    return cfg.replace(**overrides) if overrides else cfg
+
+
+def gdn_params(cfg: GdnConfig, layer: int):
+    """fp32 (conv_w [C][4] ~ N(0, 0.3), A_log = ln U(1, 16) [n_v], dt_bias ~ N(0, 1) [n_v],
+    norm_w ~ 1 + N(0, 0.1) [d_v])."""
+    conv_w = _normal((cfg.channels, 4), cfg.seed, layer, _LAYER_SLOT, _GDN_CONV, std=0.3)
+    a_log = np.log(_rng(cfg.seed, layer, _LAYER_SLOT, _GDN_ALOG).uniform(1.0, 16.0, cfg.n_v)).astype(np.float32)
+    dt_bias = _normal((cfg.n_v,), cfg.seed, layer, _LAYER_SLOT, _GDN_DT, std=1.0)
+    norm_w = (np.float32(1.0) + _normal((cfg.d_v,), cfg.seed, layer, _LAYER_SLOT, _GDN_NORM, std=0.1))
+    return conv_w, a_log, dt_bias, norm_w.astype(np.float32)
+
+
+def gdn_inputs(cfg: GdnConfig, layer: int, n_tokens: int):
+    """bf16 bit patterns ~ N(0, 1): qkv [T][C], z [T][n_v * d_v], a [T][n_v], b [T][n_v]."""
+    def bits(shape, tid):
+        return f32_to_bf16_bits(_normal(shape, cfg.seed, layer, _TOKEN_SLOT, tid, std=1.0))
+    return (bits((n_tokens, cfg.channels), _GDN_QKV), bits((n_tokens, cfg.n_v * cfg.d_v), _GDN_Z),
+            bits((n_tokens, cfg.n_v), _GDN_A), bits((n_tokens, cfg.n_v), _GDN_B))
