@@ -13,6 +13,8 @@ Workloads (synthetic, seeded, weights ~N(0, 0.02) packed to int4/int8 g64):
   pool80b        80B-shaped 48-layer stack, experts in pinned host memory,
                  2 GiB HBM pool, 1024 tokens (host-link bound)
   resident80b    the same 48-layer stack with every expert in HBM
+  gdn80b         the Gated DeltaNet decode step beside the MoE: 36 layers of
+                 16 key / 32 value heads of 128, 256 tokens one at a time
 
 A step is one pass of the workload's tokens through the whole path (router,
 top-k, expert GEMV/GEMM, combine, stack glue, pool). W untimed steps, then K
@@ -340,6 +342,90 @@ def measure(cfg, args, torch, moe, loader, synth, steps: int, warmup: int, kerne
     return res
 
 
+def gdn_step_bytes(cfg) -> int:
+    """Algorithmic bytes of one DeltaNet step kernel (one token, one layer):
+    the fp32 state read and written, the conv history read and written, the
+    conv weights, the bf16 inputs (qkv, z, a, b), the fp32 output and the
+    per-head parameters."""
+    C, Z = cfg.channels, cfg.n_v * cfg.d_v
+    state = cfg.n_v * cfg.d_k * cfg.d_v * 4
+    return 2 * state + 2 * C * 3 * 4 + C * 4 * 4 + C * 2 + Z * 2 + 2 * cfg.n_v * 2 + Z * 4 + 2 * cfg.n_v * 4 + cfg.d_v * 4
+
+
+def measure_gdn(cfg, args, torch, moe, synth, steps: int, warmup: int, kernels: bool) -> dict:
+    """Gated DeltaNet decode: each step takes the workload's tokens one after
+    another through all its layers (token-major), the state carried on."""
+    log(f"workload {cfg.name}: {cfg.description}")
+    net = moe.GatedDeltaNet(cfg.n_layers, cfg.n_k, cfg.n_v, cfg.d_k, cfg.d_v)
+    for l in range(cfg.n_layers):
+        net.set_layer(l, *synth.gdn_params(cfg, l))
+    T, L = cfg.n_tokens, cfg.n_layers
+    per = [synth.gdn_inputs(cfg, l, T) for l in range(L)]
+    dev = [torch.from_numpy(np.ascontiguousarray(np.stack([per[l][i] for l in range(L)], axis=1)).view(np.int16))
+           .cuda() for i in range(4)]
+    out = torch.empty((T, L, cfg.n_v * cfg.d_v), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        net.decode(0, L, dev[0], dev[1], dev[2], dev[3], out, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"timed {steps} steps in {elapsed:.3f}s")
+    res = {"tok_s": steps * T / elapsed, "ms_step": 1000.0 * elapsed / steps, "extra": {}, "roofline": None,
+           "inputs": per}
+    per_launch = gdn_step_bytes(cfg)
+    res["extra"]["whole_step"] = {"bytes_per_token": per_launch * L,
+                                  "GBps": round(per_launch * L * res["tok_s"] / 1e9, 1),
+                                  "frac_of_hbm_peak": round(per_launch * L * res["tok_s"] / 1e9 / HBM_PEAK_GBS, 4)}
+    if kernels:
+        net.profile(True)
+        step()
+        torch.cuda.synchronize()
+        ms, n = net.profile(False)
+        avg_s = ms / n / 1000.0
+        ach = per_launch / avg_s / 1e9
+        res["extra"]["kernels"] = {"gdn_step": {"launches": n, "avg_us": round(avg_s * 1e6, 3), "share": 1.0}}
+        res["roofline"] = {"bound": "hbm", "kernel": "gdn_step", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                           "traffic": measured_traffic("gdn_step", cfg.name),
+                           "bytes_per_launch": per_launch, "avg_launch_us": round(avg_s * 1e6, 3)}
+        log(f"kernel pass: {res['extra']['kernels']}")
+    net.close()
+    return res
+
+
+def cpu_baseline_gdn(cfg, per, budget_s: float) -> dict:
+    """The oracle as it stands, single thread: the first tokens through all layers."""
+    from oracle import deltanet as ognd
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+    import synth
+    sh = ognd.Shape(cfg.n_k, cfg.n_v, cfg.d_k, cfg.d_v)
+    params = [ognd.Params(*synth.gdn_params(cfg, l)) for l in range(cfg.n_layers)]
+    states = [ognd.zero_state(sh) for _ in range(cfg.n_layers)]
+    f = lambda b: synth.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
+    t0 = time.perf_counter()
+    done = 0
+    while done < cfg.n_tokens and time.perf_counter() - t0 < budget_s:
+        for l in range(cfg.n_layers):
+            qkv, z, a, b = per[l]
+            _, states[l] = ognd.layer_step(sh, params[l], states[l], f(qkv[done]), f(z[done]), f(a[done]), f(b[done]))
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {cfg.n_tokens} tokens through all {cfg.n_layers} layers",
+            "seconds": round(dt, 2), "cpu_model": cpu_model(), "host_cores": os.cpu_count()}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -383,6 +469,27 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         return 1
+    if args.workload in synth.GDN_CONFIGS:
+        gcfg = synth.get_gdn_config(args.workload)
+        if args.tokens is not None:
+            gcfg = gcfg.replace(n_tokens=args.tokens)
+        steps = args.steps if args.steps is not None else 5
+        warmup = args.warmup if args.warmup is not None else 1
+        r = measure_gdn(gcfg, args, torch, moe, synth, steps, warmup, not args.no_kernel_pass)
+        cpu = None
+        if not args.no_cpu_baseline:
+            log("timing the CPU oracle on a bounded sample")
+            cpu = cpu_baseline_gdn(gcfg, r["inputs"], args.cpu_seconds)
+            log(f"oracle: {cpu}")
+        print(json.dumps({
+            "metric": "MoE decode tok/s & % HBM roofline (80B-shape, bs=1); prefill % MFMA peak",
+            "value": round(r["tok_s"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(r["ms_step"], 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f32", "data": "synthetic",
+            "config": {"workload": gcfg.name, "layers": gcfg.n_layers, "key_heads": gcfg.n_k, "value_heads": gcfg.n_v,
+                       "d_k": gcfg.d_k, "d_v": gcfg.d_v, "tokens_per_step": gcfg.n_tokens, "batch": 1},
+            "roofline": r["roofline"], "cpu_baseline": cpu, "extra": r["extra"]}), flush=True)
+        return 0
     cfg = synth.get_config(args.workload)
     if args.pool_gb is not None:
         if not cfg.pool_budget:

@@ -353,6 +353,64 @@ moe_status moe_profile_enable(moe_model* m, int32_t enable);
  * Copies min(cap, families) entries; *n receives the number of families. */
 moe_status moe_profile_read(moe_model* m, moe_kernel_time_t* out, size_t cap, size_t* n);
 
+/* ----------------------------------------------- Gated DeltaNet decode ---
+ * The linear-attention step beside the MoE in 36 of the 80B model's 48
+ * layers, whose recurrent state has a fixed size, about 72 MiB over those
+ * layers (alphalab.site field test, section explaining MoE expert streaming;
+ * cheshm.ai article, paragraph on the code base, for the Gated DeltaNet /
+ * gated attention hybrid). The pages print no formula; the step is the
+ * published gated delta rule in the decode form of the Qwen3-Next layer, per
+ * value head h of key head h / (n_v_heads / n_k_heads), one token at a time:
+ *   y = silu(causal 4-tap depthwise conv of the q, k, v channels);
+ *   q = y_q / sqrt(|y_q|^2 + 1e-6) / sqrt(d_k), k = y_k / sqrt(|y_k|^2 + 1e-6);
+ *   alpha = exp(-exp(A_log[h]) * softplus(a[h] + dt_bias[h])), beta = sigmoid(b[h]);
+ *   S <- alpha S; u = beta (v - S^T k); S <- S + k u^T; o = S^T q;
+ *   out = o / sqrt(mean(o^2) + 1e-6) * norm_w * silu(z).
+ * The state S of a layer is fp32 [n_v_heads][d_v][d_k] in HBM (2 MiB at the
+ * 80B shape, 36 layers 72 MiB), plus the last three conv inputs per channel. */
+typedef struct {
+  int32_t n_layers;
+  int32_t n_k_heads;  /* query/key heads */
+  int32_t n_v_heads;  /* value heads, a multiple of n_k_heads */
+  int32_t d_k;        /* (d_k, d_v) is (32, 32), (64, 64) or (128, 128) */
+  int32_t d_v;
+} moe_gdn_config;
+typedef struct moe_gdn moe_gdn;
+
+/* Allocate parameters and zeroed state for n_layers layers on the current
+ * device. Channels C = 2 * n_k_heads * d_k + n_v_heads * d_v (q, then k, then
+ * v). Errors: MOE_EINVAL (config), MOE_ENOMEM. */
+moe_status moe_gdn_create(const moe_gdn_config* cfg, moe_gdn** out);
+/* Host fp32 parameters of one layer, copied in: conv_w [C][4] (tap 3 multiplies
+ * the newest input), a_log [n_v_heads], dt_bias [n_v_heads], norm_w [d_v]. */
+moe_status moe_gdn_set_layer(moe_gdn* g, int32_t layer, const float* conv_w, const float* a_log,
+                             const float* dt_bias, const float* norm_w);
+/* Zero every layer's state and conv history (synchronous). */
+moe_status moe_gdn_reset(moe_gdn* g);
+/* Decode n_tok tokens one after another through layers [first_layer,
+ * first_layer + n_layers) (token-major: each token through every layer of the
+ * range, then the next token), updating each layer's state in place. dev bf16
+ * inputs qkv [n_tok][n_layers][C], z [n_tok][n_layers][n_v_heads * d_v], a, b
+ * [n_tok][n_layers][n_v_heads]; dev fp32 out [n_tok][n_layers][n_v_heads *
+ * d_v]. One kernel per (token, layer), one block per value head; sequences of
+ * 16 or more steps are captured once into a HIP graph and replayed. The layers
+ * of one call must have taken equally many tokens so far (MOE_ESTATE
+ * otherwise). Errors: MOE_EINVAL, MOE_ESTATE, MOE_EHIP. */
+moe_status moe_gdn_decode(moe_gdn* g, int32_t first_layer, int32_t n_layers, const uint16_t* qkv,
+                          const uint16_t* z, const uint16_t* a, const uint16_t* b, int32_t n_tok, float* out,
+                          void* stream);
+/* Measurement support: enable = 1 makes every later step kernel take the
+ * kernel's own begin/end timestamps (steps run as ordinary launches, not
+ * graphs); each call first returns, in *total_ms and *launches (either may be
+ * NULL), the time and count recorded since the previous call, waiting for
+ * them, then sets recording per `enable`. */
+moe_status moe_gdn_profile(moe_gdn* g, int32_t enable, double* total_ms, uint64_t* launches);
+/* Test support: copy a layer's state (host fp32 [n_v_heads][d_v][d_k]) and conv
+ * history (host fp32 [C][3], oldest first) out; either may be NULL.
+ * Synchronises the device. */
+moe_status moe_gdn_read_state(moe_gdn* g, int32_t layer, float* state, float* window);
+void moe_gdn_destroy(moe_gdn* g); /* NULL is a no-op; waits for the device */
+
 /* --------------------------------------------------------------- errors ---*/
 const char* moe_last_error(void);
 

@@ -30,6 +30,8 @@ EXPORTS = [
     "moe_layer_forward_noalloc", "moe_debug_routing",
     "moe_pool_create", "moe_pool_reset", "moe_pool_stats", "moe_pool_trace", "moe_pool_destroy",
     "moe_pool_simulate", "moe_model_set_kernels", "moe_profile_enable", "moe_profile_read", "moe_last_error",
+    "moe_gdn_create", "moe_gdn_set_layer", "moe_gdn_reset", "moe_gdn_decode", "moe_gdn_profile", "moe_gdn_read_state",
+    "moe_gdn_destroy",
 ]
 
 
@@ -46,6 +48,10 @@ class Config(ctypes.Structure):
 
 class KernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_uint64), ("total_ms", ctypes.c_double)]
+
+
+class GdnConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_layers", "n_k_heads", "n_v_heads", "d_k", "d_v")]
 
 
 class PoolStats(ctypes.Structure):
@@ -103,6 +109,13 @@ def lib() -> ctypes.CDLL:
             "moe_profile_enable": (I32, [P, I32]),
             "moe_profile_read": (I32, [P, ctypes.POINTER(KernelTime), SZ, ctypes.POINTER(SZ)]),
             "moe_last_error": (ctypes.c_char_p, []),
+            "moe_gdn_create": (I32, [ctypes.POINTER(GdnConfig), ctypes.POINTER(P)]),
+            "moe_gdn_set_layer": (I32, [P, I32, P, P, P, P]),
+            "moe_gdn_reset": (I32, [P]),
+            "moe_gdn_decode": (I32, [P, I32, I32, P, P, P, P, I32, P, P]),
+            "moe_gdn_read_state": (I32, [P, I32, P, P]),
+            "moe_gdn_profile": (I32, [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(U64)]),
+            "moe_gdn_destroy": (None, [P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -364,3 +377,72 @@ class Pool:
         victim = np.empty(n.value, dtype=np.int64)
         _check(lib().moe_pool_trace(self._h, _ptr(hit), _ptr(victim), n.value, ctypes.byref(n)))
         return hit, victim
+
+
+def _check_dev(name, t, dtypes, numel):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a torch tensor on the GPU")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be of dtype {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, the call needs {numel}")
+
+
+class GatedDeltaNet:
+    """Gated DeltaNet decode layers (recurrent state in HBM)."""
+
+    def __init__(self, n_layers: int, n_k_heads: int, n_v_heads: int, d_k: int, d_v: int):
+        self.cfg = GdnConfig(n_layers, n_k_heads, n_v_heads, d_k, d_v)
+        self.channels = 2 * n_k_heads * d_k + n_v_heads * d_v
+        h = ctypes.c_void_p()
+        _check(lib().moe_gdn_create(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().moe_gdn_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_layer(self, layer: int, conv_w, a_log, dt_bias, norm_w):
+        arrs = [np.ascontiguousarray(x, dtype=np.float32) for x in (conv_w, a_log, dt_bias, norm_w)]
+        _check(lib().moe_gdn_set_layer(self._h, layer, *[_ptr(x) for x in arrs]))
+
+    def reset(self):
+        _check(lib().moe_gdn_reset(self._h))
+
+    def decode(self, first_layer: int, n_layers: int, qkv, z, a, b, out, n_tok: Optional[int] = None, stream=None):
+        import torch
+        n = qkv.shape[0] if n_tok is None else n_tok
+        if n > 0:
+            c = self.cfg
+            bf = (torch.int16, torch.bfloat16)
+            _check_dev("qkv", qkv, bf, n * n_layers * self.channels)
+            _check_dev("z", z, bf, n * n_layers * c.n_v_heads * c.d_v)
+            _check_dev("a", a, bf, n * n_layers * c.n_v_heads)
+            _check_dev("b", b, bf, n * n_layers * c.n_v_heads)
+            _check_dev("out", out, (torch.float32,), n * n_layers * c.n_v_heads * c.d_v)
+        _check(lib().moe_gdn_decode(self._h, first_layer, n_layers, _ptr(qkv), _ptr(z), _ptr(a), _ptr(b), n,
+                                    _ptr(out), _stream(stream)))
+
+    def profile(self, enable: bool):
+        """(total_ms, launches) recorded since the previous call; then record (or not) from now on."""
+        ms = ctypes.c_double()
+        n = ctypes.c_uint64()
+        _check(lib().moe_gdn_profile(self._h, 1 if enable else 0, ctypes.byref(ms), ctypes.byref(n)))
+        return ms.value, n.value
+
+    def read_state(self, layer: int):
+        c = self.cfg
+        s = np.empty((c.n_v_heads, c.d_v, c.d_k), np.float32)
+        w = np.empty((self.channels, 3), np.float32)
+        _check(lib().moe_gdn_read_state(self._h, layer, _ptr(s), _ptr(w)))
+        return s, w
