@@ -25,4 +25,10 @@ from .workload import (  # noqa: F401
     get_gdn_config,
     gdn_params,
     gdn_inputs,
+    ATTN_CONFIGS,
+    AttnConfig,
+    get_attn_config,
+    attn_params,
+    attn_cache,
+    attn_inputs,
 )

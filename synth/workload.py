@@ -266,3 +266,65 @@ def gdn_inputs(cfg: GdnConfig, layer: int, n_tokens: int):
         return f32_to_bf16_bits(_normal(shape, cfg.seed, layer, _TOKEN_SLOT, tid, std=1.0))
     return (bits((n_tokens, cfg.channels), _GDN_QKV), bits((n_tokens, cfg.n_v * cfg.d_v), _GDN_Z),
             bits((n_tokens, cfg.n_v), _GDN_A), bits((n_tokens, cfg.n_v), _GDN_B))
+
+
+# ------------------------------------------------------ gated attention step ---
+# Seeded inputs of the gated GQA decode step (the full-attention layers). Shapes
+# follow the Qwen3-Next-80B attention layer: 16 query heads, 2 KV heads of
+# dimension 256, the first quarter of each head rotated; the cache is filled
+# with `context` synthetic positions before the decoded tokens.
+
+_ATT_WQ, _ATT_WK, _ATT_KC, _ATT_VC, _ATT_Q, _ATT_G, _ATT_K, _ATT_V = 30, 31, 32, 33, 34, 35, 36, 37
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnConfig:
+    name: str
+    n_q: int
+    n_kv: int
+    d: int
+    rot: int
+    n_layers: int
+    context: int      # positions already in the cache
+    n_tokens: int     # tokens decoded after them
+    seed: int = 0
+    description: str = ""
+
+    def replace(self, **kw) -> "AttnConfig":
+        return dataclasses.replace(self, **kw)
+
+
+ATTN_CONFIGS: Dict[str, AttnConfig] = {
+    "attn_tiny": AttnConfig("attn_tiny", n_q=4, n_kv=2, d=64, rot=16, n_layers=2, context=37, n_tokens=9,
+                            description="tiny gated GQA decode: 4 query / 2 KV heads of 64, 2 layers"),
+    "attn80b": AttnConfig("attn80b", n_q=16, n_kv=2, d=256, rot=64, n_layers=12, context=8192, n_tokens=64,
+                          description="80B-shaped gated GQA decode: 12 layers, 16 query / 2 KV heads of 256, "
+                                      "8192 cached positions, 64 tokens one at a time"),
+}
+
+
+def get_attn_config(name: str, **overrides) -> AttnConfig:
+    cfg = ATTN_CONFIGS[name]
+    return cfg.replace(**overrides) if overrides else cfg
+
+
+def attn_params(cfg: AttnConfig, layer: int):
+    """fp32 q and k norm weights [d] ~ 1 + N(0, 0.1)."""
+    wq = np.float32(1.0) + _normal((cfg.d,), cfg.seed, layer, _LAYER_SLOT, _ATT_WQ, std=0.1)
+    wk = np.float32(1.0) + _normal((cfg.d,), cfg.seed, layer, _LAYER_SLOT, _ATT_WK, std=0.1)
+    return wq.astype(np.float32), wk.astype(np.float32)
+
+
+def attn_cache(cfg: AttnConfig, layer: int, n_pos: int):
+    """fp16 bit patterns of the cached positions: K ~ N(0, 1) and V ~ N(0, 1), [n_kv][n_pos][d] each."""
+    k = _normal((cfg.n_kv, n_pos, cfg.d), cfg.seed, layer, _LAYER_SLOT, _ATT_KC, std=1.0).astype(np.float16)
+    v = _normal((cfg.n_kv, n_pos, cfg.d), cfg.seed, layer, _LAYER_SLOT, _ATT_VC, std=1.0).astype(np.float16)
+    return k.view(np.uint16), v.view(np.uint16)
+
+
+def attn_inputs(cfg: AttnConfig, layer: int, n_tokens: int):
+    """bf16 bit patterns ~ N(0, 1): q and gate [T][n_q * d], k and v [T][n_kv * d]."""
+    def bits(shape, tid):
+        return f32_to_bf16_bits(_normal(shape, cfg.seed, layer, _TOKEN_SLOT, tid, std=1.0))
+    return (bits((n_tokens, cfg.n_q * cfg.d), _ATT_Q), bits((n_tokens, cfg.n_q * cfg.d), _ATT_G),
+            bits((n_tokens, cfg.n_kv * cfg.d), _ATT_K), bits((n_tokens, cfg.n_kv * cfg.d), _ATT_V))
