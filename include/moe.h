@@ -411,6 +411,70 @@ moe_status moe_gdn_profile(moe_gdn* g, int32_t enable, double* total_ms, uint64_
 moe_status moe_gdn_read_state(moe_gdn* g, int32_t layer, float* state, float* window);
 void moe_gdn_destroy(moe_gdn* g); /* NULL is a no-op; waits for the device */
 
+/* ------------------------------------ Gated attention decode, KV cache ---
+ * The full-attention step of the 12 layers (of the 80B model's 48) that keep
+ * a growing K/V cache, budgeted at 24 KiB per token in fp16 (alphalab.site
+ * field test, section explaining MoE expert streaming; cheshm.ai article,
+ * paragraph on the code base, for the gated attention / Gated DeltaNet
+ * hybrid). The pages print no formula; the step is the decode form of the
+ * Qwen3-Next gated attention layer, for the token at position p, query head h
+ * of KV group h / (n_q_heads / n_kv_heads):
+ *   q_h = rope(rms(q_h) * wq), k_g = rope(rms(k_g) * wk), rms(x) = x / sqrt(mean(x^2) + 1e-6);
+ *   rope rotates the first rot_dim dims: pairs (i, i + rot_dim/2), angle p * 1e7^(-2i/rot_dim);
+ *   K[p] = fp16(k_g), V[p] = fp16(v_g) (round to nearest even);
+ *   out_h = softmax_j(q_h . K[j] / sqrt(d), j <= p) . V * sigmoid(gate_h).
+ * Cache bytes per token and layer: 2 * n_kv_heads * head_dim * 2 (2 KiB at the
+ * 80B shape: 2 KV heads of 256). On the device, K is [n_kv][max_pos][d] and V
+ * is stored transposed, [n_kv][d][max_pos rounded up to 32]. */
+typedef struct {
+  int32_t n_layers;
+  int32_t n_q_heads;   /* query heads, n_kv_heads times 1, 2, 4, 8 or 16 */
+  int32_t n_kv_heads;  /* <= 256 */
+  int32_t head_dim;    /* 64, 128 or 256 */
+  int32_t rot_dim;     /* rotated dims, even, <= head_dim */
+  int32_t max_pos;     /* cache capacity in positions, <= 2^20 */
+} moe_attn_config;
+typedef struct moe_attn moe_attn;
+
+/* Allocate the norm weights and a zeroed cache of max_pos positions for
+ * n_layers layers on the current device. Errors: MOE_EINVAL (config),
+ * MOE_ENOMEM. */
+moe_status moe_attn_create(const moe_attn_config* cfg, moe_attn** out);
+/* Host fp32 per-head RMS-norm weights of one layer, copied in: q_norm_w,
+ * k_norm_w [head_dim]. */
+moe_status moe_attn_set_layer(moe_attn* a, int32_t layer, const float* q_norm_w, const float* k_norm_w);
+/* Write positions [first_pos, first_pos + n) of a layer's cache from host fp16
+ * bits k, v [n_kv_heads][n][head_dim] (a prefilled context). Synchronous.
+ * Errors: MOE_EINVAL (range), MOE_EHIP. */
+moe_status moe_attn_write_cache(moe_attn* a, int32_t layer, int32_t first_pos, int32_t n, const uint16_t* k,
+                                const uint16_t* v);
+/* Test support: read positions [first_pos, first_pos + n) of a layer's cache
+ * into host fp16 bits k, v [n_kv_heads][n][head_dim] (either may be NULL).
+ * Synchronises the device. */
+moe_status moe_attn_read_cache(moe_attn* a, int32_t layer, int32_t first_pos, int32_t n, uint16_t* k, uint16_t* v);
+/* Decode n_tok tokens at positions pos0, pos0 + 1, ... through layers
+ * [first_layer, first_layer + n_layers), token-major (each token through every
+ * layer of the range, then the next). Each step writes the token's K/V row
+ * at its position and attends over positions [0, p]; positions below pos0
+ * must already hold the context. dev bf16 inputs q, gate
+ * [n_tok][n_layers][n_q_heads * head_dim] and k, v [n_tok][n_layers][n_kv_heads
+ * * head_dim] (the projections); dev fp32 out [n_tok][n_layers][n_q_heads *
+ * head_dim] (before the output projection). Two kernels per (token, layer):
+ * one wave per (KV head, 32 cached positions) producing softmax partials, and
+ * their merge with the gate. Sequences of 16 or more steps are captured once
+ * into a HIP graph and replayed. Errors: MOE_EINVAL, MOE_ESTATE (a layer
+ * without moe_attn_set_layer), MOE_EHIP. */
+moe_status moe_attn_decode(moe_attn* a, int32_t first_layer, int32_t n_layers, int32_t pos0, const uint16_t* q,
+                           const uint16_t* gate, const uint16_t* k, const uint16_t* v, int32_t n_tok, float* out,
+                           void* stream);
+/* Measurement support: enable = 1 makes every later step take the kernels'
+ * own begin/end timestamps (steps run as ordinary launches, not graphs); each
+ * call first returns, in *split_ms (partials kernel), *combine_ms (merge
+ * kernel) and *launches (steps; any may be NULL), what was recorded since the
+ * previous call, waiting for it, then sets recording per `enable`. */
+moe_status moe_attn_profile(moe_attn* a, int32_t enable, double* split_ms, double* combine_ms, uint64_t* launches);
+void moe_attn_destroy(moe_attn* a); /* NULL is a no-op; waits for the device */
+
 /* --------------------------------------------------------------- errors ---*/
 const char* moe_last_error(void);
 

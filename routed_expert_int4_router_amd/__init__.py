@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
     STORE_FILE,
     STORE_HOST,
     Config,
+    GatedAttention,
     GatedDeltaNet,
     Model,
     MoeError,

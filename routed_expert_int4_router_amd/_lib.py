@@ -32,6 +32,8 @@ EXPORTS = [
     "moe_pool_simulate", "moe_model_set_kernels", "moe_profile_enable", "moe_profile_read", "moe_last_error",
     "moe_gdn_create", "moe_gdn_set_layer", "moe_gdn_reset", "moe_gdn_decode", "moe_gdn_profile", "moe_gdn_read_state",
     "moe_gdn_destroy",
+    "moe_attn_create", "moe_attn_set_layer", "moe_attn_write_cache", "moe_attn_read_cache", "moe_attn_decode",
+    "moe_attn_profile", "moe_attn_destroy",
 ]
 
 
@@ -52,6 +54,10 @@ class KernelTime(ctypes.Structure):
 
 class GdnConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("n_layers", "n_k_heads", "n_v_heads", "d_k", "d_v")]
+
+
+class AttnConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("n_layers", "n_q_heads", "n_kv_heads", "head_dim", "rot_dim", "max_pos")]
 
 
 class PoolStats(ctypes.Structure):
@@ -116,6 +122,14 @@ def lib() -> ctypes.CDLL:
             "moe_gdn_read_state": (I32, [P, I32, P, P]),
             "moe_gdn_profile": (I32, [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(U64)]),
             "moe_gdn_destroy": (None, [P]),
+            "moe_attn_create": (I32, [ctypes.POINTER(AttnConfig), ctypes.POINTER(P)]),
+            "moe_attn_set_layer": (I32, [P, I32, P, P]),
+            "moe_attn_write_cache": (I32, [P, I32, I32, I32, P, P]),
+            "moe_attn_read_cache": (I32, [P, I32, I32, I32, P, P]),
+            "moe_attn_decode": (I32, [P, I32, I32, I32, P, P, P, P, I32, P, P]),
+            "moe_attn_profile": (I32, [P, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(U64)]),
+            "moe_attn_destroy": (None, [P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -446,3 +460,71 @@ class GatedDeltaNet:
         w = np.empty((self.channels, 3), np.float32)
         _check(lib().moe_gdn_read_state(self._h, layer, _ptr(s), _ptr(w)))
         return s, w
+
+
+class GatedAttention:
+    """Gated grouped-query attention decode layers with an fp16 KV cache in HBM."""
+
+    def __init__(self, n_layers: int, n_q_heads: int, n_kv_heads: int, head_dim: int, rot_dim: int, max_pos: int):
+        self.cfg = AttnConfig(n_layers, n_q_heads, n_kv_heads, head_dim, rot_dim, max_pos)
+        h = ctypes.c_void_p()
+        _check(lib().moe_attn_create(ctypes.byref(self.cfg), ctypes.byref(h)))
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().moe_attn_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def set_layer(self, layer: int, q_norm_w, k_norm_w):
+        arrs = [np.ascontiguousarray(x, dtype=np.float32) for x in (q_norm_w, k_norm_w)]
+        for x in arrs:
+            if x.size != self.cfg.head_dim:
+                raise ValueError(f"norm weights must hold head_dim = {self.cfg.head_dim} values")
+        _check(lib().moe_attn_set_layer(self._h, layer, _ptr(arrs[0]), _ptr(arrs[1])))
+
+    def write_cache(self, layer: int, first_pos: int, k16, v16):
+        """k16, v16: fp16 bit patterns [n_kv_heads][n][head_dim] (uint16)."""
+        k16 = np.ascontiguousarray(k16, dtype=np.uint16)
+        v16 = np.ascontiguousarray(v16, dtype=np.uint16)
+        c = self.cfg
+        if k16.shape != v16.shape or k16.ndim != 3 or k16.shape[0] != c.n_kv_heads or k16.shape[2] != c.head_dim:
+            raise ValueError("k16, v16 must both be [n_kv_heads][n][head_dim]")
+        _check(lib().moe_attn_write_cache(self._h, layer, first_pos, k16.shape[1], _ptr(k16), _ptr(v16)))
+
+    def read_cache(self, layer: int, first_pos: int, n: int):
+        c = self.cfg
+        k = np.empty((c.n_kv_heads, n, c.head_dim), np.uint16)
+        v = np.empty_like(k)
+        _check(lib().moe_attn_read_cache(self._h, layer, first_pos, n, _ptr(k), _ptr(v)))
+        return k, v
+
+    def decode(self, first_layer: int, n_layers: int, pos0: int, q, gate, k, v, out, n_tok: Optional[int] = None,
+               stream=None):
+        import torch
+        n = q.shape[0] if n_tok is None else n_tok
+        if n > 0:
+            c = self.cfg
+            bf = (torch.int16, torch.bfloat16)
+            qd, kd = c.n_q_heads * c.head_dim, c.n_kv_heads * c.head_dim
+            _check_dev("q", q, bf, n * n_layers * qd)
+            _check_dev("gate", gate, bf, n * n_layers * qd)
+            _check_dev("k", k, bf, n * n_layers * kd)
+            _check_dev("v", v, bf, n * n_layers * kd)
+            _check_dev("out", out, (torch.float32,), n * n_layers * qd)
+        _check(lib().moe_attn_decode(self._h, first_layer, n_layers, pos0, _ptr(q), _ptr(gate), _ptr(k), _ptr(v), n,
+                                     _ptr(out), _stream(stream)))
+
+    def profile(self, enable: bool):
+        """(split_ms, combine_ms, steps) recorded since the previous call; then record (or not) from now on."""
+        ms_s, ms_c = ctypes.c_double(), ctypes.c_double()
+        n = ctypes.c_uint64()
+        _check(lib().moe_attn_profile(self._h, 1 if enable else 0, ctypes.byref(ms_s), ctypes.byref(ms_c),
+                                      ctypes.byref(n)))
+        return ms_s.value, ms_c.value, n.value

@@ -27,7 +27,7 @@ HIPCC = os.path.join(ROCM, "bin", "hipcc")
 ARCH = "gfx950"
 
 HOST_SOURCES = ["pack.cpp", "pool_policy.cpp", "blob_file.cpp"]
-HIP_SOURCES = ["abi.cpp", "decode.hip", "prefill.hip", "scalar.hip", "gdn.hip"]
+HIP_SOURCES = ["abi.cpp", "decode.hip", "prefill.hip", "scalar.hip", "gdn.hip", "attn.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"-I{INCLUDE}", f"-I{CSRC}"]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
