@@ -15,6 +15,9 @@ Workloads (synthetic, seeded, weights ~N(0, 0.02) packed to int4/int8 g64):
   resident80b    the same 48-layer stack with every expert in HBM
   gdn80b         the Gated DeltaNet decode step beside the MoE: 36 layers of
                  16 key / 32 value heads of 128, 256 tokens one at a time
+  attn80b        the gated GQA attention decode step beside the MoE: 12 layers
+                 of 16 query / 2 KV heads of 256 over an fp16 KV cache holding
+                 8192 positions, 64 tokens one at a time
 
 A step is one pass of the workload's tokens through the whole path (router,
 top-k, expert GEMV/GEMM, combine, stack glue, pool). W untimed steps, then K
@@ -172,6 +175,21 @@ def measured_traffic(kernel: str, workload: str):
         return None
 
 
+def copy_calibration(torch, nbytes: int) -> None:
+    """One plain device-to-device copy of nbytes: the known-size reference that
+    scales rocprofv3's FETCH_SIZE / WRITE_SIZE to bytes."""
+    if nbytes <= 0:
+        return
+    n = nbytes // 4
+    src_t = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst_t = torch.empty_like(src_t)
+    torch.cuda.synchronize()
+    dst_t.copy_(src_t)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {4 * n} bytes")
+    del src_t, dst_t
+
+
 def link_probe(torch, chunk: int, n: int = 512) -> float:
     """Host->device rate of pinned hipMemcpyAsync copies of one expert record
     (the pool's miss unit), back to back on one stream after a warm-up: the
@@ -302,15 +320,7 @@ def measure(cfg, args, torch, moe, loader, synth, steps: int, warmup: int, kerne
                          "h2d_GBps": round(st["h2d_bytes"] / (elapsed / steps) / 1e9, 2),
                          "storage_GBps": round(st["storage_bytes"] / (elapsed / steps) / 1e9, 2),
                          "link_probe_GBps": link_probe(torch, moe.expert_bytes(cfg))}
-    if args.copy_calibration > 0:
-        n = args.copy_calibration // 4
-        src_t = torch.ones(n, dtype=torch.float32, device="cuda")
-        dst_t = torch.empty_like(src_t)
-        torch.cuda.synchronize()
-        dst_t.copy_(src_t)
-        torch.cuda.synchronize()
-        log(f"copy calibration: {4 * n} bytes")
-        del src_t, dst_t
+    copy_calibration(torch, args.copy_calibration)
     if kernels:
         n_prof = max(1, min(steps, 5 if cfg.n_layers == 1 else 1))
         prof = kernel_pass(model, step, n_prof, torch)
@@ -378,6 +388,7 @@ def measure_gdn(cfg, args, torch, moe, synth, steps: int, warmup: int, kernels: 
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     log(f"timed {steps} steps in {elapsed:.3f}s")
+    copy_calibration(torch, args.copy_calibration)
     res = {"tok_s": steps * T / elapsed, "ms_step": 1000.0 * elapsed / steps, "extra": {}, "roofline": None,
            "inputs": per}
     per_launch = gdn_step_bytes(cfg)
@@ -423,6 +434,111 @@ def cpu_baseline_gdn(cfg, per, budget_s: float) -> dict:
     dt = time.perf_counter() - t0
     return {"value": done / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"first {done} of {cfg.n_tokens} tokens through all {cfg.n_layers} layers",
+            "seconds": round(dt, 2), "cpu_model": cpu_model(), "host_cores": os.cpu_count()}
+
+
+def attn_split_bytes(cfg) -> tuple:
+    """(algorithmic, scratch) bytes of one attention partials kernel, averaged
+    over the workload's tokens: the cached K and V read (fp16, positions 0..p),
+    the new K/V row written, the bf16 q of every head and the k, v inputs, the
+    norm weights; scratch = the softmax partials written for the merge (one
+    set per 128 positions)."""
+    kv_row = 2 * cfg.n_kv * cfg.d * 2
+    avg_pos = cfg.context + (cfg.n_tokens - 1) / 2.0 + 1.0
+    inputs = cfg.n_q * cfg.d * 2 + 2 * cfg.n_kv * cfg.d * 2 + 2 * cfg.d * 4
+    algo = avg_pos * kv_row + kv_row + inputs
+    blocks = np.mean([(cfg.context + t) // 128 + 1 for t in range(cfg.n_tokens)])
+    scratch = blocks * cfg.n_q * (cfg.d + 2) * 4
+    return algo, scratch
+
+
+def measure_attn(cfg, args, torch, moe, synth, steps: int, warmup: int, kernels: bool) -> dict:
+    """Gated attention decode: each step takes the workload's tokens one after
+    another through all its layers (token-major) at positions context,
+    context + 1, ...; every step rewrites the same rows, so steps are equal."""
+    log(f"workload {cfg.name}: {cfg.description}")
+    T, L = cfg.n_tokens, cfg.n_layers
+    net = moe.GatedAttention(L, cfg.n_q, cfg.n_kv, cfg.d, cfg.rot, cfg.context + T)
+    for l in range(L):
+        net.set_layer(l, *synth.attn_params(cfg, l))
+        net.write_cache(l, 0, *synth.attn_cache(cfg, l, cfg.context))
+    per = [synth.attn_inputs(cfg, l, T) for l in range(L)]
+    dev = [torch.from_numpy(np.ascontiguousarray(np.stack([per[l][i] for l in range(L)], axis=1)).view(np.int16))
+           .cuda() for i in range(4)]
+    out = torch.empty((T, L, cfg.n_q * cfg.d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        net.decode(0, L, cfg.context, dev[0], dev[1], dev[2], dev[3], out, stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    log(f"timed {steps} steps in {elapsed:.3f}s")
+    copy_calibration(torch, args.copy_calibration)
+    res = {"tok_s": steps * T / elapsed, "ms_step": 1000.0 * elapsed / steps, "extra": {}, "roofline": None,
+           "inputs": per}
+    algo, scratch = attn_split_bytes(cfg)
+    res["extra"]["whole_step"] = {"bytes_per_token": round(algo * L),
+                                  "GBps": round(algo * L * res["tok_s"] / 1e9, 1),
+                                  "frac_of_hbm_peak": round(algo * L * res["tok_s"] / 1e9 / HBM_PEAK_GBS, 4)}
+    if kernels:
+        net.profile(True)
+        step()
+        torch.cuda.synchronize()
+        ms_s, ms_c, n = net.profile(False)
+        avg_s, avg_c = ms_s / n / 1000.0, ms_c / n / 1000.0
+        ach = algo / avg_s / 1e9
+        tot = ms_s + ms_c
+        res["extra"]["kernels"] = {
+            "attn_split": {"launches": n, "avg_us": round(avg_s * 1e6, 3), "share": round(ms_s / tot, 4),
+                           "scratch_bytes_per_launch": round(scratch)},
+            "attn_combine": {"launches": n, "avg_us": round(avg_c * 1e6, 3), "share": round(ms_c / tot, 4)}}
+        res["roofline"] = {"bound": "hbm", "kernel": "attn_split", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                           "traffic": measured_traffic("attn_split", cfg.name),
+                           "bytes_per_launch": round(algo), "avg_launch_us": round(avg_s * 1e6, 3)}
+        log(f"kernel pass: {res['extra']['kernels']}")
+    net.close()
+    return res
+
+
+def cpu_baseline_attn(cfg, per, budget_s: float) -> dict:
+    """The oracle as it stands, single thread: the first tokens through all layers."""
+    from oracle import attention as oatt
+    try:
+        os.sched_setaffinity(0, {sorted(os.sched_getaffinity(0))[0]})
+    except (AttributeError, OSError):
+        pass
+    import synth
+    sh = oatt.Shape(cfg.n_q, cfg.n_kv, cfg.d, cfg.rot)
+    L, P = cfg.n_layers, cfg.context + cfg.n_tokens
+    params, caches = [], []
+    for l in range(L):
+        params.append(oatt.Params(*[np.asarray(w, np.float64) for w in synth.attn_params(cfg, l)]))
+        k16, v16 = synth.attn_cache(cfg, l, cfg.context)
+        K = np.zeros((cfg.n_kv, P, cfg.d))
+        V = np.zeros((cfg.n_kv, P, cfg.d))
+        K[:, :cfg.context] = k16.view(np.float16)
+        V[:, :cfg.context] = v16.view(np.float16)
+        caches.append((K, V))
+    f = lambda b: synth.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
+    t0 = time.perf_counter()
+    done = 0
+    while done < cfg.n_tokens and time.perf_counter() - t0 < budget_s:
+        for l in range(L):
+            q, g, k, v = (f(x[done]) for x in per[l])
+            oatt.step(sh, params[l], cfg.context + done, *caches[l], q.reshape(cfg.n_q, cfg.d),
+                      g.reshape(cfg.n_q, cfg.d), k.reshape(cfg.n_kv, cfg.d), v.reshape(cfg.n_kv, cfg.d))
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {done} of {cfg.n_tokens} tokens through all {L} layers",
             "seconds": round(dt, 2), "cpu_model": cpu_model(), "host_cores": os.cpu_count()}
 
 
@@ -488,6 +604,28 @@ def main() -> int:
             "dtype": "f32", "data": "synthetic",
             "config": {"workload": gcfg.name, "layers": gcfg.n_layers, "key_heads": gcfg.n_k, "value_heads": gcfg.n_v,
                        "d_k": gcfg.d_k, "d_v": gcfg.d_v, "tokens_per_step": gcfg.n_tokens, "batch": 1},
+            "roofline": r["roofline"], "cpu_baseline": cpu, "extra": r["extra"]}), flush=True)
+        return 0
+    if args.workload in synth.ATTN_CONFIGS:
+        acfg = synth.get_attn_config(args.workload)
+        if args.tokens is not None:
+            acfg = acfg.replace(n_tokens=args.tokens)
+        steps = args.steps if args.steps is not None else 10
+        warmup = args.warmup if args.warmup is not None else 2
+        r = measure_attn(acfg, args, torch, moe, synth, steps, warmup, not args.no_kernel_pass)
+        cpu = None
+        if not args.no_cpu_baseline:
+            log("timing the CPU oracle on a bounded sample")
+            cpu = cpu_baseline_attn(acfg, r["inputs"], args.cpu_seconds)
+            log(f"oracle: {cpu}")
+        print(json.dumps({
+            "metric": "MoE decode tok/s & % HBM roofline (80B-shape, bs=1); prefill % MFMA peak",
+            "value": round(r["tok_s"], 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+            "ms_per_step": round(r["ms_step"], 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "f16", "data": "synthetic",
+            "config": {"workload": acfg.name, "layers": acfg.n_layers, "query_heads": acfg.n_q,
+                       "kv_heads": acfg.n_kv, "head_dim": acfg.d, "rot_dim": acfg.rot, "context": acfg.context,
+                       "tokens_per_step": acfg.n_tokens, "batch": 1},
             "roofline": r["roofline"], "cpu_baseline": cpu, "extra": r["extra"]}), flush=True)
         return 0
     cfg = synth.get_config(args.workload)

@@ -425,7 +425,7 @@ void moe_gdn_destroy(moe_gdn* g); /* NULL is a no-op; waits for the device */
  *   out_h = softmax_j(q_h . K[j] / sqrt(d), j <= p) . V * sigmoid(gate_h).
  * Cache bytes per token and layer: 2 * n_kv_heads * head_dim * 2 (2 KiB at the
  * 80B shape: 2 KV heads of 256). On the device, K is [n_kv][max_pos][d] and V
- * is stored transposed, [n_kv][d][max_pos rounded up to 32]. */
+ * is kept in tiles of 32 positions, [n_kv][span][d][32]. */
 typedef struct {
   int32_t n_layers;
   int32_t n_q_heads;   /* query heads, n_kv_heads times 1, 2, 4, 8 or 16 */
@@ -459,10 +459,12 @@ moe_status moe_attn_read_cache(moe_attn* a, int32_t layer, int32_t first_pos, in
  * must already hold the context. dev bf16 inputs q, gate
  * [n_tok][n_layers][n_q_heads * head_dim] and k, v [n_tok][n_layers][n_kv_heads
  * * head_dim] (the projections); dev fp32 out [n_tok][n_layers][n_q_heads *
- * head_dim] (before the output projection). Two kernels per (token, layer):
- * one wave per (KV head, 32 cached positions) producing softmax partials, and
- * their merge with the gate. Sequences of 16 or more steps are captured once
- * into a HIP graph and replayed. Errors: MOE_EINVAL, MOE_ESTATE (a layer
+ * head_dim] (before the output projection). Per (token, layer): a kernel
+ * with one block per (KV head, 128 cached positions) producing softmax
+ * partials, then their merge with the gate, which also prepares the next
+ * step (its normed, rotated q, and its K/V row written into the cache); a
+ * call's first step is prepared by a kernel of its own. Sequences of 16 or
+ * more steps are captured once into a HIP graph and replayed. Errors: MOE_EINVAL, MOE_ESTATE (a layer
  * without moe_attn_set_layer), MOE_EHIP. */
 moe_status moe_attn_decode(moe_attn* a, int32_t first_layer, int32_t n_layers, int32_t pos0, const uint16_t* q,
                            const uint16_t* gate, const uint16_t* k, const uint16_t* v, int32_t n_tok, float* out,

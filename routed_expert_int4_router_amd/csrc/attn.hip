@@ -7,29 +7,36 @@
 // (cheshm.ai article, paragraph on the code base). The pages print no
 // formula; the step is the decode form of the Qwen3-Next gated attention
 // layer: per-head RMS norms of q and k, rotary embedding of the first `rot`
-// dims (pairs (i, i + rot/2), angle p * 1e7^(-2i/rot), computed in fp64), the
+// dims (pairs (i, i + rot/2), angle p * 1e7^(-2i/rot), the angle in fp64), the
 // new K/V row stored in fp16, softmax attention of each query head over its KV
 // group's cached rows, and the sigmoid output gate.
 //
-// Split-K decoding, bound by reading the cache (2 * d * 2 bytes per cached
-// position and KV group). Kernel 1: one wave per (KV group, 32 positions)
-// loads its K rows and V columns straight into MFMA operand registers, 16
-// bytes per load, and contracts them with the group's G query heads on
-// v_mfma_f32_16x16x32_f16: scores S[j][h] = K[j] . q_h, then
-// O[d][h] = sum_j V[j][d] P[h][j]. The G heads sharing one KV group make this
-// a real contraction (8 heads per group at the 80B shape): the vector ALU
-// would need 8 fp32 FMAs per cached byte. fp16 operands: the cache is fp16;
-// q and the softmax weights P are carried as fp16 hi + lo pairs (two MFMAs
-// each), so scores and weighted sums keep close to fp32 accuracy. Each wave
-// writes softmax partials (max, sum of exp, weighted sum of V); kernel 2 merges
-// the partials per query head and applies the output gate.
+// Per step (token, layer), bound by reading the cache (2 * d * 2 bytes per
+// cached position and KV group):
+// - prep: the G query rows of each KV group normed, rotated, scaled by
+//   1 / sqrt(d) and split into fp16 hi + lo (the MFMA operand, in a scratch
+//   buffer), and the new K/V row normed, rotated, rounded to fp16 and written
+//   into the cache. A call's first step runs it as a kernel of its own; every
+//   later step's prep rides in the previous step's merge kernel (its inputs
+//   are all given up front), so it costs no launch.
+// - partials: a block of four waves per (KV group, 128 positions); each wave
+//   loads the q operand, the K rows and V columns of its 32 positions straight
+//   into MFMA operand registers, 16 bytes per load, and contracts them on
+//   v_mfma_f32_16x16x32_f16: scores S[j][h] = K[j] . q_h, then
+//   O[d][h] = sum_j V[j][d] P[h][j]. The G heads sharing one KV group make
+//   this a real contraction (8 heads per group at the 80B shape): on the
+//   vector ALU it would take 8 fp32 FMAs per cached byte. q and the softmax
+//   weights P ride as fp16 hi + lo pairs (two MFMAs each), so scores and
+//   weighted sums keep close to fp32 accuracy. The four waves merge their
+//   softmax partials (max, sum of exp, weighted sum of V) in LDS and the block
+//   writes one set.
+// - merge: per query head, the blocks' partials folded with a running max,
+//   times sigmoid(gate); plus the next step's prep.
 //
 // Cache layout: K [n_kv][max_pos][d] (a position's row contiguous, as the
-// score contracts over d), V transposed [n_kv][d][pitch] (a dim's positions
-// contiguous, as the weighted sum contracts over positions), pitch = max_pos
-// rounded up to 32. The wave whose 32 positions hold the new one computes that
-// row itself (norm, rotation, fp16), writes it to the cache and patches it into
-// its own registers.
+// score contracts over d); V in tiles of 32 positions, [n_kv][span][d][32] (a
+// dim's 32 positions contiguous, as the weighted sum contracts over
+// positions, and a span's tile one contiguous 16 KiB at d = 256).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -52,18 +59,22 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
-constexpr int kSpan = 32;  // positions per wave of kernel 1
-constexpr int kCombineDims = 64;
-constexpr int kCombineGroups = 4;
+constexpr int kSpan = 32;                   // positions per wave of the partials kernel
+constexpr int kWaves = 4;                   // waves per block of the partials kernel
+constexpr int kBlockPos = kSpan * kWaves;   // positions per block
+constexpr int kCombineDims = 16;            // merge kernel: dims per block
+constexpr int kCombineGroups = 16;          // merge kernel: groups of partials per block
+constexpr int kPrepThreads = 256;           // prep: one thread per dim (head_dim <= 256)
+static_assert(kCombineDims * kCombineGroups == kPrepThreads, "the merge kernel's blocks run the prep");
 
 __device__ __forceinline__ float bfv(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
 struct AttnLayer {
-  const float* wq;  // [d]
-  const float* wk;  // [d]
+  const float* wq;  // [d] q norm weight
+  const float* wk;  // [d] k norm weight
   uint16_t* kc;     // [n_kv][max_pos][d] fp16
-  uint16_t* vt;     // [n_kv][d][pitch] fp16
+  uint16_t* vt;     // [n_kv][n_spans][d][32] fp16
 };
 
 struct AttnIo {
@@ -74,47 +85,102 @@ struct AttnIo {
   float* out;            // [n_q][d]
 };
 
-struct AttnWork {
-  float* ml;      // [n_kv][max_split][G][2]: max, sum of exp
-  float* o;       // [n_kv][max_split][G][d]
-  int max_split;
+struct AttnShape {
+  const double* freq;  // [d]: rotation frequency of each dim, 0 past rot
+  int n_kv, max_pos, n_spans, rot;
 };
 
-// RMS norm with weight, then rotation by position of the first `rot` dims, of
-// the rows x[R][D] held one value per (row, lane + 64c); writes the results
-// (times `scale`) to out[R][D] in LDS. cs/sn: cos, sin of this lane's angles.
-template <int D>
-__device__ __forceinline__ void norm_rope_rows(const float* x, int R, const float* w, int rot, const float* cs,
-                                               const float* sn, float scale, float* tmp, float* out) {
-  constexpr int C = D / 64;
-  const int lane = threadIdx.x;
-  for (int r = 0; r < R; ++r) {
-    float ss = 0.f;
-#pragma unroll
-    for (int c = 0; c < C; ++c) ss = fmaf(x[r * C + c], x[r * C + c], ss);
-    ss = dpp::wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)D + 1e-6f);
-#pragma unroll
-    for (int c = 0; c < C; ++c) tmp[r * D + lane + 64 * c] = x[r * C + c] * inv * w[c];
-  }
-  __syncthreads();
+struct AttnWork {
+  float* ml;       // [n_kv][max_split][G][2]: max, sum of exp
+  float* o;        // [n_kv][max_split][G][d]
+  _Float16* qop;   // [n_q][2][d]: prepared q, hi then lo
+  int max_split;   // blocks of the partials kernel per KV group at full capacity
+};
+
+struct AttnStep {  // one (token, layer) step: its layer, inputs, position
+  AttnLayer L;
+  AttnIo io;
+  int pos;
+};
+
+// Rotation of dim d of a normed row in LDS: pairs (i, i + rot/2).
+__device__ __forceinline__ float rotated(const float* row, int d, int rot, float cs, float sn) {
   const int half = rot / 2;
-  for (int r = 0; r < R; ++r) {
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int d = lane + 64 * c;
-      const float xn = tmp[r * D + d];
-      float y = xn;
-      if (d < half) y = xn * cs[c] - tmp[r * D + d + half] * sn[c];
-      else if (d < rot) y = xn * cs[c] + tmp[r * D + d - half] * sn[c];
-      out[r * D + d] = y * scale;
-    }
-  }
-  __syncthreads();
+  if (d < half) return row[d] * cs - row[d + half] * sn;
+  if (d < rot) return row[d] * cs + row[d - half] * sn;
+  return row[d];
 }
 
-// One wave: KV group g = blockIdx.x % n_kv, positions [j0, j0 + 32) with
-// j0 = 32 * (blockIdx.x / n_kv), all of them <= pos except in the last span.
+// Prep of one row of a step by a block of kPrepThreads threads (thread = dim):
+// row < n_q is query head `row`; row = n_q + g is KV group g's new K/V row.
+// The angle: pos * freq in fp64, reduced to [-pi, pi] in fp64, then sin and
+// cos in fp32 of the reduced angle split into hi + lo (a first-order
+// correction for lo). Every load is unconditional, at an in-range address.
+template <int D, int G>
+__device__ void prep_row(const AttnShape& S, const AttnStep& st, const AttnWork& W, int row, float* s_row,
+                         float* s_red) {
+  const int n_q = S.n_kv * G, t = threadIdx.x;
+  const bool isq = row < n_q;
+  const int g = isq ? row / G : row - n_q;
+  const int d = t < D ? t : D - 1;
+  const uint16_t* src = isq ? st.io.q + (size_t)row * D : st.io.k + (size_t)g * D;
+  const float x = t < D ? bfv(src[d]) : 0.f;
+  const float w = (isq ? st.L.wq : st.L.wk)[d];
+  const float vv = bfv(st.io.v[(size_t)g * D + d]);
+  float cs = 1.f, sn = 0.f;
+  if (d < S.rot) {
+    const double ang = (double)st.pos * S.freq[d];
+    const double turns = rint(ang * 0.15915494309189535);        // 1 / (2 pi)
+    double red = fma(-turns, 6.283185307179586, ang);             // 2 pi, high part
+    red = fma(-turns, 2.4492935982947064e-16, red);               // 2 pi - high part
+    const float hi = (float)red, lo = (float)(red - (double)hi);  // red = hi + lo
+    float sh, ch;
+    sincosf(hi, &sh, &ch);
+    sn = fmaf(ch, lo, sh);   // sin(hi + lo), |lo| < 2^-22
+    cs = fmaf(-sh, lo, ch);
+  }
+  const float ss = dpp::wave_sum(x * x);
+  if ((t & 63) == 0) s_red[t >> 6] = ss;
+  __syncthreads();
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPrepThreads / 64; ++i) tot += s_red[i];
+  const float inv = 1.0f / sqrtf(tot / (float)D + 1e-6f);
+  if (t < D) s_row[t] = x * inv * w;
+  __syncthreads();
+  if (t < D) {
+    const float y = rotated(s_row, t, S.rot, cs, sn);
+    if (isq) {
+      const float yq = y * (1.0f / sqrtf((float)D));
+      const _Float16 h = (_Float16)yq;
+      W.qop[(size_t)row * 2 * D + t] = h;
+      W.qop[(size_t)row * 2 * D + D + t] = (_Float16)(yq - (float)h);
+    } else {
+      st.L.kc[((size_t)g * S.max_pos + st.pos) * D + t] = f2h(y);
+      st.L.vt[(((size_t)g * S.n_spans + st.pos / kSpan) * D + t) * kSpan + st.pos % kSpan] = f2h(vv);
+    }
+  }
+  __syncthreads();  // s_row and s_red are reused
+}
+
+// A call's first step: block b < n_q + n_kv preps row b.
+template <int D, int G>
+__global__ void __launch_bounds__(kPrepThreads) attn_prep_kernel(AttnShape S, AttnStep st, AttnWork W) {
+  __shared__ float s_row[D];
+  __shared__ float s_red[kPrepThreads / 64];
+  prep_row<D, G>(S, st, W, blockIdx.x, s_row, s_red);
+}
+
+// LDS of the partials kernel: the waves' scaled weighted sums, rows of D + 16
+// floats (the padding spreads the rows of consecutive heads over the banks).
+template <int D, int G>
+constexpr size_t lds_bytes() {
+  return (size_t)kWaves * G * (D + 16) * 4;
+}
+
+// Block (KV group g = blockIdx.x % n_kv, positions [b0, b0 + 128), b0 = 128 *
+// (blockIdx.x / n_kv)); wave w takes positions [j0, j0 + 32), j0 = b0 + 32 w,
+// and is live when j0 <= pos. Position pos (this step's) is in the cache.
 //
 // MFMA 16x16x32 operand map (lane = r + 16 * gq, r < 16, gq < 4): A supplies
 // row r, B column r, each 8 consecutive k-values of the lane's group gq; C
@@ -124,217 +190,224 @@ __device__ __forceinline__ void norm_rope_rows(const float* x, int R, const floa
 //   + r % 4, so that C lane (r, gq) holds head r at positions j0 + 8 * gq +
 //   e (e = 4 t + i < 8); k-slots of step s are dims 32 s + 8 gq + [0, 8);
 // - weighted sums, C = O[d][h], tile n covers dims 16 n + [0, 16); k-slots are
-//   positions j0 + 8 gq + [0, 8): A is 16 contiguous bytes of the transposed
-//   V row of dim 16 n + r, B the lane's own 8 weights of head r.
+//   positions j0 + 8 gq + [0, 8): A is 16 contiguous bytes of the V tile row
+//   of dim 16 n + r, B the lane's own 8 weights of head r.
 template <int D, int G>
-__global__ void __launch_bounds__(64) attn_split_kernel(AttnLayer L, AttnIo io, AttnWork W, int n_kv, int max_pos,
-                                                        int pitch, int rot, int pos) {
+__global__ void __launch_bounds__(64 * kWaves) attn_split_kernel(AttnLayer L, AttnWork W, AttnShape S, int pos) {
   static_assert(D % 64 == 0 && D <= 256 && G <= 16, "shape");
-  constexpr int NS = D / 32;  // score k-steps
-  constexpr int NT = D / 16;  // weighted-sum tiles
-  constexpr int C = D / 64;   // values per lane of a D-row
-  constexpr int QP = D + 8;   // fp16 pitch of the q rows in LDS
-  __shared__ float s_tmp[G * D];
-  __shared__ float s_qf[G * D];
-  __shared__ __align__(16) _Float16 s_qh[G * QP];
-  __shared__ __align__(16) _Float16 s_ql[G * QP];
-  __shared__ __align__(16) uint16_t s_new[2 * D];  // the new position's K row, V row (fp16)
+  constexpr int NS = D / 32;   // score k-steps
+  constexpr int NT = D / 16;   // weighted-sum tiles
+  constexpr int OP = D + 16;   // LDS row pitch of the merge, floats
+  extern __shared__ __align__(16) float s_o[];   // [kWaves][G][OP]
+  __shared__ float s_ml[kWaves * G * 2];
 
-  const int lane = threadIdx.x, r = lane & 15, gq = lane >> 4;
-  const int g = blockIdx.x % n_kv, split = blockIdx.x / n_kv;
-  const int j0 = split * kSpan;
-  const bool last = pos < j0 + kSpan;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, gq = lane >> 4;
+  const int g = blockIdx.x % S.n_kv, blk = blockIdx.x / S.n_kv;
+  const int j0 = blk * kBlockPos + kSpan * w;
+  const bool live = j0 <= pos;                  // wave-uniform
+  const bool mine = live && pos < j0 + kSpan;   // this wave's span holds pos
 
-  // 1. loads: the small inputs first (their wait then leaves the cache loads
-  //    in flight), then the span's K rows and V columns
-  float qx[G * C], wq[C], wk[C], kx[C], vx[C];
+  // 1. loads, every one unconditional at an in-range address: the q operand of
+  //    column r (columns r >= G read row G - 1, then zero), the K rows (rows
+  //    past pos read row pos), the V tile (a wave past pos reads its own tile,
+  //    in range as n_spans covers whole blocks, and uses none of it)
+  const _Float16* qrow = W.qop + (size_t)(g * G + min(r, G - 1)) * 2 * D + 8 * gq;
+  f16x8 bh[NS], bl[NS];
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int c = 0; c < C; ++c) qx[h * C + c] = bfv(io.q[(size_t)(g * G + h) * D + lane + 64 * c]);
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    wq[c] = L.wq[lane + 64 * c];
-    wk[c] = last ? L.wk[lane + 64 * c] : 0.f;
-    kx[c] = last ? bfv(io.k[(size_t)g * D + lane + 64 * c]) : 0.f;
-    vx[c] = last ? bfv(io.v[(size_t)g * D + lane + 64 * c]) : 0.f;
+  for (int s = 0; s < NS; ++s) {
+    bh[s] = *reinterpret_cast<const f16x8*>(qrow + 32 * s);
+    bl[s] = *reinterpret_cast<const f16x8*>(qrow + D + 32 * s);
   }
   uint4 ka[2][NS], va[NT];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int p = min(j0 + 8 * (r >> 2) + 4 * t + (r & 3), pos);
-    const uint16_t* row = L.kc + ((size_t)g * max_pos + p) * D + 8 * gq;
+    const uint16_t* row = L.kc + ((size_t)g * S.max_pos + p) * D + 8 * gq;
 #pragma unroll
     for (int s = 0; s < NS; ++s) ka[t][s] = *reinterpret_cast<const uint4*>(row + 32 * s);
   }
+  const uint16_t* tile = L.vt + ((size_t)g * S.n_spans + j0 / kSpan) * D * kSpan;
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
-    va[n] = *reinterpret_cast<const uint4*>(L.vt + ((size_t)g * D + 16 * n + r) * pitch + j0 + 8 * gq);
+  for (int n = 0; n < NT; ++n) va[n] = *reinterpret_cast<const uint4*>(tile + (16 * n + r) * kSpan + 8 * gq);
 
-  // 2. rotation angles of this lane's dims (fp64), the G query rows normed,
-  //    rotated and scaled by 1 / sqrt(D), split into fp16 hi + lo
-  float cs[C], sn[C];
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[NT];
+  if (live) {
+    if (r >= G) {
 #pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int d = lane + 64 * c, i = d < rot / 2 ? d : d - rot / 2;
-    cs[c] = 1.f;
-    sn[c] = 0.f;
-    if (d < rot) {
-      double sd, cd;
-      sincos((double)pos * pow(1.0e7, -2.0 * i / rot), &sd, &cd);
-      cs[c] = (float)cd;
-      sn[c] = (float)sd;
+      for (int s = 0; s < NS; ++s) {
+        bh[s] = f16x8{};
+        bl[s] = f16x8{};
+      }
     }
-  }
-  norm_rope_rows<D>(qx, G, wq, rot, cs, sn, 1.0f / sqrtf((float)D), s_tmp, s_qf);
-  for (int h = 0; h < G; ++h)
+    if (mine) {
+      // V slots past pos may hold anything (a stale inf would poison 0 * v):
+      // the lane's slots e > pos - (j0 + 8 gq) are zeroed, per dword
+      const int e_last = pos - (j0 + 8 * gq);
+      uint32_t keep[4];
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int d = lane + 64 * c;
-      const float y = s_qf[h * D + d];
-      const _Float16 hi = (_Float16)y;
-      s_qh[h * QP + d] = hi;
-      s_ql[h * QP + d] = (_Float16)(y - (float)hi);
-    }
-  // 3. the new position's row (last span only): fp16 K = rotated, normed k;
-  //    fp16 V = v; both to the cache and to LDS
-  if (last) {
-    norm_rope_rows<D>(kx, 1, wk, rot, cs, sn, 1.0f, s_tmp, s_qf);
+      for (int q = 0; q < 4; ++q) keep[q] = (2 * q <= e_last ? 0xFFFFu : 0u) | (2 * q + 1 <= e_last ? 0xFFFF0000u : 0u);
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int d = lane + 64 * c;
-      const uint16_t kh = f2h(s_qf[d]), vh = f2h(vx[c]);
-      L.kc[((size_t)g * max_pos + pos) * D + d] = kh;
-      L.vt[((size_t)g * D + d) * pitch + pos] = vh;
-      s_new[d] = kh;
-      s_new[D + d] = vh;
+      for (int n = 0; n < NT; ++n) va[n] = make_uint4(va[n].x & keep[0], va[n].y & keep[1], va[n].z & keep[2],
+                                                      va[n].w & keep[3]);
     }
-  }
-  __syncthreads();
-  if (last) {
-    // K rows: the lane whose row is the new position takes it from LDS
+    // 2. scores S[j][h] = K[j] . q_h (q as hi + lo)
+    f32x4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const f16x8 a = __builtin_bit_cast(f16x8, ka[t][s]);
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh[s], sc[t], 0, 0, 0);
+        sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl[s], sc[t], 0, 0, 0);
+      }
+    // 3. softmax partials of head r over the span: lane (r, gq) holds
+    //    positions j0 + 8 gq + e, e = 4 t + i; positions past pos are masked
+    float sv[8];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-      if (j0 + 8 * (r >> 2) + 4 * t + (r & 3) == pos)
 #pragma unroll
-        for (int s = 0; s < NS; ++s) ka[t][s] = *reinterpret_cast<const uint4*>(s_new + 32 * s + 8 * gq);
-    // V columns: the new position from LDS, later positions zero
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * t + i;
+        sv[e] = j0 + 8 * gq + e <= pos ? sc[t][i] : -INFINITY;
+      }
+    m = sv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) m = fmaxf(m, sv[e]);
+    m = fmaxf(m, __shfl_xor(m, 16));
+    m = fmaxf(m, __shfl_xor(m, 32));  // finite: position j0 is live
+    f16x8 ph, pl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float p = expf(sv[e] - m);
+      const _Float16 hi = (_Float16)p;
+      ph[e] = hi;
+      pl[e] = (_Float16)(p - (float)hi);
+      l += p;
+    }
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    if (r >= G) {
+      ph = f16x8{};
+      pl = f16x8{};
+    }
+    // 4. weighted sums O[d][h] = sum_j V[j][d] P[h][j]
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      uint16_t e8[8];
-      __builtin_memcpy(e8, &va[n], 16);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int p = j0 + 8 * gq + e;
-        e8[e] = p == pos ? s_new[D + 16 * n + r] : (p > pos ? (uint16_t)0 : e8[e]);
-      }
-      __builtin_memcpy(&va[n], e8, 16);
+      const f16x8 a = __builtin_bit_cast(f16x8, va[n]);
+      o[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ph, o[n], 0, 0, 0);
+      o[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pl, o[n], 0, 0, 0);
     }
   }
 
-  // 4. scores S[j][h] = K[j] . q_h (q as hi + lo)
-  f32x4 sc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  // 5. merge of the four waves: each scales its sums by exp(m_w - M), the
+  //    block sums them; a wave with no live position (m = -inf) adds nothing
+  if (lane < G) {
+    s_ml[(w * G + lane) * 2] = m;
+    s_ml[(w * G + lane) * 2 + 1] = l;
+  }
+  __syncthreads();
+  if (live && r < G) {
+    float M = s_ml[r * 2];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    f16x8 bh = {}, bl = {};
-    if (r < G) {
-      bh = *reinterpret_cast<const f16x8*>(s_qh + r * QP + 32 * s + 8 * gq);
-      bl = *reinterpret_cast<const f16x8*>(s_ql + r * QP + 32 * s + 8 * gq);
+    for (int v = 1; v < kWaves; ++v) M = fmaxf(M, s_ml[(v * G + r) * 2]);
+    const float f = expf(m - M);
+#pragma unroll
+    for (int n = 0; n < NT; ++n)
+      *reinterpret_cast<f32x4*>(s_o + ((size_t)w * G + r) * OP + 16 * n + 4 * gq) = o[n] * f;
+  }
+  __syncthreads();
+  const size_t part = ((size_t)g * W.max_split + blk) * G;
+  for (int idx = tid; idx < G * D / 4; idx += 64 * kWaves) {
+    const int h = idx * 4 / D, d = idx * 4 % D;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v)
+      if (s_ml[(v * G + h) * 2] != -INFINITY) acc += *reinterpret_cast<const f32x4*>(s_o + ((size_t)v * G + h) * OP + d);
+    *reinterpret_cast<f32x4*>(W.o + (part + h) * D + d) = acc;
+  }
+  if (tid < G) {
+    float M = s_ml[tid * 2];
+#pragma unroll
+    for (int v = 1; v < kWaves; ++v) M = fmaxf(M, s_ml[(v * G + tid) * 2]);
+    float Ls = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float mv = s_ml[(v * G + tid) * 2];
+      if (mv != -INFINITY) Ls = fmaf(s_ml[(v * G + tid) * 2 + 1], expf(mv - M), Ls);
     }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const f16x8 a = __builtin_bit_cast(f16x8, ka[t][s]);
-      sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, sc[t], 0, 0, 0);
-      sc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, sc[t], 0, 0, 0);
-    }
-  }
-
-  // 5. softmax partials of head r over the span: lane (r, gq) holds positions
-  //    j0 + 8 gq + e, e = 4 t + i; positions past pos are masked
-  float sv[8];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * t + i;
-      sv[e] = j0 + 8 * gq + e <= pos ? sc[t][i] : -INFINITY;
-    }
-  float m = sv[0];
-#pragma unroll
-  for (int e = 1; e < 8; ++e) m = fmaxf(m, sv[e]);
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));  // finite: position j0 is always live
-  f16x8 ph, pl;
-  float l = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float p = expf(sv[e] - m);
-    const _Float16 hi = (_Float16)p;
-    ph[e] = hi;
-    pl[e] = (_Float16)(p - (float)hi);
-    l += p;
-  }
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  if (r >= G) {
-    ph = f16x8{};
-    pl = f16x8{};
-  }
-
-  // 6. weighted sums O[d][h] = sum_j V[j][d] P[h][j]
-  const size_t part = ((size_t)g * W.max_split + split) * G;
-#pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    const f16x8 a = __builtin_bit_cast(f16x8, va[n]);
-    f32x4 o = {0.f, 0.f, 0.f, 0.f};
-    o = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ph, o, 0, 0, 0);
-    o = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, pl, o, 0, 0, 0);
-    if (r < G) *reinterpret_cast<f32x4*>(W.o + (part + r) * D + 16 * n + 4 * gq) = o;
-  }
-  if (r < G && gq == 0) {
-    W.ml[(part + r) * 2] = m;
-    W.ml[(part + r) * 2 + 1] = l;
+    W.ml[(part + tid) * 2] = M;
+    W.ml[(part + tid) * 2 + 1] = Ls;
   }
 }
 
-// Block (query head hq, 64 dims), 256 threads = 4 groups of spans x 64 dims:
-// each thread folds its spans' partials with a running max, the four groups
-// merge through LDS, then out = o / l * sigmoid(gate).
+// Block (query head hq, 16 dims), 256 threads = 16 groups of partials x 16
+// dims. Each thread folds its partials eight at a time (loads issued
+// together; one rescale of its running sums per batch), the groups' sums are
+// scaled to the block's max and added through LDS, then out = o / l *
+// sigmoid(gate). With has_next, blocks b < n_q + n_kv then prep row b of the
+// next step.
 template <int D, int G>
-__global__ void __launch_bounds__(kCombineDims * kCombineGroups) attn_combine_kernel(AttnIo io, AttnWork W,
-                                                                                     int n_split) {
+__global__ void __launch_bounds__(kPrepThreads) attn_combine_kernel(AttnIo io, AttnWork W, int n_split, AttnShape S,
+                                                                    AttnStep next, int has_next) {
+  constexpr int B = 8;  // partials per batch
   __shared__ float s_m[kCombineGroups][kCombineDims], s_l[kCombineGroups][kCombineDims],
       s_o[kCombineGroups][kCombineDims];
-  const int hq = blockIdx.x / (D / kCombineDims), d0 = (blockIdx.x % (D / kCombineDims)) * kCombineDims;
+  __shared__ float s_row[D];
+  __shared__ float s_red[kPrepThreads / 64];
+  constexpr int PH = D / kCombineDims;
+  const int hq = blockIdx.x / PH, d0 = (blockIdx.x % PH) * kCombineDims;
   const int g = hq / G, h = hq % G;
   const int dl = threadIdx.x % kCombineDims, grp = threadIdx.x / kCombineDims, d = d0 + dl;
   float M = -INFINITY, l = 0.f, o = 0.f;
-  for (int s = grp; s < n_split; s += kCombineGroups) {
-    const size_t part = ((size_t)g * W.max_split + s) * G + h;
-    const float ms = W.ml[part * 2], ls = W.ml[part * 2 + 1], os = W.o[part * D + d];
-    const float Mn = fmaxf(M, ms);
-    const float a = expf(M - Mn), b = expf(ms - Mn);
-    l = fmaf(l, a, ls * b);
-    o = fmaf(o, a, os * b);
-    M = Mn;
+  for (int s0 = grp; s0 < n_split; s0 += B * kCombineGroups) {
+    float ms[B], ls[B], os[B];
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      // partials past the last are read at the last one's address (no branch
+      // around the loads) and marked empty: max -inf, weight exp(-inf) = 0
+      const int s = s0 + u * kCombineGroups;
+      const size_t part = ((size_t)g * W.max_split + min(s, n_split - 1)) * G + h;
+      ms[u] = W.ml[part * 2];
+      ls[u] = W.ml[part * 2 + 1];
+      os[u] = W.o[part * D + d];
+      if (s >= n_split) ms[u] = -INFINITY;
+    }
+    float Mb = M;
+#pragma unroll
+    for (int u = 0; u < B; ++u) Mb = fmaxf(Mb, ms[u]);   // finite: s0 < n_split
+    const float a = expf(M - Mb);
+    l *= a;
+    o *= a;
+#pragma unroll
+    for (int u = 0; u < B; ++u) {
+      const float b = expf(ms[u] - Mb);
+      l = fmaf(ls[u], b, l);
+      o = fmaf(os[u], b, o);
+    }
+    M = Mb;
   }
   s_m[grp][dl] = M;
-  s_l[grp][dl] = l;
-  s_o[grp][dl] = o;
   __syncthreads();
-  if (grp != 0) return;
   float Mt = s_m[0][dl];
 #pragma unroll
-  for (int q = 1; q < kCombineGroups; ++q) Mt = fmaxf(Mt, s_m[q][dl]);
-  float lt = 0.f, ot = 0.f;
+  for (int q = 1; q < kCombineGroups; ++q) Mt = fmaxf(Mt, s_m[q][dl]);   // finite: split 0 exists
+  const float f = expf(M - Mt);   // 0 for a group with no partials
+  s_l[grp][dl] = l * f;
+  s_o[grp][dl] = o * f;
+  __syncthreads();
+  if (grp == 0) {
+    float lt = 0.f, ot = 0.f;
 #pragma unroll
-  for (int q = 0; q < kCombineGroups; ++q) {
-    const float f = s_m[q][dl] == -INFINITY ? 0.f : expf(s_m[q][dl] - Mt);
-    lt = fmaf(s_l[q][dl], f, lt);
-    ot = fmaf(s_o[q][dl], f, ot);
+    for (int q = 0; q < kCombineGroups; ++q) {
+      lt += s_l[q][dl];
+      ot += s_o[q][dl];
+    }
+    const float gt = bfv(io.gate[(size_t)hq * D + d]);
+    io.out[(size_t)hq * D + d] = ot / lt / (1.0f + expf(-gt));
   }
-  const float gt = bfv(io.gate[(size_t)hq * D + d]);
-  io.out[(size_t)hq * D + d] = ot / lt / (1.0f + expf(-gt));
+  if (has_next && (int)blockIdx.x < S.n_kv * G + S.n_kv) prep_row<D, G>(S, next, W, blockIdx.x, s_row, s_red);
 }
 
 struct AttnGraph {
@@ -356,10 +429,11 @@ using namespace moe;
 
 struct moe_attn {
   moe_attn_config cfg{};
-  int pitch = 0;           // positions per transposed V row
+  int n_spans = 0;         // 32-position V tiles per KV group (a multiple of 4)
   float* norms = nullptr;  // [L][2][d]: q norm weight, k norm weight
+  double* freq = nullptr;  // [d]: 1e7^(-2i/rot) for dims i and i + rot/2, 0 past rot
   uint16_t* kc = nullptr;  // [L][n_kv][max_pos][d]
-  uint16_t* vt = nullptr;  // [L][n_kv][d][pitch]
+  uint16_t* vt = nullptr;  // [L][n_kv][n_spans][d][32]
   AttnWork work{};
   std::vector<uint8_t> set;
   std::vector<AttnGraph> graphs;
@@ -406,41 +480,62 @@ void record(moe_attn* a, std::vector<std::pair<hipEvent_t, hipEvent_t>>& into) {
   into.emplace_back(ev.start, ev.stop);
 }
 
+AttnLayer layer_args(moe_attn* a, int layer) {
+  const size_t D = a->cfg.head_dim, KV = a->cfg.n_kv_heads;
+  const float* w = a->norms + (size_t)layer * 2 * D;
+  return AttnLayer{w, w + D, a->kc + (size_t)layer * KV * a->cfg.max_pos * D,
+                   a->vt + (size_t)layer * KV * a->n_spans * D * kSpan};
+}
+
+AttnShape shape_of(const moe_attn* a) {
+  return AttnShape{a->freq, a->cfg.n_kv_heads, a->cfg.max_pos, a->n_spans, a->cfg.rot_dim};
+}
+
+// One call's steps in order: the first step's prep, then per step the
+// partials kernel and the merge kernel (which also preps the next step).
 template <int D, int G>
-hipError_t launch_dg(moe_attn* a, const AttnLayer& L, const AttnIo& io, int pos, hipStream_t s) {
-  const int n_kv = a->cfg.n_kv_heads, n_split = pos / kSpan + 1;
-  record(a, a->prof_split);
-  launch(attn_split_kernel<D, G>, dim3(n_kv * n_split), dim3(64), 0, s, L, io, a->work, n_kv, a->cfg.max_pos,
-         a->pitch, a->cfg.rot_dim, pos);
-  record(a, a->prof_combine);
-  launch(attn_combine_kernel<D, G>, dim3(a->cfg.n_q_heads * (D / kCombineDims)), dim3(kCombineDims * kCombineGroups),
-         0, s, io, a->work, n_split);
+hipError_t launch_steps_dg(moe_attn* a, const std::vector<AttnStep>& steps, hipStream_t s) {
+  constexpr size_t lds = lds_bytes<D, G>();
+  static std::once_flag attr_once;
+  static hipError_t attr_err = hipSuccess;
+  std::call_once(attr_once, [] {
+    attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(attn_split_kernel<D, G>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  });
+  if (attr_err != hipSuccess) return attr_err;
+  const AttnShape S = shape_of(a);
+  const int n_q = a->cfg.n_q_heads, n_kv = a->cfg.n_kv_heads;
+  launch(attn_prep_kernel<D, G>, dim3(n_q + n_kv), dim3(kPrepThreads), 0, s, S, steps[0], a->work);
+  for (size_t i = 0; i < steps.size(); ++i) {
+    const AttnStep& st = steps[i];
+    const int n_split = st.pos / kBlockPos + 1;
+    const bool has_next = i + 1 < steps.size();
+    record(a, a->prof_split);
+    launch(attn_split_kernel<D, G>, dim3(n_kv * n_split), dim3(64 * kWaves), (uint32_t)lds, s, st.L, a->work, S,
+           st.pos);
+    record(a, a->prof_combine);
+    launch(attn_combine_kernel<D, G>, dim3(n_q * (D / kCombineDims)), dim3(kPrepThreads), 0, s, st.io, a->work,
+           n_split, S, has_next ? steps[i + 1] : st, has_next ? 1 : 0);
+  }
   return hipGetLastError();
 }
 
 template <int D>
-hipError_t launch_d(moe_attn* a, const AttnLayer& L, const AttnIo& io, int pos, hipStream_t s) {
+hipError_t launch_steps_d(moe_attn* a, const std::vector<AttnStep>& steps, hipStream_t s) {
   switch (a->cfg.n_q_heads / a->cfg.n_kv_heads) {
-    case 1: return launch_dg<D, 1>(a, L, io, pos, s);
-    case 2: return launch_dg<D, 2>(a, L, io, pos, s);
-    case 4: return launch_dg<D, 4>(a, L, io, pos, s);
-    case 8: return launch_dg<D, 8>(a, L, io, pos, s);
-    default: return launch_dg<D, 16>(a, L, io, pos, s);
+    case 1: return launch_steps_dg<D, 1>(a, steps, s);
+    case 2: return launch_steps_dg<D, 2>(a, steps, s);
+    case 4: return launch_steps_dg<D, 4>(a, steps, s);
+    case 8: return launch_steps_dg<D, 8>(a, steps, s);
+    default: return launch_steps_dg<D, 16>(a, steps, s);
   }
 }
 
-AttnLayer layer_args(moe_attn* a, int layer) {
-  const size_t D = a->cfg.head_dim, KV = a->cfg.n_kv_heads;
-  const float* w = a->norms + (size_t)layer * 2 * D;
-  return AttnLayer{w, w + D, a->kc + (size_t)layer * KV * a->cfg.max_pos * D, a->vt + (size_t)layer * KV * D * a->pitch};
-}
-
-hipError_t launch_attn(moe_attn* a, int layer, const AttnIo& io, int pos, hipStream_t s) {
-  const AttnLayer L = layer_args(a, layer);
+hipError_t launch_steps(moe_attn* a, const std::vector<AttnStep>& steps, hipStream_t s) {
   switch (a->cfg.head_dim) {
-    case 64: return launch_d<64>(a, L, io, pos, s);
-    case 128: return launch_d<128>(a, L, io, pos, s);
-    default: return launch_d<256>(a, L, io, pos, s);
+    case 64: return launch_steps_d<64>(a, steps, s);
+    case 128: return launch_steps_d<128>(a, steps, s);
+    default: return launch_steps_d<256>(a, steps, s);
   }
 }
 
@@ -459,6 +554,27 @@ double drain(std::vector<std::pair<hipEvent_t, hipEvent_t>>& ev, uint64_t* n) {
   return ms;
 }
 
+// Host-side access to positions [p0, p0 + n) of one KV group's V tiles: the
+// spans covering them are copied out whole, edited or read, and (for a write)
+// copied back.
+hipError_t v_tiles(uint16_t* vt_group, size_t D, int p0, int n, uint16_t* v, bool write) {
+  const int s0 = p0 / kSpan, s1 = (p0 + n - 1) / kSpan;
+  const size_t tile = D * kSpan, count = (size_t)(s1 - s0 + 1) * tile;
+  std::vector<uint16_t> buf(count);
+  hipError_t e = hipMemcpy(buf.data(), vt_group + (size_t)s0 * tile, count * 2, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  for (int i = 0; i < n; ++i) {
+    const int p = p0 + i;
+    uint16_t* col = buf.data() + (size_t)(p / kSpan - s0) * tile + p % kSpan;
+    for (size_t d = 0; d < D; ++d) {
+      if (write) col[d * kSpan] = v[(size_t)i * D + d];
+      else v[(size_t)i * D + d] = col[d * kSpan];
+    }
+  }
+  if (!write) return hipSuccess;
+  return hipMemcpy(vt_group + (size_t)s0 * tile, buf.data(), count * 2, hipMemcpyHostToDevice);
+}
+
 }  // namespace
 
 extern "C" {
@@ -471,17 +587,25 @@ moe_status moe_attn_create(const moe_attn_config* cfg, moe_attn** out) {
   if (!why.empty()) return fail(MOE_EINVAL, "moe_attn_create: " + why);
   moe_attn* a = new moe_attn();
   a->cfg = *cfg;
-  a->pitch = (cfg->max_pos + kSpan - 1) / kSpan * kSpan;
+  a->n_spans = (cfg->max_pos + kBlockPos - 1) / kBlockPos * kWaves;
   const size_t L = cfg->n_layers, D = cfg->head_dim, KV = cfg->n_kv_heads, P = cfg->max_pos;
   const size_t G = (size_t)(cfg->n_q_heads / cfg->n_kv_heads);
-  a->work.max_split = a->pitch / kSpan;
+  a->work.max_split = a->n_spans / kWaves;
   a->set.assign(L, 0);
-  const size_t kbytes = L * KV * P * D * 2, vbytes = L * KV * D * a->pitch * 2;
+  const size_t kbytes = L * KV * P * D * 2, vbytes = L * KV * (size_t)a->n_spans * D * kSpan * 2;
+  // rotation frequencies in fp64, as the definition takes them: dims i and
+  // i + rot/2 turn by pos * 1e7^(-2i/rot)
+  std::vector<double> freq(D, 0.0);
+  for (int i = 0; i < cfg->rot_dim / 2; ++i)
+    freq[(size_t)i] = freq[(size_t)i + cfg->rot_dim / 2] = std::pow(1.0e7, -2.0 * i / cfg->rot_dim);
   bool ok = hipMalloc(&a->norms, L * 2 * D * sizeof(float)) == hipSuccess;
+  ok = ok && hipMalloc(&a->freq, D * sizeof(double)) == hipSuccess;
+  ok = ok && hipMemcpy(a->freq, freq.data(), D * sizeof(double), hipMemcpyHostToDevice) == hipSuccess;
   ok = ok && hipMalloc(&a->kc, kbytes) == hipSuccess;
   ok = ok && hipMalloc(&a->vt, vbytes) == hipSuccess;
   ok = ok && hipMalloc(&a->work.ml, KV * a->work.max_split * G * 2 * sizeof(float)) == hipSuccess;
   ok = ok && hipMalloc(&a->work.o, KV * a->work.max_split * G * D * sizeof(float)) == hipSuccess;
+  ok = ok && hipMalloc(&a->work.qop, (size_t)cfg->n_q_heads * 2 * D * sizeof(_Float16)) == hipSuccess;
   ok = ok && hipMemset(a->kc, 0, kbytes) == hipSuccess && hipMemset(a->vt, 0, vbytes) == hipSuccess;
   ok = ok && hipDeviceSynchronize() == hipSuccess;
   {
@@ -524,18 +648,13 @@ moe_status moe_attn_write_cache(moe_attn* a, int32_t layer, int32_t first_pos, i
   if (n == 0) return MOE_OK;
   if (!k || !v) return fail(MOE_EINVAL, "moe_attn_write_cache: NULL pointer");
   if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_EHIP, "moe_attn_write_cache: sync");
-  const size_t D = a->cfg.head_dim, KV = a->cfg.n_kv_heads, P = a->cfg.max_pos, pitch = a->pitch;
+  const size_t D = a->cfg.head_dim, KV = a->cfg.n_kv_heads, P = a->cfg.max_pos;
   const AttnLayer L = layer_args(a, layer);
-  // V goes in transposed: one strided 2D copy per group
   for (size_t g = 0; g < KV; ++g) {
-    const uint16_t* kg = k + g * n * D;
-    const uint16_t* vg = v + g * n * D;
-    std::vector<uint16_t> vtg(D * (size_t)n);
-    for (int p = 0; p < n; ++p)
-      for (size_t d = 0; d < D; ++d) vtg[d * n + p] = vg[(size_t)p * D + d];
-    if (hipMemcpy(L.kc + (g * P + first_pos) * D, kg, (size_t)n * D * 2, hipMemcpyHostToDevice) != hipSuccess ||
-        hipMemcpy2D(L.vt + g * D * pitch + first_pos, pitch * 2, vtg.data(), (size_t)n * 2, (size_t)n * 2, D,
-                    hipMemcpyHostToDevice) != hipSuccess)
+    std::vector<uint16_t> vg(v + g * n * D, v + (g + 1) * n * D);
+    if (hipMemcpy(L.kc + (g * P + first_pos) * D, k + g * n * D, (size_t)n * D * 2, hipMemcpyHostToDevice) !=
+            hipSuccess ||
+        v_tiles(L.vt + g * a->n_spans * D * kSpan, D, first_pos, n, vg.data(), true) != hipSuccess)
       return fail(MOE_EHIP, "moe_attn_write_cache: upload");
   }
   return MOE_OK;
@@ -550,20 +669,14 @@ moe_status moe_attn_read_cache(moe_attn* a, int32_t layer, int32_t first_pos, in
     return fail(MOE_EINVAL, "moe_attn_read_cache: positions outside [0, max_pos)");
   if (n == 0) return MOE_OK;
   if (hipDeviceSynchronize() != hipSuccess) return fail(MOE_EHIP, "moe_attn_read_cache: sync");
-  const size_t D = a->cfg.head_dim, KV = a->cfg.n_kv_heads, P = a->cfg.max_pos, pitch = a->pitch;
+  const size_t D = a->cfg.head_dim, KV = a->cfg.n_kv_heads, P = a->cfg.max_pos;
   const AttnLayer L = layer_args(a, layer);
   for (size_t g = 0; g < KV; ++g) {
     if (k && hipMemcpy(k + g * n * D, L.kc + (g * P + first_pos) * D, (size_t)n * D * 2, hipMemcpyDeviceToHost) !=
                  hipSuccess)
       return fail(MOE_EHIP, "moe_attn_read_cache: copy");
-    if (v) {
-      std::vector<uint16_t> vtg(D * (size_t)n);
-      if (hipMemcpy2D(vtg.data(), (size_t)n * 2, L.vt + g * D * pitch + first_pos, pitch * 2, (size_t)n * 2, D,
-                      hipMemcpyDeviceToHost) != hipSuccess)
-        return fail(MOE_EHIP, "moe_attn_read_cache: copy");
-      for (int p = 0; p < n; ++p)
-        for (size_t d = 0; d < D; ++d) v[g * n * D + (size_t)p * D + d] = vtg[d * n + p];
-    }
+    if (v && v_tiles(L.vt + g * a->n_spans * D * kSpan, D, first_pos, n, v + g * n * D, false) != hipSuccess)
+      return fail(MOE_EHIP, "moe_attn_read_cache: copy");
   }
   return MOE_OK;
 }
@@ -584,14 +697,17 @@ moe_status moe_attn_decode(moe_attn* a, int32_t first_layer, int32_t n_layers, i
     if (!a->set[(size_t)l]) return fail(MOE_ESTATE, "moe_attn_decode: moe_attn_set_layer was not called for a layer");
   const size_t D = a->cfg.head_dim, QD = (size_t)a->cfg.n_q_heads * D, KD = (size_t)a->cfg.n_kv_heads * D;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  std::vector<AttnStep> steps;
+  steps.reserve((size_t)n_tok * n_layers);
+  for (int t = 0; t < n_tok; ++t)
+    for (int l = first_layer; l < first_layer + n_layers; ++l) {
+      const size_t r = (size_t)t * n_layers + (l - first_layer);
+      steps.push_back(AttnStep{layer_args(a, l), AttnIo{q + r * QD, gate + r * QD, k + r * KD, v + r * KD, out + r * QD},
+                               pos0 + t});
+    }
   auto enqueue = [&](hipStream_t qs) -> moe_status {
-    for (int t = 0; t < n_tok; ++t)
-      for (int l = first_layer; l < first_layer + n_layers; ++l) {
-        const size_t r = (size_t)t * n_layers + (l - first_layer);
-        const AttnIo io{q + r * QD, gate + r * QD, k + r * KD, v + r * KD, out + r * QD};
-        const hipError_t e = launch_attn(a, l, io, pos0 + t, qs);
-        if (e != hipSuccess) return fail(MOE_EHIP, std::string("moe_attn_decode: launch: ") + hipGetErrorString(e));
-      }
+    const hipError_t e = launch_steps(a, steps, qs);
+    if (e != hipSuccess) return fail(MOE_EHIP, std::string("moe_attn_decode: launch: ") + hipGetErrorString(e));
     return MOE_OK;
   };
   if ((int64_t)n_tok * n_layers < 16 || a->prof) return enqueue(s);
@@ -668,10 +784,12 @@ void moe_attn_destroy(moe_attn* a) {
   }
   if (a->cap_stream) hipStreamDestroy(a->cap_stream);
   hipFree(a->norms);
+  hipFree(a->freq);
   hipFree(a->kc);
   hipFree(a->vt);
   hipFree(a->work.ml);
   hipFree(a->work.o);
+  hipFree(a->work.qop);
   delete a;
 }
 

@@ -9,9 +9,12 @@ into fp32 MFMA accumulation, so scores and weighted sums hold about fp32
 accuracy (relative error a few 1e-7 per sum of 8192 terms); the one place the
 two sides may differ by more is the fp16 rounding of a new K value whose fp32
 and fp64 values fall on either side of a rounding boundary (one fp16 ulp,
-2^-11 relative, in that element). The bars: per-(token, layer) relative L2
-error <= 1e-4; written V rows bit-exact (fp16 of a bf16 input); written K rows
-within one fp16 ulp, on at most 1% of the values."""
+2^-11 relative, in that element); near zero, where fp16 spacing falls below
+the fp32 rotation's own error (a few 1e-8 times the row's scale, from the fp32
+sine and cosine of the reduced angle), the bound is 2^-21 absolute instead.
+The bars: per-(token, layer) relative L2 error <= 1e-4; written V rows
+bit-exact (fp16 of a bf16 input); written K rows within max(one fp16 ulp,
+2^-21), on at most 1% of the values."""
 import numpy as np
 import pytest
 
@@ -25,6 +28,7 @@ import gpu_helpers as gh
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-4
+K_ABS = 2.0 ** -21
 
 
 def _f64(bits):
@@ -99,8 +103,9 @@ class Case:
         assert np.array_equal(vg, vo), f"layer {l}: written V rows differ"
         diff = kg != ko
         if diff.any():
-            ulp = np.abs(kg - ko) / np.spacing(np.abs(ko).astype(np.float16)).astype(np.float64)
-            assert ulp[diff].max() <= 1.0, f"layer {l}: K row off by {ulp[diff].max()} ulp"
+            bound = np.maximum(np.spacing(np.abs(ko).astype(np.float16)).astype(np.float64), K_ABS)
+            over = np.abs(kg - ko) / bound
+            assert over.max() <= 1.0, f"layer {l}: K differs by {over.max():.2f} x the bound"
             assert diff.mean() <= 0.01, f"layer {l}: {diff.mean():.3%} of K values differ"
         # the context below the new rows is untouched
         if c.context:
