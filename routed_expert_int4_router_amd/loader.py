@@ -24,10 +24,12 @@ from . import _lib
 
 
 def load_model(cfg, weights, storage: int = _lib.STORE_DEVICE, threads: int = 16, chunk: int = 64,
-               layers: Optional[range] = None, blob_path: Optional[str] = None, direct: bool = True) -> _lib.Model:
+               layers: Optional[range] = None, blob_path: Optional[str] = None, direct: bool = True,
+               progress=None) -> _lib.Model:
     """A model filled from ``weights``. A file-backed model (STORE_FILE) needs
     ``blob_path``: the records are written there (replacing the file) and the
-    model opens it, with O_DIRECT when ``direct`` and the filesystem allow."""
+    model opens it, with O_DIRECT when ``direct`` and the filesystem allow.
+    ``progress(layer)``, if given, is called after each layer is filled."""
     c = _lib.config_of(cfg)
     if storage == _lib.STORE_FILE and not blob_path:
         raise ValueError("a file-backed model needs blob_path")
@@ -35,7 +37,8 @@ def load_model(cfg, weights, storage: int = _lib.STORE_DEVICE, threads: int = 16
     try:
         if storage == _lib.STORE_FILE:
             with open(blob_path, "wb") as f:
-                fill_model(model, weights, threads=threads, chunk=chunk, layers=layers, blob_file=f)
+                fill_model(model, weights, threads=threads, chunk=chunk, layers=layers, blob_file=f,
+                           progress=progress)
                 # on storage and out of the page cache: the first read of every
                 # record comes from the device, buffered or not
                 f.flush()
@@ -44,7 +47,7 @@ def load_model(cfg, weights, storage: int = _lib.STORE_DEVICE, threads: int = 16
                     os.posix_fadvise(f.fileno(), 0, 0, os.POSIX_FADV_DONTNEED)
             model.open_blob(blob_path, 0, direct)
         else:
-            fill_model(model, weights, threads=threads, chunk=chunk, layers=layers)
+            fill_model(model, weights, threads=threads, chunk=chunk, layers=layers, progress=progress)
     except Exception:
         model.close()
         raise
@@ -63,7 +66,7 @@ def fill_dense(model: _lib.Model, weights, layers: Optional[range] = None):
 
 
 def fill_model(model: _lib.Model, weights, threads: int = 16, chunk: int = 64, layers: Optional[range] = None,
-               blob_file=None):
+               blob_file=None, progress=None):
     """Upload the dense weights and pack the experts: into the pinned blob
     (host storage), into a writable binary ``blob_file`` at gid * stride (file
     storage), or into HBM (device storage)."""
@@ -96,4 +99,6 @@ def fill_model(model: _lib.Model, weights, threads: int = 16, chunk: int = 64, l
                     blob_file.write(_lib.pack(c, wg, wu, wd).tobytes())
                 else:
                     model.set_experts(gid, _lib.pack(c, wg, wu, wd))
+            if progress is not None:
+                progress(layer)
     return model

@@ -29,13 +29,24 @@ _T0 = None
 
 
 def log(msg: str) -> None:
-    """Progress line of a long GPU test (flushed, so a slow step is visibly alive)."""
+    """Progress line of a long GPU test, flushed to stderr and appended to
+    gpurun_out/gpu_test_progress.log at the repository root: pytest captures
+    stderr, and the file shows a slow step is alive either way."""
+    import os
     import sys
     import time
     global _T0
     if _T0 is None:
         _T0 = time.time()
-    print(f"[{time.time() - _T0:8.1f}s] {msg}", file=sys.stderr, flush=True)
+    line = f"[{time.time() - _T0:8.1f}s] {msg}"
+    print(line, file=sys.stderr, flush=True)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    try:
+        os.makedirs(os.path.join(root, "gpurun_out"), exist_ok=True)
+        with open(os.path.join(root, "gpurun_out", "gpu_test_progress.log"), "a") as f:
+            f.write(line + "\n")
+    except OSError:
+        pass
 
 
 def torch_cuda():
@@ -59,7 +70,9 @@ def build(cfg: synth.Config, storage=moe.STORE_DEVICE):
     big = cfg.n_layers * cfg.n_experts >= 4096
     if big:
         log(f"loading {cfg.name}: {cfg.n_layers} layers x {cfg.n_experts} experts")
-    m = loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage)
+    prog = (lambda l: log(f"  {cfg.name}: layer {l + 1} of {cfg.n_layers} filled") if l % 8 == 7 else None) \
+        if big else None
+    m = loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage, progress=prog)
     if big:
         log(f"loaded {cfg.name}")
     return m
