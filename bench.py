@@ -262,6 +262,11 @@ def measure(cfg, args, torch, moe, loader, synth, steps: int, warmup: int, kerne
     T = cfg.n_tokens
     log(f"workload {cfg.name}: {cfg.description}")
     t0 = time.perf_counter()
+
+    def prog(layer):
+        if cfg.n_layers >= 8 and layer % 8 == 7:
+            log(f"filled {layer + 1} of {cfg.n_layers} layers ({time.perf_counter() - t0:.0f}s)")
+
     storage = moe.STORE_HOST if cfg.pool_budget else moe.STORE_DEVICE
     blob_path = None
     if cfg.pool_budget and args.storage == "file":
@@ -278,9 +283,9 @@ def measure(cfg, args, torch, moe, loader, synth, steps: int, warmup: int, kerne
         else:
             log(f"writing the blob file {blob_path} ({size} bytes)")
             model = loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage, blob_path=blob_path,
-                                      direct=not args.buffered)
+                                      direct=not args.buffered, progress=prog)
     else:
-        model = loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage)
+        model = loader.load_model(cfg, synth.SynthWeights(cfg), storage=storage, progress=prog)
     log(f"model loaded in {time.perf_counter() - t0:.1f}s")
     pool = moe.Pool(model, cfg.pool_budget) if cfg.pool_budget else None
     xb = synth.tokens(cfg.seed, T, cfg.hidden)
