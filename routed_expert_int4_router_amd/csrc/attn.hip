@@ -171,11 +171,27 @@ __global__ void __launch_bounds__(kPrepThreads) attn_prep_kernel(AttnShape S, At
   prep_row<D, G>(S, st, W, blockIdx.x, s_row, s_red);
 }
 
-// LDS of the partials kernel: the waves' scaled weighted sums, rows of D + 16
-// floats (the padding spreads the rows of consecutive heads over the banks).
+// LDS of the partials kernel: first the KV group's q operand, G rows of hi
+// and lo (2 D fp16 + 32 of padding, so consecutive heads' rows start 16 banks
+// apart), then, once every wave is past its MFMAs, the waves' scaled weighted
+// sums, rows of D + 16 floats (the same purpose).
+template <int D>
+constexpr int q_pitch() {
+  return 2 * D + 32;
+}
 template <int D, int G>
 constexpr size_t lds_bytes() {
-  return (size_t)kWaves * G * (D + 16) * 4;
+  constexpr size_t q = (size_t)G * q_pitch<D>() * 2, o = (size_t)kWaves * G * (D + 16) * 4;
+  return q > o ? q : o;
+}
+
+// Block barrier that waits for this wave's LDS accesses only (lgkmcnt(0);
+// vmcnt and expcnt at their maximum), so global loads stay in flight across
+// it; the compiler may not move memory accesses across it either.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
 // Block (KV group g = blockIdx.x % n_kv, positions [b0, b0 + 128), b0 = 128 *
@@ -198,7 +214,9 @@ __global__ void __launch_bounds__(64 * kWaves) attn_split_kernel(AttnLayer L, At
   constexpr int NS = D / 32;   // score k-steps
   constexpr int NT = D / 16;   // weighted-sum tiles
   constexpr int OP = D + 16;   // LDS row pitch of the merge, floats
-  extern __shared__ __align__(16) float s_o[];   // [kWaves][G][OP]
+  constexpr int QP = q_pitch<D>();
+  extern __shared__ __align__(16) float s_o[];   // [kWaves][G][OP], after the MFMAs
+  _Float16* s_q = reinterpret_cast<_Float16*>(s_o);   // [G][QP]: hi [D], lo [D]
   __shared__ float s_ml[kWaves * G * 2];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, r = lane & 15, gq = lane >> 4;
@@ -207,17 +225,18 @@ __global__ void __launch_bounds__(64 * kWaves) attn_split_kernel(AttnLayer L, At
   const bool live = j0 <= pos;                  // wave-uniform
   const bool mine = live && pos < j0 + kSpan;   // this wave's span holds pos
 
-  // 1. loads, every one unconditional at an in-range address: the q operand of
-  //    column r (columns r >= G read row G - 1, then zero), the K rows (rows
-  //    past pos read row pos), the V tile (a wave past pos reads its own tile,
-  //    in range as n_spans covers whole blocks, and uses none of it)
-  const _Float16* qrow = W.qop + (size_t)(g * G + min(r, G - 1)) * 2 * D + 8 * gq;
-  f16x8 bh[NS], bl[NS];
+  // 1. loads, every one unconditional at an in-range address: the group's q
+  //    operand (8 KiB at the 80B shape, shared by the block: 16 bytes per
+  //    thread per round), the K rows (rows past pos read row pos), the V tile
+  //    (a wave past pos reads its own tile, in range as n_spans covers whole
+  //    blocks, and uses none of it)
+  constexpr int QCH = G * D / 4;                         // 16-byte chunks of the q operand
+  constexpr int QR = (QCH + 64 * kWaves - 1) / (64 * kWaves);
+  const _Float16* qsrc = W.qop + (size_t)g * G * 2 * D;
+  uint4 qv[QR];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    bh[s] = *reinterpret_cast<const f16x8*>(qrow + 32 * s);
-    bl[s] = *reinterpret_cast<const f16x8*>(qrow + D + 32 * s);
-  }
+  for (int u = 0; u < QR; ++u)
+    qv[u] = *reinterpret_cast<const uint4*>(qsrc + 8 * (size_t)min(tid + 64 * kWaves * u, QCH - 1));
   uint4 ka[2][NS], va[NT];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -229,6 +248,25 @@ __global__ void __launch_bounds__(64 * kWaves) attn_split_kernel(AttnLayer L, At
   const uint16_t* tile = L.vt + ((size_t)g * S.n_spans + j0 / kSpan) * D * kSpan;
 #pragma unroll
   for (int n = 0; n < NT; ++n) va[n] = *reinterpret_cast<const uint4*>(tile + (16 * n + r) * kSpan + 8 * gq);
+
+  // the q operand to LDS (its loads came first, so waiting for them leaves
+  // the cache loads in flight), then column r's operand (columns r >= G read
+  // row G - 1, then zero)
+#pragma unroll
+  for (int u = 0; u < QR; ++u) {
+    const int idx = tid + 64 * kWaves * u;
+    if (idx < QCH) *reinterpret_cast<uint4*>(s_q + (idx / (D / 4)) * QP + 8 * (idx % (D / 4))) = qv[u];
+  }
+  lds_barrier();
+  f16x8 bh[NS], bl[NS];
+  {
+    const _Float16* qrow = s_q + min(r, G - 1) * QP + 8 * gq;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      bh[s] = *reinterpret_cast<const f16x8*>(qrow + 32 * s);
+      bl[s] = *reinterpret_cast<const f16x8*>(qrow + D + 32 * s);
+    }
+  }
 
   float m = -INFINITY, l = 0.f;
   f32x4 o[NT];
@@ -303,28 +341,34 @@ __global__ void __launch_bounds__(64 * kWaves) attn_split_kernel(AttnLayer L, At
 
   // 5. merge of the four waves: each scales its sums by exp(m_w - M), the
   //    block sums them; a wave with no live position (m = -inf) adds nothing
+  //    (its rows zero; the LDS holding the q operand is free once every
+  //    wave is past the first barrier below)
   if (lane < G) {
     s_ml[(w * G + lane) * 2] = m;
     s_ml[(w * G + lane) * 2 + 1] = l;
   }
   __syncthreads();
-  if (live && r < G) {
+  if (r < G) {
     float M = s_ml[r * 2];
 #pragma unroll
     for (int v = 1; v < kWaves; ++v) M = fmaxf(M, s_ml[(v * G + r) * 2]);
-    const float f = expf(m - M);
+    float* row = s_o + ((size_t)w * G + r) * OP + 4 * gq;
+    if (live) {
+      const float f = expf(m - M);
 #pragma unroll
-    for (int n = 0; n < NT; ++n)
-      *reinterpret_cast<f32x4*>(s_o + ((size_t)w * G + r) * OP + 16 * n + 4 * gq) = o[n] * f;
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(row + 16 * n) = o[n] * f;
+    } else {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) *reinterpret_cast<f32x4*>(row + 16 * n) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
   }
   __syncthreads();
   const size_t part = ((size_t)g * W.max_split + blk) * G;
   for (int idx = tid; idx < G * D / 4; idx += 64 * kWaves) {
     const int h = idx * 4 / D, d = idx * 4 % D;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc = *reinterpret_cast<const f32x4*>(s_o + (size_t)h * OP + d);
 #pragma unroll
-    for (int v = 0; v < kWaves; ++v)
-      if (s_ml[(v * G + h) * 2] != -INFINITY) acc += *reinterpret_cast<const f32x4*>(s_o + ((size_t)v * G + h) * OP + d);
+    for (int v = 1; v < kWaves; ++v) acc += *reinterpret_cast<const f32x4*>(s_o + ((size_t)v * G + h) * OP + d);
     *reinterpret_cast<f32x4*>(W.o + (part + h) * D + d) = acc;
   }
   if (tid < G) {
