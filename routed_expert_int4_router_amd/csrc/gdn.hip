@@ -25,7 +25,12 @@
 // sums over k are DPP reductions within the row's TPV lanes. Every block
 // recomputes its key head's q and k (a few hundred channels), cheaper than an
 // exchange between blocks. The gated RMS norm needs all d_v outputs of a
-// head, so a second, small kernel (one block per head) applies it.
+// head, which lie in 8 blocks, so each step's kernel also applies the norm of
+// the step before it (its outputs are complete by then: a few hundred bytes
+// per block, read while the state loads are in flight); a call's last step
+// is normed by a small kernel of its own (one block per head). Folding the
+// norm into one block per head instead (32 blocks of 1024 threads, 64 KiB of
+// state each) was slower: 32 CUs move the state at a fraction of 256's rate.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -47,6 +52,16 @@ namespace {
 __device__ __forceinline__ float bf(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + expf(-x)); }
 
+// One output of the gated RMS norm of a head whose d_v outputs before the
+// norm have sum of squares ss; the same expression wherever a step is normed
+// (the next step's kernel or the call's last norm kernel), so outputs do not
+// depend on how a sequence is split into calls.
+template <int DV>
+__device__ __forceinline__ float gated_norm(float o, float ss, float w, float z) {
+  const float inv = 1.0f / sqrtf(ss / (float)DV + 1e-6f);
+  return o * inv * w * silu_f(z);
+}
+
 struct GdnLayer {
   const float* conv_w;   // [C][4]
   const float* a_log;    // [Hv]
@@ -65,6 +80,17 @@ struct GdnIo {
   float* out;            // [Hv * dv]
 };
 
+// The previous step's gated norm, applied by the next step's kernel: its
+// outputs before the norm, its z, its layer's norm weight and its output.
+// With valid = 0 the pointers are any readable ones and nothing is written.
+struct GdnPrevNorm {
+  const float* o;        // [Hv][dv]
+  const uint16_t* z;     // [Hv * dv]
+  const float* norm_w;   // [dv]
+  float* out;            // [Hv * dv]
+  int valid;
+};
+
 // Threads per block and state rows per block of the state kernel.
 template <int DK, int DV>
 struct GdnTile {
@@ -77,16 +103,18 @@ struct GdnTile {
 // Block (head h, row chunk) of the state kernel: the conv, norms and gates
 // of head h (every block of the head recomputes them, a few hundred
 // channels), then rows [R c, R c + R) of the head's state: decay, S^T k,
-// delta-rule write, S^T q. Writes o before the norm to o_pre.
+// delta-rule write, S^T q. Writes o before the norm to o_pre; with
+// prev.valid, also writes rows [R c, R c + R) of head h of the previous
+// step's normed output.
 template <int DK, int DV>
-__global__ void __launch_bounds__(DV * (DK / 16) < 128 ? DV * (DK / 16) : 128) gdn_state_kernel(GdnLayer L, GdnIo io, float* o_pre, int n_k,
-                                                                         int n_v) {
+__global__ void __launch_bounds__(DV * (DK / 16) < 128 ? DV * (DK / 16) : 128) gdn_state_kernel(GdnLayer L, GdnIo io, float* o_pre, GdnPrevNorm prev,
+                                                                         int n_k, int n_v) {
   using Tl = GdnTile<DK, DV>;
   constexpr int TPV = Tl::TPV, NT = Tl::NT, R = Tl::R, NC = Tl::NC;
   static_assert(TPV >= 1 && TPV <= 16 && (TPV & (TPV - 1)) == 0, "state rows are reduced within a DPP row");
   static_assert(NT % 64 == 0, "whole waves");
   __shared__ float s_q[DK], s_k[DK], s_v[R];
-  __shared__ float s_red[2][NT / 64];
+  __shared__ float s_red[3][NT / 64];
   const int h = blockIdx.x / NC, chunk = blockIdx.x % NC;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int kh = h / (n_v / n_k);
@@ -101,6 +129,13 @@ __global__ void __launch_bounds__(DV * (DK / 16) < 128 ? DV * (DK / 16) : 128) g
 
   // gate inputs of the head, also before any wait
   const float a_in = bf(io.a[h]), b_in = bf(io.b[h]), dt = L.dt_bias[h], alog = L.a_log[h];
+  // the previous step's outputs of head h before its norm (thread t < DV: row
+  // t; NT >= DV), and z and the norm weight of this block's rows (t < R)
+  const float po_all = prev.o[(size_t)h * DV + min(t, DV - 1)];   // unconditional load, then select
+  const float po = t < DV ? po_all : 0.f;
+  const int pv = chunk * R + min(t, R - 1);
+  const float pz = bf(prev.z[(size_t)h * DV + pv]), pw = prev.norm_w[pv];
+  const float po_row = prev.o[(size_t)h * DV + pv];
 
   // 2. convolution + SiLU: q and k of the key head, v of the block's rows. The
   //    history moves on in the other buffer, each channel's by one block only
@@ -144,7 +179,8 @@ __global__ void __launch_bounds__(DV * (DK / 16) < 128 ? DV * (DK / 16) : 128) g
     }
   }
   __syncthreads();
-  // 3. L2 norms of q and k (wave sums, then the waves in order)
+  // 3. L2 norms of q and k, and the previous step's sum of o^2 (wave sums,
+  //    then the waves in order)
   {
     float sq = 0.f, sk = 0.f;
     for (int c = t; c < DK; c += NT) {
@@ -153,17 +189,21 @@ __global__ void __launch_bounds__(DV * (DK / 16) < 128 ? DV * (DK / 16) : 128) g
     }
     sq = dpp::wave_sum(sq);
     sk = dpp::wave_sum(sk);
+    const float so = dpp::wave_sum(po * po);
     if (lane == 0) {
       s_red[0][wv] = sq;
       s_red[1][wv] = sk;
+      s_red[2][wv] = so;
     }
   }
   __syncthreads();
-  float nq2 = 0.f, nk2 = 0.f;
+  float nq2 = 0.f, nk2 = 0.f, no2 = 0.f;
   for (int w = 0; w < NT / 64; ++w) {
     nq2 += s_red[0][w];
     nk2 += s_red[1][w];
+    no2 += s_red[2][w];
   }
+  if (prev.valid && t < R) prev.out[(size_t)h * DV + pv] = gated_norm<DV>(po_row, no2, pw, pz);
   const float qs = 1.0f / (sqrtf(nq2 + 1e-6f) * sqrtf((float)DK));
   const float ks = 1.0f / sqrtf(nk2 + 1e-6f);
   // 4. gates of the head
@@ -221,13 +261,15 @@ __global__ void __launch_bounds__(DV < 64 ? 64 : DV) gdn_norm_kernel(const float
   __syncthreads();
   float ss = 0.f;
   for (int q = 0; q < NW; ++q) ss += s_red[q];
-  const float inv = 1.0f / sqrtf(ss / (float)DV + 1e-6f);
-  if (live) out[(size_t)h * DV + v] = o * inv * norm_w[v] * silu_f(bf(z[(size_t)h * DV + v]));
+  if (live) out[(size_t)h * DV + v] = gated_norm<DV>(o, ss, norm_w[v], bf(z[(size_t)h * DV + v]));
 }
 
 struct GdnGraph {
   int layer0, n_layers, n_tok, parity;
   const void* qkv;
+  const void* z;
+  const void* a;
+  const void* b;
   void* out;
   hipGraphExec_t exec;
   hipEvent_t done;
@@ -248,7 +290,7 @@ struct moe_gdn {
   size_t params_per_layer = 0;
   float* state = nullptr;    // [L][Hv][dv][dk]
   float* window = nullptr;   // [L][2][C][3]
-  float* o_pre = nullptr;    // [Hv][dv]: a step's output before the norm
+  float* o_pre = nullptr;    // [2][Hv][dv]: steps' outputs before the norm (even, odd steps of a call)
   std::vector<int64_t> pos;  // tokens each layer has taken
   std::vector<uint8_t> set;
   std::vector<GdnGraph> graphs;
@@ -297,7 +339,8 @@ GdnLayer layer_args(moe_gdn* g, int l, int parity) {
 }
 
 template <int D>
-hipError_t launch_step_d(moe_gdn* g, const GdnLayer& L, const GdnIo& io, float* o_pre, hipStream_t s) {
+hipError_t launch_step_d(moe_gdn* g, const GdnLayer& L, const GdnIo& io, float* o_pre, const GdnPrevNorm& prev,
+                         hipStream_t s) {
   using Tl = GdnTile<D, D>;
   const int Hv = g->cfg.n_v_heads, Hk = g->cfg.n_k_heads;
   if (g->prof) {
@@ -307,16 +350,31 @@ hipError_t launch_step_d(moe_gdn* g, const GdnLayer& L, const GdnIo& io, float* 
     launch_events() = ev;
     g->prof_events.emplace_back(ev.start, ev.stop);
   }
-  launch(gdn_state_kernel<D, D>, dim3(Hv * Tl::NC), dim3(Tl::NT), 0, s, L, io, o_pre, Hk, Hv);
-  launch(gdn_norm_kernel<D>, dim3(Hv), dim3(D < 64 ? 64 : D), 0, s, (const float*)o_pre, L.norm_w, io.z, io.out);
+  launch(gdn_state_kernel<D, D>, dim3(Hv * Tl::NC), dim3(Tl::NT), 0, s, L, io, o_pre, prev, Hk, Hv);
   return hipGetLastError();
 }
 
-hipError_t launch_step(moe_gdn* g, const GdnLayer& L, const GdnIo& io, hipStream_t s) {
+template <int D>
+hipError_t launch_norm_d(moe_gdn* g, const GdnPrevNorm& last, hipStream_t s) {
+  launch(gdn_norm_kernel<D>, dim3(g->cfg.n_v_heads), dim3(D < 64 ? 64 : D), 0, s, last.o, last.norm_w, last.z,
+         last.out);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm(moe_gdn* g, const GdnPrevNorm& last, hipStream_t s) {
   switch (g->cfg.d_k) {
-    case 128: return launch_step_d<128>(g, L, io, g->o_pre, s);
-    case 64: return launch_step_d<64>(g, L, io, g->o_pre, s);
-    default: return launch_step_d<32>(g, L, io, g->o_pre, s);
+    case 128: return launch_norm_d<128>(g, last, s);
+    case 64: return launch_norm_d<64>(g, last, s);
+    default: return launch_norm_d<32>(g, last, s);
+  }
+}
+
+hipError_t launch_step(moe_gdn* g, const GdnLayer& L, const GdnIo& io, float* o_pre, const GdnPrevNorm& prev,
+                       hipStream_t s) {
+  switch (g->cfg.d_k) {
+    case 128: return launch_step_d<128>(g, L, io, o_pre, prev, s);
+    case 64: return launch_step_d<64>(g, L, io, o_pre, prev, s);
+    default: return launch_step_d<32>(g, L, io, o_pre, prev, s);
   }
 }
 
@@ -341,7 +399,7 @@ moe_status moe_gdn_create(const moe_gdn_config* cfg, moe_gdn** out) {
   bool ok = hipMalloc(&g->params, L * g->params_per_layer * sizeof(float)) == hipSuccess;
   ok = ok && hipMalloc(&g->state, L * Hv * dv * dk * sizeof(float)) == hipSuccess;
   ok = ok && hipMalloc(&g->window, L * 2 * g->C * 3 * sizeof(float)) == hipSuccess;
-  ok = ok && hipMalloc(&g->o_pre, Hv * dv * sizeof(float)) == hipSuccess;
+  ok = ok && hipMalloc(&g->o_pre, 2 * Hv * dv * sizeof(float)) == hipSuccess;
   ok = ok && hipMemset(g->params, 0, L * g->params_per_layer * sizeof(float)) == hipSuccess;
   ok = ok && hipMemset(g->state, 0, L * Hv * dv * dk * sizeof(float)) == hipSuccess;
   ok = ok && hipMemset(g->window, 0, L * 2 * g->C * 3 * sizeof(float)) == hipSuccess;
@@ -412,15 +470,24 @@ moe_status moe_gdn_decode(moe_gdn* g, int32_t first_layer, int32_t n_layers, con
   for (int l = first_layer; l < first_layer + n_layers; ++l)
     if ((int)(g->pos[(size_t)l] & 1) != parity)
       return fail(MOE_ESTATE, "moe_gdn_decode: the layers of one call must have taken the same number of tokens");
+  // step k (token-major) writes its outputs before the norm to o_pre half
+  // k % 2 and norms step k - 1's; the call's last step is normed on its own
   auto enqueue = [&](hipStream_t q) -> moe_status {
+    GdnPrevNorm prev{g->o_pre, z, nullptr, out, 0};
     for (int t = 0; t < n_tok; ++t) {
       for (int l = first_layer; l < first_layer + n_layers; ++l) {
         const size_t r = (size_t)t * n_layers + (l - first_layer);
         GdnIo io{qkv + r * C, z + r * Z, a + r * Hv, b + r * Hv, out + r * Z};
-        const hipError_t e = launch_step(g, layer_args(g, l, (parity + t) & 1), io, q);
+        const GdnLayer L = layer_args(g, l, (parity + t) & 1);
+        float* o_cur = g->o_pre + (r & 1) * Hv * g->cfg.d_v;
+        if (!prev.norm_w) prev.norm_w = L.norm_w;   // first step: any readable weight
+        const hipError_t e = launch_step(g, L, io, o_cur, prev, q);
         if (e != hipSuccess) return fail(MOE_EHIP, std::string("moe_gdn_decode: launch: ") + hipGetErrorString(e));
+        prev = GdnPrevNorm{o_cur, io.z, L.norm_w, io.out, 1};
       }
     }
+    const hipError_t e = launch_norm(g, prev, q);
+    if (e != hipSuccess) return fail(MOE_EHIP, std::string("moe_gdn_decode: launch: ") + hipGetErrorString(e));
     return MOE_OK;
   };
   if ((int64_t)n_tok * n_layers < 16 || g->prof) {
@@ -430,7 +497,7 @@ moe_status moe_gdn_decode(moe_gdn* g, int32_t first_layer, int32_t n_layers, con
     GdnGraph* hit = nullptr;
     for (auto& e : g->graphs)
       if (e.layer0 == first_layer && e.n_layers == n_layers && e.n_tok == n_tok && e.parity == parity &&
-          e.qkv == qkv && e.out == out)
+          e.qkv == qkv && e.z == z && e.a == a && e.b == b && e.out == out)
         hit = &e;
     if (!hit) {
       if (!g->cap_stream && hipStreamCreateWithFlags(&g->cap_stream, hipStreamNonBlocking) != hipSuccess)
@@ -445,7 +512,7 @@ moe_status moe_gdn_decode(moe_gdn* g, int32_t first_layer, int32_t n_layers, con
         return st;
       }
       if (e != hipSuccess) return fail(MOE_EHIP, "moe_gdn_decode: capture end");
-      GdnGraph ent{first_layer, n_layers, n_tok, parity, qkv, out, nullptr, nullptr, 0};
+      GdnGraph ent{first_layer, n_layers, n_tok, parity, qkv, z, a, b, out, nullptr, nullptr, 0};
       const hipError_t ei = hipGraphInstantiate(&ent.exec, graph, nullptr, nullptr, 0);
       hipGraphDestroy(graph);
       if (ei != hipSuccess) return fail(MOE_EHIP, "moe_gdn_decode: graph instantiate");
