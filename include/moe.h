@@ -392,8 +392,10 @@ moe_status moe_gdn_reset(moe_gdn* g);
  * range, then the next token), updating each layer's state in place. dev bf16
  * inputs qkv [n_tok][n_layers][C], z [n_tok][n_layers][n_v_heads * d_v], a, b
  * [n_tok][n_layers][n_v_heads]; dev fp32 out [n_tok][n_layers][n_v_heads *
- * d_v]. One kernel per (token, layer), one block per value head; sequences of
- * 16 or more steps are captured once into a HIP graph and replayed. The layers
+ * d_v]. One kernel per (token, layer) (8 blocks per value head), which also
+ * applies the previous step's gated norm, and one norm kernel after the
+ * call's last step; sequences of 16 or more steps are captured once into a
+ * HIP graph and replayed. The layers
  * of one call must have taken equally many tokens so far (MOE_ESTATE
  * otherwise). Errors: MOE_EINVAL, MOE_ESTATE, MOE_EHIP. */
 moe_status moe_gdn_decode(moe_gdn* g, int32_t first_layer, int32_t n_layers, const uint16_t* qkv,
