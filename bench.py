@@ -331,6 +331,13 @@ def measure(cfg, args, torch, moe, loader, synth, steps: int, warmup: int, kerne
         prof = kernel_pass(model, step, n_prof, torch)
         extra["kernels"] = kernel_table(prof)
         log(f"kernel pass: {extra['kernels']}")
+        if "expert_miss" in prof:
+            # a pooled layer runs its hit and shared experts (one launch, during
+            # the miss copies) and its missed experts (a second launch): the
+            # expert kernel's per-layer figure is the two together
+            prof = dict(prof)
+            n, ms = prof.pop("expert")
+            prof["expert"] = (n, ms + prof.pop("expert_miss")[1])
         if prefill:
             res["roofline"], extra["gemms"] = gemm_roofline(cfg, T, prof)
         else:

@@ -74,13 +74,14 @@ namespace {
 enum KernelKind {
   K_ROUTER, K_ROUTE, K_GATEUP, K_DOWN, K_EXPERT, K_REDUCE,
   K_PF_XPREP, K_PF_ROUTER, K_PF_ROUTE, K_PF_COUNT, K_PF_SCAN, K_PF_SCATTER, K_PF_GATEUP, K_PF_DOWN, K_PF_COMBINE,
+  K_EXPERT_MISS,
   K_COUNT
 };
 const char* const kKindName[K_COUNT] = {"router",         "route",          "gateup",         "down",
                                         "expert",         "reduce",
                                         "prefill_xprep",  "prefill_router", "prefill_route",  "prefill_count",
                                         "prefill_scan",   "prefill_scatter", "prefill_gateup", "prefill_down",
-                                        "prefill_combine"};
+                                        "prefill_combine", "expert_miss"};
 
 struct Profiler {
   bool on = false;
@@ -902,12 +903,34 @@ moe_status moe_stack_decode(moe_model* m, moe_pool* pool, const uint16_t* x0, in
           }
         }
       }
+      // The fused path runs the hit experts and the shared expert at once,
+      // while the miss copies are in flight, and the missed experts after the
+      // copies land; the reduce sums every slot's partial rows in the same
+      // fixed order either way. (Other shapes run every slot after the copies.)
+      const bool split = fused_expert_supported(m->geo) && n_miss > 0;
+      if (split) {
+        ExpertSource hits = src;
+        for (int j = 0; j <= k; ++j)
+          if (j == k || !miss[(size_t)j]) hits.sel[hits.n_sel++] = j;
+        HIP_TRY(m->prof.run(K_EXPERT, s, [&] { return launch_expert(m->geo, hits, layer_shared(m, l), b, s); }),
+                "expert launch");
+      }
       for (int c = 0; c < moe_pool::kCopyStreams && c < n_miss; ++c) {
         HIP_TRY(hipEventRecord(pool->copies_done[c], pool->copy_stream[c]), "event record");
         HIP_TRY(hipStreamWaitEvent(s, pool->copies_done[c], 0), "stream wait");
       }
-      st = expert_steps(m, l, b, src, r, s);
-      if (st) return st;
+      if (split) {
+        ExpertSource misses = src;
+        for (int j = 0; j < k; ++j)
+          if (miss[(size_t)j]) misses.sel[misses.n_sel++] = j;
+        HIP_TRY(m->prof.run(K_EXPERT_MISS, s,
+                            [&] { return launch_expert(m->geo, misses, layer_shared(m, l), b, s); }),
+                "expert launch");
+        HIP_TRY(m->prof.run(K_REDUCE, s, [&] { return launch_reduce(m->geo, b, r, s); }), "reduce launch");
+      } else {
+        st = expert_steps(m, l, b, src, r, s);
+        if (st) return st;
+      }
     }
   }
   if (pool) HIP_TRY(hipStreamSynchronize(s), "moe_stack_decode: final sync");

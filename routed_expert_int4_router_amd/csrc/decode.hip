@@ -396,7 +396,8 @@ __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, E
   __shared__ __align__(16) uint32_t lds_route[kRouteLds];
   __shared__ __align__(16) float sh_h[SL];
   const int nsl = g.I / SL;
-  const int j = __builtin_amdgcn_readfirstlane((int)blockIdx.x / nsl);
+  const int jb = (int)blockIdx.x / nsl;
+  const int j = __builtin_amdgcn_readfirstlane(src.n_sel ? src.sel[jb] : jb);
   const int sl = __builtin_amdgcn_readfirstlane((int)blockIdx.x % nsl);
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
@@ -668,7 +669,7 @@ hipError_t down_bits(const Geometry& g, const ExpertSource& src, const uint8_t* 
 template <int BITS, int LPR, int IT, int NPL>
 hipError_t expert_dq(const Geometry& g, const ExpertSource& src, const uint8_t* shared_rec, const StepBuffers& b,
                      hipStream_t s) {
-  const dim3 grid((g.k + 1) * (g.I / kSlice)), block(64 * kExpertWaves);
+  const dim3 grid((src.n_sel ? src.n_sel : g.k + 1) * (g.I / kSlice)), block(64 * kExpertWaves);
   switch (g.H <= 64 * kExpertWaves ? 1 : g.H / (64 * kExpertWaves)) {
     case 1: launch((expert_kernel<BITS, LPR, IT, NPL, 1>), grid, block, 0, s, g, src, shared_rec, b); break;
     case 2: launch((expert_kernel<BITS, LPR, IT, NPL, 2>), grid, block, 0, s, g, src, shared_rec, b); break;

@@ -15,8 +15,10 @@ struct ExpertSource {
   uint64_t stride;       // bytes between records
   int64_t gid_base;      // resident: record index = gid_base + expert id
   int32_t use_table;     // 1: record index of selection j is table[j] (pool slots)
-  int32_t pad_;
+  int32_t n_sel;         // 0: the fused expert kernel runs every slot j = 0..k (k = shared);
+                         // else only slots sel[0..n_sel) (a pool step's hits, then its misses)
   int64_t table[kMaxTopK];
+  int32_t sel[kMaxTopK + 1];
 };
 
 struct Geometry {
