@@ -367,8 +367,9 @@ __global__ void __launch_bounds__(256) down_kernel(Geometry g, ExpertSource src,
 // of expert slot j (slot k = the shared expert), 16 waves (enough waves per
 // SIMD to overlap one wave's dequantisation arithmetic with another's
 // loads). The block
-//   1. routes the token (top-k of the logits by the whole block, weights in
-//      LDS; a pool step reads the route and the record table instead),
+//   1. routes the token (top-k of the logits by the whole block, picks in
+//      LDS; wave 0 computes their weights once the block's weight loads are
+//      in flight; a pool step reads the route and the record table instead),
 //   2. issues the gate/up code rows of its SL rows and the down codes of the
 //      slice (16 bytes of every down row) together, so the weight latency is
 //      paid once,
@@ -411,12 +412,11 @@ __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, E
 #pragma unroll
     for (int q = 0; q < EPC / 8; ++q) xraw[it][q] = xp[q];
   }
-  // 1. route
-  if (j < g.k && !src.use_table) {
-    const bool pub = blockIdx.x == 0;
-    block_route<NPL, kExpertWaves>(b.logits, g.E, g.k, g.norm_topk, lds_route, pub ? b.route_idx : nullptr,
-                                   pub ? b.route_w : nullptr, nullptr);
-  }
+  // 1. route: the picks now, their weights once the weight loads are issued
+  const bool routed = j < g.k && !src.use_table;  // block-uniform
+  RouteLane<NPL> rl;
+  uint32_t pick_k = 0u, pick_e = 0u;
+  if (routed) block_route_select<NPL, kExpertWaves>(b.logits, g.E, g.k, lds_route, rl, pick_k, pick_e);
   const uint8_t* rec;
   if (j == g.k) {
     rec = shared_rec;
@@ -460,17 +460,21 @@ __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, E
     sd[q] = dsc[n];
   }
   // the slot's weight (and the published shared gate) only after every weight
-  // load is in flight; nothing is scheduled across this point
-  float wjv;
+  // load is in flight; nothing is scheduled across this point. In a routed
+  // block wave 0 computes the picks' weights now; they reach the other waves
+  // through the barrier that ends the gate/up phase.
+  __builtin_amdgcn_sched_barrier(0);
+  float wjv = 0.f;
   if (j == g.k)
     wjv = src.use_table ? b.route_gamma[0] : 1.0f / (1.0f + expf(-b.logits[g.E]));
   else if (src.use_table)
     wjv = b.route_w[j];
-  else
-    wjv = __uint_as_float(lds_route[kRouteOrdered + 2 * j]);
+  if (routed && wv == 0) {
+    const bool pub = blockIdx.x == 0;
+    route_weights<NPL>(rl, pick_k, pick_e, g.E, g.k, g.norm_topk, lds_route, pub ? b.route_idx : nullptr,
+                       pub ? b.route_w : nullptr, nullptr);
+  }
   if (blockIdx.x == 0 && threadIdx.x == 0 && !src.use_table) b.route_gamma[0] = 1.0f / (1.0f + expf(-b.logits[g.E]));
-  __builtin_amdgcn_sched_barrier(0);
-  const float wj = wjv;
 
   // 3. gate/up dots, SwiGLU -> h of the slice in LDS
   float xv[IT][EPC];
@@ -507,6 +511,7 @@ __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, E
     if (c0 == LPR - 1 && r < RPWV) sh_h[wv * RPWV + r] = swiglu(ag, au);
   }
   __syncthreads();
+  const float wj = routed ? __uint_as_float(lds_route[kRouteOrdered + 2 * j]) : wjv;
 
   // 4. partial down projection of the slice for every output row
   float hv[SL];

@@ -104,21 +104,31 @@ __device__ __forceinline__ uint32_t* route_rank_count(uint32_t* lds) {
   return lds + kRouteOut + 2 * (64 + kRouteCand + kTopkMax);
 }
 
-// Number of the values v[0..n) greater than c, reading v two at a time.
+// Number of the values v[0..n) greater than c. v is read 16 values at a
+// time, the eight 16-byte LDS reads of a batch issued together so that a
+// batch costs one LDS round trip (a read-then-wait loop pays one per pair);
+// v must hold round_up(n, 16) readable values, those at or past n are not
+// counted.
 __device__ __forceinline__ int count_greater(const uint64_t* v, int n, uint64_t c) {
   int q = 0;
-  for (int j = 0; j < n; j += 2) {
-    const ulonglong2 w = *reinterpret_cast<const ulonglong2*>(v + j);
-    q += w.x > c ? 1 : 0;
-    q += (j + 1 < n && w.y > c) ? 1 : 0;
+  for (int j0 = 0; j0 < n; j0 += 16) {
+    ulonglong2 w[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) w[u] = *reinterpret_cast<const ulonglong2*>(v + j0 + 2 * u);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      q += (j0 + 2 * u < n && w[u].x > c) ? 1 : 0;
+      q += (j0 + 2 * u + 1 < n && w[u].y > c) ? 1 : 0;
+    }
   }
   return q;
 }
 
-// Steps 3-4 and the weights, given the threshold T (one wave).
+// Steps 3-4, given the threshold T (one wave): lane q < k ends with pick q
+// (its key and its expert) and writes the expert to lds[kRouteOrdered + 2q + 1].
 template <int NPL>
-__device__ __forceinline__ void route_finish(const RouteLane<NPL>& r, uint64_t T, int E, int k, int norm_topk,
-                                             uint32_t* lds, int32_t* out_idx, float* out_w, int32_t* host_idx) {
+__device__ __forceinline__ void route_select(const RouteLane<NPL>& r, uint64_t T, int k, uint32_t* lds,
+                                             uint32_t& pick_k, uint32_t& pick_e) {
   const int lane = threadIdx.x & 63;
   uint64_t* cand = route_lane_best(lds) + 64;
   uint64_t* ranked = cand + kRouteCand;
@@ -135,7 +145,8 @@ __device__ __forceinline__ void route_finish(const RouteLane<NPL>& r, uint64_t T
     n_cand += __popcll(m[i]);
   }
 
-  uint32_t pick_k = 0u, pick_e = 0u;  // lane q keeps pick q
+  pick_k = 0u;  // lane q keeps pick q
+  pick_e = 0u;
   if (n_cand <= kRouteCand) {
     wave_lds_sync();
     const uint64_t c0 = lane < n_cand ? cand[lane] : 0ull;
@@ -173,7 +184,19 @@ __device__ __forceinline__ void route_finish(const RouteLane<NPL>& r, uint64_t T
       }
     }
   }
-  // weights: exp(l - l_max) over the picks (norm_topk) or over all E logits
+  if (lane < k) lds[kRouteOrdered + 2 * lane + 1] = pick_e;
+}
+
+// The weights of the picks (one wave, the one that ran route_select, with
+// its lane state and picks): exp(l - l_max) over the picks, normalised by
+// their sum (norm_topk) or by the sum over all E logits. Lane q < k writes
+// the bits of weight q to lds[kRouteOrdered + 2q] and, when out_idx is
+// non-NULL, out_idx[q] and out_w[q] (and host_idx[q] when that is non-NULL).
+template <int NPL>
+__device__ __forceinline__ void route_weights(const RouteLane<NPL>& r, uint32_t pick_k, uint32_t pick_e, int E, int k,
+                                              int norm_topk, uint32_t* lds, int32_t* out_idx, float* out_w,
+                                              int32_t* host_idx) {
+  const int lane = threadIdx.x & 63;
   const float l = key_logit(pick_k);
   const float lmax = key_logit(__builtin_amdgcn_readfirstlane(pick_k));
   const float z = (lane < k) ? expf(l - lmax) : 0.f;
@@ -190,13 +213,21 @@ __device__ __forceinline__ void route_finish(const RouteLane<NPL>& r, uint64_t T
   if (lane < k) {
     const float wq = z / s;
     lds[kRouteOrdered + 2 * lane] = __float_as_uint(wq);
-    lds[kRouteOrdered + 2 * lane + 1] = pick_e;
     if (out_idx) {
       out_idx[lane] = (int32_t)pick_e;
       out_w[lane] = wq;
       if (host_idx) host_idx[lane] = (int32_t)pick_e;
     }
   }
+}
+
+// Steps 3-4 and the weights, given the threshold T (one wave).
+template <int NPL>
+__device__ __forceinline__ void route_finish(const RouteLane<NPL>& r, uint64_t T, int E, int k, int norm_topk,
+                                             uint32_t* lds, int32_t* out_idx, float* out_w, int32_t* host_idx) {
+  uint32_t pick_k, pick_e;
+  route_select<NPL>(r, T, k, lds, pick_k, pick_e);
+  route_weights<NPL>(r, pick_k, pick_e, E, k, norm_topk, lds, out_idx, out_w, host_idx);
 }
 
 // T: the lane maximum of rank k - 1 (one lane has it: the 64 values are distinct).
@@ -223,21 +254,23 @@ __device__ __forceinline__ void wave_route(const float* __restrict__ logits, int
   route_finish<NPL>(r, route_threshold(r.pm, rank, k), E, k, norm_topk, lds, out_idx, out_w, host_idx);
 }
 
-// The same selection by a whole block of NW waves (every thread calls it;
-// it synchronises the block): wave 0 loads the logits and does steps 1, 3
-// and 4; the ranks of the 64 lane maxima are counted by all NW waves, each
+// The selection by a whole block of NW waves (every thread calls it; it
+// synchronises the block): wave 0 loads the logits and does steps 1, 3 and
+// 4; the ranks of the 64 lane maxima are counted by all NW waves, each
 // against 64 / NW of them, and summed with LDS atomics. On return the picks
-// and weights are in lds as for wave_route, visible to the whole block.
+// are in lds as for wave_route, visible to the whole block, and wave 0 holds
+// its lane state r and, in lane q, pick q (pick_k, pick_e): the caller runs
+// route_weights in wave 0 when it suits it, and the weights become visible to
+// the block at its next barrier.
 template <int NPL, int NW>
-__device__ __forceinline__ void block_route(const float* __restrict__ logits, int E, int k, int norm_topk, uint32_t* lds,
-                                            int32_t* out_idx, float* out_w, int32_t* host_idx) {
+__device__ __forceinline__ void block_route_select(const float* __restrict__ logits, int E, int k, uint32_t* lds,
+                                                   RouteLane<NPL>& r, uint32_t& pick_k, uint32_t& pick_e) {
   static_assert(64 % NW == 0, "the lane maxima are split evenly over the waves");
   constexpr int PER = 64 / NW;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   uint64_t* lane_best = route_lane_best(lds);
   uint32_t* rank_count = route_rank_count(lds);
-  RouteLane<NPL> r;
   if (wv == 0) {
     route_load<NPL>(logits, E, r);
     lane_best[lane] = r.pm;
@@ -254,7 +287,7 @@ __device__ __forceinline__ void block_route(const float* __restrict__ logits, in
   __syncthreads();
   if (wv == 0) {
     const int rank = (int)rank_count[lane];
-    route_finish<NPL>(r, route_threshold(r.pm, rank, k), E, k, norm_topk, lds, out_idx, out_w, host_idx);
+    route_select<NPL>(r, route_threshold(r.pm, rank, k), k, lds, pick_k, pick_e);
   }
   __syncthreads();
 }
