@@ -16,7 +16,9 @@
 //      its own (reads of one address by all lanes are LDS broadcasts). The
 //      k-th best lane maximum T is a lower bound of the whole top-k: the k
 //      lane maxima at or above T are k distinct experts.
-//   3. Experts at or above T are compacted into LDS with ballots (at most
+//   3. When exactly k experts reach T (the top-k sit in k different lanes)
+//      they are the k best lane maxima, already ranked by step 2. Otherwise
+//      the experts at or above T are compacted into LDS with ballots (at most
 //      k * NPL of them, usually little more than k), each is ranked against
 //      the others the same way, and rank r < k is pick r.
 //   4. When more than kRouteCand experts reach T (many of the best logits in
@@ -124,30 +126,44 @@ __device__ __forceinline__ int count_greater(const uint64_t* v, int n, uint64_t 
   return q;
 }
 
-// Steps 3-4, given the threshold T (one wave): lane q < k ends with pick q
-// (its key and its expert) and writes the expert to lds[kRouteOrdered + 2q + 1].
+// Steps 3-4, given the threshold T and the lane's rank among the 64 lane
+// maxima (one wave): lane q < k ends with pick q (its key and its expert) and
+// writes the expert to lds[kRouteOrdered + 2q + 1].
 template <int NPL>
-__device__ __forceinline__ void route_select(const RouteLane<NPL>& r, uint64_t T, int k, uint32_t* lds,
+__device__ __forceinline__ void route_select(const RouteLane<NPL>& r, uint64_t T, int rank, int k, uint32_t* lds,
                                              uint32_t& pick_k, uint32_t& pick_e) {
   const int lane = threadIdx.x & 63;
   uint64_t* cand = route_lane_best(lds) + 64;
   uint64_t* ranked = cand + kRouteCand;
-  // 3. compaction of the experts at or above T: all ballots first, then the
-  //    prefix offsets (scalar) and the stores
   uint64_t m[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) m[i] = __ballot(r.p[i] >= T);
   int n_cand = 0;  // uniform
 #pragma unroll
-  for (int i = 0; i < NPL; ++i) {
-    const int pos = n_cand + (int)lanes_below(m[i]);
-    if (((m[i] >> lane) & 1ull) && pos < kRouteCand) cand[pos] = r.p[i];
-    n_cand += __popcll(m[i]);
-  }
+  for (int i = 0; i < NPL; ++i) n_cand += __popcll(m[i]);
 
   pick_k = 0u;  // lane q keeps pick q
   pick_e = 0u;
-  if (n_cand <= kRouteCand) {
+  if (n_cand == k) {
+    // the only experts at or above T are the k lane maxima of rank < k (the
+    // top-k sit in k different lanes, about half the tokens at 10 of 512):
+    // their ranks among the lane maxima are the selection order
+    if (rank < k) ranked[rank] = r.pm;
+    wave_lds_sync();
+    const uint64_t pq = ranked[min(lane, k - 1)];
+    if (lane < k) {
+      pick_k = (uint32_t)(pq >> 32);
+      pick_e = ~(uint32_t)pq;
+    }
+  } else if (n_cand <= kRouteCand) {
+    // 3. compaction of the experts at or above T (prefix offsets from the
+    //    ballots), then each ranked against the others
+#pragma unroll
+    for (int i = 0, base = 0; i < NPL; ++i) {
+      const int pos = base + (int)lanes_below(m[i]);
+      if ((m[i] >> lane) & 1ull) cand[pos] = r.p[i];
+      base += __popcll(m[i]);
+    }
     wave_lds_sync();
     const uint64_t c0 = lane < n_cand ? cand[lane] : 0ull;
     const uint64_t c1 = lane + 64 < n_cand ? cand[lane + 64] : 0ull;
@@ -221,12 +237,14 @@ __device__ __forceinline__ void route_weights(const RouteLane<NPL>& r, uint32_t 
   }
 }
 
-// Steps 3-4 and the weights, given the threshold T (one wave).
+// Steps 3-4 and the weights, given the threshold T and the lane's rank
+// among the lane maxima (one wave).
 template <int NPL>
-__device__ __forceinline__ void route_finish(const RouteLane<NPL>& r, uint64_t T, int E, int k, int norm_topk,
-                                             uint32_t* lds, int32_t* out_idx, float* out_w, int32_t* host_idx) {
+__device__ __forceinline__ void route_finish(const RouteLane<NPL>& r, uint64_t T, int rank, int E, int k,
+                                             int norm_topk, uint32_t* lds, int32_t* out_idx, float* out_w,
+                                             int32_t* host_idx) {
   uint32_t pick_k, pick_e;
-  route_select<NPL>(r, T, k, lds, pick_k, pick_e);
+  route_select<NPL>(r, T, rank, k, lds, pick_k, pick_e);
   route_weights<NPL>(r, pick_k, pick_e, E, k, norm_topk, lds, out_idx, out_w, host_idx);
 }
 
@@ -251,7 +269,7 @@ __device__ __forceinline__ void wave_route(const float* __restrict__ logits, int
   lane_best[lane] = r.pm;
   wave_lds_sync();
   const int rank = count_greater(lane_best, 64, r.pm);
-  route_finish<NPL>(r, route_threshold(r.pm, rank, k), E, k, norm_topk, lds, out_idx, out_w, host_idx);
+  route_finish<NPL>(r, route_threshold(r.pm, rank, k), rank, E, k, norm_topk, lds, out_idx, out_w, host_idx);
 }
 
 // The selection by a whole block of NW waves (every thread calls it; it
@@ -287,7 +305,7 @@ __device__ __forceinline__ void block_route_select(const float* __restrict__ log
   __syncthreads();
   if (wv == 0) {
     const int rank = (int)rank_count[lane];
-    route_select<NPL>(r, route_threshold(r.pm, rank, k), k, lds, pick_k, pick_e);
+    route_select<NPL>(r, route_threshold(r.pm, rank, k), rank, k, lds, pick_k, pick_e);
   }
   __syncthreads();
 }
