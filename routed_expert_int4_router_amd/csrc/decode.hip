@@ -404,7 +404,11 @@ __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, E
   const int lane = threadIdx.x & 63;
   const int rsub = lane / LPR, c0 = lane % LPR;
 
-  // activations first: they do not depend on the routing
+  // the logits (wave 0 of a routed block) and the activations first: neither
+  // depends on the routing
+  const bool routed = j < g.k && !src.use_table;  // block-uniform
+  RouteLane<NPL> rl;
+  if (routed && wv == 0) route_issue<NPL>(b.logits, g.E, rl);
   uint4 xraw[IT][EPC / 8];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
@@ -413,10 +417,8 @@ __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, E
     for (int q = 0; q < EPC / 8; ++q) xraw[it][q] = xp[q];
   }
   // 1. route: the picks now, their weights once the weight loads are issued
-  const bool routed = j < g.k && !src.use_table;  // block-uniform
-  RouteLane<NPL> rl;
   uint32_t pick_k = 0u, pick_e = 0u;
-  if (routed) block_route_select<NPL, kExpertWaves>(b.logits, g.E, g.k, lds_route, rl, pick_k, pick_e);
+  if (routed) block_route_select<NPL, kExpertWaves>(g.E, g.k, lds_route, rl, pick_k, pick_e);
   const uint8_t* rec;
   if (j == g.k) {
     rec = shared_rec;

@@ -84,11 +84,18 @@ struct RouteLane {
   uint64_t pm;
 };
 
+// The lane's NPL logits (loads only).
 template <int NPL>
-__device__ __forceinline__ void route_load(const float* __restrict__ logits, int E, RouteLane<NPL>& r) {
+__device__ __forceinline__ void route_issue(const float* __restrict__ logits, int E, RouteLane<NPL>& r) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < NPL; ++i) r.lv[i] = logits[min(lane + 64 * i, E - 1)];
+}
+
+// Packed values and the lane maximum of logits loaded by route_issue.
+template <int NPL>
+__device__ __forceinline__ void route_keys(int E, RouteLane<NPL>& r) {
+  const int lane = threadIdx.x & 63;
   // packed (key, ~e): padding (e >= E) gets key 0, below every real logit
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
@@ -99,6 +106,12 @@ __device__ __forceinline__ void route_load(const float* __restrict__ logits, int
   r.pm = r.p[0];
 #pragma unroll
   for (int i = 1; i < NPL; ++i) r.pm = r.p[i] > r.pm ? r.p[i] : r.pm;
+}
+
+template <int NPL>
+__device__ __forceinline__ void route_load(const float* __restrict__ logits, int E, RouteLane<NPL>& r) {
+  route_issue<NPL>(logits, E, r);
+  route_keys<NPL>(E, r);
 }
 
 __device__ __forceinline__ uint64_t* route_lane_best(uint32_t* lds) { return reinterpret_cast<uint64_t*>(lds + kRouteOut); }
@@ -273,16 +286,16 @@ __device__ __forceinline__ void wave_route(const float* __restrict__ logits, int
 }
 
 // The selection by a whole block of NW waves (every thread calls it; it
-// synchronises the block): wave 0 loads the logits and does steps 1, 3 and
-// 4; the ranks of the 64 lane maxima are counted by all NW waves, each
-// against 64 / NW of them, and summed with LDS atomics. On return the picks
-// are in lds as for wave_route, visible to the whole block, and wave 0 holds
-// its lane state r and, in lane q, pick q (pick_k, pick_e): the caller runs
-// route_weights in wave 0 when it suits it, and the weights become visible to
-// the block at its next barrier.
+// synchronises the block): wave 0, whose logits the caller has loaded with
+// route_issue, does steps 1, 3 and 4; the ranks of the 64 lane maxima are
+// counted by all NW waves, each against 64 / NW of them, and summed with LDS
+// atomics. On return the picks are in lds as for wave_route, visible to the
+// whole block, and wave 0 holds its lane state r and, in lane q, pick q
+// (pick_k, pick_e): the caller runs route_weights in wave 0 when it suits it,
+// and the weights become visible to the block at its next barrier.
 template <int NPL, int NW>
-__device__ __forceinline__ void block_route_select(const float* __restrict__ logits, int E, int k, uint32_t* lds,
-                                                   RouteLane<NPL>& r, uint32_t& pick_k, uint32_t& pick_e) {
+__device__ __forceinline__ void block_route_select(int E, int k, uint32_t* lds, RouteLane<NPL>& r, uint32_t& pick_k,
+                                                   uint32_t& pick_e) {
   static_assert(64 % NW == 0, "the lane maxima are split evenly over the waves");
   constexpr int PER = 64 / NW;
   const int lane = threadIdx.x & 63;
@@ -290,7 +303,7 @@ __device__ __forceinline__ void block_route_select(const float* __restrict__ log
   uint64_t* lane_best = route_lane_best(lds);
   uint32_t* rank_count = route_rank_count(lds);
   if (wv == 0) {
-    route_load<NPL>(logits, E, r);
+    route_keys<NPL>(E, r);
     lane_best[lane] = r.pm;
     rank_count[lane] = 0u;
   }
