@@ -17,10 +17,12 @@
 //      k-th best lane maximum T is a lower bound of the whole top-k: the k
 //      lane maxima at or above T are k distinct experts.
 //   3. When exactly k experts reach T (the top-k sit in k different lanes)
-//      they are the k best lane maxima, already ranked by step 2. Otherwise
-//      the experts at or above T are compacted into LDS with ballots (at most
-//      k * NPL of them, usually little more than k), each is ranked against
-//      the others the same way, and rank r < k is pick r.
+//      they are the k best lane maxima, already ranked by step 2; when k + 1
+//      do, the one that is not a lane maximum is placed among them with two
+//      ballots. Otherwise the experts at or above T are compacted into LDS
+//      with ballots (at most k * NPL of them, usually little more than k),
+//      each is ranked against the others the same way, and rank r < k is
+//      pick r.
 //   4. When more than kRouteCand experts reach T (many of the best logits in
 //      a few lanes; only possible when k * NPL > kRouteCand), k rounds of
 //      wave max / lowest-index selection with DPP take over.
@@ -162,6 +164,25 @@ __device__ __forceinline__ void route_select(const RouteLane<NPL>& r, uint64_t T
     // top-k sit in k different lanes, about half the tokens at 10 of 512):
     // their ranks among the lane maxima are the selection order
     if (rank < k) ranked[rank] = r.pm;
+    wave_lds_sync();
+    const uint64_t pq = ranked[min(lane, k - 1)];
+    if (lane < k) {
+      pick_k = (uint32_t)(pq >> 32);
+      pick_e = ~(uint32_t)pq;
+    }
+  } else if (n_cand == k + 1) {
+    // one expert x at or above T is not a lane maximum (one lane holds two of
+    // the best k + 1). A lane maximum of rank r < k has r + [x above it]
+    // candidates above it; x has the lane maxima above it (those of rank >= k
+    // are below T).
+    uint64_t xv = 0ull;  // candidate values are never 0: the low word is ~e
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) xv = (r.p[i] >= T && r.p[i] != r.pm) ? r.p[i] : xv;
+    const uint64_t x = readlane_u64(xv, __builtin_ctzll(__ballot(xv != 0ull)));
+    const int fx = __popcll(__ballot(rank < k && r.pm > x));
+    const int f = rank + (x > r.pm ? 1 : 0);
+    if (rank < k && f < k) ranked[f] = r.pm;
+    if (lane == 0 && fx < k) ranked[fx] = x;
     wave_lds_sync();
     const uint64_t pq = ranked[min(lane, k - 1)];
     if (lane < k) {

@@ -107,6 +107,64 @@ def test_topk_exact_on_crafted_logits():
         model.close()
 
 
+def _crafted_rows_512():
+    """Router rows at 512 experts, top-10, that reach each selection path
+    (lane l holds experts l, l + 64, ...): the top-10 in ten different lanes;
+    one lane holding two of the best eleven, with the second one first, in
+    the middle or last; several lanes holding several; exact ties, signed
+    zeros, infinities and NaN throughout."""
+    rng = np.random.default_rng(11)
+    rows = []
+    r = np.zeros(512, np.float32); r[:10] = 1.0; rows.append(r)                       # distinct lanes, ties
+    r = np.zeros(512, np.float32); r[:9] = 5.0; r[64] = 5.0; rows.append(r)            # lane 0 twice, tie
+    r = np.zeros(512, np.float32); r[:9] = 5.0; r[64] = 9.0; rows.append(r)            # lane 0's second first
+    r = np.zeros(512, np.float32); r[:9] = 2.0; r[9] = 0.5; r[64] = 1.0; rows.append(r)  # extra last
+    r = np.zeros(512, np.float32); r[[0, 64, 128, 1, 65]] = 3.0; rows.append(r)        # several lanes twice
+    r = np.full(512, -np.inf, np.float32); r[[0, 64, 3, 7, 71]] = [0.0, -0.0, np.nan, 1.0, 1.0]; rows.append(r)
+    r = np.where(np.arange(512) % 3 == 0, -0.0, 0.0).astype(np.float32); r[[5, 69, 133]] = np.inf; rows.append(r)
+    for _ in range(4):
+        rows.append(rng.standard_normal(512).astype(np.float32))
+    rows.append((rng.integers(-2, 3, 512) * 0.25).astype(np.float32))
+    return rows
+
+
+def test_topk_exact_every_selection_path():
+    """x = e_0 makes logit e exactly W_r[0, e]. Each crafted row is routed by
+    the fused decode kernel (one token) and by the batched path's route
+    kernel (eight tokens), and both must give the oracle's picks exactly."""
+    cfg = synth.get_config("tiny", n_experts=512, top_k=10)
+    from oracle import moe as omoe
+    from routed_expert_int4_router_amd import loader
+    torch = gh.torch_cuda()
+    w = synth.SynthWeights(cfg)
+    for n_row, row in enumerate(_crafted_rows_512()):
+        class Crafted:
+            def __getattr__(self, n):
+                return getattr(w, n)
+
+            def router(self, layer):
+                r = w.router(layer).copy()
+                r[0, :] = row
+                return r
+
+        model = loader.load_model(cfg, Crafted())
+        want = omoe.topk_order(row, cfg.top_k)
+        for n_tok, call in ((1, model.layer_decode), (8, model.layer_forward)):
+            xb = np.zeros((n_tok, cfg.hidden), np.uint16)
+            xb[:, 0] = 0x3F80  # bf16 1.0
+            x = gh.dev_bf16(xb)
+            out = gh.dev_f32((n_tok, cfg.hidden))
+            call(0, x, out)
+            torch.cuda.synchronize()
+            idx, wts = model.debug_routing()
+            for t in range(n_tok):
+                assert list(idx[t]) == list(want), (n_row, n_tok, t, idx[t], want)
+            if np.isfinite(row[want]).all():
+                ref = omoe.route_weights(row.astype(np.float64), want, cfg.norm_topk)
+                assert np.allclose(wts[0], ref, rtol=1e-5, atol=1e-7), (n_row, wts[0], ref)
+        model.close()
+
+
 def test_topk_exact_wide_routing_and_fallback():
     """1024 experts, top-16. The selection ranks the experts at or above the
     16th-best lane maximum; when the best logits crowd into a few lanes (here
