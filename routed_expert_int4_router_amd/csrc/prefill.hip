@@ -1080,18 +1080,32 @@ __global__ void __launch_bounds__(256, 2) gemm_down_kernel(GemmArgs a) {
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no DMA in flight at exit
+  // Epilogue: the tile's y rows. Each wave stages its 64 x 64 results in LDS,
+  // 32 columns at a time, and writes every destination row as a 128-byte run
+  // of 16-byte stores (scattered 4-byte stores had made this phase a third of
+  // the block's life). The rings are free once every wave has left the loop.
+  __syncthreads();
+  constexpr int YS = 40;  // staged row stride in floats: rows m and m + 4 fall in opposite bank halves
+  static_assert(4 * BM * YS * 4 <= DN_NS * (DA_STAGE + DB_STAGE + DS_STAGE), "y staging must fit the rings");
+  float* sy = reinterpret_cast<float*>(smem) + wv * (BM * YS);
 #pragma unroll
   for (int nn = 0; nn < 2; ++nn) {
-    const int n = n0 + nl + 32 * nn;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m0 = (r >> 2) * 8 + hh * 4 + (r & 3);
+      sy[m0 * YS + mrow] = s_w[m0] * acc[2 * nn][r];
+      sy[(32 + m0) * YS + mrow] = s_w[32 + m0] * acc[2 * nn + 1][r];
+    }
+    // a wave's LDS operations complete in issue order: the reads below see
+    // the writes above, and the next pass's writes follow these reads
+    const int c4 = lane & 7;
+    float* ydst = a.y + n0 + 64 * wv + 32 * nn + 4 * c4;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int m = m0 + 32 * half;
-        const int dst = s_dst[m];
-        if (dst >= 0) a.y[(size_t)dst * a.H + n] = s_w[m] * acc[2 * nn + half][r];
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int m = 8 * i + (lane >> 3);
+      const float4 v = *reinterpret_cast<const float4*>(sy + m * YS + 4 * c4);
+      const int dst = s_dst[m];
+      if (dst >= 0) *reinterpret_cast<float4*>(ydst + (size_t)dst * a.H) = v;
     }
   }
 }
