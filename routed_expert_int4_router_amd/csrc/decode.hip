@@ -17,9 +17,13 @@
 //
 // Weight reads are 16-byte (dwordx4) loads of packed codes; each lane owns a
 // contiguous 16-byte chunk of a code row, consecutive lanes own consecutive
-// chunks, so a wave-wide load covers contiguous row bytes. Codes become floats
-// exactly (v_cvt_f32_ubyte*) and the group scale and bias are applied once per
-// chunk: dot = s * sum(q * x) + c * sum(x).
+// chunks, so a wave-wide load covers contiguous row bytes. The group scale and
+// bias are applied once per chunk: dot = s * sum(q * x) + c * sum(x). For the
+// int4 gate/up rows the chunk's products run on the dot-product unit, two codes
+// (as the exact bf16 values 128 + q) against two bf16 activations per
+// instruction (x_chunk / chunk_term); the down rows multiply fp32 h, so there
+// and for int8 the codes become floats exactly (v_cvt_f32_ubyte*) and meet
+// their operands in fp32 FMAs.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -39,6 +43,20 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_stream(const uint8_t* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// The activations of a chunk from the 16-byte words they were loaded as.
+template <int BITS>
+__device__ __forceinline__ XChunk<BITS> x_chunk_of(const uint4 (&raw)[128 / BITS / 8]) {
+  uint32_t xr[128 / BITS / 2];
+#pragma unroll
+  for (int q = 0; q < 128 / BITS / 8; ++q) {
+    xr[4 * q] = raw[q].x;
+    xr[4 * q + 1] = raw[q].y;
+    xr[4 * q + 2] = raw[q].z;
+    xr[4 * q + 3] = raw[q].w;
+  }
+  return x_chunk<BITS>(xr);
 }
 
 template <int LPR>
@@ -191,33 +209,16 @@ __global__ void __launch_bounds__(256) gateup_kernel(Geometry g, ExpertSource sr
       su[rr][it] = *reinterpret_cast<const uint32_t*>(rec + g.up_sc + ((size_t)i * groups + grp) * 4);
     }
   }
-  float xv[IT][EPC];
-  float xs[IT];
+  XChunk<BITS> xc[IT];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-#pragma unroll
-    for (int q = 0; q < EPC / 8; ++q) {
-      const uint32_t w[4] = {xraw[it][q].x, xraw[it][q].y, xraw[it][q].z, xraw[it][q].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        xv[it][8 * q + 2 * t] = bf16f(w[t] & 0xFFFFu);
-        xv[it][8 * q + 2 * t + 1] = bf16f(w[t] >> 16);
-      }
-    }
-    float s = 0.f;
-#pragma unroll
-    for (int q = 0; q < EPC; ++q) s += xv[it][q];
-    xs[it] = s;
-  }
+  for (int it = 0; it < IT; ++it) xc[it] = x_chunk_of<BITS>(xraw[it]);
 #pragma unroll
   for (int rr = 0; rr < RW; ++rr) {
     float ag = 0.f, au = 0.f;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const float dg = chunk_dot<BITS>(cg[rr][it], xv[it]);
-      const float du = chunk_dot<BITS>(cu[rr][it], xv[it]);
-      ag += group_term(sg[rr][it], dg, xs[it]);
-      au += group_term(su[rr][it], du, xs[it]);
+      ag += chunk_term<BITS>(cg[rr][it], sg[rr][it], xc[it]);
+      au += chunk_term<BITS>(cu[rr][it], su[rr][it], xc[it]);
     }
     ag = group_sum<LPR>(ag);
     au = group_sum<LPR>(au);
@@ -479,33 +480,16 @@ __global__ void __launch_bounds__(64 * kExpertWaves) expert_kernel(Geometry g, E
   if (blockIdx.x == 0 && threadIdx.x == 0 && !src.use_table) b.route_gamma[0] = 1.0f / (1.0f + expf(-b.logits[g.E]));
 
   // 3. gate/up dots, SwiGLU -> h of the slice in LDS
-  float xv[IT][EPC];
-  float xs[IT];
+  XChunk<BITS> xc[IT];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) {
-#pragma unroll
-    for (int q = 0; q < EPC / 8; ++q) {
-      const uint32_t w[4] = {xraw[it][q].x, xraw[it][q].y, xraw[it][q].z, xraw[it][q].w};
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        xv[it][8 * q + 2 * t] = bf16f(w[t] & 0xFFFFu);
-        xv[it][8 * q + 2 * t + 1] = bf16f(w[t] >> 16);
-      }
-    }
-    float sx = 0.f;
-#pragma unroll
-    for (int q = 0; q < EPC; ++q) sx += xv[it][q];
-    xs[it] = sx;
-  }
+  for (int it = 0; it < IT; ++it) xc[it] = x_chunk_of<BITS>(xraw[it]);
 #pragma unroll
   for (int rr = 0; rr < RW; ++rr) {
     float ag = 0.f, au = 0.f;
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
-      const float dg = chunk_dot<BITS>(cg[rr][it], xv[it]);
-      const float du = chunk_dot<BITS>(cu[rr][it], xv[it]);
-      ag += group_term(sg[rr][it], dg, xs[it]);
-      au += group_term(su[rr][it], du, xs[it]);
+      ag += chunk_term<BITS>(cg[rr][it], sg[rr][it], xc[it]);
+      au += chunk_term<BITS>(cu[rr][it], su[rr][it], xc[it]);
     }
     ag = group_sum<LPR>(ag);
     au = group_sum<LPR>(au);

@@ -93,8 +93,9 @@ __global__ void route_scalar_kernel(const float* __restrict__ logits, int E, int
 
 // ----------------------------------------------------------- decode gate/up ---
 // Thread (slot j, row i): h[j][i] = swiglu(gate_i . x, up_i . x), each dot the
-// sum over LPR lane partials (lane c takes chunks c, c + LPR, ...: s * sum(q x)
-// + c * sum(x) per chunk) associated as the fast kernel's reduction.
+// sum over LPR lane partials (lane c takes chunks c, c + LPR, ...: the chunk
+// term s * sum(q x) + c * sum(x) of chunk_term, on the same activation pairs)
+// associated as the fast kernel's reduction.
 template <int BITS>
 __global__ void gateup_scalar_kernel(Geometry g, const uint8_t* __restrict__ experts, uint64_t stride,
                                      int64_t gid_base, const uint8_t* __restrict__ shared_rec,
@@ -112,17 +113,16 @@ __global__ void gateup_scalar_kernel(Geometry g, const uint8_t* __restrict__ exp
   for (int c = 0; c < lpr; ++c) {
     float ag = 0.f, au = 0.f;
     for (int ch = c; ch < chunks; ch += lpr) {
-      float xv[EPC];
-      for (int q = 0; q < EPC; ++q) xv[q] = bf16f(x[ch * EPC + q]);
-      float xs = 0.f;
-      for (int q = 0; q < EPC; ++q) xs += xv[q];
+      uint32_t xr[EPC / 2];
+      for (int q = 0; q < EPC / 2; ++q) xr[q] = (uint32_t)x[ch * EPC + 2 * q] | ((uint32_t)x[ch * EPC + 2 * q + 1] << 16);
+      const XChunk<BITS> xc = x_chunk<BITS>(xr);
       const uint4 cg = *reinterpret_cast<const uint4*>(rec + g.gate_codes + (size_t)i * row_bytes + 16 * ch);
       const uint4 cu = *reinterpret_cast<const uint4*>(rec + g.up_codes + (size_t)i * row_bytes + 16 * ch);
       const int grp = ch * EPC / 64;
       const uint32_t sg = *reinterpret_cast<const uint32_t*>(rec + g.gate_sc + ((size_t)i * groups + grp) * 4);
       const uint32_t su = *reinterpret_cast<const uint32_t*>(rec + g.up_sc + ((size_t)i * groups + grp) * 4);
-      ag += group_term(sg, chunk_dot<BITS>(cg, xv), xs);
-      au += group_term(su, chunk_dot<BITS>(cu, xv), xs);
+      ag += chunk_term<BITS>(cg, sg, xc);
+      au += chunk_term<BITS>(cu, su, xc);
     }
     pg[c] = ag;
     pu[c] = au;
