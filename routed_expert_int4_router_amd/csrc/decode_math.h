@@ -134,23 +134,40 @@ __device__ __forceinline__ XChunk<BITS> x_chunk(const uint32_t (&xr)[128 / BITS 
   return r;
 }
 
+// The 32 int4 codes of a chunk as bf16 pairs (128 + q_{8t+j}, 128 + q_{8t+j+4})
+// at q[4t + j], the pairing of XChunk<4>.
+__device__ __forceinline__ void code_pairs4(const uint4 c, uint32_t (&q)[16]) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) q[4 * t + j] = ((w[t] >> (4 * j)) & 0x000F000Fu) | 0x43004300u;
+  }
+}
+
+// s * sum((128 + q) x) + (c - 128 s) * sum(x) = s * sum(q x) + c * sum(x) of a
+// chunk from its code pairs and activation pairs (even pairs into one
+// accumulator, odd into another, each in order).
+__device__ __forceinline__ float pairs_term(const uint32_t (&q)[16], uint32_t sc, const uint32_t (&xp)[16],
+                                            float xs) {
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int m = 0; m < 16; m += 2) {
+    a0 = dot2bf(q[m], xp[m], a0);
+    a1 = dot2bf(q[m + 1], xp[m + 1], a1);
+  }
+  const float s = f16f(sc & 0xFFFFu);
+  return fmaf(s, a0 + a1, fmaf(-128.0f, s, f16f(sc >> 16)) * xs);
+}
+
 // s * sum(q x) + c * sum(x) of one chunk; sc = the fp16 (s, c) pair of its
 // quantisation group (s in the low half).
 template <int BITS>
 __device__ __forceinline__ float chunk_term(const uint4 c, uint32_t sc, const XChunk<BITS>& x) {
   if constexpr (BITS == 4) {
-    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int j = 0; j < 4; j += 2) {
-        a0 = dot2bf(((w[t] >> (4 * j)) & 0x000F000Fu) | 0x43004300u, x.p[4 * t + j], a0);
-        a1 = dot2bf(((w[t] >> (4 * j + 4)) & 0x000F000Fu) | 0x43004300u, x.p[4 * t + j + 1], a1);
-      }
-    }
-    const float s = f16f(sc & 0xFFFFu);
-    return fmaf(s, a0 + a1, fmaf(-128.0f, s, f16f(sc >> 16)) * x.s);
+    uint32_t q[16];
+    code_pairs4(c, q);
+    return pairs_term(q, sc, x.p, x.s);
   } else {
     return group_term(sc, chunk_dot<8>(c, x.v), x.s);
   }

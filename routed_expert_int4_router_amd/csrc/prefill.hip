@@ -32,6 +32,7 @@
 #include <cstdint>
 #include <vector>
 
+#include "decode_math.h"
 #include "dpp.h"
 #include "launch.h"
 #include "topk.h"
@@ -54,9 +55,8 @@ constexpr int CHUNK = 512;    // pairs per bucketing chunk
 
 using Workspace = PrefillWorkspace;
 
-__device__ __forceinline__ float bf16f(uint32_t b) { return __uint_as_float(b << 16); }
-
-__device__ __forceinline__ float f16f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+// bf16f, f16f and the activation-pair helpers (x_chunk, code_pairs4,
+// pairs_term) come from decode_math.h.
 
 // Reorder the 8 bf16 of a 16-byte chunk (0,1,...,7) -> (0,4,1,5,2,6,3,7): the
 // k-order in which the nibble conversion below emits the codes of a dword.
@@ -662,6 +662,201 @@ __device__ __forceinline__ void gateup_loop(uint8_t* sA, uint8_t* sB, uint8_t* s
 #undef GU_STEP
 }
 
+// The tile's h rows (sg: [64][GU_BN + 1] fp32, after SwiGLU) under their
+// fp16 range scales into h16, with the per-row group sums, the per-row
+// factors and the tile-group scale; all 256 threads of the block.
+__device__ __forceinline__ void gateup_store_h(const GemmArgs& a, const float* sg, int nrow, int tile, int nt,
+                                               int base, int n0, int tid, int wv, int lane) {
+  constexpr int SGS = GU_BN + 1;
+  // fp16 range scales. Row m (4 threads, 16 columns each) has the natural
+  // exponent n_m: max |h_m| / 2^n_m in [2^14, 2^15). The tile-group scale is
+  // 2^T with T = the largest n_m over the tile's rows. A row within 2^12 of
+  // the tile's largest stores h / 2^T (its maximum stays >= 4, so only values
+  // below 2^-16 of it leave fp16's normal range); a smaller row stores
+  // h / 2^n_m and the factor 2^(n_m - T) that the down GEMM applies to its
+  // partial sums. hscale = 2^T, negated when any row of the tile-group has
+  // its own factor.
+  const int m = tid >> 2, qq = tid & 3;
+  float hv[16];
+  float rmax = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < 16; ++cc) {
+    hv[cc] = sg[m * SGS + 16 * qq + cc];
+    rmax = fmaxf(rmax, fabsf(hv[cc]));
+  }
+  rmax = fmaxf(rmax, __uint_as_float(dpp::mov<dpp::kQuadXor1, 0xF>(0u, __float_as_uint(rmax))));
+  rmax = fmaxf(rmax, __uint_as_float(dpp::mov<dpp::kQuadXor2, 0xF>(0u, __float_as_uint(rmax))));
+  const uint32_t nb = row_exp_biased(rmax, m < nrow);
+  __shared__ uint32_t s_tmax[4];
+  {
+    const uint32_t wm = dpp::wave_max_u32(nb);
+    if (lane == 0) s_tmax[wv] = wm;
+  }
+  __syncthreads();
+  const uint32_t tb = max(max(s_tmax[0], s_tmax[1]), max(s_tmax[2], s_tmax[3]));
+  const int T = tb ? (int)tb - 256 : 0;
+  const int er = row_exp(nb, T);  // this row's exponent
+  const bool own = m < nrow && er != T;
+  // h / 2^er in fp16 and the group sum of the values the down GEMM
+  // multiplies: this thread's 16 columns, then the row's four quarters
+  // combined as (q0 + q1) + (q2 + q3)
+  uint32_t pk[8];
+  float sum = pack16(hv, er, pk);
+  sum += __uint_as_float(dpp::mov<dpp::kQuadXor1, 0xF>(0u, __float_as_uint(sum)));
+  sum += __uint_as_float(dpp::mov<dpp::kQuadXor2, 0xF>(0u, __float_as_uint(sum)));
+  const int GI = a.I / 64;
+  if (m < nrow) {
+    uint16_t* dst = a.h16 + (size_t)(base + m) * a.I + n0 + 16 * qq;
+    *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    *reinterpret_cast<uint4*>(dst + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    if (qq == 0) {
+      a.hsum[(size_t)(base + m) * GI + nt] = sum;
+      a.hrowf[(size_t)(base + m) * GI + nt] = ldexpf(1.f, er - T);
+    }
+  }
+  const uint64_t any_own = __ballot(own);
+  __shared__ uint32_t s_own[4];
+  if (lane == 0) s_own[wv] = any_own != 0;
+  __syncthreads();
+  if (tid == 0) {
+    const float sc = ldexpf(1.f, T);
+    a.hscale[(size_t)tile * GI + nt] = (s_own[0] | s_own[1] | s_own[2] | s_own[3]) ? -sc : sc;
+  }
+}
+
+// ------------------------------------------------ gate/up, small tiles ---
+// A tile of at most kSmallRows rows (an expert that got a handful of tokens)
+// skips the matrix cores: converting a group's weights to fp16 for a 32-row
+// MFMA tile costs the same whatever the tile holds, and these tiles are a
+// large share of the weight bytes but a small share of the flops. The block
+// streams its 64 gate + 64 up code rows once and multiplies them on the
+// dot-product unit as the decode kernel does: codes as the exact bf16 values
+// 128 + q, activations as their own bf16 values re-paired to match, two
+// products per v_dot2, fp32 sums (s * sum((128 + q) x) + (c - 128 s) * sum(x)
+// per 32-code chunk). Wave w takes I columns [16w, 16w + 16) of the block, of
+// gate and of up; a lane (rsub = lane / 16, c0 = lane % 16) takes row
+// 4p + rsub of pass p (gate for p < 4, up after) at the chunks c0 + 16i; the
+// 16 lanes of a row are summed by DPP. h = silu(gate) * up then takes the
+// same range-scale epilogue as the MFMA tiles. The tiles' tokens' activations
+// are staged once per block in LDS, already paired, with their chunk sums.
+constexpr int kSmallRows = 4;
+
+// The small-tile path covers H a multiple of 512 up to 2048: one to four chunk
+// positions per lane, every code load issued before the first product.
+__host__ __device__ constexpr bool small_tiles_ok(int H) { return H % 512 == 0 && H <= 2048; }
+
+template <int NP>
+__device__ __forceinline__ void gateup_small(const GemmArgs& a, uint8_t* smem, int tile, int nt, int e, int r0,
+                                             int base, int nrow, const uint8_t* rec) {
+  constexpr int H = 512 * NP;   // hidden size of this instance
+  constexpr int NCH = H / 32;   // 32-code chunks per row
+  constexpr int G = H / 64;     // quantisation groups per row
+  constexpr int SGS = GU_BN + 1;
+  static_assert(kSmallRows * NCH * 68 + BM * SGS * 4 <= GU_NA * A_STAGE + 2 * BQ_STAGE + 2 * SQ_STAGE,
+                "small-tile staging must fit the block's LDS");
+  const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int n0 = nt * GU_BN;
+  uint32_t* xp = reinterpret_cast<uint32_t*>(smem);                        // [kSmallRows][NCH][16] pairs
+  float* xsm = reinterpret_cast<float*>(smem + kSmallRows * NCH * 64);     // [kSmallRows][NCH] chunk sums
+  float* sg = xsm + kSmallRows * NCH;                                      // [64][SGS] h
+  const int rsub = lane >> 4, c0 = lane & 15;
+  // this lane's row r = 4 (p & 3) + rsub of pass p, at the chunks c0 + 16 it
+  const size_t row0 = (size_t)(n0 + 16 * wv + rsub);
+  const uint8_t* gcode = rec + a.gate_codes + row0 * (H / 2) + 16 * c0;
+  const uint8_t* ucode = rec + a.up_codes + row0 * (H / 2) + 16 * c0;
+  const uint8_t* gsc = rec + a.gate_sc + row0 * G * 4 + 4 * (c0 >> 1);
+  const uint8_t* usc = rec + a.up_sc + row0 * G * 4 + 4 * (c0 >> 1);
+  auto load = [&](int it, uint4 (&cd)[8], uint32_t (&sc)[8]) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const size_t r = (size_t)(4 * (p & 3));
+      cd[p] = *reinterpret_cast<const uint4*>((p < 4 ? gcode : ucode) + r * (H / 2) + 256 * it);
+      sc[p] = *reinterpret_cast<const uint32_t*>((p < 4 ? gsc : usc) + r * G * 4 + 32 * it);
+    }
+  };
+  uint4 cdA[8];
+  uint32_t scA[8];
+  load(0, cdA, scA);
+  // the tokens' activations, paired, and their chunk sums
+  for (int q = tid; q < nrow * NCH; q += 256) {
+    const int m = q / NCH, c = q % NCH;
+    const int tok = e < a.E ? a.perm[base + m] / a.k : r0 + m;
+    const uint4* src = reinterpret_cast<const uint4*>(a.x + (size_t)tok * H + 32 * c);
+    uint32_t xr[16];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const uint4 v = src[u];
+      xr[4 * u] = v.x, xr[4 * u + 1] = v.y, xr[4 * u + 2] = v.z, xr[4 * u + 3] = v.w;
+    }
+    const XChunk<4> xc = x_chunk<4>(xr);
+    uint4* d = reinterpret_cast<uint4*>(xp + (size_t)(m * NCH + c) * 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) d[u] = make_uint4(xc.p[4 * u], xc.p[4 * u + 1], xc.p[4 * u + 2], xc.p[4 * u + 3]);
+    xsm[m * NCH + c] = xc.s;
+  }
+  __syncthreads();
+  float acc[8][kSmallRows];
+#pragma unroll
+  for (int p = 0; p < 8; ++p)
+#pragma unroll
+    for (int m = 0; m < kSmallRows; ++m) acc[p][m] = 0.f;
+#pragma unroll
+  for (int it = 0; it < NP; ++it) {
+    uint4 cdB[8];
+    uint32_t scB[8];
+    if (it + 1 < NP) load(it + 1, cdB, scB);
+    const int c = c0 + 16 * it;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t q[4][16];
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) code_pairs4(cdA[4 * half + pp], q[pp]);
+#pragma unroll
+      for (int m = 0; m < kSmallRows; ++m) {
+        if (m < nrow) {  // uniform
+          uint32_t xv[16];
+          const uint4* xs4 = reinterpret_cast<const uint4*>(xp + (size_t)(m * NCH + c) * 16);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const uint4 v = xs4[u];
+            xv[4 * u] = v.x, xv[4 * u + 1] = v.y, xv[4 * u + 2] = v.z, xv[4 * u + 3] = v.w;
+          }
+          const float xs = xsm[m * NCH + c];
+#pragma unroll
+          for (int pp = 0; pp < 4; ++pp)
+            acc[4 * half + pp][m] += pairs_term(q[pp], scA[4 * half + pp], xv, xs);
+        }
+      }
+    }
+    if (it + 1 < NP) {
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        cdA[p] = cdB[p];
+        scA[p] = scB[p];
+      }
+    }
+  }
+  // row totals in lane c0 = 15 of each row's 16 lanes; h to LDS (rows past
+  // the tile's end as zeros)
+#pragma unroll
+  for (int m = 0; m < kSmallRows; ++m) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) acc[p][m] = dpp::group_sum<16>(acc[p][m]);
+  }
+  if (c0 == 15) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int nl = 16 * wv + 4 * p + rsub;
+#pragma unroll
+      for (int m = 0; m < kSmallRows; ++m) sg[m * SGS + nl] = m < nrow ? silu_mul(acc[p][m], acc[p + 4][m]) : 0.f;
+    }
+  }
+  for (int q = tid; q < (BM - kSmallRows) * GU_BN; q += 256)
+    sg[(kSmallRows + q / GU_BN) * SGS + q % GU_BN] = 0.f;
+  __syncthreads();
+  gateup_store_h(a, sg, nrow, tile, nt, base, n0, tid, wv, lane);
+}
+
 __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int32_t s_tok[BM];
@@ -675,6 +870,15 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
   const int nrow = td.w;  // rows of this tile (>= 1)
   const int n0 = nt * GU_BN;
   const uint8_t* rec = e < a.E ? a.experts + (uint64_t)e * a.stride : a.shared;
+  if (small_tiles_ok(a.H) && __builtin_amdgcn_readfirstlane(nrow) <= kSmallRows) {
+    switch (a.H / 512) {
+      case 1: gateup_small<1>(a, smem, tile, nt, e, r0, base, nrow, rec); break;
+      case 2: gateup_small<2>(a, smem, tile, nt, e, r0, base, nrow, rec); break;
+      case 3: gateup_small<3>(a, smem, tile, nt, e, r0, base, nrow, rec); break;
+      default: gateup_small<4>(a, smem, tile, nt, e, r0, base, nrow, rec); break;
+    }
+    return;
+  }
   const int tid = threadIdx.x, wv = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   uint8_t* sA = smem;                                       // [NA][64 rows][8 slots of 16 B]
   uint8_t* sB = sA + GU_NA * A_STAGE;                       // [2][128 rows][8 slots of 16 B] (4 groups)
@@ -763,60 +967,7 @@ __global__ void __launch_bounds__(256, 2) gemm_gateup_kernel(GemmArgs a) {
     }
   }
   __syncthreads();
-  // fp16 range scales. Row m (4 threads, 16 columns each) has the natural
-  // exponent n_m: max |h_m| / 2^n_m in [2^14, 2^15). The tile-group scale is
-  // 2^T with T = the largest n_m over the tile's rows. A row within 2^12 of
-  // the tile's largest stores h / 2^T (its maximum stays >= 4, so only values
-  // below 2^-16 of it leave fp16's normal range); a smaller row stores
-  // h / 2^n_m and the factor 2^(n_m - T) that the down GEMM applies to its
-  // partial sums. hscale = 2^T, negated when any row of the tile-group has
-  // its own factor.
-  const int m = tid >> 2, qq = tid & 3;
-  float hv[16];
-  float rmax = 0.f;
-#pragma unroll
-  for (int cc = 0; cc < 16; ++cc) {
-    hv[cc] = sg[m * SGS + 16 * qq + cc];
-    rmax = fmaxf(rmax, fabsf(hv[cc]));
-  }
-  rmax = fmaxf(rmax, __uint_as_float(dpp::mov<dpp::kQuadXor1, 0xF>(0u, __float_as_uint(rmax))));
-  rmax = fmaxf(rmax, __uint_as_float(dpp::mov<dpp::kQuadXor2, 0xF>(0u, __float_as_uint(rmax))));
-  const uint32_t nb = row_exp_biased(rmax, m < nrow);
-  __shared__ uint32_t s_tmax[4];
-  {
-    const uint32_t wm = dpp::wave_max_u32(nb);
-    if (lane == 0) s_tmax[wv] = wm;
-  }
-  __syncthreads();
-  const uint32_t tb = max(max(s_tmax[0], s_tmax[1]), max(s_tmax[2], s_tmax[3]));
-  const int T = tb ? (int)tb - 256 : 0;
-  const int er = row_exp(nb, T);  // this row's exponent
-  const bool own = m < nrow && er != T;
-  // h / 2^er in fp16 and the group sum of the values the down GEMM
-  // multiplies: this thread's 16 columns, then the row's four quarters
-  // combined as (q0 + q1) + (q2 + q3)
-  uint32_t pk[8];
-  float sum = pack16(hv, er, pk);
-  sum += __uint_as_float(dpp::mov<dpp::kQuadXor1, 0xF>(0u, __float_as_uint(sum)));
-  sum += __uint_as_float(dpp::mov<dpp::kQuadXor2, 0xF>(0u, __float_as_uint(sum)));
-  const int GI = a.I / 64;
-  if (m < nrow) {
-    uint16_t* dst = a.h16 + (size_t)(base + m) * a.I + n0 + 16 * qq;
-    *reinterpret_cast<uint4*>(dst) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    *reinterpret_cast<uint4*>(dst + 8) = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-    if (qq == 0) {
-      a.hsum[(size_t)(base + m) * GI + nt] = sum;
-      a.hrowf[(size_t)(base + m) * GI + nt] = ldexpf(1.f, er - T);
-    }
-  }
-  const uint64_t any_own = __ballot(own);
-  __shared__ uint32_t s_own[4];
-  if (lane == 0) s_own[wv] = any_own != 0;
-  __syncthreads();
-  if (tid == 0) {
-    const float sc = ldexpf(1.f, T);
-    a.hscale[(size_t)tile * GI + nt] = (s_own[0] | s_own[1] | s_own[2] | s_own[3]) ? -sc : sc;
-  }
+  gateup_store_h(a, sg, nrow, tile, nt, base, n0, tid, wv, lane);
 }
 
 // ------------------------------------------------------- grouped GEMM 2 ---
@@ -1127,6 +1278,49 @@ __device__ __forceinline__ f16x8 ld_frag(const uint16_t* rowp, int g, int c) {
   return *reinterpret_cast<const f16x8*>(rowp + 64 * g + 8 * c);
 }
 
+// A small tile (at most kSmallRows rows) as the fast small-tile path computes
+// it: thread = column of the block; each row's 16 lane partials (a lane's
+// chunks c0, c0 + 16, ... in order) summed pairwise like the lanes' DPP
+// reduction; rows past the tile's end as zeros.
+template <int NP>
+__device__ void gateup_small_plain(const GemmArgs& a, float (*sg)[GU_BN + 1], int e, int r0, int base, int nrow,
+                                   const uint8_t* rec, int n0) {
+  constexpr int H = 512 * NP, G = H / 64;
+  const int nl = threadIdx.x;
+  const int n = n0 + nl;
+  for (int m = 0; m < BM; ++m) {
+    if (m >= nrow) {
+      sg[m][nl] = 0.f;
+      continue;
+    }
+    const int tok = e < a.E ? a.perm[base + m] / a.k : r0 + m;
+    float tot[2];
+    for (int mat = 0; mat < 2; ++mat) {
+      const uint8_t* crow = rec + (mat == 0 ? a.gate_codes : a.up_codes) + (size_t)n * (H / 2);
+      const uint8_t* srow = rec + (mat == 0 ? a.gate_sc : a.up_sc) + (size_t)n * G * 4;
+      float part[16];
+      for (int c0 = 0; c0 < 16; ++c0) {
+        float acc = 0.f;
+        for (int it = 0; it < NP; ++it) {
+          const int c = c0 + 16 * it;
+          uint32_t xr[16];
+          for (int u = 0; u < 16; ++u)
+            xr[u] = (uint32_t)a.x[(size_t)tok * H + 32 * c + 2 * u] | ((uint32_t)a.x[(size_t)tok * H + 32 * c + 2 * u + 1] << 16);
+          const XChunk<4> xc = x_chunk<4>(xr);
+          uint32_t q[16];
+          code_pairs4(*reinterpret_cast<const uint4*>(crow + 16 * c), q);
+          acc += pairs_term(q, *reinterpret_cast<const uint32_t*>(srow + 4 * (c >> 1)), xc.p, xc.s);
+        }
+        part[c0] = acc;
+      }
+      for (int w = 1; w < 16; w *= 2)
+        for (int i = 0; i < 16; i += 2 * w) part[i] = part[i] + part[i + w];
+      tot[mat] = part[0];
+    }
+    sg[m][nl] = silu_mul(tot[0], tot[1]);
+  }
+}
+
 __global__ void __launch_bounds__(64) gemm_gateup_plain_kernel(GemmArgs a) {
   __shared__ float sg[BM][GU_BN + 1], su[BM][GU_BN + 1];
   __shared__ float s_xs[BM];
@@ -1146,34 +1340,44 @@ __global__ void __launch_bounds__(64) gemm_gateup_plain_kernel(GemmArgs a) {
     s_xs[lane] = tok >= 0 ? a.xscale[tok] : 1.f;
   }
   __syncthreads();
-  const int tok0 = s_tok[mrow], tok1 = s_tok[32 + mrow];
-  const NibConst nk = nib_const();
-  for (int wv = 0; wv < 4; ++wv) {
-    const int mat = wv >> 1, nl = 32 * (wv & 1) + mrow;
-    const int n = min(n0 + nl, a.I - 1);
-    const uint8_t* crow = rec + (mat == 0 ? a.gate_codes : a.up_codes) + (size_t)n * (a.H / 2);
-    const uint8_t* srow = rec + (mat == 0 ? a.gate_sc : a.up_sc) + (size_t)n * G * 4;
-    f32x16 acc0 = {}, acc1 = {};
-    for (int g = 0; g < G; ++g) {
-      GroupFrag f;
-      f.codes = *reinterpret_cast<const uint4*>(crow + 32 * g + 16 * hh);
-      f.sc = *reinterpret_cast<const uint32_t*>(srow + 4 * g);
-      for (int st = 0; st < 4; ++st) {
-        f.a0[st] = tok0 >= 0 ? ld_frag(a.xp + (size_t)tok0 * a.H, g, 4 * hh + st) : f16x8{};
-        f.a1[st] = tok1 >= 0 ? ld_frag(a.xp + (size_t)tok1 * a.H, g, 4 * hh + st) : f16x8{};
+  if (small_tiles_ok(a.H) && nrow <= kSmallRows) {
+    switch (a.H / 512) {
+      case 1: gateup_small_plain<1>(a, sg, e, r0, base, nrow, rec, n0); break;
+      case 2: gateup_small_plain<2>(a, sg, e, r0, base, nrow, rec, n0); break;
+      case 3: gateup_small_plain<3>(a, sg, e, r0, base, nrow, rec, n0); break;
+      default: gateup_small_plain<4>(a, sg, e, r0, base, nrow, rec, n0); break;
+    }
+  } else {
+    const int tok0 = s_tok[mrow], tok1 = s_tok[32 + mrow];
+    const NibConst nk = nib_const();
+    for (int wv = 0; wv < 4; ++wv) {
+      const int mat = wv >> 1, nl = 32 * (wv & 1) + mrow;
+      const int n = min(n0 + nl, a.I - 1);
+      const uint8_t* crow = rec + (mat == 0 ? a.gate_codes : a.up_codes) + (size_t)n * (a.H / 2);
+      const uint8_t* srow = rec + (mat == 0 ? a.gate_sc : a.up_sc) + (size_t)n * G * 4;
+      f32x16 acc0 = {}, acc1 = {};
+      for (int g = 0; g < G; ++g) {
+        GroupFrag f;
+        f.codes = *reinterpret_cast<const uint4*>(crow + 32 * g + 16 * hh);
+        f.sc = *reinterpret_cast<const uint32_t*>(srow + 4 * g);
+        for (int st = 0; st < 4; ++st) {
+          f.a0[st] = tok0 >= 0 ? ld_frag(a.xp + (size_t)tok0 * a.H, g, 4 * hh + st) : f16x8{};
+          f.a1[st] = tok1 >= 0 ? ld_frag(a.xp + (size_t)tok1 * a.H, g, 4 * hh + st) : f16x8{};
+        }
+        gateup_dequant(f, nk);
+        gateup_mfma<true>(f, acc0, acc1);
       }
-      gateup_dequant(f, nk);
-      gateup_mfma<true>(f, acc0, acc1);
+      float(*dst)[GU_BN + 1] = mat == 0 ? sg : su;
+      for (int r = 0; r < 16; ++r) {
+        const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
+        dst[m][nl] = acc0[r] * s_xs[m];
+        dst[32 + m][nl] = acc1[r] * s_xs[32 + m];
+      }
     }
-    float(*dst)[GU_BN + 1] = mat == 0 ? sg : su;
-    for (int r = 0; r < 16; ++r) {
-      const int m = (r >> 2) * 8 + hh * 4 + (r & 3);
-      dst[m][nl] = acc0[r] * s_xs[m];
-      dst[32 + m][nl] = acc1[r] * s_xs[32 + m];
-    }
+    __syncthreads();
+    for (int m = 0; m < BM; ++m) sg[m][lane] = silu_mul(sg[m][lane], su[m][lane]);
+    __syncthreads();
   }
-  __syncthreads();
-  for (int m = 0; m < BM; ++m) sg[m][lane] = silu_mul(sg[m][lane], su[m][lane]);
   __syncthreads();
   // thread = row m
   const int m = lane;
