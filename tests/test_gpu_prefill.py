@@ -198,10 +198,35 @@ def test_prefill_scaled_activations_use_the_range_scales(shift, which):
     model.close()
 
 
+@pytest.mark.parametrize("shift,which", [(17, "half"), (17, "one"), (-16, "half"), (-16, "one")])
+def test_prefill_small_tiles_scaled_activations(shift, which):
+    """Experts that get at most four tokens take the dot-product path of the
+    gate/up kernel (H a multiple of 512): 12 tokens over 64 experts, top-4, so
+    nearly every tile holds one to three rows. Scaled and unscaled tokens then
+    share such tiles, whose h rows keep range factors of their own."""
+    cfg = synth.get_config("tiny", n_experts=64, top_k=4, hidden=512, inter=128, shared_inter=128)
+    n_tok = 12
+    assert _takes_prefill(cfg, n_tok)
+    model = gh.build(cfg)
+    xb = synth.tokens(cfg.seed + 31, n_tok, cfg.hidden)
+    rows = {"half": slice(0, n_tok, 2), "one": slice(3, 4)}[which]
+    x = synth.bf16_bits_to_f32(xb)
+    x[rows] *= np.float32(2.0 ** shift)
+    xb = synth.f32_to_bf16_bits(x)
+    out, idx, w = _forward(model, cfg, xb)
+    assert np.all(np.isfinite(out))
+    err, ties = gh.check_layer(cfg, OracleModel(cfg), 0, xb, out, idx, list(range(n_tok)),
+                               eps_rel=gh.prefill_eps_rel(cfg.hidden))
+    print(f"small tiles, shift {shift} on {which}: max rel L2 {err:.3e}, near-ties {ties}")
+    assert err <= gh.REL_L2_TOL
+    model.close()
+
+
 @pytest.mark.parametrize("shift", [-16, 17])
 def test_decode_scaled_activations(shift):
-    """The decode kernels (fp32 arithmetic on exact codes) on the same scaled
-    tokens: one token at a time, each within the bound."""
+    """The decode kernels (exact products of codes and activations, fp32
+    sums) on the same scaled tokens: one token at a time, each within the
+    bound."""
     cfg = synth.get_config("tiny", n_experts=8, top_k=2, hidden=256, inter=128, shared_inter=128)
     n_tok = 6
     model = gh.build(cfg)

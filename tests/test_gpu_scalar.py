@@ -60,6 +60,7 @@ def test_scalar_stack_bit_identical():
     (dict(n_experts=33, top_k=5, hidden=256, inter=64, shared_inter=64, bias="normal"), 65, 0),
     (dict(n_experts=8, top_k=2, hidden=256, inter=128, shared_inter=128), 48, -16),   # rows with own range factors
     (dict(n_experts=512, top_k=10, hidden=2048, inter=512, shared_inter=512, bias="normal"), 256, 0),
+    (dict(n_experts=64, top_k=4, hidden=512, inter=128, shared_inter=128), 12, 17),   # small tiles, mixed rows
 ])
 def test_scalar_grouped_gemms_bit_identical(variant, n_tok, scale):
     cfg = synth.get_config("tiny", **variant)
